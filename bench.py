@@ -1,0 +1,297 @@
+"""Benchmark: draft-tree verify + commit through a stack of Gated DeltaNet layers on one MI355X.
+
+One step = the whole hot path over one batch: heavy-light schedule of the batch's trees (host)
+and its upload, then for every GDN layer the tree conv (with the conv-window fold) and the tree
+verify (with the deferred-commit fold, wave by wave), then accept -> commit of one seeded path
+per sequence (role swap or compaction).  The timed region is K steps plus the final flush.
+
+Workload (default): 32 sequences, each with its own seeded 22-node top-4 tree (depth <= 12),
+48 GDN layers x 48 heads x d = 128 with independent fp32 states (4.8 GB), bf16 inputs, conv
+width 4 over 3*48*128 channels, accepted lengths uniform in 1..9.  Inputs are resident in HBM
+before timing starts.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--layers-per-call 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "verified tree nodes/sec per GDN layer + achieved HBM GB/s vs peak, 1 MI355X"
+
+
+# ----------------------------------------------------------------------------------------
+# algorithmic bytes (what the method must move; fp32 state/factors/outputs, bf16 inputs)
+# ----------------------------------------------------------------------------------------
+
+def verify_wave_bytes(view, wave, pending, H, d, in_bytes, n_layers=1):
+    """Bytes one verify launch of `wave` moves: per chain and head one start tile read, one
+    tile write per boundary node, the committed tile write + pending rows for a folding root
+    chain; per node and head q,k,v,beta,g in, o out, k,u,lg banked."""
+    tile = 4 * d * d
+    per_node = (3 * d + 2) * in_bytes + 4 * d + (8 * d + 4)
+    c0, c1 = int(view["wave_offsets"][wave]), int(view["wave_offsets"][wave + 1])
+    total = 0
+    for c in range(c0, c1):
+        nodes = view["chain_nodes"][view["chain_offsets"][c]:view["chain_offsets"][c + 1]]
+        n_store = int(np.count_nonzero(view["node_store"][nodes] >= 0))
+        total_tile = tile * (1 + n_store)
+        if view["chain_src"][c] < 0:
+            L = int(pending[view["chain_seq"][c]])
+            if L > 0:
+                total_tile += tile + L * (8 * d + 4)
+        total += H * (total_tile + len(nodes) * per_node)
+    return total * n_layers
+
+
+def conv_bytes(view, pending, C, in_bytes, n_layers=1):
+    """Per layer: x in, y out, x banked per node; window read (+ write and pending rows read
+    when folding) per sequence; the weights once."""
+    T, S = int(view["n_nodes"]), int(view["n_seqs"])
+    per_node = C * (in_bytes + 4 + 4)
+    seqs = sum(C * (12 + (12 + 4 * int(L) if L > 0 else 0)) for L in pending[:S])
+    return (T * per_node + seqs + C * 4 * in_bytes) * n_layers
+
+
+def commit_bytes(paths, H, d, C, n_layers):
+    """Compaction of branched paths: L rows of (k, u, lg per head + conv input) read + written."""
+    row = H * (8 * d + 4) + 4 * C
+    total = 0
+    for p in paths:
+        L = len(p)
+        if L and not np.array_equal(p, np.arange(L)):
+            total += 2 * L * row
+    return total * n_layers
+
+
+def fold_bytes(pending, H, d, C, n_layers):
+    tile = 4 * d * d
+    return n_layers * sum(H * (2 * tile + int(L) * (8 * d + 4)) + C * (24 + 4 * int(L))
+                          for L in pending if L > 0)
+
+
+# ----------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of (sequence, layer) pairs
+# ----------------------------------------------------------------------------------------
+
+def _oracle_pair(job):
+    config, seq, layer = job
+    from gated_deltanet_tree_amd import synth, workload
+    from oracle import conv as oconv
+    from oracle import gdn as ogdn
+    c = synth.CONFIGS[config]
+    tree = synth.config_tree(config, seq)
+    n = len(tree)
+    inp = synth.node_inputs(config, 0, layer, seq, n, c["H"], c["d"], c["dtype"])
+    inp = {k: workload.widen(v, c["dtype"]) for k, v in inp.items()}
+    x = workload.widen(synth.conv_inputs(config, 0, layer, seq, n, c["Cch"], c["dtype"]), c["dtype"])
+    W = workload.widen(synth.conv_weight(config, layer, c["Cch"], 4, c["dtype"]), c["dtype"])
+    S0 = synth.initial_state(config, layer, seq, c["H"], c["d"]).astype(np.float64)
+    X0 = synth.initial_conv_state(config, layer, seq, c["Cch"], 4).astype(np.float64)
+    path = synth.config_path(config, 0, seq, tree)
+    ogdn.verify(tree, S0, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"],
+                keep_states=False)
+    oconv.tree_conv(tree, X0, x, W)
+    ogdn.replay(S0, inp["k"], inp["v"], inp["beta"], inp["gate"], path)
+    oconv.commit_window(X0, x, path)
+    return n
+
+
+def cpu_baseline(config, n_pairs, workers):
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from gated_deltanet_tree_amd import synth
+    c = synth.CONFIGS[config]
+    rng = np.random.default_rng(1234)
+    jobs = [(config, int(rng.integers(c["Bs"])), int(rng.integers(c["Ly"]))) for _ in range(n_pairs)]
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        list(ex.map(_oracle_pair, jobs[:workers]))  # warm the workers (imports)
+        t0 = time.perf_counter()
+        nodes = sum(ex.map(_oracle_pair, jobs))
+        dt = time.perf_counter() - t0
+    return dict(value=nodes / dt, unit="node-layers/s", cores=workers, kind="oracle",
+                sample=f"{n_pairs} seeded (sequence, layer) pairs of the workload: fp64 verify of "
+                       f"every node by root-path replay, tree conv, and commit by replay; "
+                       f"{nodes} node-layers in {dt:.1f} s over {workers} processes")
+
+
+# ----------------------------------------------------------------------------------------
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--layers-per-call", type=int, default=1)
+    ap.add_argument("--cpu-pairs", type=int, default=96)
+    ap.add_argument("--cpu-workers", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: the tree verify path runs on a single GPU here; "
+              "multi-GPU sharding (by sequence or by head) is described but not run.",
+              file=sys.stderr)
+        return 2
+
+    from gated_deltanet_tree_amd import synth, workload
+    cfg = synth.CONFIGS[args.config]
+    H, d, C, Ly, dtype = cfg["H"], cfg["d"], cfg["Cch"], cfg["Ly"], cfg["dtype"]
+    in_bytes = 2 if dtype == "bf16" else 4
+
+    # The CPU baseline runs first, before this process touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(args.config, args.cpu_pairs, workers)
+
+    import torch
+    from gated_deltanet_tree_amd import binding
+    binding.lib()
+    dev = torch.device("cuda:0")
+
+    trees = workload.config_trees(args.config)
+    S = len(trees)
+    image0 = binding.hld_schedule(trees)
+    view = binding.schedule_view(image0)
+    T = int(view["n_nodes"])
+    max_nodes = int(view["max_tree"])
+    lpc = args.layers_per_call
+    assert Ly % lpc == 0
+
+    t_gen = time.perf_counter()
+    state0, conv0 = workload.host_initial_state(args.config, range(Ly), S)
+    weights = workload._to_torch(workload.host_weights(args.config, range(Ly)), dtype, dev)
+    inp = workload.device_step_inputs(args.config, 0, trees, range(Ly), dev)
+    lay = binding.alloc_layers(Ly, S, H, d, max_nodes, C, dev)
+    lay.state.copy_(torch.from_numpy(state0))
+    lay.conv_state.copy_(torch.from_numpy(conv0))
+    del state0, conv0
+    boundary = torch.empty(max(binding.verify_workspace_bytes(image0, H, d, lpc) // 4, 1),
+                           device=dev, dtype=torch.float32)
+    out = torch.empty((Ly, T, H, d), device=dev, dtype=torch.float32)
+    y = torch.empty((Ly, T, C), device=dev, dtype=torch.float32)
+    gen_s = time.perf_counter() - t_gen
+
+    n_total = args.warmup + args.steps
+    all_paths = [[synth.config_path(args.config, s, b, trees[b]) for b in range(S)]
+                 for s in range(n_total)]
+    vargs = [binding.verify_args(image0, lay, inp.q, inp.k, inp.v, inp.beta, inp.gate, out,
+                                 boundary, layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
+    cargs = [binding.conv_args(image0, lay, inp.x, weights, y, layer_begin=l, n_layers=lpc)
+             for l in range(0, Ly, lpc)]
+    va_all = binding.verify_args(image0, lay, None, None, None, None, None, None, None, 0, Ly)
+    ca_all = binding.conv_args(image0, lay, None, None, None, 0, Ly)
+    stream = torch.cuda.current_stream()
+
+    def upload(a):
+        return torch.from_numpy(a).pin_memory().to(dev, non_blocking=True)
+
+    acc = dict(verify_ms=0.0, verify_launches=0, verify_bytes=0, conv_bytes=0, commit_bytes=0,
+               conv_ms=0.0)
+
+    def step(s, timed):
+        image = binding.hld_schedule(trees)  # a1: host schedule of this step's trees
+        dev_image = upload(image)
+        pending = [int(L) for L in lay.pending_host]
+        evs = []
+        for li, l in enumerate(range(0, Ly, lpc)):
+            if timed:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            binding.tree_conv(cargs[li], image, dev_image)
+            if timed:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record(stream)
+                evs.append(("conv", e0, e1))
+            for w in range(int(view["n_waves"])):
+                if timed:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                binding.tree_verify_wave(vargs[li], image, dev_image, w)
+                if timed:
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e1.record(stream)
+                    evs.append(("verify", e0, e1))
+                    acc["verify_bytes"] += verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc)
+                    acc["verify_launches"] += 1
+            if timed:
+                acc["conv_bytes"] += conv_bytes(view, pending, C, in_bytes, lpc)
+        paths = all_paths[s]
+        flat, offs = binding.pack_paths(paths)
+        binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs))
+        if timed:
+            acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly)
+        return evs
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for s in range(args.warmup, n_total):
+        events += step(s, True)
+    flush_pending = lay.pending_host.copy()
+    binding.flush(va_all, ca_all, lay)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for kind, e0, e1 in events:
+        acc[kind + "_ms"] += e0.elapsed_time(e1)
+
+    node_layers = args.steps * T * Ly
+    total_bytes = acc["verify_bytes"] + acc["conv_bytes"] + acc["commit_bytes"] + \
+        fold_bytes(flush_pending, H, d, C, Ly)
+    v_launch_s = acc["verify_ms"] / 1e3 / max(acc["verify_launches"], 1)
+    v_launch_bytes = acc["verify_bytes"] / max(acc["verify_launches"], 1)
+    achieved = v_launch_bytes / v_launch_s / 1e9
+    compulsory = args.steps * Ly * S * H * 2 * 4 * d * d
+    result = {
+        "metric": METRIC,
+        "value": node_layers / wall,
+        "unit": "node-layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg['name']}: {S} sequences x {Ly} GDN layers x {H} heads x d{d}, "
+                        f"{T // S if S else 0}-node trees (top-{cfg['K']}, depth<={cfg['D']}), "
+                        f"bf16 q/k/v/beta/g, fp32 state, conv width 4 over {C} channels",
+            "sequences": S, "layers": Ly, "heads": H, "head_dim": d, "tree_nodes": T,
+            "chains": int(view["n_chains"]), "waves": int(view["n_waves"]),
+            "boundary_nodes": int(view["n_boundaries"]), "layers_per_call": lpc,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "kernel": "verify_chain_kernel<128, bf16>",
+            "bytes_per_launch": v_launch_bytes, "launch_us": v_launch_s * 1e6,
+        },
+        "cpu_baseline": cpu,
+        "algorithmic_GBps_step": total_bytes / wall / 1e9,
+        "algorithmic_bytes_per_step": total_bytes / args.steps,
+        "compulsory_GBps_step": compulsory / wall / 1e9,
+        "verify_ms_per_step": acc["verify_ms"] / args.steps,
+        "conv_ms_per_step": acc["conv_ms"] / args.steps,
+        "input_generation_s": gen_s,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,332 @@
+"""ctypes binding of libgdn_tree.so -- argument marshalling only.
+
+Every computation runs in the HIP library; this module converts numpy arrays and torch
+tensors (device memory on ROCm) into the pointers and sizes that include/gdn_tree.h
+declares, and raises GdnError on a non-zero status.  torch is imported before the library is
+loaded so that both share one HIP runtime.  There is no fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn_tree.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_ETREE", -3: "GDN_EPATH",
+          -4: "GDN_ECAPACITY", -5: "GDN_EDEVICE"}
+EXPORTS = [
+    "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_verify_workspace_bytes",
+    "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_conv", "gdn_commit_path",
+    "gdn_compact_factors", "gdn_flush",
+]
+IMAGE_HEADER = 16
+IMAGE_MAGIC = 0x53444E47
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+class VerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", _I32), ("n_heads", _I32), ("head_dim", _I32), ("n_nodes", _I32),
+        ("max_nodes", _I32), ("layer_begin", _I32), ("n_layers", _I32), ("in_dtype", _I32),
+        ("q", _P), ("k", _P), ("v", _P), ("beta", _P), ("gate", _P), ("state", _P),
+        ("bank_k", _P * 2), ("bank_u", _P * 2), ("bank_lg", _P * 2),
+        ("role", _P), ("pending_len", _P), ("boundary", _P), ("out", _P),
+    ]
+
+
+class ConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", _I32), ("channels", _I32), ("width", _I32), ("n_nodes", _I32),
+        ("max_nodes", _I32), ("layer_begin", _I32), ("n_layers", _I32), ("in_dtype", _I32),
+        ("x", _P), ("weight", _P), ("conv_state", _P), ("bank_x", _P * 2),
+        ("role", _P), ("pending_len", _P), ("out", _P),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (after torch, so the HIP runtime is shared)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- must precede the library: one HIP runtime per process
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gated_deltanet_tree_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.gdn_last_error.restype = ctypes.c_char_p
+    L.gdn_schedule_words.restype = ctypes.c_size_t
+    L.gdn_schedule_words.argtypes = [_I32, _I32]
+    L.gdn_hld_schedule.restype = _I32
+    L.gdn_hld_schedule.argtypes = [_I32P, _I32P, _I32, _I32P, ctypes.c_size_t]
+    L.gdn_verify_workspace_bytes.restype = ctypes.c_size_t
+    L.gdn_verify_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32]
+    L.gdn_tree_verify.restype = _I32
+    L.gdn_tree_verify.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
+    L.gdn_tree_verify_wave.restype = _I32
+    L.gdn_tree_verify_wave.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _I32, _P]
+    L.gdn_tree_conv.restype = _I32
+    L.gdn_tree_conv.argtypes = [ctypes.POINTER(ConvArgs), _I32P, _P, _P]
+    L.gdn_commit_path.restype = _I32
+    L.gdn_commit_path.argtypes = [_I32P, _I32P, _I32P, _P, _P, ctypes.POINTER(VerifyArgs),
+                                  ctypes.POINTER(ConvArgs), _I32P, _I32P, _P]
+    L.gdn_compact_factors.restype = _I32
+    L.gdn_compact_factors.argtypes = [_P, _P, ctypes.c_int64, _P, _P, _I32, _P]
+    L.gdn_flush.restype = _I32
+    L.gdn_flush.argtypes = [ctypes.POINTER(VerifyArgs), ctypes.POINTER(ConvArgs), _I32P, _P]
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GdnError(status, where, lib().gdn_last_error().decode())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+def _dev(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+# ------------------------------------------------------------------------------------
+# schedule (host)
+# ------------------------------------------------------------------------------------
+
+def schedule_words(n_seqs: int, n_nodes: int) -> int:
+    return int(lib().gdn_schedule_words(n_seqs, n_nodes))
+
+
+def hld_schedule(parents) -> np.ndarray:
+    """Schedule image (int32) of a batch of trees given as a list of local parent arrays."""
+    parents = [_i32(p) for p in parents]
+    seq_offsets = _i32(np.concatenate([[0], np.cumsum([len(p) for p in parents])]))
+    flat = _i32(np.concatenate(parents)) if parents else np.zeros(1, dtype=np.int32)
+    n_words = schedule_words(len(parents), int(seq_offsets[-1]))
+    image = np.zeros(max(n_words, IMAGE_HEADER + 3), dtype=np.int32)
+    _check(lib().gdn_hld_schedule(_ptr(flat), _ptr(seq_offsets), len(parents), _ptr(image),
+                                  image.size), "gdn_hld_schedule")
+    return image
+
+
+def schedule_view(image: np.ndarray) -> dict:
+    """Named views of a schedule image, following the layout in gdn_tree.h."""
+    S, T = int(image[1]), int(image[2])
+    n_chains, n_waves = int(image[3]), int(image[4])
+    o = IMAGE_HEADER
+    seq = image[o:o + S + 1]
+    o += S + 1
+    wave = image[o:o + n_waves + 1]
+    o += T + 1
+    chain = image[o:o + n_chains + 1]
+    o += T + 1
+    fields = {}
+    for name in ("chain_nodes", "chain_seq", "chain_src", "node_store", "node_parent",
+                 "node_depth"):
+        fields[name] = image[o:o + T]
+        o += T
+    fields["chain_seq"] = fields["chain_seq"][:n_chains]
+    fields["chain_src"] = fields["chain_src"][:n_chains]
+    return dict(n_seqs=S, n_nodes=T, n_chains=n_chains, n_waves=n_waves,
+                n_boundaries=int(image[5]), max_chain_len=int(image[6]), max_tree=int(image[7]),
+                seq_offsets=seq, wave_offsets=wave, chain_offsets=chain, **fields)
+
+
+def verify_workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, n_layers: int) -> int:
+    return int(lib().gdn_verify_workspace_bytes(_ptr(image), n_heads, head_dim, n_layers))
+
+
+# ------------------------------------------------------------------------------------
+# device calls
+# ------------------------------------------------------------------------------------
+
+@dataclass
+class Layers:
+    """Device buffers of a stack of GDN layers for one batch of sequences (torch tensors).
+
+    Shapes: state [Ly,S,H,d,d]; bank_k/bank_u [2][Ly,S,H,max_nodes,d]; bank_lg
+    [2][Ly,S,H,max_nodes]; conv_state [Ly,S,Cch,3]; bank_x [2][Ly,S,max_nodes,Cch];
+    role, pending [S] int32 (device) with host mirrors role_host, pending_host.
+    """
+    state: object
+    bank_k: list
+    bank_u: list
+    bank_lg: list
+    role: object
+    pending: object
+    role_host: np.ndarray
+    pending_host: np.ndarray
+    conv_state: object = None
+    bank_x: list = None
+
+
+def _need(t, n, what):
+    """Reject a tensor that is smaller than the call will address (or not contiguous)."""
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements, the call addresses {n}")
+
+
+def verify_args(image, layers: Layers, q, k, v, beta, gate, out, boundary,
+                layer_begin=0, n_layers=1, max_nodes=None) -> VerifyArgs:
+    import torch
+    S, T = int(image[1]), int(image[2])
+    Ly_end = layer_begin + n_layers
+    H, d = int(layers.state.shape[2]), int(layers.state.shape[3])
+    Nm = int(layers.bank_lg[0].shape[-1]) if max_nodes is None else max_nodes
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _need(t, Ly_end * T * H * d, name)
+    _need(beta, Ly_end * T * H, "beta")
+    _need(gate, Ly_end * T * H, "gate")
+    _need(layers.state, Ly_end * S * H * d * d, "state")
+    for i in range(2):
+        _need(layers.bank_k[i], Ly_end * S * H * Nm * d, "bank_k")
+        _need(layers.bank_u[i], Ly_end * S * H * Nm * d, "bank_u")
+        _need(layers.bank_lg[i], Ly_end * S * H * Nm, "bank_lg")
+    _need(layers.role, S, "role")
+    _need(layers.pending, S, "pending")
+    if boundary is not None and q is not None:
+        _need(boundary, verify_workspace_bytes(image, H, d, n_layers) // 4, "boundary")
+    a = VerifyArgs()
+    a.n_seqs, a.n_nodes = int(image[1]), int(image[2])
+    a.n_heads, a.head_dim = int(layers.state.shape[2]), int(layers.state.shape[3])
+    a.max_nodes = int(layers.bank_lg[0].shape[-1]) if max_nodes is None else max_nodes
+    a.layer_begin, a.n_layers = layer_begin, n_layers
+    a.in_dtype = GDN_BF16 if (q is not None and q.dtype == torch.bfloat16) else GDN_F32
+    a.q, a.k, a.v, a.beta, a.gate = (_dev(t) for t in (q, k, v, beta, gate))
+    a.state = _dev(layers.state)
+    for i in range(2):
+        a.bank_k[i] = _dev(layers.bank_k[i])
+        a.bank_u[i] = _dev(layers.bank_u[i])
+        a.bank_lg[i] = _dev(layers.bank_lg[i])
+    a.role, a.pending_len = _dev(layers.role), _dev(layers.pending)
+    a.boundary, a.out = _dev(boundary), _dev(out)
+    return a
+
+
+def conv_args(image, layers: Layers, x, weight, out, layer_begin=0, n_layers=1,
+              max_nodes=None) -> ConvArgs:
+    import torch
+    S, T = int(image[1]), int(image[2])
+    Ly_end = layer_begin + n_layers
+    C = int(layers.conv_state.shape[2])
+    Nm = int(layers.bank_x[0].shape[2]) if max_nodes is None else max_nodes
+    _need(x, Ly_end * T * C, "x")
+    _need(out, Ly_end * T * C, "conv out")
+    _need(weight, Ly_end * C * 4, "weight")
+    _need(layers.conv_state, Ly_end * S * C * 3, "conv_state")
+    for i in range(2):
+        _need(layers.bank_x[i], Ly_end * S * Nm * C, "bank_x")
+    a = ConvArgs()
+    a.n_seqs, a.n_nodes = int(image[1]), int(image[2])
+    a.channels, a.width = int(layers.conv_state.shape[2]), 4
+    a.max_nodes = int(layers.bank_x[0].shape[2]) if max_nodes is None else max_nodes
+    a.layer_begin, a.n_layers = layer_begin, n_layers
+    a.in_dtype = GDN_BF16 if (x is not None and x.dtype == torch.bfloat16) else GDN_F32
+    a.x, a.weight, a.out = _dev(x), _dev(weight), _dev(out)
+    a.conv_state = _dev(layers.conv_state)
+    a.bank_x[0], a.bank_x[1] = _dev(layers.bank_x[0]), _dev(layers.bank_x[1])
+    a.role, a.pending_len = _dev(layers.role), _dev(layers.pending)
+    return a
+
+
+def tree_verify(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
+    _check(lib().gdn_tree_verify(ctypes.byref(args), _ptr(image), _dev(dev_image),
+                                 _stream(stream)), "gdn_tree_verify")
+
+
+def tree_verify_wave(args: VerifyArgs, image: np.ndarray, dev_image, wave: int, stream=None):
+    _check(lib().gdn_tree_verify_wave(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
+                                      _stream(stream)), "gdn_tree_verify_wave")
+
+
+def tree_conv(args: ConvArgs, image: np.ndarray, dev_image, stream=None):
+    _check(lib().gdn_tree_conv(ctypes.byref(args), _ptr(image), _dev(dev_image),
+                               _stream(stream)), "gdn_tree_conv")
+
+
+def pack_paths(paths):
+    flat = _i32(np.concatenate([np.asarray(p, dtype=np.int32) for p in paths])) \
+        if any(len(p) for p in paths) else np.zeros(1, dtype=np.int32)
+    offsets = _i32(np.concatenate([[0], np.cumsum([len(p) for p in paths])]))
+    return flat, offsets
+
+
+def commit_path(image, paths, layers: Layers, vargs: VerifyArgs, cargs: ConvArgs | None,
+                dev_paths=None, dev_offsets=None, stream=None):
+    """Accept one root path per sequence (local ids); updates layers.role/pending (device
+    on the stream, host mirrors now).  dev_paths/dev_offsets default to fresh uploads."""
+    import torch
+    flat, offsets = pack_paths(paths)
+    if dev_paths is None:
+        dev_paths = torch.from_numpy(flat).to(layers.role.device)
+        dev_offsets = torch.from_numpy(offsets).to(layers.role.device)
+    _check(lib().gdn_commit_path(
+        _ptr(image), _ptr(flat), _ptr(offsets), _dev(dev_paths), _dev(dev_offsets),
+        ctypes.byref(vargs), ctypes.byref(cargs) if cargs is not None else None,
+        _ptr(layers.role_host), _ptr(layers.pending_host), _stream(stream)), "gdn_commit_path")
+    return dev_paths, dev_offsets
+
+
+def compact_factors(src, dst, row_elems: int, src_rows, dst_rows, stream=None):
+    _check(lib().gdn_compact_factors(_dev(src), _dev(dst), row_elems, _dev(src_rows),
+                                     _dev(dst_rows), int(src_rows.numel()), _stream(stream)),
+           "gdn_compact_factors")
+
+
+def flush(vargs: VerifyArgs, cargs: ConvArgs | None, layers: Layers, stream=None):
+    _check(lib().gdn_flush(ctypes.byref(vargs), ctypes.byref(cargs) if cargs is not None else None,
+                           _ptr(layers.pending_host), _stream(stream)), "gdn_flush")
+
+
+def alloc_layers(n_layers, n_seqs, n_heads, head_dim, max_nodes, channels=0, device="cuda"):
+    """Zero-initialised device buffers for `n_layers` layers (torch.empty/zeros on device)."""
+    import torch
+    f = dict(device=device, dtype=torch.float32)
+    Ly, S, H, d, Nm = n_layers, n_seqs, n_heads, head_dim, max_nodes
+    lay = Layers(
+        state=torch.zeros((Ly, S, H, d, d), **f),
+        bank_k=[torch.zeros((Ly, S, H, Nm, d), **f) for _ in range(2)],
+        bank_u=[torch.zeros((Ly, S, H, Nm, d), **f) for _ in range(2)],
+        bank_lg=[torch.zeros((Ly, S, H, Nm), **f) for _ in range(2)],
+        role=torch.zeros(S, device=device, dtype=torch.int32),
+        pending=torch.zeros(S, device=device, dtype=torch.int32),
+        role_host=np.zeros(S, dtype=np.int32),
+        pending_host=np.zeros(S, dtype=np.int32),
+    )
+    if channels:
+        lay.conv_state = torch.zeros((Ly, S, channels, 3), **f)
+        lay.bank_x = [torch.zeros((Ly, S, Nm, channels), **f) for _ in range(2)]
+    return lay

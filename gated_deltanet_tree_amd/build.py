@@ -1,0 +1,80 @@
+"""Build libgdn_tree.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+    python -m gated_deltanet_tree_amd.build            # build (always recompiles)
+    python -m gated_deltanet_tree_amd.build --check    # report resource usage per kernel
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libgdn_tree.so")
+ARCH = "gfx950"
+
+SOURCES = ["errors.cpp", "schedule.cpp", "verify.hip", "conv.hip", "commit.hip"]
+
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-mcode-object-version=5",
+    # packed FP32 instructions stay off: plain FMAs only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unknown-warning-option",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    extra_flags = list(extra_flags or [])
+    with tempfile.TemporaryDirectory(prefix="gdn_build_") as tmp:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [hipcc()] + HIP_FLAGS + extra_flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+            if src.endswith(".hip"):
+                cmd[1:1] = ["-x", "hip"]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        failed = []
+        for src, p in procs:
+            text, _ = p.communicate()
+            if p.returncode != 0:
+                failed.append((src, text))
+            elif verbose and text.strip():
+                print(text, flush=True)
+        if failed:
+            msg = "\n".join(f"--- {s} ---\n{t}" for s, t in failed)
+            raise RuntimeError("hipcc failed:\n" + msg)
+        tmp_out = out + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out] + objs
+        subprocess.run(cmd, check=True)
+        os.replace(tmp_out, out)
+    return out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--check", action="store_true",
+                    help="print per-kernel register/LDS usage while compiling")
+    args = ap.parse_args(argv)
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if args.check else []
+    path = build(verbose=args.verbose or args.check, extra_flags=extra)
+    print(path)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

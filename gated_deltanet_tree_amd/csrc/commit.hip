@@ -1,0 +1,241 @@
+// Accept -> commit bookkeeping, factor-bank compaction and the flush, for gfx950.
+//
+// "Lucebox SpecLA and Gated DeltaNet state-resident verification" guide, mechanism 3: the
+// two FP32 banks alternate between "pending" and "being written"; an accepted path that is
+// already in order just swaps their roles (no device copy), a branched one is compacted
+// back into path order by a gather kernel.  Mechanism 4: the flush materialises the last
+// pending path once, at the end of generation, on a switch to autoregressive decode or on
+// cancel.
+//
+// Readings: "in order" = the path is [0, 1, ..., L-1]; compaction writes rows 0..L-1 of the
+// bank that the last verify consumed (the pending one) and leaves the roles as they are.
+// The kernels re-derive the per-sequence decision from the device copy of the paths, so no
+// host-to-device copy happens inside the library.
+#include <vector>
+
+#include "gdn_device.h"
+
+namespace gdn {
+
+gdn_status flush_state(const gdn_verify_args *a, hipStream_t stream);
+gdn_status flush_conv(const gdn_conv_args *a, hipStream_t stream);
+gdn_status check_flush_verify_args(const gdn_verify_args *a);
+gdn_status check_flush_conv_args(const gdn_conv_args *a);
+
+struct CompactParams {
+    float *bk[2], *bu[2], *blg[2], *bx[2];
+    const int32_t *role, *paths, *path_off;
+    int32_t S, H, D, C, max_nodes, layer_begin;
+};
+
+__device__ __forceinline__ bool path_in_order(const int32_t *path, int L) {
+    for (int i = 0; i < L; ++i)
+        if (path[i] != i) return false;
+    return true;
+}
+
+// One workgroup per (layer, sequence): rows path[i] of the written bank -> rows i of the
+// pending bank, for the key, residual and log-gate banks of every head and the conv bank.
+__global__ __launch_bounds__(256) void compact_kernel(CompactParams P) {
+    const int seq = blockIdx.x;
+    const int layer = P.layer_begin + blockIdx.y;
+    const int beg = P.path_off[seq], L = P.path_off[seq + 1] - beg;
+    const int32_t *path = P.paths + beg;
+    if (L == 0 || path_in_order(path, L)) return;
+    const int dst = P.role[seq], src = dst ^ 1;
+    const int64_t ls = int64_t(layer) * P.S + seq;
+    const int64_t hrows = int64_t(P.H) * P.max_nodes;  // rows of one (layer, seq)
+    const int tid = threadIdx.x;
+    // key and residual rows: H * L rows of D floats each
+    const int64_t nvec = int64_t(P.H) * L * P.D;
+    for (int64_t e = tid; e < nvec; e += blockDim.x) {
+        const int d = int(e % P.D);
+        const int64_t hl = e / P.D;
+        const int i = int(hl % L), h = int(hl / L);
+        const int64_t row_dst = ls * hrows + int64_t(h) * P.max_nodes + i;
+        const int64_t row_src = ls * hrows + int64_t(h) * P.max_nodes + path[i];
+        P.bk[dst][row_dst * P.D + d] = P.bk[src][row_src * P.D + d];
+        P.bu[dst][row_dst * P.D + d] = P.bu[src][row_src * P.D + d];
+    }
+    for (int64_t e = tid; e < int64_t(P.H) * L; e += blockDim.x) {
+        const int i = int(e % L), h = int(e / L);
+        P.blg[dst][ls * hrows + int64_t(h) * P.max_nodes + i] =
+            P.blg[src][ls * hrows + int64_t(h) * P.max_nodes + path[i]];
+    }
+    if (P.bx[0] != nullptr) {
+        const int64_t base = ls * P.max_nodes * P.C;
+        for (int64_t e = tid; e < int64_t(L) * P.C; e += blockDim.x) {
+            const int i = int(e / P.C), c = int(e % P.C);
+            P.bx[dst][base + int64_t(i) * P.C + c] = P.bx[src][base + int64_t(path[i]) * P.C + c];
+        }
+    }
+}
+
+// Runs after compact_kernel on the same stream: role flip for in-order paths, new pending.
+__global__ void commit_bookkeeping_kernel(int32_t *role, int32_t *pending, const int32_t *paths,
+                                          const int32_t *path_off, int S) {
+    const int seq = blockIdx.x * blockDim.x + threadIdx.x;
+    if (seq >= S) return;
+    const int beg = path_off[seq], L = path_off[seq + 1] - beg;
+    if (L > 0 && path_in_order(paths + beg, L)) role[seq] ^= 1;
+    pending[seq] = L;
+}
+
+__global__ void clear_pending_kernel(int32_t *pending, int S) {
+    const int seq = blockIdx.x * blockDim.x + threadIdx.x;
+    if (seq < S) pending[seq] = 0;
+}
+
+__global__ __launch_bounds__(256) void row_gather_kernel(const float *src, float *dst,
+                                                         int64_t row_elems,
+                                                         const int32_t *src_rows,
+                                                         const int32_t *dst_rows) {
+    const int r = blockIdx.y;
+    const int64_t s = int64_t(src_rows[r]) * row_elems, d = int64_t(dst_rows[r]) * row_elems;
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < row_elems;
+         e += int64_t(gridDim.x) * blockDim.x)
+        dst[d + e] = src[s + e];
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *paths,
+                                      const int32_t *path_offsets, const int32_t *dev_paths,
+                                      const int32_t *dev_path_offsets,
+                                      const gdn_verify_args *va, const gdn_conv_args *ca,
+                                      int32_t *role_host, int32_t *pending_host, void *stream) {
+    clear_error();
+    if (!image_ok(host_image) || !path_offsets || !dev_path_offsets || !role_host ||
+        !pending_host)
+        return fail(GDN_EINVAL, "gdn_commit_path: null argument or malformed schedule image");
+    gdn_status st = check_flush_verify_args(va);
+    if (st != GDN_OK) return st;
+    if (ca != nullptr) {
+        st = check_flush_conv_args(ca);
+        if (st != GDN_OK) return st;
+        if (ca->role != va->role || ca->pending_len != va->pending_len ||
+            ca->n_seqs != va->n_seqs || ca->layer_begin != va->layer_begin ||
+            ca->n_layers != va->n_layers || ca->max_nodes != va->max_nodes)
+            return fail(GDN_EINVAL, "gdn_commit_path: conv args disagree with verify args on "
+                        "role/pending_len/n_seqs/layers/max_nodes");
+    }
+    const ImageView v = view_image(host_image);
+    if (v.n_seqs != va->n_seqs)
+        return fail(GDN_EINVAL, "gdn_commit_path: n_seqs differs from the schedule's");
+    if (v.max_tree > va->max_nodes)
+        return fail(GDN_ECAPACITY, "gdn_commit_path: max_nodes smaller than the largest tree");
+    const int32_t S = v.n_seqs;
+    if (S == 0) return GDN_OK;
+    if (path_offsets[0] != 0) return fail(GDN_EPATH, "gdn_commit_path: path_offsets[0] != 0");
+    const int32_t *seq_off = host_image + v.off_seq, *npar = host_image + v.off_parent;
+    bool any_compaction = false;
+    std::vector<int32_t> new_role(role_host, role_host + S), new_pending(S);
+    for (int32_t b = 0; b < S; ++b) {
+        const int32_t beg = path_offsets[b], L = path_offsets[b + 1] - beg;
+        const int32_t n_b = seq_off[b + 1] - seq_off[b];
+        if (L < 0 || L > n_b)
+            return fail(GDN_EPATH, "gdn_commit_path: sequence %d: path length %d not in [0, %d]",
+                        b, L, n_b);
+        if (L > 0 && paths == nullptr) return fail(GDN_EINVAL, "gdn_commit_path: null paths");
+        if (role_host[b] != 0 && role_host[b] != 1)
+            return fail(GDN_EINVAL, "gdn_commit_path: role[%d] = %d", b, role_host[b]);
+        bool in_order = true;
+        for (int32_t i = 0; i < L; ++i) {
+            const int32_t node = paths[beg + i];
+            if (node < 0 || node >= n_b)
+                return fail(GDN_EPATH, "gdn_commit_path: sequence %d: node %d out of range", b,
+                            node);
+            const int32_t expect_parent = i == 0 ? -1 : seq_off[b] + paths[beg + i - 1];
+            if (npar[seq_off[b] + node] != expect_parent)
+                return fail(GDN_EPATH, "gdn_commit_path: sequence %d: path[%d] = %d does not "
+                            "follow its parent", b, i, node);
+            in_order = in_order && node == i;
+        }
+        if (L > 0 && in_order) new_role[b] ^= 1;
+        if (L > 0 && !in_order) any_compaction = true;
+        new_pending[b] = L;
+    }
+    if (S > 65535 || va->n_layers > 65535)
+        return fail(GDN_EINVAL, "gdn_commit_path: n_seqs and n_layers must be <= 65535");
+    if (any_compaction && dev_paths == nullptr)
+        return fail(GDN_EINVAL, "gdn_commit_path: null dev_paths");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (any_compaction) {
+        CompactParams P{};
+        for (int i = 0; i < 2; ++i) {
+            P.bk[i] = va->bank_k[i];
+            P.bu[i] = va->bank_u[i];
+            P.blg[i] = va->bank_lg[i];
+            P.bx[i] = ca ? ca->bank_x[i] : nullptr;
+        }
+        P.role = va->role;
+        P.paths = dev_paths;
+        P.path_off = dev_path_offsets;
+        P.S = S;
+        P.H = va->n_heads;
+        P.D = va->head_dim;
+        P.C = ca ? ca->channels : 0;
+        P.max_nodes = va->max_nodes;
+        P.layer_begin = va->layer_begin;
+        hipLaunchKernelGGL(compact_kernel, dim3(S, va->n_layers), dim3(256), 0, s, P);
+        GDN_LAUNCH_CHECK("compact_kernel");
+    }
+    hipLaunchKernelGGL(commit_bookkeeping_kernel, dim3((S + 255) / 256), dim3(256), 0, s,
+                       const_cast<int32_t *>(va->role), const_cast<int32_t *>(va->pending_len),
+                       dev_paths, dev_path_offsets, S);
+    GDN_LAUNCH_CHECK("commit_bookkeeping_kernel");
+    for (int32_t b = 0; b < S; ++b) {
+        role_host[b] = new_role[b];
+        pending_host[b] = new_pending[b];
+    }
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_compact_factors(const float *src, float *dst, int64_t row_elems,
+                                          const int32_t *src_rows, const int32_t *dst_rows,
+                                          int32_t n_rows, void *stream) {
+    clear_error();
+    if (n_rows < 0 || row_elems < 0) return fail(GDN_EINVAL, "gdn_compact_factors: negative size");
+    if (n_rows == 0 || row_elems == 0) return GDN_OK;
+    if (!src || !dst || !src_rows || !dst_rows)
+        return fail(GDN_EINVAL, "gdn_compact_factors: null pointer");
+    if (n_rows > 65535) return fail(GDN_EINVAL, "gdn_compact_factors: n_rows > 65535");
+    if (src == dst) return fail(GDN_EINVAL, "gdn_compact_factors: src and dst must differ");
+    const int64_t blocks = std::min<int64_t>((row_elems + 255) / 256, 1024);
+    hipLaunchKernelGGL(row_gather_kernel, dim3(uint32_t(blocks), n_rows), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), src, dst, row_elems, src_rows, dst_rows);
+    GDN_LAUNCH_CHECK("row_gather_kernel");
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_flush(const gdn_verify_args *va, const gdn_conv_args *ca,
+                                int32_t *pending_host, void *stream) {
+    clear_error();
+    gdn_status st = check_flush_verify_args(va);
+    if (st != GDN_OK) return st;
+    if (ca != nullptr) {
+        st = check_flush_conv_args(ca);
+        if (st != GDN_OK) return st;
+        if (ca->role != va->role || ca->pending_len != va->pending_len ||
+            ca->n_seqs != va->n_seqs || ca->layer_begin != va->layer_begin ||
+            ca->n_layers != va->n_layers)
+            return fail(GDN_EINVAL, "gdn_flush: conv args disagree with verify args");
+    }
+    if (pending_host == nullptr) return fail(GDN_EINVAL, "gdn_flush: null pending_host");
+    const int32_t S = va->n_seqs;
+    if (S == 0) return GDN_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = flush_state(va, s);
+    if (st != GDN_OK) return st;
+    if (ca != nullptr) {
+        st = flush_conv(ca, s);
+        if (st != GDN_OK) return st;
+    }
+    hipLaunchKernelGGL(clear_pending_kernel, dim3((S + 255) / 256), dim3(256), 0, s,
+                       const_cast<int32_t *>(va->pending_len), S);
+    GDN_LAUNCH_CHECK("clear_pending_kernel");
+    for (int32_t b = 0; b < S; ++b) pending_host[b] = 0;
+    return GDN_OK;
+}

@@ -1,0 +1,33 @@
+// Host-side internals shared by the library's translation units: error reporting, the
+// schedule image view and launch limits.  Plain C++17, no HIP types.
+#pragma once
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/gdn_tree.h"
+
+namespace gdn {
+
+constexpr int32_t kImageMagic = 0x53444E47;
+constexpr int32_t kImageHeader = 16;
+constexpr int32_t kMaxTreeNodes = 1024;
+constexpr int32_t kMaxSeqs = 1 << 20;
+
+// Word offsets of the schedule image's arrays (see gdn_tree.h for the layout).
+struct ImageView {
+    int32_t n_seqs, n_nodes, n_chains, n_waves, n_boundaries, max_chain_len, max_tree;
+    int64_t off_seq, off_wave, off_chain, off_cnodes, off_cseq, off_csrc, off_store,
+        off_parent, off_depth;
+};
+
+size_t schedule_words(int32_t n_seqs, int32_t n_nodes);
+ImageView view_image(const int32_t *img);
+bool image_ok(const int32_t *img);
+
+// Per-thread last error; `fail` formats it and returns the status code.
+void clear_error();
+gdn_status fail(gdn_status code, const char *fmt, ...);
+
+}  // namespace gdn

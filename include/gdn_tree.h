@@ -1,0 +1,234 @@
+/*
+ * gdn_tree.h -- C ABI for verifying a speculative draft tree through Gated DeltaNet layers
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (cited by page title and section):
+ *   "Lucebox SpecLA and Gated DeltaNet state-resident verification" guide --
+ *     section "Why speculative decoding is harder for linear-attention models": every GDN
+ *       head carries a recurrent state S that each token advances with the gated delta rule,
+ *       S <- g S (I - beta k k^T) + beta v k^T, read out as o = S q; in a candidate tree
+ *       every node must see the state of its own root-to-node path, starting from the
+ *       committed state, and rejected candidates must leave that state untouched;
+ *     mechanism 1 (state-resident verification): consecutive nodes of one verify chain are
+ *       processed inside one kernel with the state tile kept on chip, read once at the
+ *       chain head and written once at its end; the depthwise conv window is handled the
+ *       same way so siblings never pick up a DFS neighbour's conv history;
+ *     mechanism 2 (HLD scheduling): heavy-light chains, only boundary states materialised,
+ *       chains grouped into dependency waves, all chains of a wave launched together;
+ *     mechanism 3 (accepted-factor cache): per node the key, the delta-rule residual
+ *       update vector, the log decay gate and the conv raw input are kept in two FP32
+ *       double-buffered banks; in-order acceptance swaps the banks, branched acceptance
+ *       compacts rows back into path order;
+ *     mechanism 4 (deferred fused commit): the next verify folds the pending factors into
+ *       the committed state before verifying; a final flush materialises the last path.
+ *   "Luce DFlash server README", section "How it works": DDTree verifies a parent-indexed
+ *     tree of candidates in one target forward; the tree-aware conv gathers each node's
+ *     window along its parent chain; after accept the state is that of the committed prefix.
+ *
+ * Conventions
+ *   - Ownership: the caller allocates every buffer. Host arrays are plain memory; device
+ *     arrays are device pointers (e.g. from torch on ROCm). The library allocates nothing,
+ *     keeps no pointer after a call returns and has no global state except a per-thread
+ *     error string (gdn_last_error).
+ *   - Streams: device calls take a hipStream_t as `void *stream` (NULL = default stream),
+ *     only enqueue work and return. Host calls (schedule, sizes) are synchronous.
+ *   - Errors: every call returns a gdn_status. All arguments are validated before anything
+ *     is enqueued; on error nothing is launched and no output is touched. GDN_EDEVICE means
+ *     the HIP runtime refused a launch; gdn_last_error() gives the text.
+ *   - Tree ids: a sequence b has N_b >= 1 nodes with local ids 0..N_b-1, node 0 the root,
+ *     parent[0] = -1 and 0 <= parent[i] < i. Global id = seq_offsets[b] + local id; T is the
+ *     total node count of the batch.
+ *   - Layers: every per-layer device array has a leading layer index; layer l's block starts
+ *     at base + l * (size of one layer's block, in elements, as given per array below).
+ *     Device calls process layers layer_begin .. layer_begin + n_layers - 1 (n_layers = 1
+ *     is the per-layer pattern of a model forward).
+ *   - Shapes: head_dim d = d_k = d_v in {16, 128}; conv width 4; N_b <= 1024.
+ *   - Numerics: inputs bf16 or fp32; state, factors and outputs fp32; accumulation fp32.
+ */
+#ifndef GDN_TREE_H
+#define GDN_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gdn_status;
+#define GDN_OK         0
+#define GDN_EINVAL    -1 /* null pointer, unsupported size or dtype, inconsistent counts */
+#define GDN_ETREE     -2 /* a parent array is not a root-first tree with parent[i] < i   */
+#define GDN_EPATH     -3 /* an accepted path is not a root path of its tree              */
+#define GDN_ECAPACITY -4 /* a caller buffer is smaller than the call needs               */
+#define GDN_EDEVICE   -5 /* the HIP runtime reported an error at enqueue                 */
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* ------------------------------------------------------------------------------------
+ * Heavy-light chain schedule (host, integer, deterministic).
+ * SpecLA guide, mechanism 2. Rules (fixed where the page leaves them open):
+ *   heavy child = child with the largest subtree, ties to the smallest index;
+ *   a chain is the heavy path from the root or from a light child, root-to-leaf;
+ *   wave(root chain) = 0, wave(c) = 1 + wave of the chain holding parent(head(c));
+ *   boundary node = node with at least one light child; its state is stored once and
+ *     every light chain hanging off it starts from it; slots by ascending global id;
+ *   chains ordered by (wave, sequence, global head id); waves merged across the batch.
+ *
+ * The schedule is one int32 image, built on the host and copied verbatim to the device.
+ * Layout for n_seqs = S and T total nodes (word offsets):
+ *   [0]  magic 0x53444E47     [1] S   [2] T   [3] n_chains   [4] n_waves
+ *   [5]  n_boundaries         [6] longest chain   [7] largest tree   [8..15] zero
+ *   seq_offsets   [S+1] at 16                       b's nodes: [seq_offsets[b], seq_offsets[b+1])
+ *   wave_offsets  [T+1] at 17+S                     wave w: chains [wave_offsets[w], ..[w+1])
+ *   chain_offsets [T+1] at 18+S+T                   chain c: chain_nodes[chain_offsets[c] ..)
+ *   chain_nodes   [T]   at 19+S+2T                  global ids, root-to-leaf within a chain
+ *   chain_seq     [T]   at 19+S+3T                  owning sequence of chain c
+ *   chain_src     [T]   at 19+S+4T                  -1: committed state, else boundary slot
+ *   node_store    [T]   at 19+S+5T                  slot written after node n, or -1
+ *   node_parent   [T]   at 19+S+6T                  global parent id, -1 for roots
+ *   node_depth    [T]   at 19+S+7T                  edges from the root
+ *   total words = 19 + S + 8T. Arrays are sized for T; only the counted prefix is used.
+ * ---------------------------------------------------------------------------------- */
+size_t gdn_schedule_words(int32_t n_seqs, int32_t n_nodes_total);
+
+/* parent_local: host [T], tree b's local parent array at parent_local[seq_offsets[b]..].
+ * seq_offsets: host [n_seqs+1], seq_offsets[0] = 0, strictly increasing.
+ * image: host [image_words], filled on success.
+ * GDN_ETREE for a malformed tree, GDN_ECAPACITY if image_words is too small. */
+gdn_status gdn_hld_schedule(const int32_t *parent_local, const int32_t *seq_offsets,
+                            int32_t n_seqs, int32_t *image, size_t image_words);
+
+/* ------------------------------------------------------------------------------------
+ * Tree verify with fused deferred commit (SpecLA guide, mechanisms 1, 2 and 4).
+ *
+ * For every node n of every tree, every head h, every layer l processed:
+ *   S_n = g_n S_parent + u_n k_n^T,  u_n = beta_n (v_n - g_n S_parent k_n)
+ *       (= g_n S_parent (I - beta_n k_n k_n^T) + beta_n v_n k_n^T)
+ *   out[n] = S_n q_n
+ * where S_parent of a root is the committed state AFTER the deferred fold:
+ *   if pending_len[b] = L > 0:  S <- exp(lg_i) S + u_i k_i^T for pending rows i = 0..L-1,
+ *   and the folded state is written back to `state` (once, by the root chain).
+ * Factors (k_n, u_n, lg_n = ln g_n) are written to row n (local id) of the write bank
+ * 1 - role[b]. Rows of the pending bank role[b] are only read.
+ *
+ * Work: one launch per dependency wave, one workgroup per (layer, chain, head); the fp32
+ * state tile stays in VGPRs for the whole chain; boundary nodes store their state once to
+ * `boundary` for the light chains of later waves.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t n_seqs;      /* S, must equal the schedule's                                   */
+    int32_t n_heads;     /* H >= 1                                                         */
+    int32_t head_dim;    /* d in {16, 128}                                                 */
+    int32_t n_nodes;     /* T, must equal the schedule's                                   */
+    int32_t max_nodes;   /* bank rows per (layer, seq, head); >= every N_b                 */
+    int32_t layer_begin; /* first layer processed                                          */
+    int32_t n_layers;    /* layers processed, >= 1                                         */
+    int32_t in_dtype;    /* gdn_dtype of q, k, v, beta, gate                               */
+    const void *q, *k;   /* [Ly][T][H][d]     (per-layer block T*H*d)                      */
+    const void *v;       /* [Ly][T][H][d]                                                  */
+    const void *beta;    /* [Ly][T][H]        (per-layer block T*H)                        */
+    const void *gate;    /* [Ly][T][H]        g in (0, 1], linear (not log)                */
+    float *state;        /* [Ly][S][H][d][d]  committed state, row = d_v index, in/out     */
+    float *bank_k[2];    /* [Ly][S][H][max_nodes][d]  keys                                 */
+    float *bank_u[2];    /* [Ly][S][H][max_nodes][d]  residual update vectors              */
+    float *bank_lg[2];   /* [Ly][S][H][max_nodes]     log decay gates                      */
+    const int32_t *role;        /* device [S]: index (0/1) of the pending bank             */
+    const int32_t *pending_len; /* device [S]: pending rows to fold, 0 = none              */
+    float *boundary;     /* device scratch, gdn_verify_workspace_bytes() bytes              */
+    float *out;          /* [Ly][T][H][d] fp32 outputs                                     */
+} gdn_verify_args;
+
+/* Bytes of `boundary` scratch for this schedule: n_layers * n_boundaries * H * d * d * 4. */
+size_t gdn_verify_workspace_bytes(const int32_t *host_image, int32_t n_heads, int32_t head_dim,
+                                  int32_t n_layers);
+
+/* host_image: the schedule on the host (read for launch sizes);
+ * dev_image: the same words in device memory (read by the kernels). */
+gdn_status gdn_tree_verify(const gdn_verify_args *args, const int32_t *host_image,
+                           const int32_t *dev_image, void *stream);
+
+/* Same work as gdn_tree_verify restricted to dependency wave `wave` (0 <= wave < n_waves):
+ * calling it for waves 0, 1, ... in order on one stream equals gdn_tree_verify. */
+gdn_status gdn_tree_verify_wave(const gdn_verify_args *args, const int32_t *host_image,
+                                const int32_t *dev_image, int32_t wave, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Tree-aware causal depthwise conv with fused conv-window fold (DFlash README, "How it
+ * works", tree-aware conv gather; SpecLA guide, mechanisms 1, 3 and 4).
+ *
+ * Fold first: if pending_len[b] = L > 0, conv_state[b] <- last 3 of
+ *   (conv_state[b] columns, bank_x[role[b]] rows 0..L-1), written back.
+ * Then for node n, channel c:
+ *   out[n][c] = sum_{j<4} weight[c][j] * win_n[j],  win_n = last 4 of
+ *   (conv_state[b][c][0..2], x along n's root path ending with x[n][c]);
+ * weight[c][3] multiplies the current token; no bias, no activation.
+ * Raw inputs x[n] (as fp32) go to row n (local id) of bank_x[1 - role[b]].
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t n_seqs;      /* S                                                              */
+    int32_t channels;    /* Cch >= 1                                                       */
+    int32_t width;       /* must be 4                                                      */
+    int32_t n_nodes;     /* T                                                              */
+    int32_t max_nodes;   /* bank rows per (layer, seq); >= every N_b                       */
+    int32_t layer_begin;
+    int32_t n_layers;
+    int32_t in_dtype;    /* gdn_dtype of x and weight                                      */
+    const void *x;       /* [Ly][T][Cch]                                                   */
+    const void *weight;  /* [Ly][Cch][4]                                                   */
+    float *conv_state;   /* [Ly][S][Cch][3] committed window, oldest first, in/out         */
+    float *bank_x[2];    /* [Ly][S][max_nodes][Cch]                                        */
+    const int32_t *role;
+    const int32_t *pending_len;
+    float *out;          /* [Ly][T][Cch] fp32                                              */
+} gdn_conv_args;
+
+gdn_status gdn_tree_conv(const gdn_conv_args *args, const int32_t *host_image,
+                         const int32_t *dev_image, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Accept -> commit (SpecLA guide, mechanism 3). Enqueue after the last layer's verify and
+ * conv of the step. For each sequence b with accepted root path P_b of length L_b:
+ *   L_b = 0            : pending_len[b] = 0 (nothing to commit)
+ *   P_b = [0..L_b-1]   : role[b] ^= 1 (the written bank becomes pending; no device copy)
+ *   otherwise          : row P_b[i] of every write bank (k, u, lg for every head, x) is
+ *                        copied to row i of the pending bank, for all n_layers layers
+ *   and pending_len[b] = L_b.
+ * paths: host, concatenated local ids; path_offsets: host [S+1].
+ * dev_paths / dev_path_offsets: the same arrays in device memory (read by the kernels).
+ * role_host / pending_host: host mirrors [S], read and updated by the call.
+ * va->role and va->pending_len (device) are updated on the stream; ca may be NULL when no
+ * conv banks are kept, otherwise its bank_x, role and pending_len must match va's.
+ * GDN_EPATH if some P_b is not a root path of tree b (nothing is enqueued then).
+ * ---------------------------------------------------------------------------------- */
+gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *paths,
+                           const int32_t *path_offsets, const int32_t *dev_paths,
+                           const int32_t *dev_path_offsets, const gdn_verify_args *va,
+                           const gdn_conv_args *ca, int32_t *role_host, int32_t *pending_host,
+                           void *stream);
+
+/* Raw row gather used by gdn_commit_path, exported for direct use:
+ * for r in [0, n_rows): dst[dst_rows[r] * row_elems ..] = src[src_rows[r] * row_elems ..]
+ * (row_elems floats each). dst_rows/src_rows are device int32 arrays. Bit-exact copy. */
+gdn_status gdn_compact_factors(const float *src, float *dst, int64_t row_elems,
+                               const int32_t *src_rows, const int32_t *dst_rows,
+                               int32_t n_rows, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Flush (SpecLA guide, mechanism 4): at the end of generation, on a switch to
+ * autoregressive decode or on cancel, fold the pending factors of every sequence into
+ * `state` (and, if ca != NULL, the pending conv inputs into conv_state) for the n_layers
+ * layers, then set pending_len to 0 (device, on the stream, and the host mirror now).
+ * A sequence with nothing pending is left bit-identical.
+ * ---------------------------------------------------------------------------------- */
+gdn_status gdn_flush(const gdn_verify_args *va, const gdn_conv_args *ca, int32_t *pending_host,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_TREE_H */

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle, element by element,
+on seeded inputs (tiny fp32 trees, every tree with N <= 6, one bf16 layer of 48 heads x 128,
+and a 48-layer stack over 10 verify + commit steps with a final flush)."""
+import numpy as np
+import pytest
+
+from gated_deltanet_tree_amd import binding, synth, workload
+from oracle import conv as oconv
+from oracle import gdn as ogdn
+
+import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    binding.lib()
+    return torch
+
+
+def _check_step(b: gh.Batch, h64, S0s, X0s, W, layer=0, write_bank=None, conv=True, host_layer=None):
+    """Compare one layer's outputs, conv outputs and written banks with the oracle.
+    S0s/X0s: per sequence committed state/window used by this verify; `host_layer` indexes
+    the host input arrays (defaults to `layer`)."""
+    hl = layer if host_layer is None else host_layer
+    o_gpu = gh.to_np(b.out[layer])
+    y_gpu = gh.to_np(b.y[layer]) if conv else None
+    refs = []
+    for s in range(b.S):
+        r = gh.oracle_seq(b.trees[s], S0s[s], X0s[s] if conv else None, W, h64, hl, s, b.offs)
+        sl = slice(b.offs[s], b.offs[s + 1])
+        gh.assert_outputs(o_gpu[sl], r["o"], what=f"o seq {s}")
+        if conv:
+            gh.assert_outputs(y_gpu[sl], r["y"], what=f"conv y seq {s}")
+            wb = write_bank[s]
+            xb = gh.to_np(b.layers.bank_x[wb][layer, s][:len(b.trees[s]), :b.C])
+            assert np.array_equal(xb, h64["x"][hl, sl]), "banked conv input not exact"
+        gh.assert_bank_rows(b, layer, s, write_bank[s], range(len(b.trees[s])),
+                            r["k"], r["u"], r["lg"])
+        refs.append(r)
+    return refs
+
+
+def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0):
+    b = gh.Batch(trees, 1, H, d, C)
+    S0 = np.stack([synth.initial_state(cfg_id, 0, s, H, d) for s in range(b.S)])[None]
+    X0 = np.stack([synth.initial_conv_state(cfg_id, 0, s, C, 4) for s in range(b.S)])[None]
+    W = synth.conv_weight(cfg_id, 0, C, 4, dtype)[None]
+    b.set_state(S0, X0)
+    Wd = workload._to_torch(W, dtype, "cuda")
+    return b, S0[0].astype(np.float64), X0[0].astype(np.float64), workload.widen(W[0], dtype), Wd
+
+
+def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d, C):
+    """Several verify+commit steps then a flush, each checked against the oracle carrying the
+    exact committed state (replay of the accepted paths)."""
+    committed, window = [s.copy() for s in S0], [x.copy() for x in X0]
+    for step, paths in enumerate(steps_paths):
+        h = gh.tiny_inputs(b.trees, step, H, d, C, dtype, cfg_id)
+        h64 = gh.widen_inputs(h, dtype)
+        inp = gh.to_device(h, dtype)
+        role_before = b.layers.role_host.copy()
+        b.step(inp, Wd)
+        torch_cuda.cuda.synchronize()
+        # the fold of the previous step's path happened inside this verify
+        gh.assert_state(gh.to_np(b.layers.state[0]), np.stack(committed), what=f"fold @ {step}")
+        cs = gh.to_np(b.layers.conv_state[0])
+        assert np.array_equal(cs, np.stack(window).astype(np.float32)), "conv window fold"
+        _check_step(b, h64, committed, window, W64, 0, write_bank=1 - role_before)
+        written = {name: [t.clone() for t in getattr(b.layers, name)]
+                   for name in ("bank_k", "bank_u", "bank_lg", "bank_x")}
+        b.commit(inp, paths, Wd)
+        torch_cuda.cuda.synchronize()
+        exp_role, exp_pend = gh.role_pending_expect(role_before, paths)
+        assert np.array_equal(b.layers.role_host, exp_role)
+        assert np.array_equal(b.layers.pending_host, exp_pend)
+        assert np.array_equal(b.layers.role.cpu().numpy(), exp_role)
+        assert np.array_equal(b.layers.pending.cpu().numpy(), exp_pend)
+        for s, path in enumerate(paths):
+            wb, pb = 1 - role_before[s], exp_role[s]
+            for name in ("bank_k", "bank_u", "bank_lg", "bank_x"):
+                src = written[name][wb][0, s]
+                dst = getattr(b.layers, name)[pb][0, s]
+                if name == "bank_x":
+                    got, ref = dst[:len(path)], src[list(path)]
+                else:
+                    got, ref = dst[:, :len(path)], src[:, list(path)]
+                assert torch_cuda.equal(got, ref), f"pending {name} rows seq {s}"
+            sl = slice(b.offs[s], b.offs[s + 1])
+            seq = {k: h64[k][0, sl] for k in h64}
+            committed[s] = ogdn.replay(committed[s], seq["k"], seq["v"], seq["beta"],
+                                       seq["gate"], path)
+            window[s] = oconv.commit_window(window[s], seq["x"], path)
+    b.flush()
+    torch_cuda.cuda.synchronize()
+    gh.assert_state(gh.to_np(b.layers.state[0]), np.stack(committed), what="flush")
+    assert np.array_equal(gh.to_np(b.layers.conv_state[0]), np.stack(window).astype(np.float32))
+    assert np.all(b.layers.pending.cpu().numpy() == 0) and np.all(b.layers.pending_host == 0)
+    before = b.layers.state.clone(), b.layers.conv_state.clone()
+    b.flush()  # nothing pending: bit-identical
+    torch_cuda.cuda.synchronize()
+    assert torch_cuda.equal(before[0], b.layers.state)
+    assert torch_cuda.equal(before[1], b.layers.conv_state)
+
+
+def test_tiny_tree_and_chain(torch_cuda):
+    """Config 0: the 7-node tree [-1,0,0,1,1,2,3] and an 8-node chain, batched, fp32, d = 16.
+    Step 0 accepts the deepest leaves ([0,1,3,6] is branched -> compaction; the chain is in
+    order -> role swap); step 1 accepts [0,2,5] and [0,1,2]; then flush."""
+    trees = [synth.TINY_TREE, synth.TINY_CHAIN]
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees)
+    paths0 = [synth.deepest_leaf_path(t) for t in trees]
+    assert list(paths0[0]) == [0, 1, 3, 6] and list(paths0[1]) == list(range(8))
+    _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, [[0, 2, 5], [0, 1, 2]], [[0], []]],
+               "f32", 0, 1, 16, 16)
+
+
+def _all_trees(N):
+    import itertools
+    for choice in itertools.product(*[range(i) for i in range(1, N)]):
+        yield np.array((-1,) + choice, dtype=np.int32)
+
+
+def test_every_small_tree_batched(torch_cuda):
+    """All 154 labelled trees with N <= 6 in one batch (d = 16, 2 heads, fp32): three steps of
+    verify + commit with seeded random paths of every length (0 included), then flush."""
+    trees = [t for N in range(1, 7) for t in _all_trees(N)]
+    assert len(trees) == 154
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=2, C=8, cfg_id=90)
+    rng = np.random.default_rng(4)
+    steps = []
+    for _ in range(3):
+        paths = []
+        for t in trees:
+            L = int(rng.integers(0, synth.node_depths(t).max() + 2))
+            paths.append(synth.random_path(rng, t, L))
+        steps.append(paths)
+    _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps, "f32", 90, 2, 16, 8)
+
+
+def test_bf16_inputs_small(torch_cuda):
+    """bf16 inputs at d = 16 over a branched batch (exercises the bf16 staging path)."""
+    rng = np.random.default_rng(8)
+    trees = [synth.make_tree(rng, 12, 3, 5) for _ in range(5)]
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=3, C=24, dtype="bf16", cfg_id=91)
+    steps = [[synth.random_path(rng, t, int(rng.integers(1, 4))) for t in trees] for _ in range(2)]
+    _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps, "bf16", 91, 3, 16, 24)
+
+
+def _layer_case(torch_cuda, config, n_layers, trees, steps, sample_layers, check_outputs_at):
+    c = synth.CONFIGS[config]
+    H, d, C, dtype = c["H"], c["d"], c["Cch"], c["dtype"]
+    b = gh.Batch(trees, n_layers, H, d, C)
+    layers = range(n_layers)
+    S0, X0 = workload.host_initial_state(config, layers, b.S)
+    W = workload.host_weights(config, layers)
+    b.set_state(S0, X0)
+    Wd = workload._to_torch(W, dtype, "cuda")
+    committed = {l: [S0[l, s].astype(np.float64) for s in range(b.S)] for l in sample_layers}
+    window = {l: [X0[l, s].astype(np.float64) for s in range(b.S)] for l in sample_layers}
+    W64 = {l: workload.widen(W[l], dtype) for l in sample_layers}
+    for step in range(steps):
+        h = workload.host_step_inputs(config, step, trees, layers)
+        inp = workload.StepInputs(**{k: workload._to_torch(v, dtype, "cuda") for k, v in h.items()})
+        role_before = b.layers.role_host.copy()
+        b.step(inp, Wd)
+        torch_cuda.cuda.synchronize()
+        h64 = {k: workload.widen(v[list(sample_layers)], dtype) for k, v in h.items()}
+        for li, l in enumerate(sample_layers):
+            gh.assert_state(gh.to_np(b.layers.state[l]), np.stack(committed[l]),
+                            what=f"committed layer {l} step {step}")
+            if step in check_outputs_at:
+                _check_step(b, h64, committed[l], window[l], W64[l], l,
+                            write_bank=1 - role_before, host_layer=li)
+        paths = [synth.config_path(config, step, s, trees[s]) for s in range(b.S)]
+        b.commit(inp, paths, Wd)
+        for li, l in enumerate(sample_layers):
+            for s, path in enumerate(paths):
+                sl = slice(b.offs[s], b.offs[s + 1])
+                committed[l][s] = ogdn.replay(committed[l][s], h64["k"][li, sl], h64["v"][li, sl],
+                                              h64["beta"][li, sl], h64["gate"][li, sl], path)
+                window[l][s] = oconv.commit_window(window[l][s], h64["x"][li, sl], path)
+    b.flush()
+    torch_cuda.cuda.synchronize()
+    for l in sample_layers:
+        gh.assert_state(gh.to_np(b.layers.state[l]), np.stack(committed[l]), what=f"flush {l}")
+        assert np.array_equal(gh.to_np(b.layers.conv_state[l]),
+                              np.stack(window[l]).astype(np.float32))
+
+
+def test_one_layer_bf16_48_heads(torch_cuda):
+    """Config 1: one layer, 48 heads x 128, bf16 inputs, the seeded 22-node top-4 tree; verify,
+    conv and banks for every node and head, then commit of a length-6 path and flush."""
+    trees = workload.config_trees(1)
+    _layer_case(torch_cuda, 1, 1, trees, steps=2, sample_layers=[0], check_outputs_at={0, 1})
+
+
+def test_48_layers_ten_steps(torch_cuda):
+    """Config 2: 48 independent layers, 10 verify steps each folding the previous step's
+    accepted length-6 path, then flush; oracle on three sampled layers (states every step,
+    outputs and banks at steps 0, 4 and 9)."""
+    trees = workload.config_trees(2)
+    _layer_case(torch_cuda, 2, 48, trees, steps=10, sample_layers=[0, 23, 47],
+                check_outputs_at={0, 4, 9})
