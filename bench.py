@@ -133,9 +133,11 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layers-per-call", type=int, default=1)
-    ap.add_argument("--cpu-pairs", type=int, default=96)
+    ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--cpu-workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one MI355X: the tree verify path runs on a single GPU here; "
@@ -196,56 +198,50 @@ def main(argv=None):
     def upload(a):
         return torch.from_numpy(a).pin_memory().to(dev, non_blocking=True)
 
-    acc = dict(verify_ms=0.0, verify_launches=0, verify_bytes=0, conv_bytes=0, commit_bytes=0,
-               conv_ms=0.0)
+    acc = dict(verify_ms=0.0, verify_launches=0, verify_bytes=0, conv_bytes=0, commit_bytes=0)
+    n_waves = int(view["n_waves"])
+    # Verify launches are timed by events recorded by the dispatches themselves (no extra
+    # packets on the stream); one pair per (step, layer call, wave).
+    ev = [[[(binding.HipEvent(), binding.HipEvent()) for _ in range(n_waves)]
+           for _ in range(len(vargs))] for _ in range(args.steps)]
 
-    def step(s, timed):
+    def step(s, timed_index):
         image = binding.hld_schedule(trees)  # a1: host schedule of this step's trees
         dev_image = upload(image)
         pending = [int(L) for L in lay.pending_host]
-        evs = []
-        for li, l in enumerate(range(0, Ly, lpc)):
-            if timed:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+        for li in range(len(vargs)):
             binding.tree_conv(cargs[li], image, dev_image)
-            if timed:
-                e1 = torch.cuda.Event(enable_timing=True)
-                e1.record(stream)
-                evs.append(("conv", e0, e1))
-            for w in range(int(view["n_waves"])):
-                if timed:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                binding.tree_verify_wave(vargs[li], image, dev_image, w)
-                if timed:
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e1.record(stream)
-                    evs.append(("verify", e0, e1))
-                    acc["verify_bytes"] += verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc)
-                    acc["verify_launches"] += 1
-            if timed:
-                acc["conv_bytes"] += conv_bytes(view, pending, C, in_bytes, lpc)
+            for w in range(n_waves):
+                if timed_index is None:
+                    binding.tree_verify_wave(vargs[li], image, dev_image, w)
+                else:
+                    e0, e1 = ev[timed_index][li][w]
+                    binding.tree_verify_wave_timed(vargs[li], image, dev_image, w, e0, e1)
         paths = all_paths[s]
         flat, offs = binding.pack_paths(paths)
         binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs))
-        if timed:
+        if timed_index is not None:  # byte accounting after the launches, off the GPU's path
+            calls = len(vargs)
+            acc["verify_bytes"] += calls * sum(verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc)
+                                               for w in range(n_waves))
+            acc["verify_launches"] += calls * n_waves
+            acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
             acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly)
-        return evs
 
     for s in range(args.warmup):
-        step(s, False)
+        step(s, None)
     torch.cuda.synchronize()
-    events = []
     t0 = time.perf_counter()
-    for s in range(args.warmup, n_total):
-        events += step(s, True)
+    for i, s in enumerate(range(args.warmup, n_total)):
+        step(s, i)
     flush_pending = lay.pending_host.copy()
     binding.flush(va_all, ca_all, lay)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for kind, e0, e1 in events:
-        acc[kind + "_ms"] += e0.elapsed_time(e1)
+    for per_step in ev:
+        for per_call in per_step:
+            for e0, e1 in per_call:
+                acc["verify_ms"] += e0.elapsed_ms(e1)
 
     node_layers = args.steps * T * Ly
     total_bytes = acc["verify_bytes"] + acc["conv_bytes"] + acc["commit_bytes"] + \
@@ -286,9 +282,22 @@ def main(argv=None):
         "algorithmic_bytes_per_step": total_bytes / args.steps,
         "compulsory_GBps_step": compulsory / wall / 1e9,
         "verify_ms_per_step": acc["verify_ms"] / args.steps,
-        "conv_ms_per_step": acc["conv_ms"] / args.steps,
         "input_generation_s": gen_s,
     }
+    if args.copy_probe:
+        src = torch.empty(1 << 28, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        reps = 10
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        result["copy_probe"] = {"bytes_per_copy": 2 * src.numel() * 4,
+                                "GBps": 2 * src.numel() * 4 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -21,7 +21,8 @@ STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_ETREE", -3: "GDN_EPATH",
           -4: "GDN_ECAPACITY", -5: "GDN_EDEVICE"}
 EXPORTS = [
     "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_verify_workspace_bytes",
-    "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_conv", "gdn_commit_path",
+    "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed", "gdn_tree_conv",
+    "gdn_commit_path",
     "gdn_compact_factors", "gdn_flush",
 ]
 IMAGE_HEADER = 16
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.gdn_tree_verify.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
     L.gdn_tree_verify_wave.restype = _I32
     L.gdn_tree_verify_wave.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _I32, _P]
+    L.gdn_tree_verify_wave_timed.restype = _I32
+    L.gdn_tree_verify_wave_timed.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _I32, _P, _P,
+                                             _P]
     L.gdn_tree_conv.restype = _I32
     L.gdn_tree_conv.argtypes = [ctypes.POINTER(ConvArgs), _I32P, _P, _P]
     L.gdn_commit_path.restype = _I32
@@ -270,6 +274,47 @@ def tree_verify(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
 def tree_verify_wave(args: VerifyArgs, image: np.ndarray, dev_image, wave: int, stream=None):
     _check(lib().gdn_tree_verify_wave(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
                                       _stream(stream)), "gdn_tree_verify_wave")
+
+
+def tree_verify_wave_timed(args: VerifyArgs, image: np.ndarray, dev_image, wave: int,
+                           start: "HipEvent", stop: "HipEvent", stream=None):
+    _check(lib().gdn_tree_verify_wave_timed(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
+                                            start.handle, stop.handle, _stream(stream)),
+           "gdn_tree_verify_wave_timed")
+
+
+class HipEvent:
+    """A timing-enabled hipEvent_t from the process's HIP runtime (the one torch loaded)."""
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            lib()
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreate(ctypes.byref(self.handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+
+    def elapsed_ms(self, stop: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        rc = self._runtime().hipEventElapsedTime(ctypes.byref(ms), self.handle, stop.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.handle:
+            self._hip.hipEventDestroy(self.handle)
 
 
 def tree_conv(args: ConvArgs, image: np.ndarray, dev_image, stream=None):

@@ -11,6 +11,7 @@
 // bank that the last verify consumed (the pending one) and leaves the roles as they are.
 // The kernels re-derive the per-sequence decision from the device copy of the paths, so no
 // host-to-device copy happens inside the library.
+#include <algorithm>
 #include <vector>
 
 #include "gdn_device.h"
@@ -34,40 +35,36 @@ __device__ __forceinline__ bool path_in_order(const int32_t *path, int L) {
     return true;
 }
 
-// One workgroup per (layer, sequence): rows path[i] of the written bank -> rows i of the
-// pending bank, for the key, residual and log-gate banks of every head and the conv bank.
+// One workgroup per (layer, sequence, path position i): row path[i] of the written bank ->
+// row i of the pending bank, for the key and residual rows of every head (float4 copies),
+// the log gates and the conv input row.  Workgroups past the path's end, or of a sequence
+// whose path is in order, exit at once.
 __global__ __launch_bounds__(256) void compact_kernel(CompactParams P) {
-    const int seq = blockIdx.x;
-    const int layer = P.layer_begin + blockIdx.y;
+    const int i = blockIdx.x, seq = blockIdx.y;
+    const int layer = P.layer_begin + blockIdx.z;
     const int beg = P.path_off[seq], L = P.path_off[seq + 1] - beg;
+    if (i >= L) return;
     const int32_t *path = P.paths + beg;
-    if (L == 0 || path_in_order(path, L)) return;
-    const int dst = P.role[seq], src = dst ^ 1;
+    if (path_in_order(path, L)) return;
+    const int dst = P.role[seq], src = dst ^ 1, from = path[i];
     const int64_t ls = int64_t(layer) * P.S + seq;
     const int64_t hrows = int64_t(P.H) * P.max_nodes;  // rows of one (layer, seq)
     const int tid = threadIdx.x;
-    // key and residual rows: H * L rows of D floats each
-    const int64_t nvec = int64_t(P.H) * L * P.D;
-    for (int64_t e = tid; e < nvec; e += blockDim.x) {
-        const int d = int(e % P.D);
-        const int64_t hl = e / P.D;
-        const int i = int(hl % L), h = int(hl / L);
-        const int64_t row_dst = ls * hrows + int64_t(h) * P.max_nodes + i;
-        const int64_t row_src = ls * hrows + int64_t(h) * P.max_nodes + path[i];
-        P.bk[dst][row_dst * P.D + d] = P.bk[src][row_src * P.D + d];
-        P.bu[dst][row_dst * P.D + d] = P.bu[src][row_src * P.D + d];
+    const int dv = P.D / 4;  // float4 per row
+    for (int e = tid; e < P.H * dv; e += blockDim.x) {
+        const int h = e / dv, q = e % dv;
+        const int64_t rd = (ls * hrows + int64_t(h) * P.max_nodes + i) * P.D;
+        const int64_t rs = (ls * hrows + int64_t(h) * P.max_nodes + from) * P.D;
+        reinterpret_cast<float4 *>(P.bk[dst] + rd)[q] = reinterpret_cast<const float4 *>(P.bk[src] + rs)[q];
+        reinterpret_cast<float4 *>(P.bu[dst] + rd)[q] = reinterpret_cast<const float4 *>(P.bu[src] + rs)[q];
     }
-    for (int64_t e = tid; e < int64_t(P.H) * L; e += blockDim.x) {
-        const int i = int(e % L), h = int(e / L);
+    for (int h = tid; h < P.H; h += blockDim.x)
         P.blg[dst][ls * hrows + int64_t(h) * P.max_nodes + i] =
-            P.blg[src][ls * hrows + int64_t(h) * P.max_nodes + path[i]];
-    }
+            P.blg[src][ls * hrows + int64_t(h) * P.max_nodes + from];
     if (P.bx[0] != nullptr) {
-        const int64_t base = ls * P.max_nodes * P.C;
-        for (int64_t e = tid; e < int64_t(L) * P.C; e += blockDim.x) {
-            const int i = int(e / P.C), c = int(e % P.C);
-            P.bx[dst][base + int64_t(i) * P.C + c] = P.bx[src][base + int64_t(path[i]) * P.C + c];
-        }
+        const float *xs = P.bx[src] + (ls * P.max_nodes + from) * P.C;
+        float *xd = P.bx[dst] + (ls * P.max_nodes + i) * P.C;
+        for (int c = tid; c < P.C; c += blockDim.x) xd[c] = xs[c];
     }
 }
 
@@ -131,6 +128,7 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
     if (path_offsets[0] != 0) return fail(GDN_EPATH, "gdn_commit_path: path_offsets[0] != 0");
     const int32_t *seq_off = host_image + v.off_seq, *npar = host_image + v.off_parent;
     bool any_compaction = false;
+    int32_t max_len = 0;
     std::vector<int32_t> new_role(role_host, role_host + S), new_pending(S);
     for (int32_t b = 0; b < S; ++b) {
         const int32_t beg = path_offsets[b], L = path_offsets[b + 1] - beg;
@@ -155,6 +153,7 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
         }
         if (L > 0 && in_order) new_role[b] ^= 1;
         if (L > 0 && !in_order) any_compaction = true;
+        if (!in_order) max_len = std::max(max_len, L);
         new_pending[b] = L;
     }
     if (S > 65535 || va->n_layers > 65535)
@@ -179,7 +178,7 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
         P.C = ca ? ca->channels : 0;
         P.max_nodes = va->max_nodes;
         P.layer_begin = va->layer_begin;
-        hipLaunchKernelGGL(compact_kernel, dim3(S, va->n_layers), dim3(256), 0, s, P);
+        hipLaunchKernelGGL(compact_kernel, dim3(max_len, S, va->n_layers), dim3(256), 0, s, P);
         GDN_LAUNCH_CHECK("compact_kernel");
     }
     hipLaunchKernelGGL(commit_bookkeeping_kernel, dim3((S + 255) / 256), dim3(256), 0, s,

@@ -9,11 +9,12 @@
 //
 // One thread per (layer, sequence, channel); consecutive threads take consecutive channels,
 // so every access to x, the banks and the output is a coalesced row segment.  The thread
-// keeps the committed window in registers, folds the pending bank rows into it, writes it
-// back once, then walks its tree in index order (parents first).  A node's window is read
-// along its parent chain: the node's own input, then up to three ancestors' inputs, then
-// committed-window entries above the root.  Ancestor inputs were read moments earlier by
-// the same thread, so they come from L1/L2, not HBM.
+// keeps the committed window in registers, folds the pending bank rows into it (only the
+// last three can survive), writes it back once, then walks its tree in index order in blocks
+// of nodes whose loads are all issued before any is used.  A node's window is read along its
+// parent chain: the node's own input, up to three ancestors' inputs, then committed-window
+// entries above the root.  Ancestor inputs were read moments earlier by the same thread, so
+// they come from cache, not HBM.
 #include "gdn_device.h"
 
 namespace gdn {
@@ -30,6 +31,10 @@ struct ConvParams {
     int32_t fold_only;
 };
 
+#ifndef GDN_CONV_BLOCK
+#define GDN_CONV_BLOCK 16  // nodes whose loads are issued together
+#endif
+
 template <typename TIn>
 __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P) {
     const int c = blockIdx.x * blockDim.x + threadIdx.x;
@@ -41,11 +46,17 @@ __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P) {
     float *cs = P.cstate + (ls * P.C + c) * 3;
     float w0 = cs[0], w1 = cs[1], w2 = cs[2];  // committed window, oldest first
     if (L > 0) {
+        // Only the last three pending inputs survive the fold.
         const float *pb = P.bank[role] + ls * P.max_nodes * P.C + c;
-        for (int i = 0; i < L; ++i) {
-            w0 = w1;
-            w1 = w2;
-            w2 = pb[int64_t(i) * P.C];
+        const float r0 = L >= 3 ? pb[int64_t(L - 3) * P.C] : 0.f;
+        const float r1 = L >= 2 ? pb[int64_t(L - 2) * P.C] : 0.f;
+        const float r2 = pb[int64_t(L - 1) * P.C];
+        if (L >= 3) {
+            w0 = r0; w1 = r1; w2 = r2;
+        } else if (L == 2) {
+            w0 = w2; w1 = r1; w2 = r2;
+        } else {
+            w0 = w1; w1 = w2; w2 = r2;
         }
         cs[0] = w0;
         cs[1] = w1;
@@ -60,26 +71,35 @@ __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P) {
     float *wb = P.bank[role ^ 1] + ls * P.max_nodes * P.C + c;
     float *y = P.out + int64_t(layer) * P.T * P.C + c;
     const int32_t *par = P.img + P.off_parent, *dep = P.img + P.off_depth;
-    for (int i = 0; i < n; ++i) {
-        const int g = off + i;
-        const float x0 = to_f32(x[int64_t(g) * P.C]);
-        wb[int64_t(i) * P.C] = x0;
-        const int depth = dep[g];
-        // Taps one, two and three steps up the parent chain, else committed-window entries.
-        float x1 = w2, x2 = w1, x3 = w0;
-        if (depth >= 1) {
-            const int a1 = par[g];
-            x1 = to_f32(x[int64_t(a1) * P.C]);
-            x2 = w2;
-            x3 = w1;
-            if (depth >= 2) {
-                const int a2 = par[a1];
-                x2 = to_f32(x[int64_t(a2) * P.C]);
-                x3 = w2;
-                if (depth >= 3) x3 = to_f32(x[int64_t(par[a2]) * P.C]);
-            }
+    for (int i0 = 0; i0 < n; i0 += GDN_CONV_BLOCK) {
+        // Issue every load of the block first: the node inputs and the up-to-three ancestor
+        // inputs of each node (ancestors were read before, so they come from cache).
+        float xv[GDN_CONV_BLOCK][4];
+#pragma unroll
+        for (int j = 0; j < GDN_CONV_BLOCK; ++j) {
+            const int i = i0 + j;
+            if (i >= n) break;
+            const int g = off + i, depth = dep[g];
+            const int a1 = depth >= 1 ? par[g] : g;
+            const int a2 = depth >= 2 ? par[a1] : a1;
+            const int a3 = depth >= 3 ? par[a2] : a2;
+            xv[j][0] = to_f32(x[int64_t(g) * P.C]);
+            xv[j][1] = to_f32(x[int64_t(a1) * P.C]);
+            xv[j][2] = to_f32(x[int64_t(a2) * P.C]);
+            xv[j][3] = to_f32(x[int64_t(a3) * P.C]);
         }
-        y[int64_t(g) * P.C] = fmaf(k3, x0, fmaf(k2, x1, fmaf(k1, x2, k0 * x3)));
+#pragma unroll
+        for (int j = 0; j < GDN_CONV_BLOCK; ++j) {
+            const int i = i0 + j;
+            if (i >= n) break;
+            const int depth = dep[off + i];
+            // Taps one, two and three steps up the parent chain, else committed-window entries.
+            const float x1 = depth >= 1 ? xv[j][1] : w2;
+            const float x2 = depth >= 2 ? xv[j][2] : (depth == 1 ? w2 : w1);
+            const float x3 = depth >= 3 ? xv[j][3] : (depth == 2 ? w2 : (depth == 1 ? w1 : w0));
+            wb[int64_t(i) * P.C] = xv[j][0];
+            y[int64_t(off + i) * P.C] = fmaf(k3, xv[j][0], fmaf(k2, x1, fmaf(k1, x2, k0 * x3)));
+        }
     }
 }
 

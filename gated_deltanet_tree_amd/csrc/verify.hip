@@ -28,6 +28,8 @@
 // Node inputs (k, q, v, beta, g) and fold rows (k, u, lg) are staged through a double-
 // buffered LDS slot: the loads for item i+1 are issued before item i is computed and land
 // in the other slot afterwards, so their latency hides behind a node of work.
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -55,7 +57,6 @@ template <int D> struct Tile {
     static constexpr int COLS = D / 8;                // columns per lane
     static constexpr int VEC = COLS >= 4 ? 4 : COLS;  // contiguous columns per access
     static constexpr int NP = COLS / VEC;             // column groups per lane
-    static constexpr int SLOT = 3 * D + 2;            // LDS floats per staged item
     static_assert(D % 16 == 0 && RW % 8 == 0, "unsupported head dim");
 };
 
@@ -81,92 +82,148 @@ template <> struct VecT<2> {
     }
 };
 
-// One thread's share of a staged item: an 8-byte chunk or a scalar, and where it goes.
-struct Staged {
-    uint2 raw;
-    int dst;   // float index in the LDS slot, -1 = nothing
-    int mode;  // 0: 2 x f32, 1: 4 x bf16, 2: f32 scalar, 3: bf16 scalar
+#ifndef GDN_VERIFY_MIN_WAVES
+#define GDN_VERIFY_MIN_WAVES 3  // waves per SIMD the register budget must allow
+#endif
+#ifndef GDN_REVERSE_LIGHT_WAVES
+#define GDN_REVERSE_LIGHT_WAVES 1
+#endif
+#ifndef GDN_STAGE_ITEMS
+#define GDN_STAGE_ITEMS 8  // items (fold rows or nodes) staged per LDS block
+#endif
+
+// Staging of a block of items into LDS.  An item is a pending fold row (fp32 k, u, lg) or a
+// node (k, q, v, beta, g in the input dtype).  Its LDS slot holds fp32 [k | q | v-or-u |
+// scalar0 | scalar1 | pad]: scalar0 = beta or lg, scalar1 = g.  Every thread owns NCH 16-byte
+// vector chunks of the block and at most one scalar; the loads for block b+1 are issued right
+// after block b is published, so their latency hides behind a whole block of work.
+template <int D, typename TIn> struct Stager {
+    static constexpr int THREADS = Tile<D>::THREADS;
+    static constexpr int PB = GDN_STAGE_ITEMS;
+    static constexpr int NODE_CV = D * int(sizeof(TIn)) / 16;  // 16-byte chunks per node vector
+    static constexpr int FOLD_CV = D * 4 / 16;                 // 16-byte chunks per fold vector
+    static constexpr int VCH = (3 * NODE_CV > 2 * FOLD_CV) ? 3 * NODE_CV : 2 * FOLD_CV;
+    static constexpr int NCH = (PB * VCH + THREADS - 1) / THREADS;
+    static constexpr int SLOT = 3 * D + 4;
+    static_assert(2 * PB <= THREADS, "one scalar per thread");
+    uint4 v[NCH];
+    uint32_t sc;
 };
 
+// Per-workgroup context of the staging helpers.  Passed by value and unpacked into scalars
+// before any pointer is selected, so that no private (scratch) copy is ever needed.
+struct ChainCtx {
+    int L, n_items, nbeg, h, layer, T, H;
+    int64_t bank_row0, off_cnodes;
+    const float *pk, *pu, *plg;
+    const void *k, *q, *v, *beta, *gate;
+    const int32_t *img;
+};
+
+__device__ __forceinline__ const void *pick3(int i, const void *a, const void *b, const void *c) {
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(a), ub = reinterpret_cast<uintptr_t>(b),
+                    uc = reinterpret_cast<uintptr_t>(c);
+    return reinterpret_cast<const void *>(i == 0 ? ua : (i == 1 ? ub : uc));
+}
+
 template <int D, typename TIn>
-__device__ __forceinline__ Staged stage_node(const VerifyParams &P, int64_t row, int tid) {
-    // row = (layer * T + node) * H + head
-    constexpr int PER = 8 / sizeof(TIn);  // elements per 8-byte chunk
-    constexpr int CPV = D / PER;          // chunks per vector
-    Staged s;
-    s.dst = -1;
-    s.mode = 0;
-    s.raw = make_uint2(0, 0);
-    if (tid < 3 * CPV) {
-        const int vec = tid / CPV, idx = tid % CPV;
-        const void *base = vec == 0 ? P.k : (vec == 1 ? P.q : P.v);
-        const uint2 *src = reinterpret_cast<const uint2 *>(
-            static_cast<const TIn *>(base) + row * D) + idx;
-        s.raw = *src;
-        s.dst = vec * D + idx * PER;
-        s.mode = sizeof(TIn) == 2 ? 1 : 0;
-    } else if (tid < 3 * CPV + 2) {
-        const void *base = tid == 3 * CPV ? P.beta : P.gate;
-        if (sizeof(TIn) == 2) {
-            s.raw.x = static_cast<const bf16_t *>(base)[row];
-            s.mode = 3;
-        } else {
-            s.raw.x = __float_as_uint(static_cast<const float *>(base)[row]);
-            s.mode = 2;
+__device__ __forceinline__ void stage_issue(Stager<D, TIn> &st, const ChainCtx c, int it0,
+                                            int tid) {
+    using SG = Stager<D, TIn>;
+    const int it1 = min(c.n_items, it0 + SG::PB);
+#pragma unroll
+    for (int i = 0; i < SG::NCH; ++i) {
+        const int j = tid + i * SG::THREADS;
+        const int item = it0 + j / SG::VCH, ch = j % SG::VCH;
+        st.v[i] = make_uint4(0, 0, 0, 0);
+        if (j >= SG::PB * SG::VCH || item >= it1) continue;
+        if (item < c.L) {
+            if (ch < 2 * SG::FOLD_CV) {
+                const float *src = static_cast<const float *>(pick3(ch < SG::FOLD_CV ? 0 : 1, c.pk, c.pu, c.pu)) +
+                                   (c.bank_row0 + item) * D;
+                st.v[i] = reinterpret_cast<const uint4 *>(src)[ch % SG::FOLD_CV];
+            }
+        } else if (ch < 3 * SG::NODE_CV) {
+            const int node = c.img[c.off_cnodes + c.nbeg + (item - c.L)];
+            const int vec = ch / SG::NODE_CV;
+            const void *base = pick3(vec, c.k, c.q, c.v);
+            const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
+            st.v[i] = reinterpret_cast<const uint4 *>(static_cast<const TIn *>(base) + row * D)
+                [ch % SG::NODE_CV];
         }
-        s.dst = 3 * D + (tid - 3 * CPV);
     }
-    return s;
-}
-
-template <int D>
-__device__ __forceinline__ Staged stage_fold(const float *bk, const float *bu, const float *blg,
-                                             int64_t rowv, int64_t rows, int tid) {
-    // rowv = element offset of the bank row's vector, rows = index into the lg bank
-    constexpr int CPV = D / 2;
-    Staged s;
-    s.dst = -1;
-    s.mode = 0;
-    s.raw = make_uint2(0, 0);
-    if (tid < 2 * CPV) {
-        const int which = tid / CPV, idx = tid % CPV;
-        const float *base = (which == 0 ? bk : bu) + rowv;
-        s.raw = reinterpret_cast<const uint2 *>(base)[idx];
-        s.dst = (which == 0 ? 0 : 2 * D) + idx * 2;
-    } else if (tid == 2 * CPV) {
-        s.raw.x = __float_as_uint(blg[rows]);
-        s.mode = 2;
-        s.dst = 3 * D;
-    }
-    return s;
-}
-
-__device__ __forceinline__ void commit_stage(const Staged &s, float *slot) {
-    if (s.dst < 0) return;
-    switch (s.mode) {
-    case 0:
-        *reinterpret_cast<float2 *>(slot + s.dst) =
-            make_float2(__uint_as_float(s.raw.x), __uint_as_float(s.raw.y));
-        break;
-    case 1:
-        *reinterpret_cast<float4 *>(slot + s.dst) = make_float4(
-            bf16_lo(s.raw.x), bf16_hi(s.raw.x), bf16_lo(s.raw.y), bf16_hi(s.raw.y));
-        break;
-    case 2: slot[s.dst] = __uint_as_float(s.raw.x); break;
-    default: slot[s.dst] = bf16_lo(s.raw.x); break;
+    st.sc = 0;
+    if (tid < 2 * SG::PB) {
+        const int item = it0 + (tid >> 1), which = tid & 1;
+        if (item < it1) {
+            if (item < c.L) {
+                if (which == 0) st.sc = __float_as_uint(c.plg[c.bank_row0 + item]);
+            } else {
+                const int node = c.img[c.off_cnodes + c.nbeg + (item - c.L)];
+                const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
+                const void *base = pick3(which, c.beta, c.gate, c.gate);
+                st.sc = sizeof(TIn) == 2 ? uint32_t(static_cast<const bf16_t *>(base)[row]) << 16
+                                         : __float_as_uint(static_cast<const float *>(base)[row]);
+            }
+        }
     }
 }
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(Tile<D>::THREADS) void verify_chain_kernel(VerifyParams P) {
+__device__ __forceinline__ void stage_commit(const Stager<D, TIn> &st, float *buf,
+                                             const ChainCtx c, int it0, int tid) {
+    using SG = Stager<D, TIn>;
+    const int it1 = min(c.n_items, it0 + SG::PB);
+#pragma unroll
+    for (int i = 0; i < SG::NCH; ++i) {
+        const int j = tid + i * SG::THREADS;
+        const int item = it0 + j / SG::VCH, ch = j % SG::VCH;
+        if (j >= SG::PB * SG::VCH || item >= it1) continue;
+        float *slot = buf + (item - it0) * SG::SLOT;
+        const uint4 x = st.v[i];
+        if (item < c.L) {
+            if (ch < 2 * SG::FOLD_CV) {
+                float *dst = slot + (ch < SG::FOLD_CV ? 0 : 2 * D) + (ch % SG::FOLD_CV) * 4;
+                *reinterpret_cast<float4 *>(dst) = make_float4(
+                    __uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                    __uint_as_float(x.w));
+            }
+        } else if (ch < 3 * SG::NODE_CV) {
+            const int vec = ch / SG::NODE_CV, idx = ch % SG::NODE_CV;
+            if (sizeof(TIn) == 2) {
+                float *dst = slot + vec * D + idx * 8;
+                *reinterpret_cast<float4 *>(dst) =
+                    make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
+                *reinterpret_cast<float4 *>(dst + 4) =
+                    make_float4(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w));
+            } else {
+                *reinterpret_cast<float4 *>(slot + vec * D + idx * 4) = make_float4(
+                    __uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                    __uint_as_float(x.w));
+            }
+        }
+    }
+    if (tid < 2 * SG::PB) {
+        const int item = it0 + (tid >> 1);
+        if (item < it1) buf[(item - it0) * SG::SLOT + 3 * D + (tid & 1)] = __uint_as_float(st.sc);
+    }
+}
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(Tile<D>::THREADS, GDN_VERIFY_MIN_WAVES)
+void verify_chain_kernel(VerifyParams P) {
     using TL = Tile<D>;
+    using SG = Stager<D, TIn>;
     constexpr int M = TL::M, NP = TL::NP, VEC = TL::VEC;
     typedef VecT<VEC> V;
-    __shared__ __align__(16) float lds[2][TL::SLOT + 2];
+    __shared__ __align__(16) float lds[2][SG::PB * SG::SLOT];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int rg = lane >> 3, cl = lane & 7;
-    const int64_t logical = xcd_logical(blockIdx.x, P.n_blocks);
+    int64_t logical = xcd_logical(blockIdx.x, P.n_blocks);
+#if GDN_REVERSE_LIGHT_WAVES
+    if (P.chain_begin > 0) logical = P.n_blocks - 1 - logical;
+#endif
 
     int layer_rel, seq, h, chain = -1;
     if (P.fold_only) {
@@ -183,138 +240,146 @@ __global__ __launch_bounds__(Tile<D>::THREADS) void verify_chain_kernel(VerifyPa
         chain = P.chain_begin + int(rem % P.n_chains);
         seq = P.img[P.off_cseq + chain];
     }
-    const int layer = P.layer_begin + layer_rel;
+    ChainCtx c;
+    c.h = h;
+    c.T = P.T;
+    c.H = P.H;
+    c.off_cnodes = P.off_cnodes;
+    c.img = P.img;
+    c.k = P.k;
+    c.q = P.q;
+    c.v = P.v;
+    c.beta = P.beta;
+    c.gate = P.gate;
+    c.layer = P.layer_begin + layer_rel;
     const int src = P.fold_only ? -1 : P.img[P.off_csrc + chain];
-    const int nbeg = P.fold_only ? 0 : P.img[P.off_chain + chain];
+    c.nbeg = P.fold_only ? 0 : P.img[P.off_chain + chain];
     const int nend = P.fold_only ? 0 : P.img[P.off_chain + chain + 1];
     const int seq_off = P.fold_only ? 0 : P.img[P.off_seq + seq];
     const int role = P.role[seq];
-    const int L = src < 0 ? P.pending[seq] : 0;
-    const int n_items = L + (nend - nbeg);
-    if (n_items == 0) return;  // flush of a sequence with nothing pending
+    c.L = src < 0 ? P.pending[seq] : 0;
+    c.n_items = c.L + (nend - c.nbeg);
+    if (c.n_items == 0) return;  // flush of a sequence with nothing pending
 
-    const int64_t sh = (int64_t(layer) * P.S + seq) * P.H + h;  // (layer, seq, head)
+    const int64_t sh = (int64_t(c.layer) * P.S + seq) * P.H + h;  // (layer, seq, head)
     float *committed = P.state + sh * D * D;
     const float *start = src < 0 ? committed
         : P.boundary + ((int64_t(layer_rel) * P.n_boundaries + src) * P.H + h) * D * D;
-    const float *pk = P.bank_k[role], *pu = P.bank_u[role], *plg = P.bank_lg[role];
+    c.pk = P.bank_k[role];
+    c.pu = P.bank_u[role];
+    c.plg = P.bank_lg[role];
     float *wk = P.bank_k[role ^ 1], *wu = P.bank_u[role ^ 1], *wlg = P.bank_lg[role ^ 1];
-    const int64_t bank_row0 = sh * P.max_nodes;  // row index of (layer, seq, head, 0)
+    c.bank_row0 = sh * P.max_nodes;  // row index of (layer, seq, head, 0)
 
-    int rows[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) rows[m] = w * TL::RW + rg + 8 * m;
-    int cols[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) cols[p] = p * 8 * VEC + cl * VEC;
+    // Element offsets inside a d x d tile: thread part + compile-time part, so every tile
+    // access is (uniform base, one 32-bit per-thread offset, immediate).
+    const int row0 = w * TL::RW + rg;  // rows row0 + 8m
+    const int col0 = cl * VEC;         // columns col0 + 8 VEC p
+    const int toff = row0 * D + col0;
+#define GDN_T(m, p) (toff + (m) * 8 * D + (p) * 8 * VEC)
+#define GDN_ROW(m) (row0 + 8 * (m))
+#define GDN_COL(p) (col0 + (p) * 8 * VEC)
 
-    // Stage item 0 and load the start tile.
-    auto stage_item = [&](int it) -> Staged {
-        if (it < L)
-            return stage_fold<D>(pk, pu, plg, (bank_row0 + it) * D, bank_row0 + it, tid);
-        const int node = P.img[P.off_cnodes + nbeg + (it - L)];
-        return stage_node<D, TIn>(P, (int64_t(layer) * P.T + node) * P.H + h, tid);
-    };
-    Staged pending_stage = stage_item(0);
-
+    SG st;
+    stage_issue<D, TIn>(st, c, 0, tid);
     float s[M][NP][VEC];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int p = 0; p < NP; ++p) V::get(start + rows[m] * D + cols[p], s[m][p]);
+        for (int p = 0; p < NP; ++p) V::get(start + GDN_T(m, p), s[m][p]);
 
-    commit_stage(pending_stage, lds[0]);
-    __syncthreads();
-
-    for (int it = 0; it < n_items; ++it) {
-        const float *slot = lds[it & 1];
-        const bool more = it + 1 < n_items;
-        if (more) pending_stage = stage_item(it + 1);
-
-        if (it < L) {
-            // Deferred commit: S <- exp(lg) S + u k^T with a pending bank row.
-            const float gl = expf(slot[3 * D]);
-            float u[M];
+    for (int it0 = 0, blk = 0; it0 < c.n_items; it0 += SG::PB, ++blk) {
+        float *buf = lds[blk & 1];
+        stage_commit<D, TIn>(st, buf, c, it0, tid);
+        __syncthreads();
+        if (it0 + SG::PB < c.n_items) stage_issue<D, TIn>(st, c, it0 + SG::PB, tid);
+        const int it1 = min(c.n_items, it0 + SG::PB);
+        for (int it = it0; it < it1; ++it) {
+            const float *slot = buf + (it - it0) * SG::SLOT;
+            // Both item kinds end in the same rank-1 update S <- g S + u k^T:
+            //   pending fold row: g = exp(lg), u = banked residual;
+            //   node:             g = gate,    u = beta (v - g S k).
+            const bool fold = it < c.L;
+            float g, u[M], o[M], kq = 0.f;
+            int node = 0;
+            if (fold) {
+                g = expf(slot[3 * D]);
 #pragma unroll
-            for (int m = 0; m < M; ++m) u[m] = slot[2 * D + rows[m]];
+                for (int m = 0; m < M; ++m) u[m] = slot[2 * D + GDN_ROW(m)];
+            } else {
+                node = P.img[P.off_cnodes + c.nbeg + (it - c.L)];
+                float a[M], b[M];
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                float kc[VEC];
-                V::get(slot + cols[p], kc);
+                for (int m = 0; m < M; ++m) a[m] = b[m] = 0.f;
 #pragma unroll
-                for (int m = 0; m < M; ++m)
+                for (int p = 0; p < NP; ++p) {
+                    float kc[VEC], qc[VEC];
+                    V::get(slot + GDN_COL(p), kc);
+                    V::get(slot + D + GDN_COL(p), qc);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) s[m][p][e] = fmaf(u[m], kc[e], gl * s[m][p][e]);
-            }
-            if (it == L - 1) {  // the committed state is written back exactly once
+                    for (int e = 0; e < VEC; ++e) kq = fmaf(kc[e], qc[e], kq);
 #pragma unroll
-                for (int m = 0; m < M; ++m)
+                    for (int m = 0; m < M; ++m)
 #pragma unroll
-                    for (int p = 0; p < NP; ++p) V::put(committed + rows[m] * D + cols[p], s[m][p]);
-            }
-        } else {
-            const int node = P.img[P.off_cnodes + nbeg + (it - L)];
-            float a[M], b[M], kq = 0.f;
+                        for (int e = 0; e < VEC; ++e) {
+                            a[m] = fmaf(s[m][p][e], kc[e], a[m]);
+                            b[m] = fmaf(s[m][p][e], qc[e], b[m]);
+                        }
+                }
+                kq = octet_sum(kq);
 #pragma unroll
-            for (int m = 0; m < M; ++m) a[m] = b[m] = 0.f;
+                for (int m = 0; m < M; ++m) {
+                    a[m] = octet_sum(a[m]);
+                    b[m] = octet_sum(b[m]);
+                }
+                const float beta = slot[3 * D];
+                g = slot[3 * D + 1];
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                float kc[VEC], qc[VEC];
-                V::get(slot + cols[p], kc);
-                V::get(slot + D + cols[p], qc);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) kq = fmaf(kc[e], qc[e], kq);
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        a[m] = fmaf(s[m][p][e], kc[e], a[m]);
-                        b[m] = fmaf(s[m][p][e], qc[e], b[m]);
-                    }
-            }
-            kq = octet_sum(kq);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                a[m] = octet_sum(a[m]);
-                b[m] = octet_sum(b[m]);
-            }
-            const float beta = slot[3 * D], g = slot[3 * D + 1];
-            float u[M], o[M];
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                u[m] = beta * (slot[2 * D + rows[m]] - g * a[m]);
-                o[m] = fmaf(u[m], kq, g * b[m]);
+                for (int m = 0; m < M; ++m) {
+                    u[m] = beta * (slot[2 * D + GDN_ROW(m)] - g * a[m]);
+                    o[m] = fmaf(u[m], kq, g * b[m]);
+                }
             }
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 float kc[VEC];
-                V::get(slot + cols[p], kc);
+                V::get(slot + GDN_COL(p), kc);
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) s[m][p][e] = fmaf(u[m], kc[e], g * s[m][p][e]);
             }
 
+            if (fold) {
+                if (it == c.L - 1) {  // the committed state is written back exactly once
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+#pragma unroll
+                        for (int p = 0; p < NP; ++p) V::put(committed + GDN_T(m, p), s[m][p]);
+                }
+                continue;
+            }
+
             // Outputs and factors: lane cl == m of each octet writes row m's o and u.
             const int local = node - seq_off;
-            float *orow = P.out + ((int64_t(layer) * P.T + node) * P.H + h) * D;
-            float *urow = wu + (bank_row0 + local) * D;
+            float *orow = P.out + ((int64_t(c.layer) * P.T + node) * P.H + h) * D;
+            float *urow = wu + (c.bank_row0 + local) * D;
 #pragma unroll
             for (int m = 0; m < M; ++m)
                 if (cl == m) {
-                    orow[rows[m]] = o[m];
-                    urow[rows[m]] = u[m];
+                    orow[GDN_ROW(m)] = o[m];
+                    urow[GDN_ROW(m)] = u[m];
                 }
             if (w == 0 && rg == 0) {
-                float *krow = wk + (bank_row0 + local) * D;
+                float *krow = wk + (c.bank_row0 + local) * D;
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
                     float kc[VEC];
-                    V::get(slot + cols[p], kc);
-                    V::put(krow + cols[p], kc);
+                    V::get(slot + GDN_COL(p), kc);
+                    V::put(krow + GDN_COL(p), kc);
                 }
             }
-            if (tid == 0) wlg[bank_row0 + local] = logf(g);
+            if (tid == 0) wlg[c.bank_row0 + local] = logf(g);
 
             const int slot_id = P.img[P.off_store + node];
             if (slot_id >= 0) {  // boundary node: its state seeds later light chains
@@ -323,30 +388,37 @@ __global__ __launch_bounds__(Tile<D>::THREADS) void verify_chain_kernel(VerifyPa
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
-                    for (int p = 0; p < NP; ++p) V::put(dst + rows[m] * D + cols[p], s[m][p]);
+                    for (int p = 0; p < NP; ++p) V::put(dst + GDN_T(m, p), s[m][p]);
             }
         }
-
-        if (more) commit_stage(pending_stage, lds[(it + 1) & 1]);
-        __syncthreads();
     }
+#undef GDN_T
+#undef GDN_ROW
+#undef GDN_COL
 }
 
 template <int D, typename TIn>
-static gdn_status launch_verify(const VerifyParams &P, hipStream_t stream) {
+static gdn_status launch_verify(const VerifyParams &P, hipStream_t stream, hipEvent_t start,
+                                hipEvent_t stop) {
     if (P.n_blocks <= 0) return GDN_OK;
-    hipLaunchKernelGGL((verify_chain_kernel<D, TIn>), dim3(uint32_t(P.n_blocks)),
-                       dim3(Tile<D>::THREADS), 0, stream, P);
+    if (start == nullptr && stop == nullptr) {
+        hipLaunchKernelGGL((verify_chain_kernel<D, TIn>), dim3(uint32_t(P.n_blocks)),
+                           dim3(Tile<D>::THREADS), 0, stream, P);
+    } else {  // timestamps taken by the dispatch itself: no extra packets on the stream
+        hipExtLaunchKernelGGL((verify_chain_kernel<D, TIn>), dim3(uint32_t(P.n_blocks)),
+                              dim3(Tile<D>::THREADS), 0, stream, start, stop, 0, P);
+    }
     GDN_LAUNCH_CHECK("verify_chain_kernel");
     return GDN_OK;
 }
 
-static gdn_status dispatch_verify(const VerifyParams &P, int d, int dtype, hipStream_t stream) {
+static gdn_status dispatch_verify(const VerifyParams &P, int d, int dtype, hipStream_t stream,
+                                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
     if (d == 128)
-        return dtype == GDN_BF16 ? launch_verify<128, bf16_t>(P, stream)
-                                 : launch_verify<128, float>(P, stream);
-    return dtype == GDN_BF16 ? launch_verify<16, bf16_t>(P, stream)
-                             : launch_verify<16, float>(P, stream);
+        return dtype == GDN_BF16 ? launch_verify<128, bf16_t>(P, stream, start, stop)
+                                 : launch_verify<128, float>(P, stream, start, stop);
+    return dtype == GDN_BF16 ? launch_verify<16, bf16_t>(P, stream, start, stop)
+                             : launch_verify<16, float>(P, stream, start, stop);
 }
 
 static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule_inputs) {
@@ -366,6 +438,13 @@ static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule
     if (need_schedule_inputs &&
         (!a->q || !a->k || !a->v || !a->beta || !a->gate || !a->out))
         return fail(GDN_EINVAL, "verify args: null q/k/v/beta/gate/out");
+    // Tiles, rows and vectors are moved in 16-byte pieces.
+    const void *aligned[] = {a->q, a->k, a->v, a->state, a->bank_k[0], a->bank_k[1],
+                             a->bank_u[0], a->bank_u[1], a->boundary, a->out};
+    for (const void *p : aligned)
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(GDN_EINVAL, "verify args: q/k/v/state/bank/boundary/out pointers must "
+                        "be 16-byte aligned");
     return GDN_OK;
 }
 
@@ -403,7 +482,8 @@ static gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_ima
 }
 
 static gdn_status run_wave(VerifyParams P, const int32_t *host_image, const ImageView &v,
-                           const gdn_verify_args *a, int wave, hipStream_t stream) {
+                           const gdn_verify_args *a, int wave, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
     const int32_t c0 = host_image[v.off_wave + wave], c1 = host_image[v.off_wave + wave + 1];
     P.chain_begin = c0;
     P.n_chains = c1 - c0;
@@ -411,7 +491,7 @@ static gdn_status run_wave(VerifyParams P, const int32_t *host_image, const Imag
     if (P.n_blocks > 0xFFFFFFFFll)
         return fail(GDN_EINVAL, "gdn_tree_verify: %lld workgroups exceed one launch",
                     (long long)P.n_blocks);
-    return dispatch_verify(P, a->head_dim, a->in_dtype, stream);
+    return dispatch_verify(P, a->head_dim, a->in_dtype, stream, start, stop);
 }
 
 }  // namespace gdn
@@ -451,6 +531,25 @@ extern "C" gdn_status gdn_tree_verify_wave(const gdn_verify_args *a, const int32
     if (wave < 0 || wave >= v.n_waves)
         return fail(GDN_EINVAL, "gdn_tree_verify_wave: wave %d not in [0, %d)", wave, v.n_waves);
     return run_wave(P, host_image, v, a, wave, static_cast<hipStream_t>(stream));
+}
+
+extern "C" gdn_status gdn_tree_verify_wave_timed(const gdn_verify_args *a,
+                                                 const int32_t *host_image,
+                                                 const int32_t *dev_image, int32_t wave,
+                                                 void *start_event, void *stop_event,
+                                                 void *stream) {
+    clear_error();
+    VerifyParams P;
+    ImageView v;
+    gdn_status st = verify_setup(a, host_image, dev_image, P, v);
+    if (st != GDN_OK) return st;
+    if (wave < 0 || wave >= v.n_waves)
+        return fail(GDN_EINVAL, "gdn_tree_verify_wave_timed: wave %d not in [0, %d)", wave,
+                    v.n_waves);
+    if (start_event == nullptr || stop_event == nullptr)
+        return fail(GDN_EINVAL, "gdn_tree_verify_wave_timed: null event");
+    return run_wave(P, host_image, v, a, wave, static_cast<hipStream_t>(stream),
+                    static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
 }
 
 // Flush helpers used by gdn_flush (commit.hip).

@@ -44,6 +44,8 @@
  *     is the per-layer pattern of a model forward).
  *   - Shapes: head_dim d = d_k = d_v in {16, 128}; conv width 4; N_b <= 1024.
  *   - Numerics: inputs bf16 or fp32; state, factors and outputs fp32; accumulation fp32.
+ *   - Alignment: q, k, v, state, key/residual banks, boundary and out must be 16-byte
+ *     aligned (tiles and rows move in 16-byte pieces); GDN_EINVAL otherwise.
  */
 #ifndef GDN_TREE_H
 #define GDN_TREE_H
@@ -155,6 +157,14 @@ gdn_status gdn_tree_verify(const gdn_verify_args *args, const int32_t *host_imag
  * calling it for waves 0, 1, ... in order on one stream equals gdn_tree_verify. */
 gdn_status gdn_tree_verify_wave(const gdn_verify_args *args, const int32_t *host_image,
                                 const int32_t *dev_image, int32_t wave, void *stream);
+
+/* Same as gdn_tree_verify_wave, with the kernel's start and end timestamps recorded into
+ * two caller-created HIP events (hipEvent_t, passed as void *) by the dispatch itself, so
+ * timing adds no packet to the stream; hipEventElapsedTime(start, stop) then gives the
+ * kernel's duration. GDN_EINVAL if either event is NULL. */
+gdn_status gdn_tree_verify_wave_timed(const gdn_verify_args *args, const int32_t *host_image,
+                                      const int32_t *dev_image, int32_t wave, void *start_event,
+                                      void *stop_event, void *stream);
 
 /* ------------------------------------------------------------------------------------
  * Tree-aware causal depthwise conv with fused conv-window fold (DFlash README, "How it
