@@ -23,6 +23,9 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COUNTERS = os.path.join(ROOT, "profiles", "verify_chain_kernel_batched32x48_counters.json")
+VERIFY_SRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc", "verify.hip")
 METRIC = "verified tree nodes/sec per GDN layer + achieved HBM GB/s vs peak, 1 MI355X"
 
 
@@ -79,6 +82,18 @@ def fold_bytes(pending, H, d, C, n_layers):
 # ----------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample of (sequence, layer) pairs
 # ----------------------------------------------------------------------------------------
+
+def measured_traffic(config, lpc):
+    """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    or None when the verify source changed since they were taken (or another workload)."""
+    import hashlib
+    if config != 3 or lpc != 1 or not os.path.exists(COUNTERS):
+        return None
+    rec = json.load(open(COUNTERS))
+    if hashlib.sha256(open(VERIFY_SRC, "rb").read()).hexdigest() != rec["verify_source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
 
 def _oracle_pair(job):
     config, seq, layer = job
@@ -250,6 +265,7 @@ def main(argv=None):
     v_launch_bytes = acc["verify_bytes"] / max(acc["verify_launches"], 1)
     achieved = v_launch_bytes / v_launch_s / 1e9
     compulsory = args.steps * Ly * S * H * 2 * 4 * d * d
+    traffic_bytes = measured_traffic(args.config, lpc)
     result = {
         "metric": METRIC,
         "value": node_layers / wall,
@@ -273,7 +289,9 @@ def main(argv=None):
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None if traffic_bytes is None else traffic_bytes / v_launch_s / 1e9,
+            "traffic_bytes_per_launch": traffic_bytes,
             "kernel": "verify_chain_kernel<128, bf16>",
             "bytes_per_launch": v_launch_bytes, "launch_us": v_launch_s * 1e6,
         },

@@ -111,6 +111,7 @@ static gdn_status check_conv_args(const gdn_conv_args *a, bool need_inputs) {
         return fail(GDN_EINVAL, "conv args: bad channels/n_layers/layer_begin/n_seqs/max_nodes");
     if (a->in_dtype != GDN_F32 && a->in_dtype != GDN_BF16)
         return fail(GDN_EINVAL, "conv args: in_dtype %d", a->in_dtype);
+    if (a->n_seqs == 0) return GDN_OK;  // empty batch: nothing is read or written
     if (!a->conv_state || !a->bank_x[0] || !a->bank_x[1] || !a->role || !a->pending_len)
         return fail(GDN_EINVAL, "conv args: null conv_state/bank/role/pending_len");
     if (need_inputs && (!a->x || !a->weight || !a->out))

@@ -430,6 +430,7 @@ static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule
         return fail(GDN_EINVAL, "verify args: bad n_heads/n_layers/layer_begin/n_seqs/max_nodes");
     if (a->in_dtype != GDN_F32 && a->in_dtype != GDN_BF16)
         return fail(GDN_EINVAL, "verify args: in_dtype %d", a->in_dtype);
+    if (a->n_seqs == 0) return GDN_OK;  // empty batch: nothing is read or written
     if (!a->state || !a->role || !a->pending_len)
         return fail(GDN_EINVAL, "verify args: null state/role/pending_len");
     for (int i = 0; i < 2; ++i)

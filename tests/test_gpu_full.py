@@ -1,0 +1,234 @@
+"""GPU parity at full workload sizes, in the launch configuration bench.py times (one GDN
+layer per call), checked on seeded samples of (sequence, layer) pairs the oracle can compute;
+plus GPU invariants that hold at any size (sibling isolation, power-of-two scaling,
+run-to-run determinism, all bit-exact) and edge cases (single-node trees, an empty batch,
+a 1024-node tree, a 128-node chain, oversized bank rows, empty commits)."""
+import numpy as np
+import pytest
+
+from gated_deltanet_tree_amd import binding, synth, workload
+from oracle import conv as oconv
+from oracle import gdn as ogdn
+
+import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    binding.lib()
+    return torch
+
+
+def _full_case(torch, config, steps, n_samples, seed):
+    """Run `steps` verify+commit steps of a full config, then flush; check sampled pairs."""
+    c = synth.CONFIGS[config]
+    H, d, C, dtype, Ly = c["H"], c["d"], c["Cch"], c["dtype"], c["Ly"]
+    trees = workload.config_trees(config)
+    b = gh.Batch(trees, Ly, H, d, C)
+    S0, X0 = workload.host_initial_state(config, range(Ly), b.S)
+    W = workload.host_weights(config, range(Ly))
+    b.set_state(S0, X0)
+    Wd = workload._to_torch(W, dtype, "cuda")
+    rng = np.random.default_rng(seed)
+    pairs = sorted({(int(rng.integers(Ly)), int(rng.integers(b.S))) for _ in range(n_samples)})
+    committed = {p: S0[p[0], p[1]].astype(np.float64) for p in pairs}
+    window = {p: X0[p[0], p[1]].astype(np.float64) for p in pairs}
+    for step in range(steps):
+        h = workload.host_step_inputs(config, step, trees, range(Ly))
+        inp = workload.StepInputs(**{k: workload._to_torch(v, dtype, "cuda") for k, v in h.items()})
+        role_before = b.layers.role_host.copy()
+        b.step(inp, Wd)
+        torch.cuda.synchronize()
+        for (l, s) in pairs:
+            sl = slice(b.offs[s], b.offs[s + 1])
+            h64 = {k: workload.widen(v[l, sl], dtype) for k, v in h.items()}
+            gh.assert_state(gh.to_np(b.layers.state[l, s]), committed[(l, s)],
+                            what=f"committed layer {l} seq {s} step {step}")
+            assert np.array_equal(gh.to_np(b.layers.conv_state[l, s]),
+                                  window[(l, s)].astype(np.float32))
+            o, states = ogdn.verify(trees[s], committed[(l, s)], h64["q"], h64["k"], h64["v"],
+                                    h64["beta"], h64["gate"])
+            kf, uf, lg = ogdn.factors(trees[s], committed[(l, s)], h64["k"], h64["v"],
+                                      h64["beta"], h64["gate"], states)
+            gh.assert_outputs(gh.to_np(b.out[l, sl]), o, what=f"o layer {l} seq {s}")
+            y = oconv.tree_conv(trees[s], window[(l, s)], h64["x"], workload.widen(W[l], dtype))
+            gh.assert_outputs(gh.to_np(b.y[l, sl]), y, what=f"y layer {l} seq {s}")
+            gh.assert_bank_rows(b, l, s, 1 - role_before[s], range(len(trees[s])), kf, uf, lg)
+        paths = [synth.config_path(config, step, s, trees[s]) for s in range(b.S)]
+        b.commit(inp, paths, Wd)
+        for (l, s) in pairs:
+            sl = slice(b.offs[s], b.offs[s + 1])
+            h64 = {k: workload.widen(v[l, sl], dtype) for k, v in h.items()}
+            committed[(l, s)] = ogdn.replay(committed[(l, s)], h64["k"], h64["v"], h64["beta"],
+                                            h64["gate"], paths[s])
+            window[(l, s)] = oconv.commit_window(window[(l, s)], h64["x"], paths[s])
+    b.flush()
+    torch.cuda.synchronize()
+    for (l, s) in pairs:
+        gh.assert_state(gh.to_np(b.layers.state[l, s]), committed[(l, s)], what=f"flush {l} {s}")
+        assert np.array_equal(gh.to_np(b.layers.conv_state[l, s]), window[(l, s)].astype(np.float32))
+
+
+def test_batched_32x48_full_size(torch_cuda):
+    """The benchmarked workload: 32 sequences x 48 layers x 48 heads x 128, 22-node top-4
+    trees, two verify+commit steps (the second folds the first's accepted paths), flush."""
+    _full_case(torch_cuda, 3, steps=2, n_samples=6, seed=31)
+
+
+def test_wide_deep_64_node_trees_full_size(torch_cuda):
+    """64-node top-8 trees of depth up to 16, batch 8, 48 layers: long heavy chains and
+    many sibling boundaries."""
+    _full_case(torch_cuda, 4, steps=2, n_samples=4, seed=41)
+
+
+def test_pure_16_node_chains_full_size(torch_cuda):
+    """Batch 8 of 16-node pure chains (block-diffusion draft blocks), 48 layers: every
+    acceptance is in order, so commits only swap bank roles."""
+    _full_case(torch_cuda, 5, steps=2, n_samples=4, seed=51)
+
+
+# ---------------------------------------------------------------------------------------
+# invariants at the one-layer 48-head shape
+# ---------------------------------------------------------------------------------------
+
+def _one_layer(torch, h, S0, trees, dtype="bf16"):
+    b = gh.Batch(trees, 1, 48, 128, 0)
+    b.set_state(S0[None])
+    inp = workload.StepInputs(**{k: workload._to_torch(v, dtype, "cuda") for k, v in h.items()},
+                              x=None)
+    b.step(inp)
+    torch.cuda.synchronize()
+    return b
+
+
+def _config1_inputs():
+    trees = workload.config_trees(1)
+    h = workload.host_step_inputs(1, 0, trees, range(1))
+    h.pop("x")
+    S0 = synth.initial_state(1, 0, 0, 48, 128)
+    return trees, h, S0
+
+
+def test_sibling_isolation_bit_identical(torch_cuda):
+    """Changing every input of one node changes its subtree's outputs and leaves every other
+    node's output bit-identical (same schedule, same inputs elsewhere)."""
+    trees, h, S0 = _config1_inputs()
+    parent = trees[0]
+    base = gh.to_np(_one_layer(torch_cuda, h, S0, trees).out[0])
+    for m in (3, 13, 17):
+        h2 = {k: v.copy() for k, v in h.items()}
+        for k in ("q", "k", "v"):
+            h2[k][0, m] = synth.f32_to_bf16(-synth.bf16_to_f32(h2[k][0, m]))
+        h2["beta"][0, m] = synth.f32_to_bf16(0.5 * synth.bf16_to_f32(h2["beta"][0, m]))
+        out = gh.to_np(_one_layer(torch_cuda, h2, S0, trees).out[0])
+        sub = {n for n in range(len(parent)) if m in ogdn.root_path(parent, n)}
+        for n in range(len(parent)):
+            if n in sub:
+                assert not np.array_equal(out[n], base[n]), (m, n)
+            else:
+                assert np.array_equal(out[n], base[n]), (m, n)
+
+
+def test_power_of_two_scaling_bit_exact(torch_cuda):
+    """Scaling the committed state and every v by 2 scales outputs, residual vectors and
+    boundary-derived states by exactly 2 (no rounding difference anywhere)."""
+    trees, h, S0 = _config1_inputs()
+    b1 = _one_layer(torch_cuda, h, S0, trees)
+    h2 = {k: v.copy() for k, v in h.items()}
+    h2["v"] = synth.f32_to_bf16(2 * synth.bf16_to_f32(h2["v"]))
+    b2 = _one_layer(torch_cuda, h2, 2 * S0, trees)
+    assert torch_cuda.equal(b2.out, 2 * b1.out)
+    assert torch_cuda.equal(b2.layers.bank_u[1], 2 * b1.layers.bank_u[1])
+    assert torch_cuda.equal(b2.layers.bank_k[1], b1.layers.bank_k[1])
+
+
+def test_run_to_run_deterministic(torch_cuda):
+    trees, h, S0 = _config1_inputs()
+    b1 = _one_layer(torch_cuda, h, S0, trees)
+    b2 = _one_layer(torch_cuda, h, S0, trees)
+    assert torch_cuda.equal(b1.out, b2.out)
+    for name in ("bank_k", "bank_u", "bank_lg"):
+        assert torch_cuda.equal(getattr(b1.layers, name)[1], getattr(b2.layers, name)[1])
+
+
+# ---------------------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------------------
+
+def _edge_run(torch, trees, H, d, C, steps_paths, cfg_id, max_nodes=None, dtype="f32"):
+    b = gh.Batch(trees, 1, H, d, C, max_nodes=max_nodes)
+    S0 = np.stack([synth.initial_state(cfg_id, 0, s, H, d) for s in range(b.S)])
+    X0 = np.stack([synth.initial_conv_state(cfg_id, 0, s, C, 4) for s in range(b.S)])
+    W = synth.conv_weight(cfg_id, 0, C, 4, dtype)
+    b.set_state(S0[None], X0[None])
+    Wd = workload._to_torch(W[None], dtype, "cuda")
+    committed = [S0[s].astype(np.float64) for s in range(b.S)]
+    window = [X0[s].astype(np.float64) for s in range(b.S)]
+    for step, paths in enumerate(steps_paths):
+        hh = gh.tiny_inputs(trees, step, H, d, C, dtype, cfg_id)
+        h64 = gh.widen_inputs(hh, dtype)
+        inp = gh.to_device(hh, dtype)
+        b.step(inp, Wd)
+        torch.cuda.synchronize()
+        o_gpu, y_gpu = gh.to_np(b.out[0]), gh.to_np(b.y[0])
+        for s in range(b.S):
+            sl = slice(b.offs[s], b.offs[s + 1])
+            o, _ = ogdn.verify(trees[s], committed[s], h64["q"][0, sl], h64["k"][0, sl],
+                               h64["v"][0, sl], h64["beta"][0, sl], h64["gate"][0, sl],
+                               keep_states=False)
+            gh.assert_outputs(o_gpu[sl], o, what=f"o seq {s}")
+            y = oconv.tree_conv(trees[s], window[s], h64["x"][0, sl], workload.widen(W, dtype))
+            gh.assert_outputs(y_gpu[sl], y, what=f"y seq {s}")
+            committed[s] = ogdn.replay(committed[s], h64["k"][0, sl], h64["v"][0, sl],
+                                       h64["beta"][0, sl], h64["gate"][0, sl], paths[s])
+            window[s] = oconv.commit_window(window[s], h64["x"][0, sl], paths[s])
+        b.commit(inp, paths, Wd)
+    b.flush()
+    torch.cuda.synchronize()
+    gh.assert_state(gh.to_np(b.layers.state[0]), np.stack(committed), what="flush")
+    assert np.array_equal(gh.to_np(b.layers.conv_state[0]), np.stack(window).astype(np.float32))
+
+
+def test_single_node_trees(torch_cuda):
+    """Trees of one node (the root only), with accept-nothing and accept-root steps."""
+    trees = [np.array([-1], dtype=np.int32)] * 5
+    steps = [[[0], [], [0], [], [0]], [[], [0], [0], [], []], [[0]] * 5]
+    _edge_run(torch_cuda, trees, 2, 16, 8, steps, 92)
+
+
+def test_largest_tree_1024_nodes(torch_cuda):
+    """A 1024-node tree (the largest accepted), deep and bushy, d = 16."""
+    rng = np.random.default_rng(9)
+    tree = synth.make_tree(rng, 1024, 6, 40)
+    steps = [[synth.random_path(rng, tree, 30)], [synth.random_path(rng, tree, 7)]]
+    _edge_run(torch_cuda, [tree], 1, 16, 8, steps, 93)
+
+
+def test_long_chain_d128_and_padded_banks(torch_cuda):
+    """A 128-node chain at d = 128 (many staging blocks in one workgroup), next to a branched
+    tree, with bank rows padded beyond the largest tree."""
+    rng = np.random.default_rng(10)
+    trees = [np.arange(-1, 127, dtype=np.int32), synth.make_tree(rng, 40, 4, 12)]
+    steps = [[np.arange(100), synth.random_path(rng, trees[1], 5)],
+             [np.arange(3), synth.random_path(rng, trees[1], 9)]]
+    _edge_run(torch_cuda, trees, 3, 128, 16, steps, 94, max_nodes=160, dtype="bf16")
+
+
+def test_empty_batch_is_a_no_op(torch_cuda):
+    import ctypes
+    image = binding.hld_schedule([])
+    L = binding.lib()
+    va, ca = binding.VerifyArgs(), binding.ConvArgs()
+    va.n_heads, va.head_dim, va.max_nodes, va.n_layers, va.in_dtype = 1, 16, 1, 1, 0
+    ca.channels, ca.width, ca.max_nodes, ca.n_layers = 4, 4, 1, 1
+    stream = torch_cuda.cuda.current_stream().cuda_stream
+    dev = torch_cuda.zeros(32, dtype=torch_cuda.int32, device="cuda")
+    assert L.gdn_tree_verify(ctypes.byref(va), binding._ptr(image), dev.data_ptr(), stream) == 0
+    assert L.gdn_tree_conv(ctypes.byref(ca), binding._ptr(image), dev.data_ptr(), stream) == 0
+    pend = np.zeros(1, dtype=np.int32)
+    assert L.gdn_flush(ctypes.byref(va), ctypes.byref(ca), binding._ptr(pend), stream) == 0
+    torch_cuda.cuda.synchronize()
