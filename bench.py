@@ -26,6 +26,8 @@ HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COUNTERS = os.path.join(ROOT, "profiles", "verify_chain_kernel_batched32x48_counters.json")
 VERIFY_SRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc", "verify.hip")
+COUNTERS_UT = os.path.join(ROOT, "profiles", "verify_ut_kernel_batched32x48_counters.json")
+VERIFY_UT_SRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc", "verify_ut.hip")
 METRIC = "verified tree nodes/sec per GDN layer + achieved HBM GB/s vs peak, 1 MI355X"
 
 
@@ -50,6 +52,21 @@ def verify_wave_bytes(view, wave, pending, H, d, in_bytes, n_layers=1):
             if L > 0:
                 total_tile += tile + L * (8 * d + 4)
         total += H * (total_tile + len(nodes) * per_node)
+    return total * n_layers
+
+
+def ut_bytes(view, pending, H, d, in_bytes, n_layers=1):
+    """Bytes one UT verify launch moves: per (sequence, head) the committed tile read, plus its
+    write-back and the pending rows when folding; per node and head the same inputs, output
+    and banked factors as the chain path.  No boundary tiles."""
+    tile = 4 * d * d
+    per_node = (3 * d + 2) * in_bytes + 4 * d + (8 * d + 4)
+    total = 0
+    S = int(view["n_seqs"])
+    for b in range(S):
+        L = int(pending[b])
+        n_b = int(view["seq_offsets"][b + 1] - view["seq_offsets"][b])
+        total += H * (tile + (tile + L * (8 * d + 4) if L > 0 else 0) + n_b * per_node)
     return total * n_layers
 
 
@@ -83,14 +100,16 @@ def fold_bytes(pending, H, d, C, n_layers):
 # CPU baseline: the oracle as it stands, on a bounded sample of (sequence, layer) pairs
 # ----------------------------------------------------------------------------------------
 
-def measured_traffic(config, lpc):
+def measured_traffic(config, lpc, verify):
     """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     or None when the verify source changed since they were taken (or another workload)."""
     import hashlib
-    if config != 3 or lpc != 1 or not os.path.exists(COUNTERS):
+    path = COUNTERS if verify == "chain" else COUNTERS_UT
+    src = VERIFY_SRC if verify == "chain" else VERIFY_UT_SRC
+    if config != 3 or lpc != 1 or not os.path.exists(path):
         return None
-    rec = json.load(open(COUNTERS))
-    if hashlib.sha256(open(VERIFY_SRC, "rb").read()).hexdigest() != rec["verify_source_sha256"]:
+    rec = json.load(open(path))
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["verify_source_sha256"]:
         return None
     return rec["traffic_bytes_per_launch"]
 
@@ -148,6 +167,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layers-per-call", type=int, default=1)
+    ap.add_argument("--verify", choices=["chain", "ut"], default="chain",
+                    help="chain: heavy-light chains in dependency waves; ut: tree-masked UT form")
     ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--cpu-workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -217,7 +238,8 @@ def main(argv=None):
     n_waves = int(view["n_waves"])
     # Verify launches are timed by events recorded by the dispatches themselves (no extra
     # packets on the stream); one pair per (step, layer call, wave).
-    ev = [[[(binding.HipEvent(), binding.HipEvent()) for _ in range(n_waves)]
+    launches = 1 if args.verify == "ut" else n_waves
+    ev = [[[(binding.HipEvent(), binding.HipEvent()) for _ in range(launches)]
            for _ in range(len(vargs))] for _ in range(args.steps)]
 
     def step(s, timed_index):
@@ -226,6 +248,13 @@ def main(argv=None):
         pending = [int(L) for L in lay.pending_host]
         for li in range(len(vargs)):
             binding.tree_conv(cargs[li], image, dev_image)
+            if args.verify == "ut":
+                if timed_index is None:
+                    binding.tree_verify_ut(vargs[li], image, dev_image)
+                else:
+                    e0, e1 = ev[timed_index][li][0]
+                    binding.tree_verify_ut_timed(vargs[li], image, dev_image, e0, e1)
+                continue
             for w in range(n_waves):
                 if timed_index is None:
                     binding.tree_verify_wave(vargs[li], image, dev_image, w)
@@ -237,9 +266,12 @@ def main(argv=None):
         binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs))
         if timed_index is not None:  # byte accounting after the launches, off the GPU's path
             calls = len(vargs)
-            acc["verify_bytes"] += calls * sum(verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc)
-                                               for w in range(n_waves))
-            acc["verify_launches"] += calls * n_waves
+            if args.verify == "ut":
+                acc["verify_bytes"] += calls * ut_bytes(view, pending, H, d, in_bytes, lpc)
+            else:
+                acc["verify_bytes"] += calls * sum(
+                    verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc) for w in range(n_waves))
+            acc["verify_launches"] += calls * launches
             acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
             acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly)
 
@@ -265,7 +297,7 @@ def main(argv=None):
     v_launch_bytes = acc["verify_bytes"] / max(acc["verify_launches"], 1)
     achieved = v_launch_bytes / v_launch_s / 1e9
     compulsory = args.steps * Ly * S * H * 2 * 4 * d * d
-    traffic_bytes = measured_traffic(args.config, lpc)
+    traffic_bytes = measured_traffic(args.config, lpc, args.verify)
     result = {
         "metric": METRIC,
         "value": node_layers / wall,
@@ -286,13 +318,15 @@ def main(argv=None):
             "sequences": S, "layers": Ly, "heads": H, "head_dim": d, "tree_nodes": T,
             "chains": int(view["n_chains"]), "waves": int(view["n_waves"]),
             "boundary_nodes": int(view["n_boundaries"]), "layers_per_call": lpc,
+            "verify": args.verify,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": None if traffic_bytes is None else traffic_bytes / v_launch_s / 1e9,
             "traffic_bytes_per_launch": traffic_bytes,
-            "kernel": "verify_chain_kernel<128, bf16>",
+            "kernel": ("verify_chain_kernel" if args.verify == "chain" else "verify_ut_kernel")
+                      + "<128, bf16>",
             "bytes_per_launch": v_launch_bytes, "launch_us": v_launch_s * 1e6,
         },
         "cpu_baseline": cpu,

@@ -21,7 +21,8 @@ STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_ETREE", -3: "GDN_EPATH",
           -4: "GDN_ECAPACITY", -5: "GDN_EDEVICE"}
 EXPORTS = [
     "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_verify_workspace_bytes",
-    "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed", "gdn_tree_conv",
+    "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed",
+    "gdn_tree_verify_ut", "gdn_tree_verify_ut_timed", "gdn_tree_conv",
     "gdn_commit_path",
     "gdn_compact_factors", "gdn_flush",
 ]
@@ -86,6 +87,10 @@ def lib() -> ctypes.CDLL:
     L.gdn_tree_verify_wave_timed.restype = _I32
     L.gdn_tree_verify_wave_timed.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _I32, _P, _P,
                                              _P]
+    L.gdn_tree_verify_ut.restype = _I32
+    L.gdn_tree_verify_ut.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
+    L.gdn_tree_verify_ut_timed.restype = _I32
+    L.gdn_tree_verify_ut_timed.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P, _P, _P]
     L.gdn_tree_conv.restype = _I32
     L.gdn_tree_conv.argtypes = [ctypes.POINTER(ConvArgs), _I32P, _P, _P]
     L.gdn_commit_path.restype = _I32
@@ -281,6 +286,18 @@ def tree_verify_wave_timed(args: VerifyArgs, image: np.ndarray, dev_image, wave:
     _check(lib().gdn_tree_verify_wave_timed(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
                                             start.handle, stop.handle, _stream(stream)),
            "gdn_tree_verify_wave_timed")
+
+
+def tree_verify_ut(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
+    _check(lib().gdn_tree_verify_ut(ctypes.byref(args), _ptr(image), _dev(dev_image),
+                                    _stream(stream)), "gdn_tree_verify_ut")
+
+
+def tree_verify_ut_timed(args: VerifyArgs, image: np.ndarray, dev_image, start: "HipEvent",
+                         stop: "HipEvent", stream=None):
+    _check(lib().gdn_tree_verify_ut_timed(ctypes.byref(args), _ptr(image), _dev(dev_image),
+                                          start.handle, stop.handle, _stream(stream)),
+           "gdn_tree_verify_ut_timed")
 
 
 class HipEvent:

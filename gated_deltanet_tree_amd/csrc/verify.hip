@@ -30,187 +30,13 @@
 // in the other slot afterwards, so their latency hides behind a node of work.
 #include <hip/hip_ext.h>
 
-#include "gdn_device.h"
+#include "verify_common.h"
 
 namespace gdn {
 
-struct VerifyParams {
-    const void *q, *k, *v, *beta, *gate;
-    float *state;
-    float *bank_k[2], *bank_u[2], *bank_lg[2];
-    const int32_t *role, *pending;
-    float *boundary;
-    float *out;
-    const int32_t *img;
-    int64_t off_seq, off_chain, off_cnodes, off_cseq, off_csrc, off_store;
-    int32_t S, H, T, max_nodes, n_boundaries, layer_begin;
-    int32_t chain_begin, n_chains;  // chains of this wave
-    int64_t n_blocks;
-    int32_t fold_only;  // flush: one workgroup per (layer, seq, head), fold + store only
-};
-
-template <int D> struct Tile {
-    static constexpr int RW = D >= 32 ? 32 : D;       // rows per wave
-    static constexpr int NW = D / RW;                 // waves per workgroup
-    static constexpr int THREADS = 64 * NW;
-    static constexpr int M = RW / 8;                  // rows per lane
-    static constexpr int COLS = D / 8;                // columns per lane
-    static constexpr int VEC = COLS >= 4 ? 4 : COLS;  // contiguous columns per access
-    static constexpr int NP = COLS / VEC;             // column groups per lane
-    static_assert(D % 16 == 0 && RW % 8 == 0, "unsupported head dim");
-};
-
-template <int VEC> struct VecT;
-template <> struct VecT<4> {
-    typedef float4 type;
-    static __device__ __forceinline__ void get(const float *p, float *o) {
-        float4 t = *reinterpret_cast<const float4 *>(p);
-        o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
-    }
-    static __device__ __forceinline__ void put(float *p, const float *o) {
-        *reinterpret_cast<float4 *>(p) = make_float4(o[0], o[1], o[2], o[3]);
-    }
-};
-template <> struct VecT<2> {
-    typedef float2 type;
-    static __device__ __forceinline__ void get(const float *p, float *o) {
-        float2 t = *reinterpret_cast<const float2 *>(p);
-        o[0] = t.x; o[1] = t.y;
-    }
-    static __device__ __forceinline__ void put(float *p, const float *o) {
-        *reinterpret_cast<float2 *>(p) = make_float2(o[0], o[1]);
-    }
-};
-
-#ifndef GDN_VERIFY_MIN_WAVES
-#define GDN_VERIFY_MIN_WAVES 3  // waves per SIMD the register budget must allow
-#endif
-#ifndef GDN_REVERSE_LIGHT_WAVES
-#define GDN_REVERSE_LIGHT_WAVES 1
-#endif
-#ifndef GDN_STAGE_ITEMS
-#define GDN_STAGE_ITEMS 8  // items (fold rows or nodes) staged per LDS block
-#endif
-
-// Staging of a block of items into LDS.  An item is a pending fold row (fp32 k, u, lg) or a
-// node (k, q, v, beta, g in the input dtype).  Its LDS slot holds fp32 [k | q | v-or-u |
-// scalar0 | scalar1 | pad]: scalar0 = beta or lg, scalar1 = g.  Every thread owns NCH 16-byte
-// vector chunks of the block and at most one scalar; the loads for block b+1 are issued right
-// after block b is published, so their latency hides behind a whole block of work.
-template <int D, typename TIn> struct Stager {
-    static constexpr int THREADS = Tile<D>::THREADS;
-    static constexpr int PB = GDN_STAGE_ITEMS;
-    static constexpr int NODE_CV = D * int(sizeof(TIn)) / 16;  // 16-byte chunks per node vector
-    static constexpr int FOLD_CV = D * 4 / 16;                 // 16-byte chunks per fold vector
-    static constexpr int VCH = (3 * NODE_CV > 2 * FOLD_CV) ? 3 * NODE_CV : 2 * FOLD_CV;
-    static constexpr int NCH = (PB * VCH + THREADS - 1) / THREADS;
-    static constexpr int SLOT = 3 * D + 4;
-    static_assert(2 * PB <= THREADS, "one scalar per thread");
-    uint4 v[NCH];
-    uint32_t sc;
-};
-
-// Per-workgroup context of the staging helpers.  Passed by value and unpacked into scalars
-// before any pointer is selected, so that no private (scratch) copy is ever needed.
-struct ChainCtx {
-    int L, n_items, nbeg, h, layer, T, H;
-    int64_t bank_row0, off_cnodes;
-    const float *pk, *pu, *plg;
-    const void *k, *q, *v, *beta, *gate;
-    const int32_t *img;
-};
-
-__device__ __forceinline__ const void *pick3(int i, const void *a, const void *b, const void *c) {
-    const uintptr_t ua = reinterpret_cast<uintptr_t>(a), ub = reinterpret_cast<uintptr_t>(b),
-                    uc = reinterpret_cast<uintptr_t>(c);
-    return reinterpret_cast<const void *>(i == 0 ? ua : (i == 1 ? ub : uc));
-}
-
+// fp32 inputs need twice the staging registers; they get a 2-wave budget to avoid spills.
 template <int D, typename TIn>
-__device__ __forceinline__ void stage_issue(Stager<D, TIn> &st, const ChainCtx c, int it0,
-                                            int tid) {
-    using SG = Stager<D, TIn>;
-    const int it1 = min(c.n_items, it0 + SG::PB);
-#pragma unroll
-    for (int i = 0; i < SG::NCH; ++i) {
-        const int j = tid + i * SG::THREADS;
-        const int item = it0 + j / SG::VCH, ch = j % SG::VCH;
-        st.v[i] = make_uint4(0, 0, 0, 0);
-        if (j >= SG::PB * SG::VCH || item >= it1) continue;
-        if (item < c.L) {
-            if (ch < 2 * SG::FOLD_CV) {
-                const float *src = static_cast<const float *>(pick3(ch < SG::FOLD_CV ? 0 : 1, c.pk, c.pu, c.pu)) +
-                                   (c.bank_row0 + item) * D;
-                st.v[i] = reinterpret_cast<const uint4 *>(src)[ch % SG::FOLD_CV];
-            }
-        } else if (ch < 3 * SG::NODE_CV) {
-            const int node = c.img[c.off_cnodes + c.nbeg + (item - c.L)];
-            const int vec = ch / SG::NODE_CV;
-            const void *base = pick3(vec, c.k, c.q, c.v);
-            const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
-            st.v[i] = reinterpret_cast<const uint4 *>(static_cast<const TIn *>(base) + row * D)
-                [ch % SG::NODE_CV];
-        }
-    }
-    st.sc = 0;
-    if (tid < 2 * SG::PB) {
-        const int item = it0 + (tid >> 1), which = tid & 1;
-        if (item < it1) {
-            if (item < c.L) {
-                if (which == 0) st.sc = __float_as_uint(c.plg[c.bank_row0 + item]);
-            } else {
-                const int node = c.img[c.off_cnodes + c.nbeg + (item - c.L)];
-                const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
-                const void *base = pick3(which, c.beta, c.gate, c.gate);
-                st.sc = sizeof(TIn) == 2 ? uint32_t(static_cast<const bf16_t *>(base)[row]) << 16
-                                         : __float_as_uint(static_cast<const float *>(base)[row]);
-            }
-        }
-    }
-}
-
-template <int D, typename TIn>
-__device__ __forceinline__ void stage_commit(const Stager<D, TIn> &st, float *buf,
-                                             const ChainCtx c, int it0, int tid) {
-    using SG = Stager<D, TIn>;
-    const int it1 = min(c.n_items, it0 + SG::PB);
-#pragma unroll
-    for (int i = 0; i < SG::NCH; ++i) {
-        const int j = tid + i * SG::THREADS;
-        const int item = it0 + j / SG::VCH, ch = j % SG::VCH;
-        if (j >= SG::PB * SG::VCH || item >= it1) continue;
-        float *slot = buf + (item - it0) * SG::SLOT;
-        const uint4 x = st.v[i];
-        if (item < c.L) {
-            if (ch < 2 * SG::FOLD_CV) {
-                float *dst = slot + (ch < SG::FOLD_CV ? 0 : 2 * D) + (ch % SG::FOLD_CV) * 4;
-                *reinterpret_cast<float4 *>(dst) = make_float4(
-                    __uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
-                    __uint_as_float(x.w));
-            }
-        } else if (ch < 3 * SG::NODE_CV) {
-            const int vec = ch / SG::NODE_CV, idx = ch % SG::NODE_CV;
-            if (sizeof(TIn) == 2) {
-                float *dst = slot + vec * D + idx * 8;
-                *reinterpret_cast<float4 *>(dst) =
-                    make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
-                *reinterpret_cast<float4 *>(dst + 4) =
-                    make_float4(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w));
-            } else {
-                *reinterpret_cast<float4 *>(slot + vec * D + idx * 4) = make_float4(
-                    __uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
-                    __uint_as_float(x.w));
-            }
-        }
-    }
-    if (tid < 2 * SG::PB) {
-        const int item = it0 + (tid >> 1);
-        if (item < it1) buf[(item - it0) * SG::SLOT + 3 * D + (tid & 1)] = __uint_as_float(st.sc);
-    }
-}
-
-template <int D, typename TIn>
-__global__ __launch_bounds__(Tile<D>::THREADS, GDN_VERIFY_MIN_WAVES)
+__global__ __launch_bounds__(Tile<D>::THREADS, sizeof(TIn) == 2 ? GDN_VERIFY_MIN_WAVES : 2)
 void verify_chain_kernel(VerifyParams P) {
     using TL = Tile<D>;
     using SG = Stager<D, TIn>;
@@ -241,6 +67,7 @@ void verify_chain_kernel(VerifyParams P) {
         seq = P.img[P.off_cseq + chain];
     }
     ChainCtx c;
+    c.node_base = -1;
     c.h = h;
     c.T = P.T;
     c.H = P.H;
@@ -281,7 +108,7 @@ void verify_chain_kernel(VerifyParams P) {
 #define GDN_COL(p) (col0 + (p) * 8 * VEC)
 
     SG st;
-    stage_issue<D, TIn>(st, c, 0, tid);
+    stage_issue(st, c, 0, tid);
     float s[M][NP][VEC];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -290,9 +117,9 @@ void verify_chain_kernel(VerifyParams P) {
 
     for (int it0 = 0, blk = 0; it0 < c.n_items; it0 += SG::PB, ++blk) {
         float *buf = lds[blk & 1];
-        stage_commit<D, TIn>(st, buf, c, it0, tid);
+        stage_commit(st, buf, c, it0, tid);
         __syncthreads();
-        if (it0 + SG::PB < c.n_items) stage_issue<D, TIn>(st, c, it0 + SG::PB, tid);
+        if (it0 + SG::PB < c.n_items) stage_issue(st, c, it0 + SG::PB, tid);
         const int it1 = min(c.n_items, it0 + SG::PB);
         for (int it = it0; it < it1; ++it) {
             const float *slot = buf + (it - it0) * SG::SLOT;
@@ -449,8 +276,9 @@ static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule
     return GDN_OK;
 }
 
-static gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
-                               const int32_t *dev_image, VerifyParams &P, ImageView &v) {
+gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
+                        const int32_t *dev_image, VerifyParams &P, ImageView &v,
+                        bool need_boundary) {
     gdn_status st = check_verify_args(a, true);
     if (st != GDN_OK) return st;
     if (!image_ok(host_image) || dev_image == nullptr)
@@ -462,7 +290,7 @@ static gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_ima
     if (v.max_tree > a->max_nodes)
         return fail(GDN_ECAPACITY, "gdn_tree_verify: max_nodes %d < largest tree %d",
                     a->max_nodes, v.max_tree);
-    if (v.n_boundaries > 0 && a->boundary == nullptr)
+    if (need_boundary && v.n_boundaries > 0 && a->boundary == nullptr)
         return fail(GDN_EINVAL, "gdn_tree_verify: schedule has %d boundary nodes but no "
                     "boundary workspace", v.n_boundaries);
     P = VerifyParams{};
@@ -512,7 +340,7 @@ extern "C" gdn_status gdn_tree_verify(const gdn_verify_args *a, const int32_t *h
     clear_error();
     VerifyParams P;
     ImageView v;
-    gdn_status st = verify_setup(a, host_image, dev_image, P, v);
+    gdn_status st = verify_setup(a, host_image, dev_image, P, v, true);
     if (st != GDN_OK || a->n_seqs == 0) return st;
     for (int w = 0; w < v.n_waves; ++w) {
         st = run_wave(P, host_image, v, a, w, static_cast<hipStream_t>(stream));
@@ -527,7 +355,7 @@ extern "C" gdn_status gdn_tree_verify_wave(const gdn_verify_args *a, const int32
     clear_error();
     VerifyParams P;
     ImageView v;
-    gdn_status st = verify_setup(a, host_image, dev_image, P, v);
+    gdn_status st = verify_setup(a, host_image, dev_image, P, v, true);
     if (st != GDN_OK) return st;
     if (wave < 0 || wave >= v.n_waves)
         return fail(GDN_EINVAL, "gdn_tree_verify_wave: wave %d not in [0, %d)", wave, v.n_waves);
@@ -542,7 +370,7 @@ extern "C" gdn_status gdn_tree_verify_wave_timed(const gdn_verify_args *a,
     clear_error();
     VerifyParams P;
     ImageView v;
-    gdn_status st = verify_setup(a, host_image, dev_image, P, v);
+    gdn_status st = verify_setup(a, host_image, dev_image, P, v, true);
     if (st != GDN_OK) return st;
     if (wave < 0 || wave >= v.n_waves)
         return fail(GDN_EINVAL, "gdn_tree_verify_wave_timed: wave %d not in [0, %d)", wave,

@@ -166,6 +166,26 @@ gdn_status gdn_tree_verify_wave_timed(const gdn_verify_args *args, const int32_t
                                       const int32_t *dev_image, int32_t wave, void *start_event,
                                       void *stop_event, void *stream);
 
+/* Tree-masked UT verify (SpecLA guide, mechanism 1: the topology-mask / UT decomposition
+ * form of the same verify). Same arguments, results and bank/fold contract as
+ * gdn_tree_verify, computed in one launch per call with no boundary tiles: unrolling the
+ * recurrence down a node's root path gives
+ *   u_n = beta_n (v_n - G_n S0 k_n - sum_{j strict ancestor} E(n,j) (k_n.k_j) u_j)
+ *   out[n] = G_n S0 q_n + sum_{j ancestor or n} E(n,j) (q_n.k_j) u_j
+ * with G_n the product of the gates on n's root path and E(n,j) the product of the gates
+ * strictly below j down to n; S0 is the committed state after the deferred fold.
+ * `boundary` is not used (may be NULL). A tree must fit the kernel's 64 KiB LDS budget
+ * (about 64 nodes at d = 128 with bf16 inputs, 50 with fp32); larger trees give GDN_EINVAL
+ * and should use gdn_tree_verify. */
+gdn_status gdn_tree_verify_ut(const gdn_verify_args *args, const int32_t *host_image,
+                              const int32_t *dev_image, void *stream);
+
+/* gdn_tree_verify_ut with dispatch-recorded start/stop HIP events (see
+ * gdn_tree_verify_wave_timed). */
+gdn_status gdn_tree_verify_ut_timed(const gdn_verify_args *args, const int32_t *host_image,
+                                    const int32_t *dev_image, void *start_event,
+                                    void *stop_event, void *stream);
+
 /* ------------------------------------------------------------------------------------
  * Tree-aware causal depthwise conv with fused conv-window fold (DFlash README, "How it
  * works", tree-aware conv gather; SpecLA guide, mechanisms 1, 3 and 4).

@@ -49,8 +49,11 @@ def to_np(t):
 class Batch:
     """One batch of trees on the device with its schedule and layer buffers."""
 
-    def __init__(self, trees, n_layers, H, d, C, max_nodes=None, device="cuda"):
+    def __init__(self, trees, n_layers, H, d, C, max_nodes=None, device="cuda", mode="chain"):
+        """mode: "chain" = heavy-light chains in dependency waves (gdn_tree_verify),
+        "ut" = tree-masked UT form in one launch (gdn_tree_verify_ut)."""
         import torch
+        self.mode = mode
         self.trees = [np.asarray(t, dtype=np.int32) for t in trees]
         self.image = binding.hld_schedule(self.trees)
         self.view = binding.schedule_view(self.image)
@@ -87,7 +90,10 @@ class Batch:
         for layer in range(self.Ly):
             if self.C:
                 binding.tree_conv(self.cargs(inp, layer, weight), self.image, self.dev_image)
-            binding.tree_verify(self.vargs(inp, layer), self.image, self.dev_image)
+            if self.mode == "ut":
+                binding.tree_verify_ut(self.vargs(inp, layer), self.image, self.dev_image)
+            else:
+                binding.tree_verify(self.vargs(inp, layer), self.image, self.dev_image)
 
     def commit(self, inp, paths, weight=None):
         va = binding.verify_args(self.image, self.layers, None, None, None, None, None, None,

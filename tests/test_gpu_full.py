@@ -23,12 +23,15 @@ def torch_cuda():
     return torch
 
 
-def _full_case(torch, config, steps, n_samples, seed):
+MODES = ["chain", "ut"]
+
+
+def _full_case(torch, config, steps, n_samples, seed, mode="chain"):
     """Run `steps` verify+commit steps of a full config, then flush; check sampled pairs."""
     c = synth.CONFIGS[config]
     H, d, C, dtype, Ly = c["H"], c["d"], c["Cch"], c["dtype"], c["Ly"]
     trees = workload.config_trees(config)
-    b = gh.Batch(trees, Ly, H, d, C)
+    b = gh.Batch(trees, Ly, H, d, C, mode=mode)
     S0, X0 = workload.host_initial_state(config, range(Ly), b.S)
     W = workload.host_weights(config, range(Ly))
     b.set_state(S0, X0)
@@ -73,30 +76,33 @@ def _full_case(torch, config, steps, n_samples, seed):
         assert np.array_equal(gh.to_np(b.layers.conv_state[l, s]), window[(l, s)].astype(np.float32))
 
 
-def test_batched_32x48_full_size(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_batched_32x48_full_size(torch_cuda, mode):
     """The benchmarked workload: 32 sequences x 48 layers x 48 heads x 128, 22-node top-4
     trees, two verify+commit steps (the second folds the first's accepted paths), flush."""
-    _full_case(torch_cuda, 3, steps=2, n_samples=6, seed=31)
+    _full_case(torch_cuda, 3, steps=2, n_samples=6, seed=31, mode=mode)
 
 
-def test_wide_deep_64_node_trees_full_size(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_wide_deep_64_node_trees_full_size(torch_cuda, mode):
     """64-node top-8 trees of depth up to 16, batch 8, 48 layers: long heavy chains and
     many sibling boundaries."""
-    _full_case(torch_cuda, 4, steps=2, n_samples=4, seed=41)
+    _full_case(torch_cuda, 4, steps=2, n_samples=4, seed=41, mode=mode)
 
 
-def test_pure_16_node_chains_full_size(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_pure_16_node_chains_full_size(torch_cuda, mode):
     """Batch 8 of 16-node pure chains (block-diffusion draft blocks), 48 layers: every
     acceptance is in order, so commits only swap bank roles."""
-    _full_case(torch_cuda, 5, steps=2, n_samples=4, seed=51)
+    _full_case(torch_cuda, 5, steps=2, n_samples=4, seed=51, mode=mode)
 
 
 # ---------------------------------------------------------------------------------------
 # invariants at the one-layer 48-head shape
 # ---------------------------------------------------------------------------------------
 
-def _one_layer(torch, h, S0, trees, dtype="bf16"):
-    b = gh.Batch(trees, 1, 48, 128, 0)
+def _one_layer(torch, h, S0, trees, dtype="bf16", mode="chain"):
+    b = gh.Batch(trees, 1, 48, 128, 0, mode=mode)
     b.set_state(S0[None])
     inp = workload.StepInputs(**{k: workload._to_torch(v, dtype, "cuda") for k, v in h.items()},
                               x=None)
@@ -113,18 +119,19 @@ def _config1_inputs():
     return trees, h, S0
 
 
-def test_sibling_isolation_bit_identical(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_sibling_isolation_bit_identical(torch_cuda, mode):
     """Changing every input of one node changes its subtree's outputs and leaves every other
     node's output bit-identical (same schedule, same inputs elsewhere)."""
     trees, h, S0 = _config1_inputs()
     parent = trees[0]
-    base = gh.to_np(_one_layer(torch_cuda, h, S0, trees).out[0])
+    base = gh.to_np(_one_layer(torch_cuda, h, S0, trees, mode=mode).out[0])
     for m in (3, 13, 17):
         h2 = {k: v.copy() for k, v in h.items()}
         for k in ("q", "k", "v"):
             h2[k][0, m] = synth.f32_to_bf16(-synth.bf16_to_f32(h2[k][0, m]))
         h2["beta"][0, m] = synth.f32_to_bf16(0.5 * synth.bf16_to_f32(h2["beta"][0, m]))
-        out = gh.to_np(_one_layer(torch_cuda, h2, S0, trees).out[0])
+        out = gh.to_np(_one_layer(torch_cuda, h2, S0, trees, mode=mode).out[0])
         sub = {n for n in range(len(parent)) if m in ogdn.root_path(parent, n)}
         for n in range(len(parent)):
             if n in sub:
@@ -133,23 +140,25 @@ def test_sibling_isolation_bit_identical(torch_cuda):
                 assert np.array_equal(out[n], base[n]), (m, n)
 
 
-def test_power_of_two_scaling_bit_exact(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_power_of_two_scaling_bit_exact(torch_cuda, mode):
     """Scaling the committed state and every v by 2 scales outputs, residual vectors and
     boundary-derived states by exactly 2 (no rounding difference anywhere)."""
     trees, h, S0 = _config1_inputs()
-    b1 = _one_layer(torch_cuda, h, S0, trees)
+    b1 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
     h2 = {k: v.copy() for k, v in h.items()}
     h2["v"] = synth.f32_to_bf16(2 * synth.bf16_to_f32(h2["v"]))
-    b2 = _one_layer(torch_cuda, h2, 2 * S0, trees)
+    b2 = _one_layer(torch_cuda, h2, 2 * S0, trees, mode=mode)
     assert torch_cuda.equal(b2.out, 2 * b1.out)
     assert torch_cuda.equal(b2.layers.bank_u[1], 2 * b1.layers.bank_u[1])
     assert torch_cuda.equal(b2.layers.bank_k[1], b1.layers.bank_k[1])
 
 
-def test_run_to_run_deterministic(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_run_to_run_deterministic(torch_cuda, mode):
     trees, h, S0 = _config1_inputs()
-    b1 = _one_layer(torch_cuda, h, S0, trees)
-    b2 = _one_layer(torch_cuda, h, S0, trees)
+    b1 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
+    b2 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
     assert torch_cuda.equal(b1.out, b2.out)
     for name in ("bank_k", "bank_u", "bank_lg"):
         assert torch_cuda.equal(getattr(b1.layers, name)[1], getattr(b2.layers, name)[1])
@@ -159,8 +168,9 @@ def test_run_to_run_deterministic(torch_cuda):
 # edge cases
 # ---------------------------------------------------------------------------------------
 
-def _edge_run(torch, trees, H, d, C, steps_paths, cfg_id, max_nodes=None, dtype="f32"):
-    b = gh.Batch(trees, 1, H, d, C, max_nodes=max_nodes)
+def _edge_run(torch, trees, H, d, C, steps_paths, cfg_id, max_nodes=None, dtype="f32",
+              mode="chain"):
+    b = gh.Batch(trees, 1, H, d, C, max_nodes=max_nodes, mode=mode)
     S0 = np.stack([synth.initial_state(cfg_id, 0, s, H, d) for s in range(b.S)])
     X0 = np.stack([synth.initial_conv_state(cfg_id, 0, s, C, 4) for s in range(b.S)])
     W = synth.conv_weight(cfg_id, 0, C, 4, dtype)
@@ -193,11 +203,12 @@ def _edge_run(torch, trees, H, d, C, steps_paths, cfg_id, max_nodes=None, dtype=
     assert np.array_equal(gh.to_np(b.layers.conv_state[0]), np.stack(window).astype(np.float32))
 
 
-def test_single_node_trees(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_single_node_trees(torch_cuda, mode):
     """Trees of one node (the root only), with accept-nothing and accept-root steps."""
     trees = [np.array([-1], dtype=np.int32)] * 5
     steps = [[[0], [], [0], [], [0]], [[], [0], [0], [], []], [[0]] * 5]
-    _edge_run(torch_cuda, trees, 2, 16, 8, steps, 92)
+    _edge_run(torch_cuda, trees, 2, 16, 8, steps, 92, mode=mode)
 
 
 def test_largest_tree_1024_nodes(torch_cuda):
@@ -216,6 +227,33 @@ def test_long_chain_d128_and_padded_banks(torch_cuda):
     steps = [[np.arange(100), synth.random_path(rng, trees[1], 5)],
              [np.arange(3), synth.random_path(rng, trees[1], 9)]]
     _edge_run(torch_cuda, trees, 3, 128, 16, steps, 94, max_nodes=160, dtype="bf16")
+
+
+def test_ut_rejects_trees_beyond_its_lds_budget(torch_cuda):
+    """The UT path keeps a whole tree's keys and residual vectors in 64 KiB of LDS; a
+    128-node tree at d = 128 does not fit and is refused before any launch."""
+    trees = [np.arange(-1, 127, dtype=np.int32)]
+    b = gh.Batch(trees, 1, 2, 128, 0, mode="ut")
+    h = gh.tiny_inputs(trees, 0, 2, 128, 4, "bf16", 95)
+    h.pop("x")
+    inp = workload.StepInputs(**{k: workload._to_torch(v, "bf16", "cuda") for k, v in h.items()},
+                              x=None)
+    before = b.out.clone()
+    with pytest.raises(binding.GdnError) as e:
+        binding.tree_verify_ut(b.vargs(inp, 0), b.image, b.dev_image)
+    assert e.value.status == -1 and "LDS" in str(e.value)
+    torch_cuda.cuda.synchronize()
+    assert torch_cuda.equal(before, b.out)
+
+
+def test_ut_largest_fitting_tree_64_nodes_d128(torch_cuda):
+    """64-node top-8 trees of depth <= 16 at d = 128, bf16 (close to the UT path's LDS
+    budget), next to a 16-node chain."""
+    rng = np.random.default_rng(12)
+    trees = [synth.make_tree(rng, 64, 8, 16), np.arange(-1, 15, dtype=np.int32)]
+    steps = [[synth.random_path(rng, trees[0], 12), np.arange(10)],
+             [synth.random_path(rng, trees[0], 3), np.arange(16)]]
+    _edge_run(torch_cuda, trees, 2, 128, 16, steps, 96, dtype="bf16", mode="ut")
 
 
 def test_empty_batch_is_a_no_op(torch_cuda):

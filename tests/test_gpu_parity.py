@@ -44,8 +44,11 @@ def _check_step(b: gh.Batch, h64, S0s, X0s, W, layer=0, write_bank=None, conv=Tr
     return refs
 
 
-def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0):
-    b = gh.Batch(trees, 1, H, d, C)
+MODES = ["chain", "ut"]
+
+
+def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0, mode="chain"):
+    b = gh.Batch(trees, 1, H, d, C, mode=mode)
     S0 = np.stack([synth.initial_state(cfg_id, 0, s, H, d) for s in range(b.S)])[None]
     X0 = np.stack([synth.initial_conv_state(cfg_id, 0, s, C, 4) for s in range(b.S)])[None]
     W = synth.conv_weight(cfg_id, 0, C, 4, dtype)[None]
@@ -106,12 +109,13 @@ def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d,
     assert torch_cuda.equal(before[1], b.layers.conv_state)
 
 
-def test_tiny_tree_and_chain(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_tree_and_chain(torch_cuda, mode):
     """Config 0: the 7-node tree [-1,0,0,1,1,2,3] and an 8-node chain, batched, fp32, d = 16.
     Step 0 accepts the deepest leaves ([0,1,3,6] is branched -> compaction; the chain is in
     order -> role swap); step 1 accepts [0,2,5] and [0,1,2]; then flush."""
     trees = [synth.TINY_TREE, synth.TINY_CHAIN]
-    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees)
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, mode=mode)
     paths0 = [synth.deepest_leaf_path(t) for t in trees]
     assert list(paths0[0]) == [0, 1, 3, 6] and list(paths0[1]) == list(range(8))
     _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, [[0, 2, 5], [0, 1, 2]], [[0], []]],
@@ -124,12 +128,13 @@ def _all_trees(N):
         yield np.array((-1,) + choice, dtype=np.int32)
 
 
-def test_every_small_tree_batched(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_every_small_tree_batched(torch_cuda, mode):
     """All 154 labelled trees with N <= 6 in one batch (d = 16, 2 heads, fp32): three steps of
     verify + commit with seeded random paths of every length (0 included), then flush."""
     trees = [t for N in range(1, 7) for t in _all_trees(N)]
     assert len(trees) == 154
-    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=2, C=8, cfg_id=90)
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=2, C=8, cfg_id=90, mode=mode)
     rng = np.random.default_rng(4)
     steps = []
     for _ in range(3):
@@ -141,19 +146,22 @@ def test_every_small_tree_batched(torch_cuda):
     _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps, "f32", 90, 2, 16, 8)
 
 
-def test_bf16_inputs_small(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_bf16_inputs_small(torch_cuda, mode):
     """bf16 inputs at d = 16 over a branched batch (exercises the bf16 staging path)."""
     rng = np.random.default_rng(8)
     trees = [synth.make_tree(rng, 12, 3, 5) for _ in range(5)]
-    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=3, C=24, dtype="bf16", cfg_id=91)
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=3, C=24, dtype="bf16", cfg_id=91,
+                                     mode=mode)
     steps = [[synth.random_path(rng, t, int(rng.integers(1, 4))) for t in trees] for _ in range(2)]
     _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps, "bf16", 91, 3, 16, 24)
 
 
-def _layer_case(torch_cuda, config, n_layers, trees, steps, sample_layers, check_outputs_at):
+def _layer_case(torch_cuda, config, n_layers, trees, steps, sample_layers, check_outputs_at,
+                mode="chain"):
     c = synth.CONFIGS[config]
     H, d, C, dtype = c["H"], c["d"], c["Cch"], c["dtype"]
-    b = gh.Batch(trees, n_layers, H, d, C)
+    b = gh.Batch(trees, n_layers, H, d, C, mode=mode)
     layers = range(n_layers)
     S0, X0 = workload.host_initial_state(config, layers, b.S)
     W = workload.host_weights(config, layers)
@@ -191,17 +199,20 @@ def _layer_case(torch_cuda, config, n_layers, trees, steps, sample_layers, check
                               np.stack(window[l]).astype(np.float32))
 
 
-def test_one_layer_bf16_48_heads(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_one_layer_bf16_48_heads(torch_cuda, mode):
     """Config 1: one layer, 48 heads x 128, bf16 inputs, the seeded 22-node top-4 tree; verify,
     conv and banks for every node and head, then commit of a length-6 path and flush."""
     trees = workload.config_trees(1)
-    _layer_case(torch_cuda, 1, 1, trees, steps=2, sample_layers=[0], check_outputs_at={0, 1})
+    _layer_case(torch_cuda, 1, 1, trees, steps=2, sample_layers=[0], check_outputs_at={0, 1},
+                mode=mode)
 
 
-def test_48_layers_ten_steps(torch_cuda):
+@pytest.mark.parametrize("mode", MODES)
+def test_48_layers_ten_steps(torch_cuda, mode):
     """Config 2: 48 independent layers, 10 verify steps each folding the previous step's
     accepted length-6 path, then flush; oracle on three sampled layers (states every step,
     outputs and banks at steps 0, 4 and 9)."""
     trees = workload.config_trees(2)
     _layer_case(torch_cuda, 2, 48, trees, steps=10, sample_layers=[0, 23, 47],
-                check_outputs_at={0, 4, 9})
+                check_outputs_at={0, 4, 9}, mode=mode)
