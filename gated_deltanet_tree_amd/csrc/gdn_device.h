@@ -33,8 +33,8 @@ __device__ __forceinline__ float octet_sum(float x) {
 // Workgroups are dealt round-robin to the 8 XCDs. Give XCD x a contiguous range of logical
 // work items so neighbours in logical order (sibling chains reading one boundary state,
 // consecutive channels) share an L2.  Bijective on [0, n).
-__device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t n) {
-    const int64_t q = n >> 3, r = n & 7, x = b & 7, k = b >> 3;
+__device__ __forceinline__ uint32_t xcd_logical(uint32_t b, uint32_t n) {
+    const uint32_t q = n >> 3, r = n & 7, x = b & 7, k = b >> 3;
     return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 

@@ -13,6 +13,10 @@ namespace gdn {
 constexpr int32_t kImageMagic = 0x53444E47;
 constexpr int32_t kImageHeader = 16;
 constexpr int32_t kMaxTreeNodes = 1024;
+// Largest grid of one verify or flush launch: the total work-item count of a dispatch
+// (blocks x 256 threads at most) must fit in 32 bits, and the kernels' block arithmetic is
+// 32-bit.
+constexpr int64_t kMaxBlocks = 0xFFFFFFFFll / 256;
 constexpr int32_t kMaxSeqs = 1 << 20;
 
 // Word offsets of the schedule image's arrays (see gdn_tree.h for the layout).

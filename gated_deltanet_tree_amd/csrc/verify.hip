@@ -46,28 +46,28 @@ void verify_chain_kernel(VerifyParams P) {
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int rg = lane >> 3, cl = lane & 7;
-    int64_t logical = xcd_logical(blockIdx.x, P.n_blocks);
+    // Grids are capped at kMaxBlocks workgroups, so block arithmetic stays in 32 bits.
+    uint32_t logical = xcd_logical(blockIdx.x, uint32_t(P.n_blocks));
 #if GDN_REVERSE_LIGHT_WAVES
-    if (P.chain_begin > 0) logical = P.n_blocks - 1 - logical;
+    if (P.chain_begin > 0) logical = uint32_t(P.n_blocks) - 1 - logical;
 #endif
 
     int layer_rel, seq, h, chain = -1;
     if (P.fold_only) {
-        const int64_t per = int64_t(P.S) * P.H;
+        const uint32_t per = uint32_t(P.S) * uint32_t(P.H);
         layer_rel = int(logical / per);
-        const int64_t rem = logical % per;
-        seq = int(rem / P.H);
-        h = int(rem % P.H);
+        const uint32_t rem = logical % per;
+        seq = int(rem / uint32_t(P.H));
+        h = int(rem % uint32_t(P.H));
     } else {
-        const int64_t per = int64_t(P.n_chains) * P.H;
+        const uint32_t per = uint32_t(P.n_chains) * uint32_t(P.H);
         layer_rel = int(logical / per);
-        const int64_t rem = logical % per;
-        h = int(rem / P.n_chains);
-        chain = P.chain_begin + int(rem % P.n_chains);
+        const uint32_t rem = logical % per;
+        h = int(rem / uint32_t(P.n_chains));
+        chain = P.chain_begin + int(rem % uint32_t(P.n_chains));
         seq = P.img[P.off_cseq + chain];
     }
     ChainCtx c;
-    c.node_base = -1;
     c.h = h;
     c.T = P.T;
     c.H = P.H;
@@ -107,13 +107,14 @@ void verify_chain_kernel(VerifyParams P) {
 #define GDN_ROW(m) (row0 + 8 * (m))
 #define GDN_COL(p) (col0 + (p) * 8 * VEC)
 
-    SG st;
-    stage_issue(st, c, 0, tid);
+    // The start tile is issued first: its address needs only the chain's own fields.
     float s[M][NP][VEC];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int p = 0; p < NP; ++p) V::get(start + GDN_T(m, p), s[m][p]);
+    SG st;
+    stage_issue(st, c, 0, tid);
 
     for (int it0 = 0, blk = 0; it0 < c.n_items; it0 += SG::PB, ++blk) {
         float *buf = lds[blk & 1];
@@ -317,7 +318,7 @@ static gdn_status run_wave(VerifyParams P, const int32_t *host_image, const Imag
     P.chain_begin = c0;
     P.n_chains = c1 - c0;
     P.n_blocks = int64_t(a->n_layers) * P.n_chains * a->n_heads;
-    if (P.n_blocks > 0xFFFFFFFFll)
+    if (P.n_blocks > kMaxBlocks)
         return fail(GDN_EINVAL, "gdn_tree_verify: %lld workgroups exceed one launch",
                     (long long)P.n_blocks);
     return dispatch_verify(P, a->head_dim, a->in_dtype, stream, start, stop);
@@ -401,7 +402,7 @@ gdn_status flush_state(const gdn_verify_args *a, hipStream_t stream) {
     P.layer_begin = a->layer_begin;
     P.fold_only = 1;
     P.n_blocks = int64_t(a->n_layers) * a->n_seqs * a->n_heads;
-    if (P.n_blocks > 0xFFFFFFFFll) return fail(GDN_EINVAL, "gdn_flush: too many workgroups");
+    if (P.n_blocks > kMaxBlocks) return fail(GDN_EINVAL, "gdn_flush: too many workgroups");
     return dispatch_verify(P, a->head_dim, a->in_dtype, stream);
 }
 gdn_status check_flush_verify_args(const gdn_verify_args *a) { return check_verify_args(a, false); }

@@ -67,9 +67,13 @@ template <> struct VecT<2> {
 
 // Staging of a block of items into LDS.  An item is a pending fold row (fp32 k, u, lg) or a
 // node (k, q, v, beta, g in the input dtype).  Its LDS slot holds fp32 [k | q | v-or-u |
-// scalar0 | scalar1 | pad]: scalar0 = beta or lg, scalar1 = g.  Every thread owns NCH 16-byte
-// vector chunks of the block and at most one scalar; the loads for block b+1 are issued right
-// after block b is published, so their latency hides behind a whole block of work.
+// scalar0 | scalar1 | pad]: scalar0 = beta or lg, scalar1 = g.
+//   - The block's node ids are uniform: they are read with scalar loads and stay in SGPRs.
+//   - Every thread owns NCH 16-byte vector chunks of the block's vectors; the first 2 PB
+//     threads also fetch one per-item scalar each.
+// Loads keep their raw bits until stage_commit, so issuing them never waits on memory; the
+// loads for block b+1 are issued right after block b is published, so their latency hides
+// behind a whole block of work.
 template <int D, typename TIn, int PB_ = GDN_STAGE_ITEMS> struct Stager {
     static constexpr int THREADS = Tile<D>::THREADS;
     static constexpr int PB = PB_;
@@ -78,17 +82,15 @@ template <int D, typename TIn, int PB_ = GDN_STAGE_ITEMS> struct Stager {
     static constexpr int VCH = (3 * NODE_CV > 2 * FOLD_CV) ? 3 * NODE_CV : 2 * FOLD_CV;
     static constexpr int NCH = (PB * VCH + THREADS - 1) / THREADS;
     static constexpr int SLOT = 3 * D + 4;
-    static_assert(2 * PB <= THREADS, "one scalar per thread");
-    uint4 v[NCH];
-    uint32_t sc;
+    uint4 v[NCH];     // per thread: raw vector chunks
+    uint32_t sc;      // per thread: raw bits of one per-item scalar (thread < 2 PB)
+    int node[PB];     // uniform: global node id of each node item
 };
 
 // Per-workgroup context of the staging helpers.  Passed by value and unpacked into scalars
 // before any pointer is selected, so that no private (scratch) copy is ever needed.
 struct ChainCtx {
     int L, n_items, nbeg, h, layer, T, H;
-    int node_base;  // >= 0: item L + i is global node node_base + i (whole tree in index order);
-                    // < 0: it is chain_nodes[nbeg + i] of the schedule image
     int64_t bank_row0, off_cnodes;
     const float *pk, *pu, *plg;
     const void *k, *q, *v, *beta, *gate;
@@ -107,9 +109,36 @@ __device__ __forceinline__ void stage_issue(Stager<D, TIn, PB> &st, const ChainC
     using SG = Stager<D, TIn, PB>;
     const int it1 = min(c.n_items, it0 + SG::PB);
 #pragma unroll
+    for (int jj = 0; jj < SG::PB; ++jj) {  // uniform: node ids of the block
+        const int item = it0 + jj;
+        st.node[jj] = (item >= c.L && item < it1) ? c.img[c.off_cnodes + c.nbeg + (item - c.L)] : 0;
+    }
+    // Thread t < 2 PB fetches scalar t / PB (0: beta or lg, 1: g) of item it0 + t % PB; the
+    // raw bits are converted only in stage_commit, so nothing here waits for memory.
+    st.sc = 0;
+    if (tid < 2 * SG::PB) {
+        const int rel = tid % SG::PB, which = tid / SG::PB, item = it0 + rel;
+        if (item < it1) {
+            if (item < c.L) {
+                if (which == 0) st.sc = __float_as_uint(c.plg[c.bank_row0 + item]);
+            } else {
+                int node = st.node[0];
+#pragma unroll
+                for (int jj = 1; jj < SG::PB; ++jj)
+                    if (rel == jj) node = st.node[jj];
+                const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
+                const TIn *src = static_cast<const TIn *>(which == 0 ? c.beta : c.gate) + row;
+                if (sizeof(TIn) == 2)
+                    st.sc = *reinterpret_cast<const uint16_t *>(src);
+                else
+                    st.sc = *reinterpret_cast<const uint32_t *>(src);
+            }
+        }
+    }
+#pragma unroll
     for (int i = 0; i < SG::NCH; ++i) {
         const int j = tid + i * SG::THREADS;
-        const int item = it0 + j / SG::VCH, ch = j % SG::VCH;
+        const int rel = j / SG::VCH, item = it0 + rel, ch = j % SG::VCH;
         st.v[i] = make_uint4(0, 0, 0, 0);
         if (j >= SG::PB * SG::VCH || item >= it1) continue;
         if (item < c.L) {
@@ -119,29 +148,15 @@ __device__ __forceinline__ void stage_issue(Stager<D, TIn, PB> &st, const ChainC
                 st.v[i] = reinterpret_cast<const uint4 *>(src)[ch % SG::FOLD_CV];
             }
         } else if (ch < 3 * SG::NODE_CV) {
-            const int node = c.node_base >= 0 ? c.node_base + (item - c.L)
-                                              : c.img[c.off_cnodes + c.nbeg + (item - c.L)];
+            int node = st.node[0];
+#pragma unroll
+            for (int jj = 1; jj < SG::PB; ++jj)
+                if (rel == jj) node = st.node[jj];
             const int vec = ch / SG::NODE_CV;
             const void *base = pick3(vec, c.k, c.q, c.v);
             const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
             st.v[i] = reinterpret_cast<const uint4 *>(static_cast<const TIn *>(base) + row * D)
                 [ch % SG::NODE_CV];
-        }
-    }
-    st.sc = 0;
-    if (tid < 2 * SG::PB) {
-        const int item = it0 + (tid >> 1), which = tid & 1;
-        if (item < it1) {
-            if (item < c.L) {
-                if (which == 0) st.sc = __float_as_uint(c.plg[c.bank_row0 + item]);
-            } else {
-                const int node = c.node_base >= 0 ? c.node_base + (item - c.L)
-                                                  : c.img[c.off_cnodes + c.nbeg + (item - c.L)];
-                const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
-                const void *base = pick3(which, c.beta, c.gate, c.gate);
-                st.sc = sizeof(TIn) == 2 ? uint32_t(static_cast<const bf16_t *>(base)[row]) << 16
-                                         : __float_as_uint(static_cast<const float *>(base)[row]);
-            }
         }
     }
 }
@@ -181,8 +196,11 @@ __device__ __forceinline__ void stage_commit(const Stager<D, TIn, PB> &st, float
         }
     }
     if (tid < 2 * SG::PB) {
-        const int item = it0 + (tid >> 1);
-        if (item < it1) buf[(item - it0) * SG::SLOT + 3 * D + (tid & 1)] = __uint_as_float(st.sc);
+        const int rel = tid % SG::PB, which = tid / SG::PB, item = it0 + rel;
+        if (item < it1) {
+            const bool raw16 = sizeof(TIn) == 2 && item >= c.L;
+            buf[rel * SG::SLOT + 3 * D + which] = __uint_as_float(raw16 ? st.sc << 16 : st.sc);
+        }
     }
 }
 

@@ -155,10 +155,11 @@ void verify_ut_kernel(VerifyParams P, int n_max, int np_max, int nf_max) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
     const int rg = lane >> 3, cl = lane & 7, oc = tid >> 3;
-    const int64_t logical = xcd_logical(blockIdx.x, P.n_blocks);
-    const int64_t per = int64_t(P.S) * P.H;
+    // Grids are capped at kMaxBlocks workgroups, so block arithmetic stays in 32 bits.
+    const uint32_t logical = xcd_logical(blockIdx.x, uint32_t(P.n_blocks));
+    const uint32_t per = uint32_t(P.S) * uint32_t(P.H);
     const int layer_rel = int(logical / per);
-    const int seq = int((logical % per) / P.H), h = int(logical % P.H);
+    const int seq = int((logical % per) / uint32_t(P.H)), h = int(logical % uint32_t(P.H));
     const int layer = P.layer_begin + layer_rel;
     const int seq_off = P.img[P.off_seq + seq];
     const int n = P.img[P.off_seq + seq + 1] - seq_off;
@@ -167,6 +168,19 @@ void verify_ut_kernel(VerifyParams P, int n_max, int np_max, int nf_max) {
     float *committed = P.state + sh * D * D;
     const int64_t row0_bank = sh * P.max_nodes;
     float *wk = P.bank_k[role ^ 1], *wu = P.bank_u[role ^ 1], *wlg = P.bank_lg[role ^ 1];
+
+    // The committed tile is requested first: its address needs only the workgroup's ids.
+    const int row0 = w * TL::RW + rg;
+    const int col0 = cl * VEC;
+    const int toff = row0 * D + col0;
+#define GDN_T(m, p) (toff + (m) * 8 * D + (p) * 8 * VEC)
+#define GDN_ROW(m) (row0 + 8 * (m))
+#define GDN_COL(p) (col0 + (p) * 8 * VEC)
+    float s[M][NP][VEC];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) V::get(committed + GDN_T(m, p), s[m][p]);
 
     // ---- 0. direct loads of the tree's inputs, tables and pending rows into LDS ----------
     const int64_t node_row0 = (int64_t(layer) * P.T + seq_off) * P.H + h;  // node 0's row
@@ -209,17 +223,6 @@ void verify_ut_kernel(VerifyParams P, int n_max, int np_max, int nf_max) {
                 to_lds<4>(plg + min(base + lane, L - 1), lds + lay.fold_lg + size_t(base) * 4);
         }
     }
-    const int row0 = w * TL::RW + rg;
-    const int col0 = cl * VEC;
-    const int toff = row0 * D + col0;
-#define GDN_T(m, p) (toff + (m) * 8 * D + (p) * 8 * VEC)
-#define GDN_ROW(m) (row0 + 8 * (m))
-#define GDN_COL(p) (col0 + (p) * 8 * VEC)
-    float s[M][NP][VEC];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int p = 0; p < NP; ++p) V::get(committed + GDN_T(m, p), s[m][p]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -438,7 +441,7 @@ static gdn_status run_ut(const gdn_verify_args *a, const int32_t *host_image,
     P.off_parent = v.off_parent;
     P.off_depth = v.off_depth;
     P.n_blocks = int64_t(a->n_layers) * a->n_seqs * a->n_heads;
-    if (P.n_blocks > 0xFFFFFFFFll)
+    if (P.n_blocks > kMaxBlocks)
         return fail(GDN_EINVAL, "gdn_tree_verify_ut: too many workgroups for one launch");
     // Largest tree and largest number of (node, strict ancestor) pairs of any tree; pending
     // fold rows are bounded by the bank rows.
