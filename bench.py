@@ -214,8 +214,8 @@ def main(argv=None):
     lay.state.copy_(torch.from_numpy(state0))
     lay.conv_state.copy_(torch.from_numpy(conv0))
     del state0, conv0
-    boundary = torch.empty(max(binding.verify_workspace_bytes(image0, H, d, lpc) // 4, 1),
-                           device=dev, dtype=torch.float32)
+    workspace = torch.empty(max(binding.workspace_bytes(image0, H, d, dtype == "bf16", lpc) // 4,
+                                1), device=dev, dtype=torch.float32)
     out = torch.empty((Ly, T, H, d), device=dev, dtype=torch.float32)
     y = torch.empty((Ly, T, C), device=dev, dtype=torch.float32)
     gen_s = time.perf_counter() - t_gen
@@ -224,7 +224,7 @@ def main(argv=None):
     all_paths = [[synth.config_path(args.config, s, b, trees[b]) for b in range(S)]
                  for s in range(n_total)]
     vargs = [binding.verify_args(image0, lay, inp.q, inp.k, inp.v, inp.beta, inp.gate, out,
-                                 boundary, layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
+                                 workspace, layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
     cargs = [binding.conv_args(image0, lay, inp.x, weights, y, layer_begin=l, n_layers=lpc)
              for l in range(0, Ly, lpc)]
     va_all = binding.verify_args(image0, lay, None, None, None, None, None, None, None, 0, Ly)

@@ -21,6 +21,7 @@ STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_ETREE", -3: "GDN_EPATH",
           -4: "GDN_ECAPACITY", -5: "GDN_EDEVICE"}
 EXPORTS = [
     "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_verify_workspace_bytes",
+    "gdn_verify_ut_workspace_bytes",
     "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed",
     "gdn_tree_verify_ut", "gdn_tree_verify_ut_timed", "gdn_tree_conv",
     "gdn_commit_path",
@@ -47,7 +48,7 @@ class VerifyArgs(ctypes.Structure):
         ("max_nodes", _I32), ("layer_begin", _I32), ("n_layers", _I32), ("in_dtype", _I32),
         ("q", _P), ("k", _P), ("v", _P), ("beta", _P), ("gate", _P), ("state", _P),
         ("bank_k", _P * 2), ("bank_u", _P * 2), ("bank_lg", _P * 2),
-        ("role", _P), ("pending_len", _P), ("boundary", _P), ("out", _P),
+        ("role", _P), ("pending_len", _P), ("workspace", _P), ("out", _P),
     ]
 
 
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_hld_schedule.argtypes = [_I32P, _I32P, _I32, _I32P, ctypes.c_size_t]
     L.gdn_verify_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_verify_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32]
+    L.gdn_verify_ut_workspace_bytes.restype = ctypes.c_size_t
+    L.gdn_verify_ut_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32, _I32]
     L.gdn_tree_verify.restype = _I32
     L.gdn_tree_verify.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
     L.gdn_tree_verify_wave.restype = _I32
@@ -171,7 +174,22 @@ def schedule_view(image: np.ndarray) -> dict:
 
 
 def verify_workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, n_layers: int) -> int:
+    """Workspace bytes of the chain verify (boundary states) for this schedule."""
     return int(lib().gdn_verify_workspace_bytes(_ptr(image), n_heads, head_dim, n_layers))
+
+
+def verify_ut_workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, bf16: bool,
+                              n_layers: int) -> int:
+    """Workspace bytes of the UT verify (pair tables) for this schedule; 0 if none."""
+    return int(lib().gdn_verify_ut_workspace_bytes(_ptr(image), n_heads, head_dim,
+                                                   GDN_BF16 if bf16 else GDN_F32, n_layers))
+
+
+def workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, bf16: bool,
+                    n_layers: int) -> int:
+    """Workspace bytes that serve both verify paths."""
+    return max(verify_workspace_bytes(image, n_heads, head_dim, n_layers),
+               verify_ut_workspace_bytes(image, n_heads, head_dim, bf16, n_layers))
 
 
 # ------------------------------------------------------------------------------------
@@ -208,7 +226,7 @@ def _need(t, n, what):
         raise ValueError(f"{what} holds {t.numel()} elements, the call addresses {n}")
 
 
-def verify_args(image, layers: Layers, q, k, v, beta, gate, out, boundary,
+def verify_args(image, layers: Layers, q, k, v, beta, gate, out, workspace,
                 layer_begin=0, n_layers=1, max_nodes=None) -> VerifyArgs:
     import torch
     S, T = int(image[1]), int(image[2])
@@ -226,9 +244,11 @@ def verify_args(image, layers: Layers, q, k, v, beta, gate, out, boundary,
         _need(layers.bank_lg[i], Ly_end * S * H * Nm, "bank_lg")
     _need(layers.role, S, "role")
     _need(layers.pending, S, "pending")
-    if boundary is not None and q is not None:
-        _need(boundary, verify_workspace_bytes(image, H, d, n_layers) // 4, "boundary")
+    _need(workspace, 0, "workspace")
     a = VerifyArgs()
+    # kept for the size check of each entry point (the two paths need different workspaces)
+    a.ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.sizes = (H, d, n_layers)
     a.n_seqs, a.n_nodes = int(image[1]), int(image[2])
     a.n_heads, a.head_dim = int(layers.state.shape[2]), int(layers.state.shape[3])
     a.max_nodes = int(layers.bank_lg[0].shape[-1]) if max_nodes is None else max_nodes
@@ -241,7 +261,7 @@ def verify_args(image, layers: Layers, q, k, v, beta, gate, out, boundary,
         a.bank_u[i] = _dev(layers.bank_u[i])
         a.bank_lg[i] = _dev(layers.bank_lg[i])
     a.role, a.pending_len = _dev(layers.role), _dev(layers.pending)
-    a.boundary, a.out = _dev(boundary), _dev(out)
+    a.workspace, a.out = _dev(workspace), _dev(out)
     return a
 
 
@@ -271,30 +291,45 @@ def conv_args(image, layers: Layers, x, weight, out, layer_begin=0, n_layers=1,
     return a
 
 
+def _need_ws(args: VerifyArgs, image: np.ndarray, ut: bool):
+    if args.q is None:
+        return
+    H, d, n_layers = args.sizes
+    need = (verify_ut_workspace_bytes(image, H, d, args.in_dtype == GDN_BF16, n_layers) if ut
+            else verify_workspace_bytes(image, H, d, n_layers))
+    if need and args.ws_bytes < need:
+        raise ValueError(f"workspace holds {args.ws_bytes} bytes, the call needs {need}")
+
+
 def tree_verify(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
+    _need_ws(args, image, False)
     _check(lib().gdn_tree_verify(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                  _stream(stream)), "gdn_tree_verify")
 
 
 def tree_verify_wave(args: VerifyArgs, image: np.ndarray, dev_image, wave: int, stream=None):
+    _need_ws(args, image, False)
     _check(lib().gdn_tree_verify_wave(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
                                       _stream(stream)), "gdn_tree_verify_wave")
 
 
 def tree_verify_wave_timed(args: VerifyArgs, image: np.ndarray, dev_image, wave: int,
                            start: "HipEvent", stop: "HipEvent", stream=None):
+    _need_ws(args, image, False)
     _check(lib().gdn_tree_verify_wave_timed(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
                                             start.handle, stop.handle, _stream(stream)),
            "gdn_tree_verify_wave_timed")
 
 
 def tree_verify_ut(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
+    _need_ws(args, image, True)
     _check(lib().gdn_tree_verify_ut(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                     _stream(stream)), "gdn_tree_verify_ut")
 
 
 def tree_verify_ut_timed(args: VerifyArgs, image: np.ndarray, dev_image, start: "HipEvent",
                          stop: "HipEvent", stream=None):
+    _need_ws(args, image, True)
     _check(lib().gdn_tree_verify_ut_timed(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                           start.handle, stop.handle, _stream(stream)),
            "gdn_tree_verify_ut_timed")

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P) {
     const int seq = blockIdx.y;
     const int layer = P.layer_begin + blockIdx.z;
     if (c >= P.C) return;
-    const int role = P.role[seq], L = P.pending[seq];
+    const int role = P.role[seq], L = min(max(P.pending[seq], 0), P.max_nodes);  // bank rows
     const int64_t ls = int64_t(layer) * P.S + seq;  // (layer, seq)
     float *cs = P.cstate + (ls * P.C + c) * 3;
     float w0 = cs[0], w1 = cs[1], w2 = cs[2];  // committed window, oldest first

@@ -1,0 +1,38 @@
+// Helpers shared by the tree-masked UT verify kernels (gfx950).
+#pragma once
+
+#include "verify_common.h"
+
+namespace gdn {
+
+constexpr size_t kUtMaxLdsBytes = 160 * 1024;  // one workgroup may take the whole CU's LDS
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__host__ __device__ constexpr size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+// One 64-lane direct load from per-lane source addresses into LDS at lds_base, which must be
+// the same for the whole wave.  16-byte loads land at lds_base + 16 l; 4-byte and 2-byte loads
+// land at lds_base + 4 l, a 2-byte value zero-extended to a dword.
+template <int BYTES> __device__ __forceinline__ void to_lds(const void *src, void *lds_base);
+template <> __device__ __forceinline__ void to_lds<16>(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
+}
+template <> __device__ __forceinline__ void to_lds<4>(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 4, 0, 0);
+}
+template <> __device__ __forceinline__ void to_lds<2>(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 2, 0, 0);
+}
+
+// beta or gate as fp32 from its dword slot (bf16 arrives zero-extended in the low half)
+template <typename TIn> __device__ __forceinline__ float slot_f32(uint32_t x) {
+    return sizeof(TIn) == 2 ? __uint_as_float(x << 16) : __uint_as_float(x);
+}
+
+// The matrix-core UT kernels (bf16 inputs, d = 128) and their workspace size.
+size_t ut_mfma_workspace_bytes(int n_layers, int S, int H, int n_max, int np_max);
+gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int np_max, int nf_max,
+                          hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+}  // namespace gdn

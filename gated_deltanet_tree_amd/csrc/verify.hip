@@ -84,7 +84,7 @@ void verify_chain_kernel(VerifyParams P) {
     const int nend = P.fold_only ? 0 : P.img[P.off_chain + chain + 1];
     const int seq_off = P.fold_only ? 0 : P.img[P.off_seq + seq];
     const int role = P.role[seq];
-    c.L = src < 0 ? P.pending[seq] : 0;
+    c.L = src < 0 ? min(max(P.pending[seq], 0), P.max_nodes) : 0;  // clamp: bank rows
     c.n_items = c.L + (nend - c.nbeg);
     if (c.n_items == 0) return;  // flush of a sequence with nothing pending
 
@@ -269,10 +269,10 @@ static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule
         return fail(GDN_EINVAL, "verify args: null q/k/v/beta/gate/out");
     // Tiles, rows and vectors are moved in 16-byte pieces.
     const void *aligned[] = {a->q, a->k, a->v, a->state, a->bank_k[0], a->bank_k[1],
-                             a->bank_u[0], a->bank_u[1], a->boundary, a->out};
+                             a->bank_u[0], a->bank_u[1], a->workspace, a->out};
     for (const void *p : aligned)
         if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
-            return fail(GDN_EINVAL, "verify args: q/k/v/state/bank/boundary/out pointers must "
+            return fail(GDN_EINVAL, "verify args: q/k/v/state/bank/workspace/out pointers must "
                         "be 16-byte aligned");
     return GDN_OK;
 }
@@ -291,7 +291,7 @@ gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
     if (v.max_tree > a->max_nodes)
         return fail(GDN_ECAPACITY, "gdn_tree_verify: max_nodes %d < largest tree %d",
                     a->max_nodes, v.max_tree);
-    if (need_boundary && v.n_boundaries > 0 && a->boundary == nullptr)
+    if (need_boundary && v.n_boundaries > 0 && a->workspace == nullptr)
         return fail(GDN_EINVAL, "gdn_tree_verify: schedule has %d boundary nodes but no "
                     "boundary workspace", v.n_boundaries);
     P = VerifyParams{};
@@ -302,7 +302,7 @@ gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
         P.bank_u[i] = a->bank_u[i];
         P.bank_lg[i] = a->bank_lg[i];
     }
-    P.role = a->role; P.pending = a->pending_len; P.boundary = a->boundary; P.out = a->out;
+    P.role = a->role; P.pending = a->pending_len; P.boundary = a->workspace; P.out = a->out;
     P.img = dev_image;
     P.off_seq = v.off_seq; P.off_chain = v.off_chain; P.off_cnodes = v.off_cnodes;
     P.off_cseq = v.off_cseq; P.off_csrc = v.off_csrc; P.off_store = v.off_store;

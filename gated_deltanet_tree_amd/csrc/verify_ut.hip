@@ -33,15 +33,9 @@
 
 #include <algorithm>
 
-#include "verify_common.h"
+#include "ut_common.h"
 
 namespace gdn {
-
-constexpr size_t kUtMaxLdsBytes = 160 * 1024;  // one workgroup may take the whole CU's LDS
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__host__ __device__ constexpr size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 // Byte offsets of the dynamic LDS regions for trees of at most n nodes, np (node, strict
 // ancestor) pairs and at most nf pending fold rows.  Regions filled by direct loads are
@@ -69,20 +63,6 @@ template <int D, typename TIn> struct UtLayout {
     }
 };
 
-// One 64-lane direct load from per-lane source addresses into LDS at lds_base, which must be
-// the same for the whole wave.  16-byte loads land at lds_base + 16 l; 4-byte and 2-byte loads
-// land at lds_base + 4 l, a 2-byte value zero-extended to a dword.
-template <int BYTES> __device__ __forceinline__ void to_lds(const void *src, void *lds_base);
-template <> __device__ __forceinline__ void to_lds<16>(const void *src, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
-}
-template <> __device__ __forceinline__ void to_lds<4>(const void *src, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 4, 0, 0);
-}
-template <> __device__ __forceinline__ void to_lds<2>(const void *src, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 2, 0, 0);
-}
-
 // VEC (4 or 2) consecutive elements of input vector `vec` (0 k, 1 q, 2 v) of a node, fp32.
 template <int D, typename TIn, int VEC>
 __device__ __forceinline__ void in_vec(const char *lds, int node, int vec, int col, float *o) {
@@ -108,11 +88,6 @@ __device__ __forceinline__ void in_vec(const char *lds, int node, int vec, int c
         o[0] = x.x;
         o[1] = x.y;
     }
-}
-
-// beta or gate as fp32 from its dword slot (bf16 arrives zero-extended in the low half)
-template <typename TIn> __device__ __forceinline__ float slot_f32(uint32_t x) {
-    return sizeof(TIn) == 2 ? __uint_as_float(x << 16) : __uint_as_float(x);
 }
 
 template <int D, typename TIn>
@@ -163,7 +138,7 @@ void verify_ut_kernel(VerifyParams P, int n_max, int np_max, int nf_max) {
     const int layer = P.layer_begin + layer_rel;
     const int seq_off = P.img[P.off_seq + seq];
     const int n = P.img[P.off_seq + seq + 1] - seq_off;
-    const int role = P.role[seq], L = P.pending[seq];
+    const int role = P.role[seq], L = min(max(P.pending[seq], 0), P.max_nodes);
     const int64_t sh = (int64_t(layer) * P.S + seq) * P.H + h;
     float *committed = P.state + sh * D * D;
     const int64_t row0_bank = sh * P.max_nodes;
@@ -431,6 +406,19 @@ gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
                         const int32_t *dev_image, VerifyParams &P, ImageView &v,
                         bool need_boundary);
 
+// Largest tree and largest number of (node, strict ancestor) pairs of any tree of a schedule.
+static void ut_tree_bounds(const int32_t *host_image, const ImageView &v, int &n_max,
+                           int &np_max) {
+    n_max = v.max_tree;
+    np_max = 0;
+    for (int b = 0; b < v.n_seqs; ++b) {
+        int pairs = 0;
+        for (int g = host_image[v.off_seq + b]; g < host_image[v.off_seq + b + 1]; ++g)
+            pairs += host_image[v.off_depth + g];
+        np_max = std::max(np_max, pairs);
+    }
+}
+
 static gdn_status run_ut(const gdn_verify_args *a, const int32_t *host_image,
                          const int32_t *dev_image, void *stream, hipEvent_t start,
                          hipEvent_t stop) {
@@ -443,21 +431,13 @@ static gdn_status run_ut(const gdn_verify_args *a, const int32_t *host_image,
     P.n_blocks = int64_t(a->n_layers) * a->n_seqs * a->n_heads;
     if (P.n_blocks > kMaxBlocks)
         return fail(GDN_EINVAL, "gdn_tree_verify_ut: too many workgroups for one launch");
-    // Largest tree and largest number of (node, strict ancestor) pairs of any tree; pending
-    // fold rows are bounded by the bank rows.
-    const int n_max = v.max_tree;
-    int np_max = 0;
-    for (int b = 0; b < v.n_seqs; ++b) {
-        int pairs = 0;
-        for (int g = host_image[v.off_seq + b]; g < host_image[v.off_seq + b + 1]; ++g)
-            pairs += host_image[v.off_depth + g];
-        np_max = std::max(np_max, pairs);
-    }
+    int n_max = 0, np_max = 0;
+    ut_tree_bounds(host_image, v, n_max, np_max);
     const int nf_max = a->max_nodes;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a->head_dim == 128)
         return a->in_dtype == GDN_BF16
-            ? launch_ut<128, bf16_t>(P, n_max, np_max, nf_max, s, start, stop)
+            ? launch_ut_mfma(P, n_max, np_max, nf_max, s, start, stop)
             : launch_ut<128, float>(P, n_max, np_max, nf_max, s, start, stop);
     return a->in_dtype == GDN_BF16
         ? launch_ut<16, bf16_t>(P, n_max, np_max, nf_max, s, start, stop)
@@ -467,6 +447,17 @@ static gdn_status run_ut(const gdn_verify_args *a, const int32_t *host_image,
 }  // namespace gdn
 
 using namespace gdn;
+
+extern "C" size_t gdn_verify_ut_workspace_bytes(const int32_t *host_image, int32_t n_heads,
+                                                int32_t head_dim, int32_t in_dtype,
+                                                int32_t n_layers) {
+    if (!image_ok(host_image) || n_heads < 1 || n_layers < 1) return 0;
+    if (head_dim != 128 || in_dtype != GDN_BF16) return 0;  // only the matrix-core path
+    const ImageView v = view_image(host_image);
+    int n_max = 0, np_max = 0;
+    ut_tree_bounds(host_image, v, n_max, np_max);
+    return ut_mfma_workspace_bytes(n_layers, v.n_seqs, n_heads, n_max, np_max);
+}
 
 extern "C" gdn_status gdn_tree_verify_ut(const gdn_verify_args *a, const int32_t *host_image,
                                          const int32_t *dev_image, void *stream) {

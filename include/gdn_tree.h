@@ -44,7 +44,7 @@
  *     is the per-layer pattern of a model forward).
  *   - Shapes: head_dim d = d_k = d_v in {16, 128}; conv width 4; N_b <= 1024.
  *   - Numerics: inputs bf16 or fp32; state, factors and outputs fp32; accumulation fp32.
- *   - Alignment: q, k, v, state, key/residual banks, boundary and out must be 16-byte
+ *   - Alignment: q, k, v, state, key/residual banks, workspace and out must be 16-byte
  *     aligned (tiles and rows move in 16-byte pieces); GDN_EINVAL otherwise.
  */
 #ifndef GDN_TREE_H
@@ -119,7 +119,7 @@ gdn_status gdn_hld_schedule(const int32_t *parent_local, const int32_t *seq_offs
  *
  * Work: one launch per dependency wave, one workgroup per (layer, chain, head); the fp32
  * state tile stays in VGPRs for the whole chain; boundary nodes store their state once to
- * `boundary` for the light chains of later waves.
+ * `workspace` for the light chains of later waves.
  * ---------------------------------------------------------------------------------- */
 typedef struct {
     int32_t n_seqs;      /* S, must equal the schedule's                                   */
@@ -140,11 +140,14 @@ typedef struct {
     float *bank_lg[2];   /* [Ly][S][H][max_nodes]     log decay gates                      */
     const int32_t *role;        /* device [S]: index (0/1) of the pending bank             */
     const int32_t *pending_len; /* device [S]: pending rows to fold, 0 = none              */
-    float *boundary;     /* device scratch, gdn_verify_workspace_bytes() bytes              */
+    float *workspace;    /* device scratch: gdn_verify_workspace_bytes() bytes of boundary  */
+                         /* states for gdn_tree_verify*, gdn_verify_ut_workspace_bytes()    */
+                         /* bytes of pair tables for gdn_tree_verify_ut*                    */
     float *out;          /* [Ly][T][H][d] fp32 outputs                                     */
 } gdn_verify_args;
 
-/* Bytes of `boundary` scratch for this schedule: n_layers * n_boundaries * H * d * d * 4. */
+/* Bytes of `workspace` that gdn_tree_verify needs for this schedule (the boundary states):
+ * n_layers * n_boundaries * H * d * d * 4. */
 size_t gdn_verify_workspace_bytes(const int32_t *host_image, int32_t n_heads, int32_t head_dim,
                                   int32_t n_layers);
 
@@ -174,14 +177,25 @@ gdn_status gdn_tree_verify_wave_timed(const gdn_verify_args *args, const int32_t
  *   out[n] = G_n S0 q_n + sum_{j ancestor or n} E(n,j) (q_n.k_j) u_j
  * with G_n the product of the gates on n's root path and E(n,j) the product of the gates
  * strictly below j down to n; S0 is the committed state after the deferred fold.
- * `boundary` is not used (may be NULL). A tree must fit the kernel's 64 KiB LDS budget
- * (about 64 nodes at d = 128 with bf16 inputs, 50 with fp32); larger trees give GDN_EINVAL
- * and should use gdn_tree_verify. */
+ * bf16 inputs at d = 128 run on the matrix cores in two launches: a one-wave-per-head pass
+ * forms the tree tables, the pair products and the tree-masked inverse, and writes them to
+ * `workspace` (gdn_verify_ut_workspace_bytes() bytes, overwritten by every call); the main
+ * pass folds, writes the committed state once and forms every output.  Other dtypes and
+ * head dims run one vector launch and need no workspace (may be NULL).  A tree must fit the
+ * LDS budget of one workgroup (160 KiB: about 64 nodes at d = 128 with bf16 inputs); larger
+ * trees give GDN_EINVAL and should use gdn_tree_verify. */
+/* Bytes of `workspace` that gdn_tree_verify_ut needs for this schedule: for bf16 inputs at
+ * d = 128, n_layers * S * H * (n_max + n_max + P_max) * 16 with n_max the largest tree and
+ * P_max the largest count of (node, strict ancestor) pairs of a tree; 0 otherwise. */
+size_t gdn_verify_ut_workspace_bytes(const int32_t *host_image, int32_t n_heads,
+                                     int32_t head_dim, int32_t in_dtype, int32_t n_layers);
+
 gdn_status gdn_tree_verify_ut(const gdn_verify_args *args, const int32_t *host_image,
                               const int32_t *dev_image, void *stream);
 
 /* gdn_tree_verify_ut with dispatch-recorded start/stop HIP events (see
- * gdn_tree_verify_wave_timed). */
+ * gdn_tree_verify_wave_timed); with two launches the start event is stamped by the first
+ * and the stop event by the second. */
 gdn_status gdn_tree_verify_ut_timed(const gdn_verify_args *args, const int32_t *host_image,
                                     const int32_t *dev_image, void *start_event,
                                     void *stop_event, void *stream);

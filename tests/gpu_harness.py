@@ -63,8 +63,9 @@ class Batch:
         self.Ly, self.H, self.d, self.C = n_layers, H, d, C
         self.max_nodes = max_nodes or max(len(t) for t in trees)
         self.layers = binding.alloc_layers(n_layers, self.S, H, d, self.max_nodes, C, device)
-        ws = binding.verify_workspace_bytes(self.image, H, d, 1)
-        self.boundary = torch.zeros(max(ws // 4, 1), device=device, dtype=torch.float32)
+        # one workspace serves both verify paths (bf16 is the larger UT case)
+        ws = binding.workspace_bytes(self.image, H, d, True, 1)
+        self.workspace = torch.zeros(max(ws // 4, 1), device=device, dtype=torch.float32)
         self.out = torch.zeros((n_layers, self.T, H, d), device=device, dtype=torch.float32)
         self.y = torch.zeros((n_layers, self.T, max(C, 1)), device=device, dtype=torch.float32)
         self.device = device
@@ -78,7 +79,7 @@ class Batch:
 
     def vargs(self, inp, layer):
         return binding.verify_args(self.image, self.layers, inp.q, inp.k, inp.v, inp.beta,
-                                   inp.gate, self.out, self.boundary, layer_begin=layer,
+                                   inp.gate, self.out, self.workspace, layer_begin=layer,
                                    n_layers=1)
 
     def cargs(self, inp, layer, weight):

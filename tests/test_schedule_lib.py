@@ -121,7 +121,7 @@ def test_device_calls_validate_before_launch():
     assert b"head_dim" in L.gdn_last_error()
     args.head_dim = 16
     assert L.gdn_tree_verify(ctypes.byref(args), binding._ptr(image), 1, None) == -1  # nulls
-    for name in ("state", "role", "pending_len", "q", "k", "v", "beta", "gate", "out", "boundary"):
+    for name in ("state", "role", "pending_len", "q", "k", "v", "beta", "gate", "out", "workspace"):
         setattr(args, name, 16)
     for i in range(2):
         args.bank_k[i] = args.bank_u[i] = args.bank_lg[i] = 16
