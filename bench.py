@@ -214,8 +214,8 @@ def main(argv=None):
     lay.state.copy_(torch.from_numpy(state0))
     lay.conv_state.copy_(torch.from_numpy(conv0))
     del state0, conv0
-    workspace = torch.empty(max(binding.workspace_bytes(image0, H, d, dtype == "bf16", lpc) // 4,
-                                1), device=dev, dtype=torch.float32)
+    workspace = torch.empty(max(binding.verify_workspace_bytes(image0, H, d, lpc) // 4, 1),
+                            device=dev, dtype=torch.float32)
     out = torch.empty((Ly, T, H, d), device=dev, dtype=torch.float32)
     y = torch.empty((Ly, T, C), device=dev, dtype=torch.float32)
     gen_s = time.perf_counter() - t_gen

@@ -21,7 +21,6 @@ STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_ETREE", -3: "GDN_EPATH",
           -4: "GDN_ECAPACITY", -5: "GDN_EDEVICE"}
 EXPORTS = [
     "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_verify_workspace_bytes",
-    "gdn_verify_ut_workspace_bytes",
     "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed",
     "gdn_tree_verify_ut", "gdn_tree_verify_ut_timed", "gdn_tree_conv",
     "gdn_commit_path",
@@ -81,8 +80,6 @@ def lib() -> ctypes.CDLL:
     L.gdn_hld_schedule.argtypes = [_I32P, _I32P, _I32, _I32P, ctypes.c_size_t]
     L.gdn_verify_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_verify_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32]
-    L.gdn_verify_ut_workspace_bytes.restype = ctypes.c_size_t
-    L.gdn_verify_ut_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32, _I32]
     L.gdn_tree_verify.restype = _I32
     L.gdn_tree_verify.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
     L.gdn_tree_verify_wave.restype = _I32
@@ -178,18 +175,7 @@ def verify_workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, n_lay
     return int(lib().gdn_verify_workspace_bytes(_ptr(image), n_heads, head_dim, n_layers))
 
 
-def verify_ut_workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, bf16: bool,
-                              n_layers: int) -> int:
-    """Workspace bytes of the UT verify (pair tables) for this schedule; 0 if none."""
-    return int(lib().gdn_verify_ut_workspace_bytes(_ptr(image), n_heads, head_dim,
-                                                   GDN_BF16 if bf16 else GDN_F32, n_layers))
 
-
-def workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, bf16: bool,
-                    n_layers: int) -> int:
-    """Workspace bytes that serve both verify paths."""
-    return max(verify_workspace_bytes(image, n_heads, head_dim, n_layers),
-               verify_ut_workspace_bytes(image, n_heads, head_dim, bf16, n_layers))
 
 
 # ------------------------------------------------------------------------------------
@@ -246,7 +232,7 @@ def verify_args(image, layers: Layers, q, k, v, beta, gate, out, workspace,
     _need(layers.pending, S, "pending")
     _need(workspace, 0, "workspace")
     a = VerifyArgs()
-    # kept for the size check of each entry point (the two paths need different workspaces)
+    # kept for the size check of the chain entry points
     a.ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.sizes = (H, d, n_layers)
     a.n_seqs, a.n_nodes = int(image[1]), int(image[2])
@@ -291,45 +277,43 @@ def conv_args(image, layers: Layers, x, weight, out, layer_begin=0, n_layers=1,
     return a
 
 
-def _need_ws(args: VerifyArgs, image: np.ndarray, ut: bool):
+def _need_ws(args: VerifyArgs, image: np.ndarray):
+    """The chain verify writes boundary states into the workspace: check its size."""
     if args.q is None:
         return
     H, d, n_layers = args.sizes
-    need = (verify_ut_workspace_bytes(image, H, d, args.in_dtype == GDN_BF16, n_layers) if ut
-            else verify_workspace_bytes(image, H, d, n_layers))
+    need = verify_workspace_bytes(image, H, d, n_layers)
     if need and args.ws_bytes < need:
         raise ValueError(f"workspace holds {args.ws_bytes} bytes, the call needs {need}")
 
 
 def tree_verify(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
-    _need_ws(args, image, False)
+    _need_ws(args, image)
     _check(lib().gdn_tree_verify(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                  _stream(stream)), "gdn_tree_verify")
 
 
 def tree_verify_wave(args: VerifyArgs, image: np.ndarray, dev_image, wave: int, stream=None):
-    _need_ws(args, image, False)
+    _need_ws(args, image)
     _check(lib().gdn_tree_verify_wave(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
                                       _stream(stream)), "gdn_tree_verify_wave")
 
 
 def tree_verify_wave_timed(args: VerifyArgs, image: np.ndarray, dev_image, wave: int,
                            start: "HipEvent", stop: "HipEvent", stream=None):
-    _need_ws(args, image, False)
+    _need_ws(args, image)
     _check(lib().gdn_tree_verify_wave_timed(ctypes.byref(args), _ptr(image), _dev(dev_image), wave,
                                             start.handle, stop.handle, _stream(stream)),
            "gdn_tree_verify_wave_timed")
 
 
 def tree_verify_ut(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
-    _need_ws(args, image, True)
     _check(lib().gdn_tree_verify_ut(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                     _stream(stream)), "gdn_tree_verify_ut")
 
 
 def tree_verify_ut_timed(args: VerifyArgs, image: np.ndarray, dev_image, start: "HipEvent",
                          stop: "HipEvent", stream=None):
-    _need_ws(args, image, True)
     _check(lib().gdn_tree_verify_ut_timed(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                           start.handle, stop.handle, _stream(stream)),
            "gdn_tree_verify_ut_timed")

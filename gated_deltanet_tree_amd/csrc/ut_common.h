@@ -30,8 +30,7 @@ template <typename TIn> __device__ __forceinline__ float slot_f32(uint32_t x) {
     return sizeof(TIn) == 2 ? __uint_as_float(x << 16) : __uint_as_float(x);
 }
 
-// The matrix-core UT kernels (bf16 inputs, d = 128) and their workspace size.
-size_t ut_mfma_workspace_bytes(int n_layers, int S, int H, int n_max, int np_max);
+// The matrix-core UT kernel (bf16 inputs, d = 128).
 gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int np_max, int nf_max,
                           hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 

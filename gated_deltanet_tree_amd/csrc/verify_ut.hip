@@ -448,17 +448,6 @@ static gdn_status run_ut(const gdn_verify_args *a, const int32_t *host_image,
 
 using namespace gdn;
 
-extern "C" size_t gdn_verify_ut_workspace_bytes(const int32_t *host_image, int32_t n_heads,
-                                                int32_t head_dim, int32_t in_dtype,
-                                                int32_t n_layers) {
-    if (!image_ok(host_image) || n_heads < 1 || n_layers < 1) return 0;
-    if (head_dim != 128 || in_dtype != GDN_BF16) return 0;  // only the matrix-core path
-    const ImageView v = view_image(host_image);
-    int n_max = 0, np_max = 0;
-    ut_tree_bounds(host_image, v, n_max, np_max);
-    return ut_mfma_workspace_bytes(n_layers, v.n_seqs, n_heads, n_max, np_max);
-}
-
 extern "C" gdn_status gdn_tree_verify_ut(const gdn_verify_args *a, const int32_t *host_image,
                                          const int32_t *dev_image, void *stream) {
     clear_error();

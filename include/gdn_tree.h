@@ -140,9 +140,8 @@ typedef struct {
     float *bank_lg[2];   /* [Ly][S][H][max_nodes]     log decay gates                      */
     const int32_t *role;        /* device [S]: index (0/1) of the pending bank             */
     const int32_t *pending_len; /* device [S]: pending rows to fold, 0 = none              */
-    float *workspace;    /* device scratch: gdn_verify_workspace_bytes() bytes of boundary  */
-                         /* states for gdn_tree_verify*, gdn_verify_ut_workspace_bytes()    */
-                         /* bytes of pair tables for gdn_tree_verify_ut*                    */
+    float *workspace;    /* device scratch of gdn_tree_verify*: gdn_verify_workspace_bytes() */
+                         /* bytes of boundary states; not used by gdn_tree_verify_ut*       */
     float *out;          /* [Ly][T][H][d] fp32 outputs                                     */
 } gdn_verify_args;
 
@@ -177,25 +176,16 @@ gdn_status gdn_tree_verify_wave_timed(const gdn_verify_args *args, const int32_t
  *   out[n] = G_n S0 q_n + sum_{j ancestor or n} E(n,j) (q_n.k_j) u_j
  * with G_n the product of the gates on n's root path and E(n,j) the product of the gates
  * strictly below j down to n; S0 is the committed state after the deferred fold.
- * bf16 inputs at d = 128 run on the matrix cores in two launches: a one-wave-per-head pass
- * forms the tree tables, the pair products and the tree-masked inverse, and writes them to
- * `workspace` (gdn_verify_ut_workspace_bytes() bytes, overwritten by every call); the main
- * pass folds, writes the committed state once and forms every output.  Other dtypes and
- * head dims run one vector launch and need no workspace (may be NULL).  A tree must fit the
- * LDS budget of one workgroup (160 KiB: about 64 nodes at d = 128 with bf16 inputs); larger
- * trees give GDN_EINVAL and should use gdn_tree_verify. */
-/* Bytes of `workspace` that gdn_tree_verify_ut needs for this schedule: for bf16 inputs at
- * d = 128, n_layers * S * H * (n_max + n_max + P_max) * 16 with n_max the largest tree and
- * P_max the largest count of (node, strict ancestor) pairs of a tree; 0 otherwise. */
-size_t gdn_verify_ut_workspace_bytes(const int32_t *host_image, int32_t n_heads,
-                                     int32_t head_dim, int32_t in_dtype, int32_t n_layers);
-
+ * bf16 inputs at d = 128 run on the matrix cores (the S0 products and the pair products);
+ * other dtypes and head dims run on the vector units.  One launch per call; `workspace` is not
+ * used (may be NULL).  A tree must fit the LDS budget of one workgroup (160 KiB: about 64
+ * nodes at d = 128 with bf16 inputs); larger trees give GDN_EINVAL and should use
+ * gdn_tree_verify. */
 gdn_status gdn_tree_verify_ut(const gdn_verify_args *args, const int32_t *host_image,
                               const int32_t *dev_image, void *stream);
 
 /* gdn_tree_verify_ut with dispatch-recorded start/stop HIP events (see
- * gdn_tree_verify_wave_timed); with two launches the start event is stamped by the first
- * and the stop event by the second. */
+ * gdn_tree_verify_wave_timed). */
 gdn_status gdn_tree_verify_ut_timed(const gdn_verify_args *args, const int32_t *host_image,
                                     const int32_t *dev_image, void *start_event,
                                     void *stop_event, void *stream);

@@ -63,8 +63,7 @@ class Batch:
         self.Ly, self.H, self.d, self.C = n_layers, H, d, C
         self.max_nodes = max_nodes or max(len(t) for t in trees)
         self.layers = binding.alloc_layers(n_layers, self.S, H, d, self.max_nodes, C, device)
-        # one workspace serves both verify paths (bf16 is the larger UT case)
-        ws = binding.workspace_bytes(self.image, H, d, True, 1)
+        ws = binding.verify_workspace_bytes(self.image, H, d, 1)
         self.workspace = torch.zeros(max(ws // 4, 1), device=device, dtype=torch.float32)
         self.out = torch.zeros((n_layers, self.T, H, d), device=device, dtype=torch.float32)
         self.y = torch.zeros((n_layers, self.T, max(C, 1)), device=device, dtype=torch.float32)
