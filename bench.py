@@ -2,8 +2,13 @@
 
 One step = the whole hot path over one batch: heavy-light schedule of the batch's trees (host)
 and its upload, then for every GDN layer the tree conv (with the conv-window fold) and the tree
-verify (with the deferred-commit fold, wave by wave), then accept -> commit of one seeded path
-per sequence (role swap or compaction).  The timed region is K steps plus the final flush.
+verify (with the deferred-commit fold), then accept -> commit of one seeded path per sequence
+(role swap or compaction).  The timed region is K steps plus the final flush.
+
+Both verify paths are timed, one after the other, on the same resident workload:
+  ut     the tree-masked form on the matrix cores, one launch per layer (the headline value);
+  chain  heavy-light chains launched wave by wave (reported under "paths").
+They compute the same outputs, factor banks and committed states.
 
 Workload (default): 32 sequences, each with its own seeded 22-node top-4 tree (depth <= 12),
 48 GDN layers x 48 heads x d = 128 with independent fp32 states (4.8 GB), bf16 inputs, conv
@@ -24,10 +29,18 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
-COUNTERS = os.path.join(ROOT, "profiles", "verify_chain_kernel_batched32x48_counters.json")
-VERIFY_SRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc", "verify.hip")
-COUNTERS_UT = os.path.join(ROOT, "profiles", "verify_ut_kernel_batched32x48_counters.json")
-VERIFY_UT_SRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc", "verify_ut.hip")
+CSRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc")
+# Committed rocprofv3 HBM counter records of each verify kernel on the batched workload, and
+# the sources that kernel is built from: a record only counts while their hash still matches.
+COUNTERS = {
+    "chain": os.path.join(ROOT, "profiles", "verify_chain_kernel_batched32x48_counters.json"),
+    "ut": os.path.join(ROOT, "profiles", "verify_ut_mfma_kernel_batched32x48_counters.json"),
+}
+KERNEL_SOURCES = {
+    "chain": ["verify.hip", "verify_common.h", "gdn_device.h"],
+    "ut": ["verify_ut_mfma.hip", "ut_common.h", "verify_common.h", "gdn_device.h"],
+}
+KERNEL = {"chain": "verify_chain_kernel<128, bf16>", "ut": "verify_ut_mfma_kernel"}
 METRIC = "verified tree nodes/sec per GDN layer + achieved HBM GB/s vs peak, 1 MI355X"
 
 
@@ -100,16 +113,22 @@ def fold_bytes(pending, H, d, C, n_layers):
 # CPU baseline: the oracle as it stands, on a bounded sample of (sequence, layer) pairs
 # ----------------------------------------------------------------------------------------
 
+def kernel_source_sha256(verify):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[verify]:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(config, lpc, verify):
     """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
-    or None when the verify source changed since they were taken (or another workload)."""
-    import hashlib
-    path = COUNTERS if verify == "chain" else COUNTERS_UT
-    src = VERIFY_SRC if verify == "chain" else VERIFY_UT_SRC
+    or None when the kernel's sources changed since they were taken (or another workload)."""
+    path = COUNTERS[verify]
     if config != 3 or lpc != 1 or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["verify_source_sha256"]:
+    if kernel_source_sha256(verify) != rec.get("kernel_sources_sha256"):
         return None
     return rec["traffic_bytes_per_launch"]
 
@@ -167,8 +186,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layers-per-call", type=int, default=1)
-    ap.add_argument("--verify", choices=["chain", "ut"], default="chain",
-                    help="chain: heavy-light chains in dependency waves; ut: tree-masked UT form")
+    ap.add_argument("--verify", choices=["ut", "chain"], default="ut",
+                    help="headline path (both are timed): ut = tree-masked form on the matrix "
+                         "cores; chain = heavy-light chains in dependency waves")
+    ap.add_argument("--only", action="store_true", help="time the headline path only")
     ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--cpu-workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -234,78 +255,99 @@ def main(argv=None):
     def upload(a):
         return torch.from_numpy(a).pin_memory().to(dev, non_blocking=True)
 
-    acc = dict(verify_ms=0.0, verify_launches=0, verify_bytes=0, conv_bytes=0, commit_bytes=0)
     n_waves = int(view["n_waves"])
-    # Verify launches are timed by events recorded by the dispatches themselves (no extra
-    # packets on the stream); one pair per (step, layer call, wave).
-    launches = 1 if args.verify == "ut" else n_waves
-    ev = [[[(binding.HipEvent(), binding.HipEvent()) for _ in range(launches)]
-           for _ in range(len(vargs))] for _ in range(args.steps)]
 
-    def step(s, timed_index):
-        image = binding.hld_schedule(trees)  # a1: host schedule of this step's trees
-        dev_image = upload(image)
-        pending = [int(L) for L in lay.pending_host]
-        for li in range(len(vargs)):
-            binding.tree_conv(cargs[li], image, dev_image)
-            if args.verify == "ut":
-                if timed_index is None:
-                    binding.tree_verify_ut(vargs[li], image, dev_image)
+    def run_path(verify):
+        acc = dict(verify_ms=0.0, verify_launches=0, verify_bytes=0, conv_bytes=0,
+                   commit_bytes=0)
+        # Verify launches are timed by events recorded by the dispatches themselves (no extra
+        # packets on the stream); one pair per (step, layer call, launch).
+        launches = 1 if verify == "ut" else n_waves
+        ev = [[[(binding.HipEvent(), binding.HipEvent()) for _ in range(launches)]
+               for _ in range(len(vargs))] for _ in range(args.steps)]
+
+        def step(s, timed_index):
+            image = binding.hld_schedule(trees)  # a1: host schedule of this step's trees
+            dev_image = upload(image)
+            pending = [int(L) for L in lay.pending_host]
+            for li in range(len(vargs)):
+                binding.tree_conv(cargs[li], image, dev_image)
+                if verify == "ut":
+                    if timed_index is None:
+                        binding.tree_verify_ut(vargs[li], image, dev_image)
+                    else:
+                        e0, e1 = ev[timed_index][li][0]
+                        binding.tree_verify_ut_timed(vargs[li], image, dev_image, e0, e1)
+                    continue
+                for w in range(n_waves):
+                    if timed_index is None:
+                        binding.tree_verify_wave(vargs[li], image, dev_image, w)
+                    else:
+                        e0, e1 = ev[timed_index][li][w]
+                        binding.tree_verify_wave_timed(vargs[li], image, dev_image, w, e0, e1)
+            paths = all_paths[s]
+            flat, offs = binding.pack_paths(paths)
+            binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs))
+            if timed_index is not None:  # byte accounting after the launches, off the GPU's path
+                calls = len(vargs)
+                if verify == "ut":
+                    acc["verify_bytes"] += calls * ut_bytes(view, pending, H, d, in_bytes, lpc)
                 else:
-                    e0, e1 = ev[timed_index][li][0]
-                    binding.tree_verify_ut_timed(vargs[li], image, dev_image, e0, e1)
-                continue
-            for w in range(n_waves):
-                if timed_index is None:
-                    binding.tree_verify_wave(vargs[li], image, dev_image, w)
-                else:
-                    e0, e1 = ev[timed_index][li][w]
-                    binding.tree_verify_wave_timed(vargs[li], image, dev_image, w, e0, e1)
-        paths = all_paths[s]
-        flat, offs = binding.pack_paths(paths)
-        binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs))
-        if timed_index is not None:  # byte accounting after the launches, off the GPU's path
-            calls = len(vargs)
-            if args.verify == "ut":
-                acc["verify_bytes"] += calls * ut_bytes(view, pending, H, d, in_bytes, lpc)
-            else:
-                acc["verify_bytes"] += calls * sum(
-                    verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc) for w in range(n_waves))
-            acc["verify_launches"] += calls * launches
-            acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
-            acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly)
+                    acc["verify_bytes"] += calls * sum(
+                        verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc)
+                        for w in range(n_waves))
+                acc["verify_launches"] += calls * launches
+                acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
+                acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly)
 
-    for s in range(args.warmup):
-        step(s, None)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i, s in enumerate(range(args.warmup, n_total)):
-        step(s, i)
-    flush_pending = lay.pending_host.copy()
-    binding.flush(va_all, ca_all, lay)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for per_step in ev:
-        for per_call in per_step:
-            for e0, e1 in per_call:
-                acc["verify_ms"] += e0.elapsed_ms(e1)
+        for s in range(args.warmup):
+            step(s, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i, s in enumerate(range(args.warmup, n_total)):
+            step(s, i)
+        flush_pending = lay.pending_host.copy()
+        binding.flush(va_all, ca_all, lay)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for per_step in ev:
+            for per_call in per_step:
+                for e0, e1 in per_call:
+                    acc["verify_ms"] += e0.elapsed_ms(e1)
+        total_bytes = acc["verify_bytes"] + acc["conv_bytes"] + acc["commit_bytes"] + \
+            fold_bytes(flush_pending, H, d, C, Ly)
+        v_launch_s = acc["verify_ms"] / 1e3 / max(acc["verify_launches"], 1)
+        v_launch_bytes = acc["verify_bytes"] / max(acc["verify_launches"], 1)
+        achieved = v_launch_bytes / v_launch_s / 1e9
+        traffic_bytes = measured_traffic(args.config, lpc, verify)
+        return {
+            "value": args.steps * T * Ly / wall,
+            "ms_per_step": wall * 1e3 / args.steps,
+            "roofline": {
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS,
+                "traffic": None if traffic_bytes is None else traffic_bytes / v_launch_s / 1e9,
+                "traffic_bytes_per_launch": traffic_bytes,
+                "kernel": KERNEL[verify],
+                "bytes_per_launch": v_launch_bytes, "launch_us": v_launch_s * 1e6,
+            },
+            "algorithmic_GBps_step": total_bytes / wall / 1e9,
+            "algorithmic_bytes_per_step": total_bytes / args.steps,
+            "compulsory_GBps_step": args.steps * Ly * S * H * 2 * 4 * d * d / wall / 1e9,
+            "verify_ms_per_step": acc["verify_ms"] / args.steps,
+        }
 
-    node_layers = args.steps * T * Ly
-    total_bytes = acc["verify_bytes"] + acc["conv_bytes"] + acc["commit_bytes"] + \
-        fold_bytes(flush_pending, H, d, C, Ly)
-    v_launch_s = acc["verify_ms"] / 1e3 / max(acc["verify_launches"], 1)
-    v_launch_bytes = acc["verify_bytes"] / max(acc["verify_launches"], 1)
-    achieved = v_launch_bytes / v_launch_s / 1e9
-    compulsory = args.steps * Ly * S * H * 2 * 4 * d * d
-    traffic_bytes = measured_traffic(args.config, lpc, args.verify)
+    order = [args.verify] + ([] if args.only else [p for p in ("ut", "chain") if p != args.verify])
+    runs = {p: run_path(p) for p in order}
+    head = runs[args.verify]
     result = {
         "metric": METRIC,
-        "value": node_layers / wall,
+        "value": head["value"],
         "unit": "node-layers/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -320,20 +362,13 @@ def main(argv=None):
             "boundary_nodes": int(view["n_boundaries"]), "layers_per_call": lpc,
             "verify": args.verify,
         },
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if traffic_bytes is None else traffic_bytes / v_launch_s / 1e9,
-            "traffic_bytes_per_launch": traffic_bytes,
-            "kernel": ("verify_chain_kernel" if args.verify == "chain" else "verify_ut_kernel")
-                      + "<128, bf16>",
-            "bytes_per_launch": v_launch_bytes, "launch_us": v_launch_s * 1e6,
-        },
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
-        "algorithmic_GBps_step": total_bytes / wall / 1e9,
-        "algorithmic_bytes_per_step": total_bytes / args.steps,
-        "compulsory_GBps_step": compulsory / wall / 1e9,
-        "verify_ms_per_step": acc["verify_ms"] / args.steps,
+        "algorithmic_GBps_step": head["algorithmic_GBps_step"],
+        "algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"],
+        "compulsory_GBps_step": head["compulsory_GBps_step"],
+        "verify_ms_per_step": head["verify_ms_per_step"],
+        "paths": runs,
         "input_generation_s": gen_s,
     }
     if args.copy_probe:
