@@ -337,6 +337,22 @@ def main(argv=None):
             "verify_ms_per_step": acc["verify_ms"] / args.steps,
         }
 
+    # Draft-tree builder (host): the batch's trees from seeded synthetic drafts, budget 22,
+    # top-4, tau 6, chain pre-seed, 15 draft positions.
+    drafts = [synth.draft_scores(args.config, 0, b, 15, 4) for b in range(S)]
+    d_lp = np.stack([x[0] for x in drafts])
+    d_tok = np.stack([x[1] for x in drafts])
+    binding.ddtree_build(d_lp, d_tok, None, budget=22, tau=6.0)
+    reps = 200
+    t_b = time.perf_counter()
+    for _ in range(reps):
+        built = binding.ddtree_build(d_lp, d_tok, None, budget=22, tau=6.0)
+    us_batch = (time.perf_counter() - t_b) / reps * 1e6
+    ddtree = {"trees": S, "budget": 22, "top_k": 4, "positions": 15, "tau": 6.0,
+              "chain_seed": True, "us_per_batch": us_batch,
+              "nodes_per_batch": int(sum(len(t["parent"]) for t in built)),
+              "note": "host call through the binding (marshalling included), one thread"}
+
     order = [args.verify] + ([] if args.only else [p for p in ("ut", "chain") if p != args.verify])
     runs = {p: run_path(p) for p in order}
     head = runs[args.verify]
@@ -369,6 +385,7 @@ def main(argv=None):
         "compulsory_GBps_step": head["compulsory_GBps_step"],
         "verify_ms_per_step": head["verify_ms_per_step"],
         "paths": runs,
+        "ddtree_build": ddtree,
         "input_generation_s": gen_s,
     }
     if args.copy_probe:

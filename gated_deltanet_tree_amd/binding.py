@@ -20,7 +20,8 @@ GDN_F32, GDN_BF16 = 0, 1
 STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_ETREE", -3: "GDN_EPATH",
           -4: "GDN_ECAPACITY", -5: "GDN_EDEVICE"}
 EXPORTS = [
-    "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_verify_workspace_bytes",
+    "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_ddtree_build",
+    "gdn_verify_workspace_bytes",
     "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed",
     "gdn_tree_verify_ut", "gdn_tree_verify_ut_timed", "gdn_tree_conv",
     "gdn_commit_path",
@@ -39,6 +40,7 @@ class GdnError(RuntimeError):
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I32P = ctypes.POINTER(ctypes.c_int32)
+_FP = ctypes.POINTER(ctypes.c_float)
 
 
 class VerifyArgs(ctypes.Structure):
@@ -78,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.gdn_schedule_words.argtypes = [_I32, _I32]
     L.gdn_hld_schedule.restype = _I32
     L.gdn_hld_schedule.argtypes = [_I32P, _I32P, _I32, _I32P, ctypes.c_size_t]
+    L.gdn_ddtree_build.restype = _I32
+    L.gdn_ddtree_build.argtypes = [_FP, _I32P, _I32P, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                   _I32, _I32P, _I32P, _I32P, _I32P, _FP, _I32P]
     L.gdn_verify_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_verify_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32]
     L.gdn_tree_verify.restype = _I32
@@ -168,6 +173,37 @@ def schedule_view(image: np.ndarray) -> dict:
     return dict(n_seqs=S, n_nodes=T, n_chains=n_chains, n_waves=n_waves,
                 n_boundaries=int(image[5]), max_chain_len=int(image[6]), max_tree=int(image[7]),
                 seq_offsets=seq, wave_offsets=wave, chain_offsets=chain, **fields)
+
+
+def ddtree_build(logp, tokens=None, root_tokens=None, budget=22, tau=6.0, chain_seed=True):
+    """Best-first draft trees of a batch: logp [B][L][K] (or [L][K]) fp32 log-probabilities,
+    tokens of the same shape (optional).  Returns a list of dicts parent/depth/rank/score
+    (and token) per tree, each cut to its node count."""
+    lp = np.ascontiguousarray(logp, dtype=np.float32)
+    single = lp.ndim == 2
+    if single:
+        lp = lp[None]
+    B, L, K = lp.shape
+    tk = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, L, K)
+    rt = None if root_tokens is None else _i32(np.reshape(root_tokens, (B,)))
+    out = {name: np.full((B, budget), -1, dtype=np.int32) for name in ("parent", "depth", "rank",
+                                                                        "token")}
+    sc = np.zeros((B, budget), dtype=np.float32)
+    n = np.zeros(B, dtype=np.int32)
+    fp = lambda a: a.ctypes.data_as(_FP)  # noqa: E731
+    _check(lib().gdn_ddtree_build(fp(lp), None if tk is None else _ptr(tk),
+                                  None if rt is None else _ptr(rt), B, L, K, budget,
+                                  ctypes.c_float(tau), int(bool(chain_seed)), _ptr(out["parent"]),
+                                  _ptr(out["depth"]), _ptr(out["rank"]),
+                                  None if tk is None else _ptr(out["token"]), fp(sc), _ptr(n)),
+           "gdn_ddtree_build")
+    trees = []
+    for b in range(B):
+        m = int(n[b])
+        t = {k: v[b, :m].copy() for k, v in out.items() if k != "token" or tk is not None}
+        t["score"] = sc[b, :m].copy()
+        trees.append(t)
+    return trees[0] if single else trees
 
 
 def verify_workspace_bytes(image: np.ndarray, n_heads: int, head_dim: int, n_layers: int) -> int:

@@ -23,7 +23,7 @@ import numpy as np
 ROOT_SEED = 20261202
 STREAMS = {
     "tree": 0, "q": 1, "k": 2, "v": 3, "beta": 4, "gate": 5, "state": 6,
-    "x": 7, "weight": 8, "conv_state": 9, "path": 10,
+    "x": 7, "weight": 8, "conv_state": 9, "path": 10, "draft": 11,
 }
 
 # Workload presets. d = head dim (d_k = d_v), H = heads, N = nodes per tree, K = top-k,
@@ -152,6 +152,22 @@ def config_path(config: int, step: int, seq: int, parent: np.ndarray) -> np.ndar
     else:
         length = int(rng.integers(1, int(node_depths(parent).max()) + 2))
     return random_path(rng, parent, length)
+
+
+def draft_scores(config: int, step: int, seq: int, positions: int, top_k: int,
+                 vocab: int = 64) -> tuple[np.ndarray, np.ndarray]:
+    """Synthetic draft of one sequence: for each of `positions` tokens after the root, the
+    top-k candidates (ids, fp32 log-probabilities sorted descending) of a softmax over `vocab`
+    logits ~ N(0, s^2), with s falling from 4 to 1.5 along the block (later positions are less
+    certain).  Returns (logp [positions][top_k], tokens [positions][top_k])."""
+    rng = rng_for(config, step, 0, seq, "draft")
+    scale = np.linspace(4.0, 1.5, max(positions, 1))[:positions, None]
+    logits = rng.normal(size=(positions, vocab)) * scale
+    logp = logits - np.log(np.exp(logits - logits.max(axis=1, keepdims=True)).sum(
+        axis=1, keepdims=True)) - logits.max(axis=1, keepdims=True)
+    order = np.argsort(-logp, axis=1, kind="stable")[:, :top_k]
+    lp = np.take_along_axis(logp, order, axis=1).astype(np.float32)
+    return np.minimum(lp, np.float32(0.0)), order.astype(np.int32)
 
 
 # ----------------------------------------------------------------------------------------

@@ -105,6 +105,43 @@ gdn_status gdn_hld_schedule(const int32_t *parent_local, const int32_t *seq_offs
                             int32_t n_seqs, int32_t *image, size_t image_words);
 
 /* ------------------------------------------------------------------------------------
+ * Draft-tree builder (host): best-first tree over the draft's top-K candidates per position,
+ * with a node budget, confidence pruning and a greedy-chain pre-seed.
+ * Luce DFlash server README, "How it works" (best-first tree of up to 22 nodes spanning the
+ * top-K branches of each position; chain pre-seed); SpecLA guide, the section on enabling it
+ * with one flag (budget 22, tau 6, top-k 4; nodes scoring below q* - tau are pruned).
+ *
+ * For tree b, position i (0-based, the i-th token after the root) has top_k candidates with
+ * log-probabilities logp[b][i][0..top_k-1], sorted descending (candidate 0 is the greedy
+ * token), every value finite and <= 0.  A node at depth d takes candidate k of position d-1;
+ * its children are the candidates of position d.
+ *   score(root) = 0, score(node) = score(parent) + logp, fp32, summed along the path;
+ *   q*(d) = the greedy chain's score at depth d = the best score at depth d;
+ *   a node with score < q*(d) - tau (fp32) is pruned with its subtree; tau = INFINITY prunes
+ *   nothing; tau < 0 or NaN is GDN_EINVAL;
+ *   the budget counts the root;
+ *   chain_seed != 0 places the greedy chain first (depths 1 .. min(n_positions, budget-1));
+ *   every further node is the best remaining candidate: higher score first, then the
+ *   shallower, then the smaller sequence of candidate ranks along the path.
+ * Node ids are insertion order, so parent[i] < i: parent[b][0 .. n_nodes[b]) is directly a
+ * valid `parent_local` tree for gdn_hld_schedule.
+ *
+ * logp:        host [n_trees][n_positions][top_k] fp32.
+ * tokens:      host [n_trees][n_positions][top_k] token ids, or NULL when token is NULL.
+ * root_tokens: host [n_trees], or NULL (the root's token is then -1).
+ * parent, depth, rank, token, score: host [n_trees][budget], caller-owned outputs; rank is
+ *   the candidate index of the node at its position (-1 for the root); slots at or beyond
+ *   n_nodes[b] are set to -1 (score 0).  token may be NULL.
+ * n_nodes:     host [n_trees], nodes of each tree (1 <= n_nodes[b] <= budget).
+ * Limits: 0 <= n_positions <= 16, 1 <= top_k <= 16, budget >= 1; otherwise GDN_EINVAL and
+ * nothing is written.  Deterministic; no device work. */
+gdn_status gdn_ddtree_build(const float *logp, const int32_t *tokens,
+                            const int32_t *root_tokens, int32_t n_trees, int32_t n_positions,
+                            int32_t top_k, int32_t budget, float tau, int32_t chain_seed,
+                            int32_t *parent, int32_t *depth, int32_t *rank, int32_t *token,
+                            float *score, int32_t *n_nodes);
+
+/* ------------------------------------------------------------------------------------
  * Tree verify with fused deferred commit (SpecLA guide, mechanisms 1, 2 and 4).
  *
  * For every node n of every tree, every head h, every layer l processed:
