@@ -178,6 +178,20 @@ def replay(S0, k, v, beta, gate, path):
     return S
 
 
+def prefill(S0, q, k, v, beta, gate, step=gdn_step):
+    """Sequential prefill of a token sequence (SpecLA guide, the flush section: after a flush
+    the runtime continues without speculation; the GDN layer then runs over plain token
+    sequences): for t = 0..T-1, S <- g S (I - beta k k^T) + beta v k^T and o_t = S q_t.
+    Returns (o [T,H,dv], S_T).  This is the definition the chunked kernel must reach."""
+    S0, q, k, v, beta, gate = _as64(S0, q, k, v, beta, gate)
+    S = S0.copy()
+    out = np.empty((len(k),) + S.shape[:2])
+    for t in range(len(k)):
+        S = step(S, k[t], v[t], beta[t], gate[t])
+        out[t] = np.einsum("hij,hj->hi", S, q[t])
+    return out, S
+
+
 def fold(S0, kf, uf, lgf):
     """Apply accepted factors in path order: S <- exp(lg) S + u k^T (SpecLA guide, mechanisms
     3 and 4).  kf [L,H,dk], uf [L,H,dv], lgf [L,H].  Used only to pin `factors`."""

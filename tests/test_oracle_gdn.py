@@ -255,3 +255,49 @@ def test_rejects_bad_trees():
     for bad in ([0, 0], [-1, 1], [-1, 0, 2], [-1, -1]):
         with pytest.raises(ValueError):
             gdn.check_tree(bad)
+
+
+# ---------------------------------------------------------------------------------------
+# sequential prefill (the plain sequence path after a flush)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 2, 7, 16, 33])
+def test_prefill_equals_chain_verify_and_replay(T):
+    """A token sequence is a tree without branching: prefill outputs equal the per-path
+    verify of the chain tree, and its final state equals the replay of the whole path."""
+    rng = np.random.default_rng(400 + T)
+    S0, q, k, v, beta, gate = _inputs(T, 2, 16, rng)
+    o, S = gdn.prefill(S0, q, k, v, beta, gate)
+    chain = np.arange(-1, T - 1)
+    o_ref, _ = gdn.verify(chain, S0, q, k, v, beta, gate, keep_states=False)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, gdn.replay(S0, k, v, beta, gate, np.arange(T)), rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_prefill_matrix_form_and_split_sequences():
+    """The literal d x d projector form gives the same prefill, and prefilling A then B from
+    A's final state equals prefilling A+B."""
+    rng = np.random.default_rng(450)
+    S0, q, k, v, beta, gate = _inputs(20, 3, 8, rng)
+    o, S = gdn.prefill(S0, q, k, v, beta, gate)
+    o2, S2 = gdn.prefill(S0, q, k, v, beta, gate, step=gdn.gdn_step_matrix)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-13)
+    oa, Sa = gdn.prefill(S0, q[:9], k[:9], v[:9], beta[:9], gate[:9])
+    ob, Sb = gdn.prefill(Sa, q[9:], k[9:], v[9:], beta[9:], gate[9:])
+    np.testing.assert_allclose(np.concatenate([oa, ob]), o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Sb, S, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_empty_and_zero_gate():
+    rng = np.random.default_rng(460)
+    S0, q, k, v, beta, gate = _inputs(3, 1, 8, rng)
+    o, S = gdn.prefill(S0, q[:0], k[:0], v[:0], beta[:0], gate[:0])
+    assert o.shape == (0, 1, 8) and np.array_equal(S, S0)
+    gate = gate.copy()
+    gate[1] = 0.0  # a zero gate erases the history: S_1 = beta v k^T
+    _, S = gdn.prefill(S0, q[:2], k[:2], v[:2], beta[:2], gate[:2])
+    want = gdn.prefill(np.zeros_like(S0), q[1:2], k[1:2], v[1:2], beta[1:2],
+                       np.ones_like(gate[1:2]))[1]
+    np.testing.assert_allclose(S, want, rtol=1e-12, atol=1e-13)
