@@ -24,7 +24,7 @@ EXPORTS = [
     "gdn_verify_workspace_bytes",
     "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed",
     "gdn_tree_verify_ut", "gdn_tree_verify_ut_timed", "gdn_tree_conv",
-    "gdn_commit_path",
+    "gdn_commit_path", "gdn_prefill", "gdn_prefill_timed",
     "gdn_compact_factors", "gdn_flush",
 ]
 IMAGE_HEADER = 16
@@ -50,6 +50,15 @@ class VerifyArgs(ctypes.Structure):
         ("q", _P), ("k", _P), ("v", _P), ("beta", _P), ("gate", _P), ("state", _P),
         ("bank_k", _P * 2), ("bank_u", _P * 2), ("bank_lg", _P * 2),
         ("role", _P), ("pending_len", _P), ("workspace", _P), ("out", _P),
+    ]
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", _I32), ("n_heads", _I32), ("head_dim", _I32), ("n_tokens", _I32),
+        ("layer_begin", _I32), ("n_layers", _I32), ("in_dtype", _I32), ("reserved", _I32),
+        ("q", _P), ("k", _P), ("v", _P), ("beta", _P), ("gate", _P), ("seq_offsets", _P),
+        ("state", _P), ("out", _P),
     ]
 
 
@@ -96,6 +105,10 @@ def lib() -> ctypes.CDLL:
     L.gdn_tree_verify_ut.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
     L.gdn_tree_verify_ut_timed.restype = _I32
     L.gdn_tree_verify_ut_timed.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P, _P, _P]
+    L.gdn_prefill.restype = _I32
+    L.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _I32P, _P]
+    L.gdn_prefill_timed.restype = _I32
+    L.gdn_prefill_timed.argtypes = [ctypes.POINTER(PrefillArgs), _I32P, _P, _P, _P]
     L.gdn_tree_conv.restype = _I32
     L.gdn_tree_conv.argtypes = [ctypes.POINTER(ConvArgs), _I32P, _P, _P]
     L.gdn_commit_path.restype = _I32
@@ -353,6 +366,41 @@ def tree_verify_ut_timed(args: VerifyArgs, image: np.ndarray, dev_image, start: 
     _check(lib().gdn_tree_verify_ut_timed(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                           start.handle, stop.handle, _stream(stream)),
            "gdn_tree_verify_ut_timed")
+
+
+def prefill_args(host_offsets, dev_offsets, q, k, v, beta, gate, state, out, layer_begin=0,
+                 n_layers=1):
+    """Arguments of gdn_prefill; q/k/v [Ly][T][H][d], beta/gate [Ly][T][H], state
+    [Ly][S][H][d][d], out [Ly][T][H][d] (torch tensors), offsets [S+1] (numpy + device)."""
+    import torch
+    host_offsets = _i32(host_offsets)
+    S, T = len(host_offsets) - 1, int(host_offsets[-1])
+    H, d = int(state.shape[2]), int(state.shape[3])
+    Ly_end = layer_begin + n_layers
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _need(t, Ly_end * T * H * d, name)
+    _need(beta, Ly_end * T * H, "beta")
+    _need(gate, Ly_end * T * H, "gate")
+    _need(state, Ly_end * S * H * d * d, "state")
+    _need(dev_offsets, S + 1, "seq_offsets")
+    a = PrefillArgs()
+    a.n_seqs, a.n_heads, a.head_dim, a.n_tokens = S, H, d, T
+    a.layer_begin, a.n_layers = layer_begin, n_layers
+    a.in_dtype = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
+    a.q, a.k, a.v, a.beta, a.gate = (_dev(t) for t in (q, k, v, beta, gate))
+    a.seq_offsets, a.state, a.out = _dev(dev_offsets), _dev(state), _dev(out)
+    a.host_offsets = host_offsets
+    return a
+
+
+def prefill(args: PrefillArgs, stream=None):
+    _check(lib().gdn_prefill(ctypes.byref(args), _ptr(args.host_offsets), _stream(stream)),
+           "gdn_prefill")
+
+
+def prefill_timed(args: PrefillArgs, start: "HipEvent", stop: "HipEvent", stream=None):
+    _check(lib().gdn_prefill_timed(ctypes.byref(args), _ptr(args.host_offsets), start.handle,
+                                   stop.handle, _stream(stream)), "gdn_prefill_timed")
 
 
 class HipEvent:

@@ -228,6 +228,43 @@ gdn_status gdn_tree_verify_ut_timed(const gdn_verify_args *args, const int32_t *
                                     void *stop_event, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Chunked prefill (SpecLA guide, the flush section: after a flush, or without speculation,
+ * the GDN layer runs over plain token sequences; the sequence path shares the commit
+ * semantics of the tree path).  For every sequence b, head h and layer l processed:
+ *   for t in the sequence, in order:  S <- g_t S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *                                     out[t] = S q_t,
+ * starting from the committed state; the final S is written back to `state`.  Pending
+ * factors are not read: call gdn_flush first when a tree verify left any.
+ * Work: one 64-thread workgroup per (layer, sequence, head, block of 32 state rows) walks the
+ * sequence in chunks of 16 tokens on the matrix cores (tree-masked form of a chain).
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t n_seqs;      /* S                                                               */
+    int32_t n_heads;     /* H >= 1                                                          */
+    int32_t head_dim;    /* d, must be 128                                                  */
+    int32_t n_tokens;    /* T: tokens of all sequences, packed                              */
+    int32_t layer_begin; /* first layer processed                                           */
+    int32_t n_layers;    /* layers processed, >= 1                                          */
+    int32_t in_dtype;    /* must be GDN_BF16                                                */
+    int32_t reserved;
+    const void *q, *k, *v;      /* [Ly][T][H][d] bf16, 16-byte aligned                       */
+    const void *beta, *gate;    /* [Ly][T][H] bf16, gate = g in (0, 1] (linear)              */
+    const int32_t *seq_offsets; /* device [S+1]: sequence b holds tokens [off[b], off[b+1])  */
+    float *state;        /* [Ly][S][H][d][d] fp32 committed states, in/out, 16-byte aligned */
+    float *out;          /* [Ly][T][H][d] fp32 outputs, 16-byte aligned                     */
+} gdn_prefill_args;
+
+/* host_seq_offsets: the same offsets on the host (validated: 0 .. n_tokens, non-decreasing).
+ * GDN_EINVAL for other head dims or dtypes, bad offsets, null or misaligned pointers; nothing
+ * is launched then.  Empty sequences leave their states untouched. */
+gdn_status gdn_prefill(const gdn_prefill_args *args, const int32_t *host_seq_offsets,
+                       void *stream);
+
+/* gdn_prefill with dispatch-recorded start/stop HIP events (see gdn_tree_verify_wave_timed). */
+gdn_status gdn_prefill_timed(const gdn_prefill_args *args, const int32_t *host_seq_offsets,
+                             void *start_event, void *stop_event, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Tree-aware causal depthwise conv with fused conv-window fold (DFlash README, "How it
  * works", tree-aware conv gather; SpecLA guide, mechanisms 1, 3 and 4).
  *
