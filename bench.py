@@ -109,6 +109,62 @@ def fold_bytes(pending, H, d, C, n_layers):
                           for L in pending if L > 0)
 
 
+def prefill_bytes(T, S, H, d):
+    """One prefill call over T tokens of S sequences: q, k, v (bf16) and beta, g (bf16) in,
+    o (fp32) out per (token, head); every (sequence, head) state read and written once."""
+    return T * H * (3 * d * 2 + 2 * 2 + 4 * d) + 2 * S * H * d * d * 4
+
+
+def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, layers=4,
+                  reps=3):
+    """Chunked prefill of S sequences of `length` tokens, one layer per call.  Inputs are
+    drawn on the device from a seeded generator (q, k unit-normalised, beta = sigmoid,
+    g = exp(-softplus)), bf16, resident before timing."""
+    import torch.nn.functional as F
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.ROOT_SEED + 4)
+    T = S * length
+
+    def draw(*shape):
+        return torch.randn(*shape, device=dev, generator=gen)
+
+    def unit(x):
+        return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    q, k = unit(draw(layers, T, H, d)), unit(draw(layers, T, H, d))
+    v = draw(layers, T, H, d).to(torch.bfloat16)
+    beta = torch.sigmoid(draw(layers, T, H)).to(torch.bfloat16)
+    gate = torch.exp(-F.softplus(draw(layers, T, H))).to(torch.bfloat16)
+    state = 0.02 * draw(layers, S, H, d, d)
+    out = torch.empty(layers, T, H, d, device=dev)
+    offs = np.arange(0, T + 1, length, dtype=np.int32)
+    dev_offs = torch.from_numpy(offs).to(dev)
+    calls = [binding.prefill_args(offs, dev_offs, q, k, v, beta, gate, state, out,
+                                  layer_begin=l, n_layers=1) for l in range(layers)]
+    for a in calls:  # warm-up
+        binding.prefill(a)
+    torch.cuda.synchronize()
+    ev = [[(binding.HipEvent(), binding.HipEvent()) for _ in calls] for _ in range(reps)]
+    t0 = time.perf_counter()
+    for r in range(reps):
+        for a, (e0, e1) in zip(calls, ev[r]):
+            binding.prefill_timed(a, e0, e1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = sum(e0.elapsed_ms(e1) for per in ev for e0, e1 in per) / 1e3 / (reps * layers)
+    per_call = prefill_bytes(T, S, H, d)
+    achieved = per_call / launch_s / 1e9
+    return {
+        "workload": f"{S} sequences x {length} tokens x {H} heads x d{d}, bf16 inputs, fp32 "
+                    f"state, one layer per call, {layers} layers x {reps} repeats",
+        "value": reps * layers * T / wall, "unit": "token-layers/s",
+        "ms_per_layer": wall * 1e3 / (reps * layers),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "kernel": "prefill_kernel",
+                     "bytes_per_launch": per_call, "launch_us": launch_s * 1e6},
+    }
+
+
 # ----------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample of (sequence, layer) pairs
 # ----------------------------------------------------------------------------------------
@@ -190,6 +246,7 @@ def main(argv=None):
                     help="headline path (both are timed): ut = tree-masked form on the matrix "
                          "cores; chain = heavy-light chains in dependency waves")
     ap.add_argument("--only", action="store_true", help="time the headline path only")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill line")
     ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--cpu-workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -386,6 +443,7 @@ def main(argv=None):
         "verify_ms_per_step": head["verify_ms_per_step"],
         "paths": runs,
         "ddtree_build": ddtree,
+        "prefill": None if args.no_prefill else prefill_bench(torch, binding, synth, dev),
         "input_generation_s": gen_s,
     }
     if args.copy_probe:

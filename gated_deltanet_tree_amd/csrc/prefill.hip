@@ -58,6 +58,7 @@ struct PrefillLds {
     char in[kInChunks * 16];         // k | q | v rows of the chunk, bf16
     uint32_t bg[2][kC];              // beta | gate slots (bf16 zero-extended)
     float G[kC], gam[kC];            // G_t and E(C-1, t)
+    float E[kC][kC];                 // E[t][s]: product of the gates of tokens s+1 .. t
     float Tm[kC][kC], Cm[kC][kC];    // read as whole rows by every lane (broadcast)
     float W[kC][kRowPad], GR[kC][kRowPad], Ug[kC][kRowPad];
 };
@@ -159,16 +160,21 @@ void prefill_kernel(PrefillParams P) {
         }
         __builtin_amdgcn_s_waitcnt(0);  // the chunk is in LDS
         wave_order();
-        if (lane < kC) {  // G_t over tokens 0..t; gamma_t = E(nc-1, t) over t+1..nc-1
-            float gp = 1.f, gs = 1.f;
+        if (lane < kC) {  // G_t over tokens 0..t; row s of E by a running product over t > s
+            float gv[kC];
+#pragma unroll
+            for (int m = 0; m < kC; ++m) gv[m] = slot_f32<bf16_t>(sm.bg[1][m]);
+            float gp = 1.f, e = 1.f;
+#pragma unroll
             for (int m = 0; m < kC; ++m) {
-                const float g = slot_f32<bf16_t>(sm.bg[1][m]);
-                if (m <= lane) gp *= g;
-                if (m > lane && m < nc) gs *= g;
+                if (m <= lane) gp *= gv[m];
+                if (m > lane) e *= gv[m];
+                sm.E[m][lane] = m > lane ? e : (m == lane ? 1.f : 0.f);
             }
             sm.G[lane] = gp;
-            sm.gam[lane] = lane < nc ? gs : 0.f;
         }
+        wave_order();
+        if (lane < kC) sm.gam[lane] = lane < nc ? sm.E[nc - 1][lane] : 0.f;  // E(nc-1, t)
 
         // ---- 2. pair products [k; q] K^T: T and C -------------------------------------
         // M tile jt stacks k (rows 0-7) and q (rows 8-15) of tokens 8jt .. 8jt+7; N = the 16
@@ -187,8 +193,7 @@ void prefill_kernel(PrefillParams P) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 8 * jt + 4 * (lg & 1) + r, sk = lr;
-                float e = 1.f;  // E(t, sk) = product of the gates of tokens sk+1 .. t
-                for (int m = sk + 1; m <= t; ++m) e *= slot_f32<bf16_t>(sm.bg[1][m]);
+                const float e = sm.E[t][sk];
                 const bool in_t = t < nc && sk < nc;
                 if (lg >= 2)
                     sm.Cm[t][sk] = (in_t && sk <= t) ? e * acc[r] : 0.f;
@@ -227,7 +232,6 @@ void prefill_kernel(PrefillParams P) {
                         acc[jt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[nt], acc[jt][nt], 0, 0, 0);
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);  // one k-step's split at a time
             }
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt)
@@ -280,27 +284,38 @@ void prefill_kernel(PrefillParams P) {
         wave_order();
 
         // ---- 5. S^T <- G S^T + K^T (gamma u) ------------------------------------------------
+        // 16 independent accumulator tiles per k-step, so the matrix-core ops pipeline.
         {
             const float Ge = sm.G[nc - 1];
+            floatx4 a4[2][8];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) {
-                    floatx4 a4 = {Ge * s[nt][mt][0], Ge * s[nt][mt][1], Ge * s[nt][mt][2],
-                                  Ge * s[nt][mt][3]};
+                for (int mt = 0; mt < 8; ++mt)
+                    a4[nt][mt] = floatx4{Ge * s[nt][mt][0], Ge * s[nt][mt][1], Ge * s[nt][mt][2],
+                                         Ge * s[nt][mt][3]};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const int t = 4 * ks + lg;  // k index of this lane
-                        const float kv = bf16_at(sm.in + size_t(t) * kNodeBytes, 16 * mt + lr);
-                        const float uv = sm.Ug[t][16 * nt + lr];
-                        a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, uv, a4, 0, 0, 0);
-                    }
-                    s[nt][mt][0] = a4[0];
-                    s[nt][mt][1] = a4[1];
-                    s[nt][mt][2] = a4[2];
-                    s[nt][mt][3] = a4[3];
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int ks = 0; ks < 4; ++ks) {
+                const int t = 4 * ks + lg;  // k index of this lane
+                float kv[8], uv[2];
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+                    kv[mt] = bf16_at(sm.in + size_t(t) * kNodeBytes, 16 * mt + lr);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) uv[nt] = sm.Ug[t][16 * nt + lr];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt)
+                        a4[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[mt], uv[nt],
+                                                                          a4[nt][mt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[nt][mt][e] = a4[nt][mt][e];
         }
         wave_order();  // the next chunk's loads overwrite the inputs read above
     }
