@@ -183,9 +183,25 @@ def schedule_view(image: np.ndarray) -> dict:
         o += T
     fields["chain_seq"] = fields["chain_seq"][:n_chains]
     fields["chain_src"] = fields["chain_src"][:n_chains]
+    ut = None
+    if int(image[8]) >= 0:  # tree-masked verify plan
+        rec_base = image[o:o + S + 1]
+        o += S + 1
+        node_rec = image[o:o + T]
+        o += T
+        lv_base = image[o:o + S + 1]
+        o += S + 1
+        lvn = image[o:o + int(lv_base[-1])]
+        o += T + S
+        lvnode = image[o:o + T]
+        o += T
+        rec_anc = image[o:o + int(rec_base[-1])]
+        ut = dict(records=int(image[8]), max_records=int(image[9]), max_levels=int(image[10]),
+                  rec_base=rec_base, node_rec=node_rec, lv_base=lv_base, lvn=lvn,
+                  lvnode=lvnode, rec_anc=rec_anc)
     return dict(n_seqs=S, n_nodes=T, n_chains=n_chains, n_waves=n_waves,
                 n_boundaries=int(image[5]), max_chain_len=int(image[6]), max_tree=int(image[7]),
-                seq_offsets=seq, wave_offsets=wave, chain_offsets=chain, **fields)
+                seq_offsets=seq, wave_offsets=wave, chain_offsets=chain, ut_plan=ut, **fields)
 
 
 def ddtree_build(logp, tokens=None, root_tokens=None, budget=22, tau=6.0, chain_seed=True):

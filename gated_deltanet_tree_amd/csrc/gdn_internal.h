@@ -18,12 +18,19 @@ constexpr int32_t kMaxTreeNodes = 1024;
 // 32-bit.
 constexpr int64_t kMaxBlocks = 0xFFFFFFFFll / 256;
 constexpr int32_t kMaxSeqs = 1 << 20;
+// Record budget of the tree-masked verify plan in the schedule image, per node: a batch whose
+// trees need more (sum of depth + 1 over its nodes > 32 T) gets no plan.
+constexpr int32_t kUtRecordsPerNode = 32;
 
 // Word offsets of the schedule image's arrays (see gdn_tree.h for the layout).
 struct ImageView {
     int32_t n_seqs, n_nodes, n_chains, n_waves, n_boundaries, max_chain_len, max_tree;
     int64_t off_seq, off_wave, off_chain, off_cnodes, off_cseq, off_csrc, off_store,
         off_parent, off_depth;
+    // tree-masked verify plan (ut_records < 0: absent)
+    int32_t ut_records, ut_max_records, ut_max_levels;
+    int64_t off_ut_rec_base, off_ut_node_rec, off_ut_lv_base, off_ut_lvn, off_ut_lvnode,
+        off_ut_rec_anc;
 };
 
 size_t schedule_words(int32_t n_seqs, int32_t n_nodes);

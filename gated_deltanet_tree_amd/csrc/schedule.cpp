@@ -16,7 +16,9 @@
 namespace gdn {
 
 size_t schedule_words(int32_t n_seqs, int32_t n_nodes) {
-    return size_t(kImageHeader) + 3 + size_t(n_seqs) + 8 * size_t(n_nodes);
+    const size_t S = size_t(n_seqs), T = size_t(n_nodes);
+    return size_t(kImageHeader) + 3 + S + 8 * T                // chains, waves, nodes
+           + 2 + 3 * S + 3 * T + size_t(kUtRecordsPerNode) * T;  // tree-masked verify plan
 }
 
 ImageView view_image(const int32_t *img) {
@@ -38,6 +40,15 @@ ImageView view_image(const int32_t *img) {
     v.off_store = v.off_cnodes + 3 * T;
     v.off_parent = v.off_cnodes + 4 * T;
     v.off_depth = v.off_cnodes + 5 * T;
+    v.ut_records = img[8];
+    v.ut_max_records = img[9];
+    v.ut_max_levels = img[10];
+    v.off_ut_rec_base = v.off_depth + T;
+    v.off_ut_node_rec = v.off_ut_rec_base + S + 1;
+    v.off_ut_lv_base = v.off_ut_node_rec + T;
+    v.off_ut_lvn = v.off_ut_lv_base + S + 1;
+    v.off_ut_lvnode = v.off_ut_lvn + T + S;
+    v.off_ut_rec_anc = v.off_ut_lvnode + T;
     return v;
 }
 
@@ -163,5 +174,50 @@ extern "C" gdn_status gdn_hld_schedule(const int32_t *parent_local, const int32_
     image[5] = n_boundaries;
     image[6] = longest;
     image[7] = max_tree;
+
+    // Tree-masked verify plan: per tree, nodes by (depth, id) with the first position of each
+    // depth level, and one block of depth + 1 records per node in that order (the node, then
+    // its ancestors nearest first, local ids).
+    int64_t records = 0;
+    for (int32_t g = 0; g < T; ++g) records += ndep[g] + 1;
+    if (records > int64_t(kUtRecordsPerNode) * T) {
+        image[8] = -1;  // too deep for the plan budget: no tree-masked verify for this batch
+        return GDN_OK;
+    }
+    v = view_image(image);
+    int32_t *rec_base = image + v.off_ut_rec_base, *node_rec = image + v.off_ut_node_rec,
+            *lv_base = image + v.off_ut_lv_base, *lvn = image + v.off_ut_lvn,
+            *lvnode = image + v.off_ut_lvnode, *rec_anc = image + v.off_ut_rec_anc;
+    int32_t max_records = 0, max_levels = 0;
+    rec_base[0] = 0;
+    lv_base[0] = 0;
+    std::vector<int32_t> order;
+    for (int32_t b = 0; b < n_seqs; ++b) {
+        const int32_t off = seq_offsets[b], n = seq_offsets[b + 1] - off;
+        int32_t dmax = 0;
+        for (int32_t i = 0; i < n; ++i) dmax = std::max(dmax, ndep[off + i]);
+        int32_t *first = lvn + lv_base[b];
+        for (int32_t d = 0; d <= dmax + 1; ++d) first[d] = 0;
+        for (int32_t i = 0; i < n; ++i) ++first[ndep[off + i] + 1];
+        for (int32_t d = 0; d <= dmax; ++d) first[d + 1] += first[d];
+        order.assign(size_t(n), 0);  // counting sort by depth, ids ascending within a level
+        std::vector<int32_t> fill(first, first + dmax + 1);
+        for (int32_t i = 0; i < n; ++i) order[fill[ndep[off + i]]++] = i;
+        int32_t pos = 0;
+        int32_t *recs = rec_anc + rec_base[b];
+        for (int32_t j = 0; j < n; ++j) {
+            const int32_t t = order[j];
+            lvnode[off + j] = t;
+            node_rec[off + t] = pos;
+            for (int32_t a = t; a >= 0; a = parent_local[off + a]) recs[pos++] = a;  // root: -1
+        }
+        rec_base[b + 1] = rec_base[b] + pos;
+        lv_base[b + 1] = lv_base[b] + dmax + 2;
+        max_records = std::max(max_records, pos);
+        max_levels = std::max(max_levels, dmax + 2);
+    }
+    image[8] = int32_t(records);
+    image[9] = max_records;
+    image[10] = max_levels;
     return GDN_OK;
 }

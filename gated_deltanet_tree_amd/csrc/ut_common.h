@@ -31,7 +31,7 @@ template <typename TIn> __device__ __forceinline__ float slot_f32(uint32_t x) {
 }
 
 // The matrix-core UT kernel (bf16 inputs, d = 128).
-gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int np_max, int nf_max,
-                          hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int nrec_max, int nlv_max,
+                          int nf_max, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 }  // namespace gdn

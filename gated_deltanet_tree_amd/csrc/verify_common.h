@@ -16,6 +16,9 @@ struct VerifyParams {
     float *out;
     const int32_t *img;
     int64_t off_seq, off_chain, off_cnodes, off_cseq, off_csrc, off_store, off_parent, off_depth;
+    // tree-masked verify plan in the image (see gdn_tree.h)
+    int64_t off_ut_rec_base, off_ut_node_rec, off_ut_lv_base, off_ut_lvn, off_ut_lvnode,
+        off_ut_rec_anc;
     int32_t S, H, T, max_nodes, n_boundaries, layer_begin;
     int32_t chain_begin, n_chains;  // chains of this wave
     int64_t n_blocks;

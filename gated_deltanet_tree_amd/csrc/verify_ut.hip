@@ -435,10 +435,22 @@ static gdn_status run_ut(const gdn_verify_args *a, const int32_t *host_image,
     ut_tree_bounds(host_image, v, n_max, np_max);
     const int nf_max = a->max_nodes;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a->head_dim == 128 && a->in_dtype == GDN_BF16) {
+        if (v.ut_records < 0)
+            return fail(GDN_EINVAL, "gdn_tree_verify_ut: the schedule has no tree-masked plan "
+                        "(its trees need more than %d records per node); use gdn_tree_verify",
+                        kUtRecordsPerNode);
+        P.off_ut_rec_base = v.off_ut_rec_base;
+        P.off_ut_node_rec = v.off_ut_node_rec;
+        P.off_ut_lv_base = v.off_ut_lv_base;
+        P.off_ut_lvn = v.off_ut_lvn;
+        P.off_ut_lvnode = v.off_ut_lvnode;
+        P.off_ut_rec_anc = v.off_ut_rec_anc;
+        return launch_ut_mfma(P, n_max, v.ut_max_records, v.ut_max_levels, nf_max, s, start,
+                              stop);
+    }
     if (a->head_dim == 128)
-        return a->in_dtype == GDN_BF16
-            ? launch_ut_mfma(P, n_max, np_max, nf_max, s, start, stop)
-            : launch_ut<128, float>(P, n_max, np_max, nf_max, s, start, stop);
+        return launch_ut<128, float>(P, n_max, np_max, nf_max, s, start, stop);
     return a->in_dtype == GDN_BF16
         ? launch_ut<16, bf16_t>(P, n_max, np_max, nf_max, s, start, stop)
         : launch_ut<16, float>(P, n_max, np_max, nf_max, s, start, stop);

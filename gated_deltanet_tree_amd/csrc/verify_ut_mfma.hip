@@ -12,14 +12,15 @@
 // One workgroup of 4 waves per (layer, sequence, head):
 //   0. direct global->LDS loads of k, q, v, beta, g, parents, depths and the pending fold
 //      rows; one barrier; then the state tile loads into VGPRs are issued, to land while
-//   1. the tree tables are built: nodes grouped by depth level, one block of records per node
-//      (itself, then its ancestors nearest first) with the gate products E and G_n;
+//   1. the tree's plan (from the schedule image: nodes grouped by depth level, one block of
+//      records per node, itself then its ancestors nearest first) gets the gate products E
+//      and G_n; keys and log-gates are banked;
 //   2. the pair products [k; q] K^T run on the matrix cores and give T and C on the records;
 //   3. the pending rows are folded, S <- exp(lg) S + u k^T, and S is written back once;
 //   4. [k; q] S0^T runs on the matrix cores; its epilogue writes w_n and G_n r_n to LDS;
-//   5. T U = W is solved level by level: the (node, row) items of one level are independent,
-//      u overwrites w in place;
-//   6. o_n per (node, row); u_n, k_n and ln g_n are banked.
+//   5. T U = W is solved level by level, o_n formed in the same pass over each node's
+//      ancestors: the (node, row) items of one level are independent and u overwrites w in
+//      place; u is banked.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16, fp32 accumulate): wave w owns state rows
 // [32w, 32w+32); lane l holds rows 32w + 16nt + (l % 16) and columns 16mt + 4(l / 16) + e
@@ -40,7 +41,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUtD = 128;
 
-// LDS regions for trees of at most n nodes, nrec ancestor-or-self records and nf pending rows.
+// LDS regions for trees of at most n nodes, nrec records and nlv level entries, and at most nf
+// pending rows.  Regions filled by direct loads are padded to whole 64-lane instructions.
 struct UtLayout5 {
     static constexpr int D = kUtD;
     static constexpr int CPV = D * 2 / 16;  // 16-byte chunks per bf16 vector
@@ -50,9 +52,12 @@ struct UtLayout5 {
     static constexpr int NODE_BYTES = CPN * 16;
     static constexpr int WS = D + 4;        // row stride of W and GR in floats (same reason)
     static constexpr int CPR = D * 4 / 16;  // 16-byte chunks per fp32 fold row
-    size_t in, bg, pd, work, fold_k, fold_u, fold_lg, gr, tabs, total;
-    __host__ __device__ UtLayout5(int n, int nrec, int nf) {
-        const size_t n64 = round_up(size_t(n), 64);
+    size_t in, bg, pd, work, fold_k, fold_u, fold_lg, gr, plan, tabs, total;
+    size_t n64, lv64, rec64;
+    __host__ __device__ UtLayout5(int n, int nrec, int nlv, int nf) {
+        n64 = round_up(size_t(n), 64);
+        lv64 = round_up(size_t(nlv), 64);
+        rec64 = round_up(size_t(nrec), 64);
         in = 0;
         bg = in + round_up(size_t(n) * CPN, 64) * 16;  // beta | gate  [n64] x u32
         pd = bg + 2 * n64 * 4;                         // parent | depth [n64] int
@@ -64,9 +69,11 @@ struct UtLayout5 {
         const size_t fold_bytes = 2 * fk + round_up(size_t(nf), 64) * 4;
         gr = work + size_t(n) * WS * 4;
         const size_t wg_bytes = size_t(2) * n * WS * 4;
-        tabs = work + (wg_bytes > fold_bytes ? wg_bytes : fold_bytes);
-        // poff[n] | gam[n] | kq[n] | maxdep | lvn[n+2] | lvnode[n] | recM | recE | recC | recQ
-        total = tabs + (size_t(5) * n + 3 + size_t(4) * nrec) * 4;
+        // plan (direct loads): poff [n64] | lvnode [n64] | lvn [lv64] | recM [rec64]
+        plan = work + (wg_bytes > fold_bytes ? wg_bytes : fold_bytes);
+        tabs = plan + (2 * n64 + lv64 + rec64) * 4;
+        // gam[n] | kq[n] | recE | recC | recQ [nrec]
+        total = tabs + (size_t(2) * n + size_t(3) * nrec) * 4;
     }
 };
 
@@ -121,12 +128,13 @@ __device__ __forceinline__ UtUnit ut_unit(const VerifyParams &P) {
 // one workgroup of 4 waves per (layer, sequence, head)
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
-void verify_ut_mfma_kernel(VerifyParams P, int n_max, int nrec_max, int nf_max) {
+void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int n_max,
+                           int nrec_max, int nlv_max, int nf_max) {
     constexpr int D = kUtD, THREADS = 256, NW = 4, JC = 4;
     using LY = UtLayout5;
     extern __shared__ __align__(16) float dyn[];
     char *lds = reinterpret_cast<char *>(dyn);
-    const LY lay(n_max, nrec_max, nf_max);
+    const LY lay(n_max, nrec_max, nlv_max, nf_max);
     const size_t n64 = round_up(size_t(n_max), 64);
     const char *IN = lds + lay.in;
     const uint32_t *Bl = reinterpret_cast<const uint32_t *>(lds + lay.bg);
@@ -138,17 +146,16 @@ void verify_ut_mfma_kernel(VerifyParams P, int n_max, int nrec_max, int nf_max) 
     const float *FK = reinterpret_cast<const float *>(lds + lay.fold_k);
     const float *FU = reinterpret_cast<const float *>(lds + lay.fold_u);
     const float *FL = reinterpret_cast<const float *>(lds + lay.fold_lg);
-    int *poff = reinterpret_cast<int *>(lds + lay.tabs);  // first record of each node
-    float *gam = reinterpret_cast<float *>(poff + n_max);
+    // Plan of this tree (from the schedule image): record q of node n is q = poff[n] for n
+    // itself and poff[n] + 1 + t for its ancestor at distance t + 1; recM = that node.
+    int *poff = reinterpret_cast<int *>(lds + lay.plan);
+    int *lvnode = poff + lay.n64;   // nodes ordered by depth, then index
+    int *lvn = lvnode + lay.n64;    // first entry of each depth level in lvnode
+    int *recM = lvn + lay.lv64;
+    float *gam = reinterpret_cast<float *>(lds + lay.tabs);
     float *kq = gam + n_max;
-    int *maxdep = reinterpret_cast<int *>(kq + n_max);
-    int *lvn = maxdep + 1;          // first entry of each depth level in lvnode
-    int *lvnode = lvn + n_max + 2;  // nodes ordered by depth, then index
-    // Record q of node n: q = poff[n] is n itself, poff[n] + 1 + t its ancestor at distance
-    // t + 1.  recM = that node, recE = E(n, it), recC = T[n][it], recQ = C[n][it].
-    int *recM = lvnode + n_max;
-    float *recE = reinterpret_cast<float *>(recM + nrec_max);
-    float *recC = recE + nrec_max, *recQ = recC + nrec_max;
+    // recE = E(n, that node), recC = T[n][it], recQ = C[n][it]
+    float *recE = kq + n_max, *recC = recE + nrec_max, *recQ = recC + nrec_max;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -192,6 +199,19 @@ void verify_ut_mfma_kernel(VerifyParams P, int n_max, int nrec_max, int nf_max) 
                 to_lds<4>(src, lds + lay.pd + size_t(base - 2 * int(n64)) * 4);
             }
         }
+        if (n > 0) {  // the tree's plan: node blocks, level lists, ancestor records
+            const int r0 = P.img[P.off_ut_rec_base + seq], nrec = P.img[P.off_ut_rec_base + seq + 1] - r0;
+            const int l0 = P.img[P.off_ut_lv_base + seq], nlv = P.img[P.off_ut_lv_base + seq + 1] - l0;
+            const int32_t *srcs[4] = {P.img + P.off_ut_node_rec + seq_off,
+                                      P.img + P.off_ut_lvnode + seq_off, P.img + P.off_ut_lvn + l0,
+                                      P.img + P.off_ut_rec_anc + r0};
+            const int counts[4] = {n, n, nlv, nrec};
+            int *dsts[4] = {poff, lvnode, lvn, recM};
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                for (int base = w * 64; base < counts[a]; base += NW * 64)
+                    to_lds<4>(srcs[a] + min(base + lane, counts[a] - 1), dsts[a] + base);
+        }
         if (L > 0) {
             const float *pk = P.bank_k[role] + row0_bank * D, *pu = P.bank_u[role] + row0_bank * D;
             const int rows_chunks = L * LY::CPR;
@@ -227,51 +247,30 @@ void verify_ut_mfma_kernel(VerifyParams P, int n_max, int nrec_max, int nf_max) 
             }
     }
 
-    // ---- 1. tables: nodes by depth level, record blocks, gate products ------------------
-    if (w == 0) {
-        int dmax = 0;
-        for (int c = 0; c < n; c += 64) dmax = max(dmax, c + lane < n ? dep[c + lane] : 0);
-#pragma unroll
-        for (int d2 = 32; d2 >= 1; d2 >>= 1) dmax = max(dmax, __shfl_xor(dmax, d2));
-        int rbase = 0, nbase = 0;
-        for (int lv = 0; lv <= dmax; ++lv) {
-            if (lane == 0) lvn[lv] = nbase;
-            int run = 0;
-            for (int c = 0; c < n; c += 64) {
-                const int t = c + lane;
-                const bool on = t < n && dep[t] == lv;
-                const uint64_t m = __ballot(on);
-                const int below = __builtin_amdgcn_mbcnt_hi(
-                    uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0));
-                if (on) {
-                    poff[t] = rbase + (run + below) * (lv + 1);
-                    lvnode[nbase + run + below] = t;
-                }
-                run += __popcll(m);
-            }
-            rbase += run * (lv + 1);
-            nbase += run;
-        }
-        if (lane == 0) {
-            lvn[dmax + 1] = nbase;
-            *maxdep = dmax;
-        }
-    }
-    __syncthreads();
+    // ---- 1. gate products along every record block ------------------------------------
+    //   E(n, anc_0) = g_n, E(n, anc_{t+1}) = E(n, anc_t) g_{anc_t}, G_n = E(n, root) g_root.
     for (int t = tid; t < n; t += THREADS) {
         const int o = poff[t], dt = dep[t];
-        recM[o] = t;
         float E = slot_f32<bf16_t>(Gt[t]);
-        int a = par[t] - seq_off;  // global -> local; only depth(t) steps: never the root's -1
         for (int s2 = 0; s2 < dt; ++s2) {
-            recM[o + 1 + s2] = a;
             recE[o + 1 + s2] = E;
-            E *= slot_f32<bf16_t>(Gt[a]);
-            a = par[a] - seq_off;
+            E *= slot_f32<bf16_t>(Gt[recM[o + 1 + s2]]);
         }
         gam[t] = E;
     }
     __syncthreads();
+    {  // banked keys (exact fp32 widening) and log-gates: stores only, issued early
+        float *wk = P.bank_k[role ^ 1], *wlg = P.bank_lg[role ^ 1];
+        for (int e = tid; e < n * (D / 4); e += THREADS) {
+            const int nd = e / (D / 4), c = (e % (D / 4)) * 4;
+            const uint2 x =
+                *reinterpret_cast<const uint2 *>(IN + size_t(nd) * LY::NODE_BYTES + c * 2);
+            *reinterpret_cast<float4 *>(wk + (row0_bank + nd) * D + c) =
+                make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
+        }
+        for (int t = tid; t < n; t += THREADS)
+            wlg[row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
+    }
 
     // ---- 2. pair coefficients: [k; q] K^T on the matrix cores ---------------------------
     // M tile jt stacks k (rows 0-7) and q (rows 8-15) of nodes 8jt .. 8jt+7; N tile at holds
@@ -400,91 +399,62 @@ void verify_ut_mfma_kernel(VerifyParams P, int n_max, int nrec_max, int nf_max) 
     }
     __syncthreads();
 
-    // ---- 5. u_n = w_n - sum_{a strict ancestor} T[n][a] u_a, level by level ---------------
-    // Roots (level 0) have u = w.  Nodes of one level depend only on lower levels, so a
-    // level's (node, row) items run in parallel and u overwrites w in place.  Ancestor ids and
-    // coefficients are read GK at a time before the rows they select, so a chunk of GK
-    // ancestors costs two LDS round trips.
-    constexpr int GK = 8;
-    const int i = tid & (D - 1), half = tid >> 7;
-    const int dmax = *maxdep;
-    for (int lv = 1; lv <= dmax; ++lv) {
-        const int j1 = lvn[lv + 1];
-        for (int j = lvn[lv] + half; j < j1; j += THREADS / D) {
-            const int nd = lvnode[j], q1 = poff[nd] + 1;
-            float u = Wm[nd * LY::WS + i];
-            for (int t0 = 0; t0 < lv; t0 += GK) {
-                int m[GK];
-                float c[GK], x[GK];
-#pragma unroll
-                for (int g = 0; g < GK; ++g) {
-                    const bool on = t0 + g < lv;
-                    m[g] = on ? recM[q1 + t0 + g] : nd;
-                    c[g] = on ? recC[q1 + t0 + g] : 0.f;
-                }
-#pragma unroll
-                for (int g = 0; g < GK; ++g) x[g] = Wm[m[g] * LY::WS + i];
-#pragma unroll
-                for (int g = 0; g < GK; ++g) u = fmaf(-c[g], x[g], u);
-            }
-            Wm[nd * LY::WS + i] = u;
-        }
-        __syncthreads();
-    }
-
-    // ---- 6. o_n = G_n r_n + (q_n . k_n) u_n + sum_a C[n][a] u_a; banked k, u, ln g ---------
+    // ---- 5. level by level: u_n = w_n - sum_{a strict ancestor} T[n][a] u_a, then o_n ----
+    //   o_n = G_n r_n + (q_n . k_n) u_n + sum_a C[n][a] u_a.
+    // Nodes of one level depend only on lower levels, so a level's (node, row) items run in
+    // parallel, u overwrites w in place, and one pass over a node's ancestors serves both
+    // sums (roots, level 0, have u = w).
+    // Two waves share one node's 128 rows, so within a wave the node is uniform: its ancestor
+    // ids are read with scalar loads from the plan in the image, and only the rows of u and
+    // the coefficients come from LDS.
     {
-        float *wk = P.bank_k[role ^ 1], *wu = P.bank_u[role ^ 1], *wlg = P.bank_lg[role ^ 1];
+        float *wu = P.bank_u[role ^ 1];
         float *out0 = P.out + node_row0 * D;
-        for (int nd = half; nd < n; nd += THREADS / D) {
-            const int q1 = poff[nd] + 1, dn = dep[nd];
-            const float un_i = Wm[nd * LY::WS + i];
-            float o = fmaf(kq[nd], un_i, GR[nd * LY::WS + i]);
-            for (int t0 = 0; t0 < dn; t0 += GK) {
-                int m[GK];
-                float c[GK], x[GK];
-#pragma unroll
-                for (int g = 0; g < GK; ++g) {
-                    const bool on = t0 + g < dn;
-                    m[g] = on ? recM[q1 + t0 + g] : nd;
-                    c[g] = on ? recQ[q1 + t0 + g] : 0.f;
+        const int i = tid & (D - 1);
+        const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
+        const int lv0 = n > 0 ? plan[P.off_ut_lv_base + seq] : 0;
+        const int dmax = n > 0 ? plan[P.off_ut_lv_base + seq + 1] - lv0 - 2 : -1;
+        // `plan` is the image again, declared read-only and unaliased: uniform reads of it
+        // become scalar loads
+        const int32_t *anc = plan + P.off_ut_rec_anc + (n > 0 ? plan[P.off_ut_rec_base + seq] : 0);
+        const int32_t *lvl = plan + P.off_ut_lvn + lv0;
+        const int32_t *nodes = plan + P.off_ut_lvnode + seq_off;
+        const int32_t *blk = plan + P.off_ut_node_rec + seq_off;
+        for (int lv = 0; lv <= dmax; ++lv) {
+            const int j1 = lvl[lv + 1];
+            for (int j = lvl[lv] + half; j < j1; j += THREADS / D) {
+                const int nd = nodes[j], q1 = blk[nd] + 1;
+                float u = Wm[nd * LY::WS + i], o = 0.f;
+#pragma unroll 4
+                for (int t = 0; t < lv; ++t) {
+                    const float x = Wm[anc[q1 + t] * LY::WS + i];
+                    u = fmaf(-recC[q1 + t], x, u);
+                    o = fmaf(recQ[q1 + t], x, o);
                 }
-#pragma unroll
-                for (int g = 0; g < GK; ++g) x[g] = Wm[m[g] * LY::WS + i];
-#pragma unroll
-                for (int g = 0; g < GK; ++g) o = fmaf(c[g], x[g], o);
+                Wm[nd * LY::WS + i] = u;
+                wu[(row0_bank + nd) * D + i] = u;
+                out0[int64_t(nd) * P.H * D + i] = o + fmaf(kq[nd], u, GR[nd * LY::WS + i]);
             }
-            wu[(row0_bank + nd) * D + i] = un_i;
-            out0[int64_t(nd) * P.H * D + i] = o;
+            __syncthreads();
         }
-        for (int e = tid; e < n * (D / 4); e += THREADS) {
-            const int nd = e / (D / 4), c = (e % (D / 4)) * 4;
-            const uint2 x =
-                *reinterpret_cast<const uint2 *>(IN + size_t(nd) * LY::NODE_BYTES + c * 2);
-            *reinterpret_cast<float4 *>(wk + (row0_bank + nd) * D + c) =
-                make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
-        }
-        for (int t = tid; t < n; t += THREADS)
-            wlg[row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
     }
 }
 
-gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int np_max, int nf_max,
-                          hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    const int nrec_max = np_max + n_max;
-    const size_t lds = UtLayout5(n_max, nrec_max, nf_max).total;
+gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int nrec_max, int nlv_max,
+                          int nf_max, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    const size_t lds = UtLayout5(n_max, nrec_max, nlv_max, nf_max).total;
     if (lds > kUtMaxLdsBytes)
-        return fail(GDN_EINVAL, "gdn_tree_verify_ut: trees of %d nodes with %d ancestor pairs "
+        return fail(GDN_EINVAL, "gdn_tree_verify_ut: trees of %d nodes with %d records "
                     "and %d bank rows need %zu bytes of LDS (limit %zu); use gdn_tree_verify",
-                    n_max, np_max, nf_max, lds, kUtMaxLdsBytes);
+                    n_max, nrec_max, nf_max, lds, kUtMaxLdsBytes);
     if (P.n_blocks <= 0) return GDN_OK;
     const dim3 grid(uint32_t(P.n_blocks));
     if (start == nullptr && stop == nullptr)
-        hipLaunchKernelGGL(verify_ut_mfma_kernel, grid, dim3(256), lds, stream, P, n_max,
-                           nrec_max, nf_max);
+        hipLaunchKernelGGL(verify_ut_mfma_kernel, grid, dim3(256), lds, stream, P, P.img, n_max,
+                           nrec_max, nlv_max, nf_max);
     else
         hipExtLaunchKernelGGL(verify_ut_mfma_kernel, grid, dim3(256), uint32_t(lds), stream,
-                              start, stop, 0, P, n_max, nrec_max, nf_max);
+                              start, stop, 0, P, P.img, n_max, nrec_max, nlv_max, nf_max);
     GDN_LAUNCH_CHECK("verify_ut_mfma_kernel");
     return GDN_OK;
 }

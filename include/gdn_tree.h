@@ -83,7 +83,10 @@ const char *gdn_last_error(void);
  * The schedule is one int32 image, built on the host and copied verbatim to the device.
  * Layout for n_seqs = S and T total nodes (word offsets):
  *   [0]  magic 0x53444E47     [1] S   [2] T   [3] n_chains   [4] n_waves
- *   [5]  n_boundaries         [6] longest chain   [7] largest tree   [8..15] zero
+ *   [5]  n_boundaries         [6] longest chain   [7] largest tree
+ *   [8]  R = tree-masked verify records (sum over nodes of depth + 1), or -1 when R > 32 T
+ *        and the plan below is absent (gdn_tree_verify_ut then refuses the batch)
+ *   [9]  most records of one tree     [10] most depth levels + 1 of one tree   [11..15] zero
  *   seq_offsets   [S+1] at 16                       b's nodes: [seq_offsets[b], seq_offsets[b+1])
  *   wave_offsets  [T+1] at 17+S                     wave w: chains [wave_offsets[w], ..[w+1])
  *   chain_offsets [T+1] at 18+S+T                   chain c: chain_nodes[chain_offsets[c] ..)
@@ -93,7 +96,18 @@ const char *gdn_last_error(void);
  *   node_store    [T]   at 19+S+5T                  slot written after node n, or -1
  *   node_parent   [T]   at 19+S+6T                  global parent id, -1 for roots
  *   node_depth    [T]   at 19+S+7T                  edges from the root
- *   total words = 19 + S + 8T. Arrays are sized for T; only the counted prefix is used.
+ * Tree-masked verify plan (per tree: nodes ordered by (depth, local id); each node owns a
+ * block of depth + 1 records, blocks in that order: the node, then its ancestors nearest
+ * first), with P = 19 + S + 8T:
+ *   rec_base      [S+1] at P                         tree b's records: [rec_base[b], ..[b+1])
+ *   node_rec      [T]   at P+S+1                     node's first record, relative to its tree
+ *   lv_base       [S+1] at P+S+1+T                   tree b's level offsets start in lvn
+ *   lvn           [T+S] at P+2S+2+T                  per tree: first position of depth level
+ *                                                    d in lvnode, d = 0 .. dmax+1
+ *   lvnode        [T]   at P+3S+2+2T                 per tree (at seq_offsets[b]): local ids
+ *                                                    by (depth, id)
+ *   rec_anc       [32T] at P+3S+2+3T                 local node id of each record
+ *   total words = 21 + 4S + 43T. Arrays are sized for T; only the counted prefix is used.
  * ---------------------------------------------------------------------------------- */
 size_t gdn_schedule_words(int32_t n_seqs, int32_t n_nodes_total);
 

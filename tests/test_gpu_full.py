@@ -229,21 +229,30 @@ def test_long_chain_d128_and_padded_banks(torch_cuda):
     _edge_run(torch_cuda, trees, 3, 128, 16, steps, 94, max_nodes=160, dtype="bf16")
 
 
-def test_ut_rejects_trees_beyond_its_lds_budget(torch_cuda):
-    """The UT path keeps a whole tree's keys and residual vectors in 64 KiB of LDS; a
-    128-node tree at d = 128 does not fit and is refused before any launch."""
-    trees = [np.arange(-1, 127, dtype=np.int32)]
+def _ut_refused(torch, trees, seed):
     b = gh.Batch(trees, 1, 2, 128, 0, mode="ut")
-    h = gh.tiny_inputs(trees, 0, 2, 128, 4, "bf16", 95)
+    h = gh.tiny_inputs(trees, 0, 2, 128, 4, "bf16", seed)
     h.pop("x")
     inp = workload.StepInputs(**{k: workload._to_torch(v, "bf16", "cuda") for k, v in h.items()},
                               x=None)
     before = b.out.clone()
     with pytest.raises(binding.GdnError) as e:
         binding.tree_verify_ut(b.vargs(inp, 0), b.image, b.dev_image)
-    assert e.value.status == -1 and "LDS" in str(e.value)
-    torch_cuda.cuda.synchronize()
-    assert torch_cuda.equal(before, b.out)
+    torch.cuda.synchronize()
+    assert torch.equal(before, b.out)  # refused before any launch
+    return e.value
+
+
+def test_ut_rejects_trees_beyond_its_budgets(torch_cuda):
+    """The UT path keeps a whole tree in one workgroup's LDS and reads its record plan from
+    the schedule: a 128-node chain needs 8256 records, above the plan's 32 per node; a wide
+    150-node tree has a plan but needs more than 160 KiB of LDS.  Both are refused before
+    any launch."""
+    e = _ut_refused(torch_cuda, [np.arange(-1, 127, dtype=np.int32)], 95)
+    assert e.status == -1 and "plan" in str(e)
+    rng = np.random.default_rng(95)
+    e = _ut_refused(torch_cuda, [synth.make_tree(rng, 150, 8, 12)], 96)
+    assert e.status == -1 and "LDS" in str(e)
 
 
 def test_ut_largest_fitting_tree_64_nodes_d128(torch_cuda):

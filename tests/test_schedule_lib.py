@@ -160,3 +160,27 @@ def test_commit_rejects_bad_paths_before_launch():
                                None)
         assert rc == -3, bad
         assert role[0] == 0 and pend[0] == 3
+
+
+def test_ut_plan_matches_oracle_bit_exact():
+    """The tree-masked verify plan in the image equals the oracle's construction."""
+    rng = np.random.default_rng(31)
+    batches = [[np.array([-1, 0, 0, 1, 1, 2, 3])],
+               [synth.make_tree(rng, 22, 4, 12) for _ in range(32)],
+               [synth.make_tree(rng, 64, 8, 16) for _ in range(8)] + [np.array([-1])],
+               [np.arange(-1, 15) for _ in range(4)]]
+    for trees in batches:
+        image = binding.hld_schedule(trees)
+        got = binding.schedule_view(image)["ut_plan"]
+        want = hld.ut_plan(trees)
+        for key in ("rec_base", "node_rec", "lv_base", "lvn", "lvnode", "rec_anc"):
+            assert np.array_equal(got[key], want[key]), key
+        assert got["records"] == int(want["rec_base"][-1])
+        assert got["max_records"] == int(np.max(np.diff(want["rec_base"])))
+        assert got["max_levels"] == int(np.max(np.diff(want["lv_base"])))
+
+
+def test_ut_plan_absent_when_too_deep():
+    """A 1024-node chain needs 1024*1025/2 records, above the 32-per-node budget."""
+    image = binding.hld_schedule([np.arange(-1, 1023)])
+    assert int(image[8]) == -1 and binding.schedule_view(image)["ut_plan"] is None
