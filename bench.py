@@ -35,10 +35,12 @@ CSRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc")
 COUNTERS = {
     "chain": os.path.join(ROOT, "profiles", "verify_chain_kernel_batched32x48_counters.json"),
     "ut": os.path.join(ROOT, "profiles", "verify_ut_mfma_kernel_batched32x48_counters.json"),
+    "prefill": os.path.join(ROOT, "profiles", "prefill_kernel_8x2048x48_counters.json"),
 }
 KERNEL_SOURCES = {
     "chain": ["verify.hip", "verify_common.h", "gdn_device.h"],
     "ut": ["verify_ut_mfma.hip", "ut_common.h", "verify_common.h", "gdn_device.h"],
+    "prefill": ["prefill.hip", "ut_common.h", "verify_common.h", "gdn_device.h"],
 }
 KERNEL = {"chain": "verify_chain_kernel<128, bf16>", "ut": "verify_ut_mfma_kernel"}
 METRIC = "verified tree nodes/sec per GDN layer + achieved HBM GB/s vs peak, 1 MI355X"
@@ -154,6 +156,8 @@ def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, lay
     launch_s = sum(e0.elapsed_ms(e1) for per in ev for e0, e1 in per) / 1e3 / (reps * layers)
     per_call = prefill_bytes(T, S, H, d)
     achieved = per_call / launch_s / 1e9
+    default = (S, length, H, d) == (8, 2048, 48, 128)
+    traffic = recorded_traffic("prefill") if default else None
     return {
         "workload": f"{S} sequences x {length} tokens x {H} heads x d{d}, bf16 inputs, fp32 "
                     f"state, one layer per call, {layers} layers x {reps} repeats",
@@ -161,6 +165,7 @@ def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, lay
         "ms_per_layer": wall * 1e3 / (reps * layers),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "kernel": "prefill_kernel",
+                     "traffic": None if traffic is None else traffic / launch_s / 1e9,
                      "bytes_per_launch": per_call, "launch_us": launch_s * 1e6},
     }
 
@@ -180,11 +185,18 @@ def kernel_source_sha256(verify):
 def measured_traffic(config, lpc, verify):
     """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     or None when the kernel's sources changed since they were taken (or another workload)."""
-    path = COUNTERS[verify]
-    if config != 3 or lpc != 1 or not os.path.exists(path):
+    if config != 3 or lpc != 1:
+        return None
+    return recorded_traffic(verify)
+
+
+def recorded_traffic(kernel):
+    """Bytes per launch of a committed counter record, or None when it is absent or stale."""
+    path = COUNTERS[kernel]
+    if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if kernel_source_sha256(verify) != rec.get("kernel_sources_sha256"):
+    if kernel_source_sha256(kernel) != rec.get("kernel_sources_sha256"):
         return None
     return rec["traffic_bytes_per_launch"]
 
