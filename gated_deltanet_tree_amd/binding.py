@@ -24,6 +24,7 @@ EXPORTS = [
     "gdn_verify_workspace_bytes",
     "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed",
     "gdn_tree_verify_ut", "gdn_tree_verify_ut_timed", "gdn_tree_conv",
+    "gdn_tree_conv_verify", "gdn_tree_conv_verify_timed",
     "gdn_commit_path", "gdn_prefill", "gdn_prefill_timed",
     "gdn_compact_factors", "gdn_flush",
 ]
@@ -109,6 +110,12 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _I32P, _P]
     L.gdn_prefill_timed.restype = _I32
     L.gdn_prefill_timed.argtypes = [ctypes.POINTER(PrefillArgs), _I32P, _P, _P, _P]
+    L.gdn_tree_conv_verify.restype = _I32
+    L.gdn_tree_conv_verify.argtypes = [ctypes.POINTER(VerifyArgs), ctypes.POINTER(ConvArgs),
+                                       _I32P, _P, _P]
+    L.gdn_tree_conv_verify_timed.restype = _I32
+    L.gdn_tree_conv_verify_timed.argtypes = [ctypes.POINTER(VerifyArgs),
+                                             ctypes.POINTER(ConvArgs), _I32P, _P, _P, _P, _P]
     L.gdn_tree_conv.restype = _I32
     L.gdn_tree_conv.argtypes = [ctypes.POINTER(ConvArgs), _I32P, _P, _P]
     L.gdn_commit_path.restype = _I32
@@ -304,7 +311,8 @@ def verify_args(image, layers: Layers, q, k, v, beta, gate, out, workspace,
     a.n_heads, a.head_dim = int(layers.state.shape[2]), int(layers.state.shape[3])
     a.max_nodes = int(layers.bank_lg[0].shape[-1]) if max_nodes is None else max_nodes
     a.layer_begin, a.n_layers = layer_begin, n_layers
-    a.in_dtype = GDN_BF16 if (q is not None and q.dtype == torch.bfloat16) else GDN_F32
+    ref = q if q is not None else beta  # the fused conv -> verify call passes no q/k/v
+    a.in_dtype = GDN_BF16 if (ref is not None and ref.dtype == torch.bfloat16) else GDN_F32
     a.q, a.k, a.v, a.beta, a.gate = (_dev(t) for t in (q, k, v, beta, gate))
     a.state = _dev(layers.state)
     for i in range(2):
@@ -382,6 +390,22 @@ def tree_verify_ut_timed(args: VerifyArgs, image: np.ndarray, dev_image, start: 
     _check(lib().gdn_tree_verify_ut_timed(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                           start.handle, stop.handle, _stream(stream)),
            "gdn_tree_verify_ut_timed")
+
+
+def tree_conv_verify(vargs: VerifyArgs, cargs: ConvArgs, image: np.ndarray, dev_image,
+                     stream=None):
+    """Fused conv -> SiLU -> unit-length q/k -> tree-masked verify (gdn_tree_conv_verify);
+    vargs carries no q/k/v, cargs no conv output."""
+    _check(lib().gdn_tree_conv_verify(ctypes.byref(vargs), ctypes.byref(cargs), _ptr(image),
+                                      _dev(dev_image), _stream(stream)), "gdn_tree_conv_verify")
+
+
+def tree_conv_verify_timed(vargs: VerifyArgs, cargs: ConvArgs, image: np.ndarray, dev_image,
+                           start: "HipEvent", stop: "HipEvent", stream=None):
+    _check(lib().gdn_tree_conv_verify_timed(ctypes.byref(vargs), ctypes.byref(cargs),
+                                            _ptr(image), _dev(dev_image), start.handle,
+                                            stop.handle, _stream(stream)),
+           "gdn_tree_conv_verify_timed")
 
 
 def prefill_args(host_offsets, dev_offsets, q, k, v, beta, gate, state, out, layer_begin=0,

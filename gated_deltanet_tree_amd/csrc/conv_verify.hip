@@ -1,0 +1,694 @@
+// Fused tree conv -> SiLU -> unit length prologue feeding the tree-masked verify, on the matrix
+// cores (gfx950, bf16 inputs, d = 128).
+//
+// Pages: "Luce DFlash server README", section "How it works": in tree verify each node's conv
+// window is gathered along its parent chain, and the conv feeds the recurrent layer.  "Lucebox
+// SpecLA and Gated DeltaNet state-resident verification" guide: mechanism 1 (the conv window
+// gets the state-resident treatment; the topology-mask form of the verify), mechanism 3 (the
+// conv raw input is banked beside the key, the residual vector and the log gate), mechanism 4
+// (pending factors and pending conv inputs are folded into the committed state and window
+// before the verify).  The pages do not write out how the conv output becomes q, k and v; this
+// kernel takes the plain reading of a hybrid GDN layer: the conv runs over 3 H d channels laid
+// out [q heads | k heads | v heads], every conv output goes through SiLU (y / (1 + e^-y)), q and
+// k are divided by their Euclidean length (floored at 1e-6) and v is used as it comes.
+//
+// With S0 the committed state after the fold, G_n the product of the gates on n's root path and
+// E(n,a) the product of the gates strictly below a down to n, the verify is the tree-masked form
+//   T[n][a] = beta_n E(n,a) (k_n . k_a)  (a a strict ancestor; T[n][n] = 1),
+//   w_n = beta_n (v_n - G_n S0 k_n),   T u = w,
+//   o_n = G_n S0 q_n + sum_{a in A(n)} C'[n][a] u_a,  C'[n][a] = E(n,a) (q_n . k_a), C'[n][n] = q_n . k_n.
+// The system is not solved level by level here: one wave forms Y = T^-1 and Z = C' Y on the
+// tree's records, after which every (node, state row) is independent:
+//   u_n = sum_{a in A(n)} Y[n][a] w_a,   o_n = G_n S0 q_n + sum_{a in A(n)} Z[n][a] w_a.
+//
+// One workgroup of 4 waves per (layer, sequence, head):
+//   0. direct loads of the head's q, k and v conv-input rows of every node, beta, g, parents,
+//      depths and the tree's plan; each of the head's 3 x 128 channels folds its committed conv
+//      window with the pending conv inputs, writes it back once and keeps it in LDS;
+//   1. the state tile loads are issued; prologue: per node, conv of the q and k channels along
+//      the parent chain, SiLU, unit length, fp32 rows to LDS, raw inputs and keys banked; gate
+//      products along every record block;
+//   2. the pending fold rows start loading; pair products [k; q] K^T on the matrix cores;
+//   3. wave 0 forms Y and Z level by level while every wave folds the pending rows into its
+//      part of the tile; the committed state is written back once;
+//   4. [k; q] S0^T on the matrix cores; the epilogue evaluates the v channels' conv and SiLU and
+//      writes w_n and G_n S0 q_n;
+//   5. u and o of every (node, row); u banked, o stored.
+// Matrix-core layout as in the bf16 UT kernel (v_mfma_f32_16x16x32_bf16): wave w owns state rows
+// [32w, 32w+32), lane l holds rows 32w + 16nt + (l % 16) and columns 16mt + 4(l/16) + e.  q and k
+// are fp32 here, so both operands enter as exact three-term bf16 splits, and each product keeps
+// the six terms that lie above the fp32 rounding level.
+#include <hip/hip_ext.h>
+
+#include "mfma_common.h"
+#include "ut_common.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kCvD = 128;
+constexpr float kNormFloor = 1e-6f;
+
+struct ConvVerifyParams {
+    VerifyParams V;
+    const bf16_t *x;     // [Ly][T][C] conv inputs
+    const bf16_t *w;     // [Ly][C][4] conv weights, tap 3 multiplies the node's own input
+    float *cstate;       // [Ly][S][C][3] committed conv window, oldest first
+    float *bank_x[2];    // [Ly][S][max_nodes][C] conv-input banks
+    int32_t C;           // 3 H d
+};
+
+// LDS regions for trees of at most n nodes, nrec records and nlv level entries, with nfc pending
+// rows folded per LDS chunk.  Region 1 holds the bf16 conv-input planes [v | q | k]; once the
+// prologue has consumed q and k, their part takes the fold rows, then G_n S0 q_n.  The v plane
+// lives until the S0 epilogue.  KQ holds the fp32 k and q rows (k_n at row 2n, q_n at 2n + 1);
+// W takes its place after the S0 products when n <= 32 (all M tiles fit one pass).
+struct CvLayout {
+    static constexpr int D = kCvD;
+    static constexpr int XROW = D * 2;      // bytes of one bf16 conv-input row of one block
+    static constexpr int KS = D + 4;        // fp32 row stride (floats): 16 rows hit distinct banks
+    static constexpr int CPR = D * 4 / 16;  // 16-byte chunks per fp32 fold row
+    size_t xv, xq, fold_k, fold_u, fold_lg, gr, kq, wu, bg, pd, plan, tabs, x0s, total;
+    size_t n64, lv64, rec64;
+    bool alias_w;
+
+    __host__ __device__ static size_t fold_chunks(int r) { return round_up(size_t(r) * CPR, 64); }
+    __host__ __device__ static size_t fold_bytes(int r) {
+        return 2 * fold_chunks(r) * 16 + round_up(size_t(r), 64) * 4;
+    }
+    // direct-load footprint of the three conv-input planes
+    __host__ __device__ static size_t xin_bytes(int n) { return round_up(size_t(48) * n, 64) * 16; }
+    __host__ __device__ static size_t gr_bytes(int n) { return size_t(n) * KS * 4; }
+    // Pending rows per fold chunk that fit in region 1 as sized for the planes and GR.
+    static int fold_rows(int n, int nf) {
+        const size_t room = std::max(xin_bytes(n) - size_t(n) * XROW, gr_bytes(n));
+        int r = 1;
+        while (r < nf && fold_bytes(r + 1) <= room) ++r;
+        return r;
+    }
+
+    __host__ __device__ CvLayout(int n, int nrec, int nlv, int nfc) {
+        n64 = round_up(size_t(n), 64);
+        lv64 = round_up(size_t(nlv), 64);
+        rec64 = round_up(size_t(nrec), 64);
+        xv = 0;
+        xq = size_t(n) * XROW;
+        fold_k = xq;
+        fold_u = xq + fold_chunks(nfc) * 16;
+        fold_lg = fold_u + fold_chunks(nfc) * 16;
+        gr = xq;
+        size_t r1 = xin_bytes(n);
+        if (xq + fold_bytes(nfc) > r1) r1 = xq + fold_bytes(nfc);
+        if (xq + gr_bytes(n) > r1) r1 = xq + gr_bytes(n);
+        kq = round_up(r1, 16);
+        const size_t kq_bytes = size_t(2) * n * KS * 4;
+        alias_w = n <= 32;
+        wu = alias_w ? kq : kq + kq_bytes;
+        size_t p = kq + kq_bytes + (alias_w ? 0 : gr_bytes(n));
+        bg = p;                   // beta | gate [n64] u32 slots
+        p += 2 * n64 * 4;
+        pd = p;                   // parent | depth [n64] int (global parent ids)
+        p += 2 * n64 * 4;
+        plan = p;                 // poff [n64] | lvnode [n64] | lvn [lv64] | recM [rec64]
+        p += (2 * n64 + lv64 + rec64) * 4;
+        tabs = p;                 // gam | kqd [n] | recE=recY | recC | recQ | recZ | recP [nrec]
+        p += (size_t(2) * n + size_t(5) * nrec) * 4;
+        x0s = round_up(p, 16);    // folded conv window [3 taps][3 D channels]
+        total = x0s + size_t(3) * 3 * D * 4;
+    }
+};
+
+__device__ __forceinline__ float silu(float y) { return y / (1.f + expf(-y)); }
+
+// conv of one channel at a node: taps up the parent chain, committed-window entries above the
+// root (w0 oldest); weight tap 3 multiplies the node's own input.
+__device__ __forceinline__ float conv4(const float wt[4], float x0, float x1, float x2, float x3,
+                                       int dt, float c0, float c1, float c2) {
+    const float a1 = dt >= 1 ? x1 : c2;
+    const float a2 = dt >= 2 ? x2 : (dt == 1 ? c2 : c1);
+    const float a3 = dt >= 3 ? x3 : (dt == 2 ? c2 : (dt == 1 ? c1 : c0));
+    return fmaf(wt[3], x0, fmaf(wt[2], a1, fmaf(wt[1], a2, wt[0] * a3)));
+}
+
+// acc += A B for operands given as three-term splits: the six products above 2^-24 relative,
+// smallest first.
+__device__ __forceinline__ floatx4 mfma6(const bf16x8 &ah, const bf16x8 &am, const bf16x8 &al,
+                                         const bf16x8 &bh, const bf16x8 &bm, const bf16x8 &bl,
+                                         floatx4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+    return acc;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
+void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, int n_max,
+                        int nrec_max, int nlv_max, int nfc) {
+    constexpr int D = kCvD, THREADS = 256, NW = 4, JC = 4;
+    using LY = CvLayout;
+    const VerifyParams &P = CP.V;
+    extern __shared__ __align__(16) float dyn[];
+    char *lds = reinterpret_cast<char *>(dyn);
+    const LY lay(n_max, nrec_max, nlv_max, nfc);
+    const size_t n64 = lay.n64;
+    const uint32_t *Bl = reinterpret_cast<const uint32_t *>(lds + lay.bg);
+    const uint32_t *Gt = Bl + n64;
+    const int *par = reinterpret_cast<const int *>(lds + lay.pd);
+    const int *dep = par + n64;
+    float *KQ = reinterpret_cast<float *>(lds + lay.kq);
+    float *Wm = reinterpret_cast<float *>(lds + lay.wu);
+    float *GR = reinterpret_cast<float *>(lds + lay.gr);
+    const float *FK = reinterpret_cast<const float *>(lds + lay.fold_k);
+    const float *FU = reinterpret_cast<const float *>(lds + lay.fold_u);
+    const float *FL = reinterpret_cast<const float *>(lds + lay.fold_lg);
+    // Plan of this tree (from the schedule image): record poff[n] is n itself, poff[n] + d its
+    // ancestor at distance d; recM = that node.
+    int *poff = reinterpret_cast<int *>(lds + lay.plan);
+    int *lvnode = poff + n64;   // nodes ordered by depth, then index
+    int *lvn = lvnode + n64;    // first entry of each depth level in lvnode
+    int *recM = lvn + lay.lv64;
+    float *gam = reinterpret_cast<float *>(lds + lay.tabs);
+    float *kqd = gam + n_max;
+    // recE = E(n, that node), later Y[n][that node]; recC = T, recQ = C', recZ = Z on the
+    // ancestor records; recP = poff of the record's node.
+    float *recE = kqd + n_max, *recC = recE + nrec_max, *recQ = recC + nrec_max;
+    float *recZ = recQ + nrec_max;
+    int *recP = reinterpret_cast<int *>(recZ + nrec_max);
+    float *recY = recE;
+    float *X0s = reinterpret_cast<float *>(lds + lay.x0s);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const UtUnit un = ut_unit(P);
+    const int layer = P.layer_begin + un.layer_rel, seq = un.seq, h = un.h;
+    const int seq_off = P.img[P.off_seq + seq];
+    const int n = P.img[P.off_seq + seq + 1] - seq_off;
+    // pending counts come from the commit call, which bounds them by the bank rows; the clamp
+    // keeps a corrupted count from reading past the banks.
+    const int role = P.role[seq], L = min(max(P.pending[seq], 0), P.max_nodes);
+    const int64_t sh = (int64_t(layer) * P.S + seq) * P.H + h;
+    const int64_t ls = int64_t(layer) * P.S + seq;
+    float *committed = P.state + sh * D * D;
+    const int64_t row0_bank = sh * P.max_nodes;
+    const int64_t node_row0 = (int64_t(layer) * P.T + seq_off) * P.H + h;  // node 0's (beta, g, o) row
+    const int C = CP.C, HD = P.H * D;
+    // node 0's conv inputs, q block of head h; block b adds b H d
+    const bf16_t *xrow0 = CP.x + (int64_t(layer) * P.T + seq_off) * C + h * D;
+    // q and k weights of this lane's two channels 2 lane, 2 lane + 1 (8 bf16 each, 16 bytes)
+    const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
+    const uint4 wq = *reinterpret_cast<const uint4 *>(wq_src);
+    const uint4 wk = *reinterpret_cast<const uint4 *>(wq_src + int64_t(HD) * 4);
+
+    // ---- 0. direct loads; conv-window fold ------------------------------------------------
+    {
+        const int total = 48 * n;  // planes v | q | k, 16 chunks per node row
+        for (int base = w * 64; base < total; base += NW * 64) {
+            const int c = min(base + lane, total - 1);  // padding lanes re-read the last chunk
+            const int p = c / (16 * n), r = c - p * 16 * n, node = r >> 4, idx = r & 15;
+            const int blk = p == 0 ? 2 : p - 1;
+            const char *src = reinterpret_cast<const char *>(xrow0 + int64_t(node) * C +
+                                                             blk * HD) + idx * 16;
+            to_lds<16>(src, lds + lay.xv + size_t(base) * 16);
+        }
+        for (int base = w * 64; base < int(4 * n64); base += NW * 64) {
+            if (n == 0) break;
+            const int which = base / int(n64), t = min(base % int(n64) + lane, n - 1);
+            if (which < 2) {  // beta, gate
+                const bf16_t *src = static_cast<const bf16_t *>(which == 0 ? P.beta : P.gate) +
+                                    node_row0 + int64_t(t) * P.H;
+                to_lds<2>(src, lds + lay.bg + size_t(base) * 4);
+            } else {  // parent, depth (global ids / edges)
+                const int32_t *src =
+                    P.img + (which == 2 ? P.off_parent : P.off_depth) + seq_off + t;
+                to_lds<4>(src, lds + lay.pd + size_t(base - 2 * int(n64)) * 4);
+            }
+        }
+        if (n > 0) {  // the tree's plan: node blocks, level lists, ancestor records
+            const int r0 = P.img[P.off_ut_rec_base + seq], nrec = P.img[P.off_ut_rec_base + seq + 1] - r0;
+            const int l0 = P.img[P.off_ut_lv_base + seq], nlv = P.img[P.off_ut_lv_base + seq + 1] - l0;
+            const int32_t *srcs[4] = {P.img + P.off_ut_node_rec + seq_off,
+                                      P.img + P.off_ut_lvnode + seq_off, P.img + P.off_ut_lvn + l0,
+                                      P.img + P.off_ut_rec_anc + r0};
+            const int counts[4] = {n, n, nlv, nrec};
+            int *dsts[4] = {poff, lvnode, lvn, recM};
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                for (int base = w * 64; base < counts[a]; base += NW * 64)
+                    to_lds<4>(srcs[a] + min(base + lane, counts[a] - 1), dsts[a] + base);
+        }
+        // Fold: only the last three pending inputs survive; one thread owns each channel, reads
+        // its window and writes it back, so no other thread sees a half-updated window.
+        const float *pend = CP.bank_x[role] + ls * P.max_nodes * C;
+        for (int cc = tid; cc < 3 * D; cc += THREADS) {
+            const int64_t ch = int64_t(cc >> 7) * HD + h * D + (cc & (D - 1));
+            float *cs = CP.cstate + (ls * C + ch) * 3;
+            float w0 = cs[0], w1 = cs[1], w2 = cs[2];
+            if (L > 0) {
+                const float *pb = pend + ch;
+                const float r2 = pb[int64_t(L - 1) * C];
+                const float r1 = L >= 2 ? pb[int64_t(L - 2) * C] : 0.f;
+                const float r0 = L >= 3 ? pb[int64_t(L - 3) * C] : 0.f;
+                if (L >= 3) {
+                    w0 = r0; w1 = r1; w2 = r2;
+                } else if (L == 2) {
+                    w0 = w2; w1 = r1; w2 = r2;
+                } else {
+                    w0 = w1; w1 = w2; w2 = r2;
+                }
+                cs[0] = w0;
+                cs[1] = w1;
+                cs[2] = w2;
+            }
+            X0s[cc] = w0;
+            X0s[3 * D + cc] = w1;
+            X0s[6 * D + cc] = w2;
+        }
+    }
+    __syncthreads();  // waits for every direct load (the barrier's fence covers them)
+
+    // The state tile is requested now; its latency hides behind the prologue and the pair
+    // products, which need only LDS.
+    float s[2][8][4];  // rows 32w + 16nt + lr, columns 16mt + 4lg + e
+    {
+        const float *tile = committed + (32 * w + lr) * D + 4 * lg;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * nt * D + 16 * mt);
+                s[nt][mt][0] = x.x;
+                s[nt][mt][1] = x.y;
+                s[nt][mt][2] = x.z;
+                s[nt][mt][3] = x.w;
+            }
+    }
+
+    // ---- 1. prologue: q and k from the conv; raw inputs and keys banked -------------------
+    {
+        const char *XV = lds + lay.xv;
+        const char *XQ = XV + size_t(n) * LY::XROW, *XK = XQ + size_t(n) * LY::XROW;
+        // taps of channels 2 lane + e (e < 2) of the q (b = 0) and k (b = 1) blocks
+        float wt[2][2][4], cw[2][2][3];
+        const uint4 wraw[2] = {wq, wk};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t r4[4] = {wraw[b].x, wraw[b].y, wraw[b].z, wraw[b].w};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                wt[b][e][0] = bf16_lo(r4[2 * e]);
+                wt[b][e][1] = bf16_hi(r4[2 * e]);
+                wt[b][e][2] = bf16_lo(r4[2 * e + 1]);
+                wt[b][e][3] = bf16_hi(r4[2 * e + 1]);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) cw[b][e][j] = X0s[j * 3 * D + b * D + 2 * lane + e];
+            }
+        }
+        float *wk_bank = P.bank_k[role ^ 1];
+        float *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D + 2 * lane;
+        for (int nd = w; nd < n; nd += NW) {
+            const int dt = dep[nd];
+            const int p1 = dt >= 1 ? par[nd] - seq_off : nd;
+            const int p2 = dt >= 2 ? par[p1] - seq_off : p1;
+            const int p3 = dt >= 3 ? par[p2] - seq_off : p2;
+            const int rows[4] = {nd, p1, p2, p3};
+            float y[2][2], ss[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const char *pl = b == 0 ? XQ : XK;
+                uint32_t xw[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    xw[t] = *reinterpret_cast<const uint32_t *>(pl + size_t(rows[t]) * LY::XROW + 4 * lane);
+                ss[b] = 0.f;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float x0 = e ? bf16_hi(xw[0]) : bf16_lo(xw[0]);
+                    const float x1 = e ? bf16_hi(xw[1]) : bf16_lo(xw[1]);
+                    const float x2 = e ? bf16_hi(xw[2]) : bf16_lo(xw[2]);
+                    const float x3 = e ? bf16_hi(xw[3]) : bf16_lo(xw[3]);
+                    const float v = silu(conv4(wt[b][e], x0, x1, x2, x3, dt, cw[b][e][0],
+                                               cw[b][e][1], cw[b][e][2]));
+                    y[b][e] = v;
+                    ss[b] = fmaf(v, v, ss[b]);
+                }
+                // raw conv inputs of the q and k blocks to the write bank
+                *reinterpret_cast<float2 *>(bx + int64_t(nd) * C + b * HD) =
+                    make_float2(bf16_lo(xw[0]), bf16_hi(xw[0]));
+            }
+            {  // raw conv inputs of the v block
+                const uint32_t xv = *reinterpret_cast<const uint32_t *>(XV + size_t(nd) * LY::XROW + 4 * lane);
+                *reinterpret_cast<float2 *>(bx + int64_t(nd) * C + 2 * HD) =
+                    make_float2(bf16_lo(xv), bf16_hi(xv));
+            }
+            const float sq = wave_sum(ss[0]), sk = wave_sum(ss[1]);
+            const float iq = 1.f / fmaxf(sqrtf(sq), kNormFloor);
+            const float ik = 1.f / fmaxf(sqrtf(sk), kNormFloor);
+            const float2 kv = make_float2(y[1][0] * ik, y[1][1] * ik);
+            const float2 qv = make_float2(y[0][0] * iq, y[0][1] * iq);
+            *reinterpret_cast<float2 *>(KQ + size_t(2 * nd) * LY::KS + 2 * lane) = kv;
+            *reinterpret_cast<float2 *>(KQ + size_t(2 * nd + 1) * LY::KS + 2 * lane) = qv;
+            *reinterpret_cast<float2 *>(wk_bank + (row0_bank + nd) * D + 2 * lane) = kv;
+        }
+    }
+    // gate products along every record block:
+    //   E(n, anc_0) = g_n, E(n, anc_{t+1}) = E(n, anc_t) g_{anc_t}, G_n = E(n, root) g_root.
+    for (int t = tid; t < n; t += THREADS) {
+        const int o = poff[t], dt = dep[t];
+        float E = slot_f32<bf16_t>(Gt[t]);
+        for (int s2 = 0; s2 < dt; ++s2) {
+            const int a = recM[o + 1 + s2];
+            recE[o + 1 + s2] = E;
+            recP[o + 1 + s2] = poff[a];
+            E *= slot_f32<bf16_t>(Gt[a]);
+        }
+        gam[t] = E;
+        P.bank_lg[role ^ 1][row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
+    }
+    __syncthreads();  // q and k rows, gate products, record offsets
+
+    // ---- 2. pending fold rows (first chunk) start loading; pair products ------------------
+    const int fk_chunks = int(LY::fold_chunks(nfc));
+    auto issue_fold = [&](int f0, int cnt) {
+        const float *pk = P.bank_k[role] + (row0_bank + f0) * D;
+        const float *pu = P.bank_u[role] + (row0_bank + f0) * D;
+        const int rows_chunks = cnt * LY::CPR;
+        for (int base = w * 64; base < 2 * fk_chunks; base += NW * 64) {
+            const int which = base / fk_chunks, b2 = base % fk_chunks;
+            if (b2 >= rows_chunks) continue;
+            const int c = min(b2 + lane, rows_chunks - 1);
+            const float *src = (which == 0 ? pk : pu) + c * 4;
+            to_lds<16>(src, lds + lay.fold_k + size_t(base) * 16);
+        }
+        const float *plg = P.bank_lg[role] + row0_bank + f0;
+        for (int base = w * 64; base < cnt; base += NW * 64)
+            to_lds<4>(plg + min(base + lane, cnt - 1), lds + lay.fold_lg + size_t(base) * 4);
+    };
+    if (L > 0) issue_fold(0, min(L, nfc));
+
+    // M tile jt stacks k (rows 0-7) and q (rows 8-15) of nodes 8jt .. 8jt+7; N tile at holds the
+    // keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: k . k_a for lg < 2 and
+    // q . k_a for lg >= 2, of node 8jt + 4(lg & 1) + r, with a = 16at + lr.
+    const int JT = (n + 7) >> 3, AT = (n + 15) >> 4;
+    for (int ti = w; ti < JT * AT; ti += NW) {
+        const int jt = ti / AT, at = ti % AT;
+        const int xn = 8 * jt + (lr & 7), kn = 16 * at + lr;
+        const float *xrow = KQ + size_t(2 * xn + (lr >> 3)) * LY::KS;
+        const float *krow = KQ + size_t(2 * kn) * LY::KS;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 ah = {}, am = {}, al = {}, bh = {}, bm = {}, bl = {};
+            if (xn < n) row_operand_split(xrow, 32 * kb + 4 * lg, ah, am, al);
+            if (kn < n) row_operand_split(krow, 32 * kb + 4 * lg, bh, bm, bl);
+            acc = mfma6(ah, am, al, bh, bm, bl, acc);
+        }
+        const int an = 16 * at + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int nd = 8 * jt + 4 * (lg & 1) + r;
+            const bool is_q = lg >= 2;
+            if (nd >= n || an >= n) continue;
+            if (an == nd) {
+                if (is_q) kqd[nd] = acc[r];
+                continue;
+            }
+            const int dn = dep[nd], da = dep[an];
+            if (da >= dn) continue;
+            const int q = poff[nd] + dn - da;  // record of the ancestor at distance dn - da
+            if (recM[q] != an) continue;
+            if (is_q)
+                recQ[q] = recE[q] * acc[r];
+            else
+                recC[q] = slot_f32<bf16_t>(Bl[nd]) * recE[q] * acc[r];
+        }
+    }
+    __syncthreads();  // T, C', q.k on the records; the first fold chunk has landed
+
+    // v-channel taps of this lane's state rows 32w + 16nt + lr, for the S0 epilogue
+    uint2 wvr[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+        wvr[nt] = *reinterpret_cast<const uint2 *>(CP.w + (int64_t(layer) * C + 2 * HD + h * D +
+                                                           32 * w + 16 * nt + lr) * 4);
+
+    // ---- 3. Y = T^-1 and Z = C' Y on the records (wave 0); fold ----------------------------
+    // Record (n, t) = ancestor a_t of n at distance t + 1, at q1 + t with q1 = poff[n] + 1:
+    //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
+    //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
+    // where Y[a_s][a_t] is record poff[a_s] + t - s.  Level by level: every term read belongs to
+    // a shallower node.  Y and Z of a node with itself are 1 and q_n.k_n and are not stored.
+    if (w == 0 && n > 0) {
+        const int dmax = plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2;
+        for (int lv = 1; lv <= dmax; ++lv) {
+            const int j0 = lvn[lv], items = (lvn[lv + 1] - j0) * lv;
+            for (int it = lane; it < items; it += 64) {
+                const int j = j0 + it / lv, t = it % lv;
+                const int nd = lvnode[j];
+                const int q1 = poff[nd] + 1;
+                float ys = recC[q1 + t], zs = recQ[q1 + t];
+                for (int s2 = 0; s2 < t; ++s2) {
+                    const float yv = recY[recP[q1 + s2] + (t - s2)];
+                    ys = fmaf(recC[q1 + s2], yv, ys);
+                    zs = fmaf(recQ[q1 + s2], yv, zs);
+                }
+                recY[q1 + t] = -ys;
+                recZ[q1 + t] = fmaf(kqd[nd], -ys, zs);
+            }
+            wave_order();
+        }
+    }
+
+    // deferred commit: fold the pending rows, write the committed state once
+    for (int f0 = 0; f0 < L; f0 += nfc) {
+        const int cnt = min(L - f0, nfc);
+        if (f0 > 0) {  // later chunks (more pending rows than one chunk holds)
+            __syncthreads();
+            issue_fold(f0, cnt);
+            __syncthreads();
+        }
+        for (int f = 0; f < cnt; ++f) {
+            const float gf = expf(FL[f]);
+            const float u0 = FU[f * D + 32 * w + lr], u1 = FU[f * D + 32 * w + 16 + lr];
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const float4 k4 = *reinterpret_cast<const float4 *>(FK + f * D + 16 * mt + 4 * lg);
+                const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s[0][mt][e] = fmaf(u0, kk[e], gf * s[0][mt][e]);
+                    s[1][mt][e] = fmaf(u1, kk[e], gf * s[1][mt][e]);
+                }
+            }
+        }
+    }
+    if (L > 0) {
+        float *tile = committed + (32 * w + lr) * D + 4 * lg;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                *reinterpret_cast<float4 *>(tile + 16 * nt * D + 16 * mt) =
+                    make_float4(s[nt][mt][0], s[nt][mt][1], s[nt][mt][2], s[nt][mt][3]);
+    }
+    __syncthreads();  // fold rows are dead (their LDS becomes GR); Y and Z are complete
+
+    // ---- 4. p_n = S0 k_n, r_n = S0 q_n on the matrix cores; w_n and G_n r_n to LDS -------
+    {
+        const char *XV = lds + lay.xv;
+        for (int jt0 = 0; jt0 < JT; jt0 += JC) {
+            // One half of the wave's state rows at a time (nt outer): only that half's split
+            // is live, and the first half's tile registers die before the second half runs.
+            floatx4 acc[JC][2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+                for (int jc = 0; jc < JC; ++jc) acc[jc][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    bf16x8 bh, bm, bl;
+                    const float x[8] = {s[nt][2 * kb][0],     s[nt][2 * kb][1],
+                                        s[nt][2 * kb][2],     s[nt][2 * kb][3],
+                                        s[nt][2 * kb + 1][0], s[nt][2 * kb + 1][1],
+                                        s[nt][2 * kb + 1][2], s[nt][2 * kb + 1][3]};
+                    split3(x, bh, bm, bl);
+#pragma unroll
+                    for (int jc = 0; jc < JC; ++jc) {
+                        const int jt = jt0 + jc;
+                        if (jt >= JT) break;
+                        const int xn = 8 * jt + (lr & 7);
+                        bf16x8 ah = {}, am = {}, al = {};
+                        if (xn < n)
+                            row_operand_split(KQ + size_t(2 * xn + (lr >> 3)) * LY::KS,
+                                              32 * kb + 4 * lg, ah, am, al);
+                        acc[jc][nt] = mfma6(ah, am, al, bh, bm, bl, acc[jc][nt]);
+                    }
+                }
+            }
+            if (lay.alias_w) __syncthreads();  // every wave is done with KQ before W replaces it
+            // Lane (lr, lg) holds rows 4lg + r of each M tile: p of node 8jt + 4lg + r for lg < 2,
+            // r of node 8jt + 4(lg - 2) + r for lg >= 2, at state row 32w + 16nt + lr.
+#pragma unroll
+            for (int jc = 0; jc < JC; ++jc) {
+                const int jt = jt0 + jc;
+                if (jt >= JT) break;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int nd = 8 * jt + 4 * (lg & 1) + r;
+                    if (nd >= n) continue;
+                    const float G = gam[nd];
+                    if (lg < 2) {
+                        const int dt = dep[nd];
+                        const int p1 = dt >= 1 ? par[nd] - seq_off : nd;
+                        const int p2 = dt >= 2 ? par[p1] - seq_off : p1;
+                        const int p3 = dt >= 3 ? par[p2] - seq_off : p2;
+                        const float beta = slot_f32<bf16_t>(Bl[nd]);
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt) {
+                            const int i = 32 * w + 16 * nt + lr;
+                            const float wv[4] = {bf16_lo(wvr[nt].x), bf16_hi(wvr[nt].x),
+                                                 bf16_lo(wvr[nt].y), bf16_hi(wvr[nt].y)};
+                            const float *cv = X0s + 2 * D + i;  // v channel i, taps 0..2
+                            const float v = silu(conv4(
+                                wv, bf16_at(XV + size_t(nd) * LY::XROW, i),
+                                bf16_at(XV + size_t(p1) * LY::XROW, i),
+                                bf16_at(XV + size_t(p2) * LY::XROW, i),
+                                bf16_at(XV + size_t(p3) * LY::XROW, i), dt, cv[0], cv[3 * D],
+                                cv[6 * D]));
+                            Wm[nd * LY::KS + i] = beta * fmaf(-G, acc[jc][nt][r], v);
+                        }
+                    } else {
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt)
+                            GR[nd * LY::KS + 32 * w + 16 * nt + lr] = G * acc[jc][nt][r];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
+    {
+        float *wu = P.bank_u[role ^ 1];
+        float *out0 = P.out + node_row0 * D;
+        // row from the wave and lane ids (nothing carried from the kernel start)
+        const int i = 64 * (w & 1) + int(__lane_id());
+        const int half = w >> 1;
+        for (int nd = half; nd < n; nd += THREADS / D) {
+            const int q1 = poff[nd] + 1, dn = dep[nd];
+            const float wn = Wm[nd * LY::KS + i];
+            float u = wn, o = fmaf(kqd[nd], wn, GR[nd * LY::KS + i]);
+#pragma unroll 4
+            for (int t = 0; t < dn; ++t) {
+                const float x = Wm[recM[q1 + t] * LY::KS + i];
+                u = fmaf(recY[q1 + t], x, u);
+                o = fmaf(recZ[q1 + t], x, o);
+            }
+            wu[(row0_bank + nd) * D + i] = u;
+            out0[int64_t(nd) * P.H * D + i] = o;
+        }
+    }
+}
+
+namespace {
+
+gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
+                           const int32_t *host_image, const int32_t *dev_image, void *stream,
+                           hipEvent_t start, hipEvent_t stop) {
+    VerifyParams P;
+    ImageView v;
+    gdn_status st = verify_setup(va, host_image, dev_image, P, v, false, false);
+    if (st != GDN_OK) return st;
+    if (va->head_dim != kCvD || va->in_dtype != GDN_BF16)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: needs head_dim 128 and bf16 beta/gate "
+                    "(got %d, dtype %d)", va->head_dim, va->in_dtype);
+    if (ca == nullptr) return fail(GDN_EINVAL, "gdn_tree_conv_verify: null conv args");
+    if (ca->in_dtype != GDN_BF16 || ca->width != 4)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: needs bf16 x/weight and conv width 4");
+    if (int64_t(ca->channels) != 3ll * va->n_heads * kCvD)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: channels %d != 3 * n_heads * 128",
+                    ca->channels);
+    if (ca->n_seqs != va->n_seqs || ca->n_nodes != va->n_nodes ||
+        ca->max_nodes != va->max_nodes || ca->layer_begin != va->layer_begin ||
+        ca->n_layers != va->n_layers)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: conv and verify args disagree on "
+                    "n_seqs/n_nodes/max_nodes/layer_begin/n_layers");
+    if (va->n_seqs == 0) return GDN_OK;  // empty batch: nothing is read or written
+    if (ca->role != va->role || ca->pending_len != va->pending_len)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: conv and verify args must share the "
+                    "role and pending_len arrays");
+    if (!ca->x || !ca->weight || !ca->conv_state || !ca->bank_x[0] || !ca->bank_x[1])
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: null x/weight/conv_state/bank_x");
+    if (reinterpret_cast<uintptr_t>(ca->x) % 16 || reinterpret_cast<uintptr_t>(ca->weight) % 16)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: x and weight must be 16-byte aligned");
+    if (v.ut_records < 0)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: the schedule has no tree-masked plan "
+                    "(its trees need more than %d records per node)", kUtRecordsPerNode);
+    P.off_parent = v.off_parent;
+    P.off_depth = v.off_depth;
+    P.off_ut_rec_base = v.off_ut_rec_base;
+    P.off_ut_node_rec = v.off_ut_node_rec;
+    P.off_ut_lv_base = v.off_ut_lv_base;
+    P.off_ut_lvn = v.off_ut_lvn;
+    P.off_ut_lvnode = v.off_ut_lvnode;
+    P.off_ut_rec_anc = v.off_ut_rec_anc;
+    P.n_blocks = int64_t(va->n_layers) * va->n_seqs * va->n_heads;
+    if (P.n_blocks > kMaxBlocks)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: too many workgroups for one launch");
+    const int n_max = v.max_tree, nrec_max = v.ut_max_records, nlv_max = v.ut_max_levels;
+    const int nfc = CvLayout::fold_rows(n_max, va->max_nodes);
+    const size_t lds = CvLayout(n_max, nrec_max, nlv_max, nfc).total;
+    if (lds > kUtMaxLdsBytes)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: trees of %d nodes with %d records need "
+                    "%zu bytes of LDS (limit %zu)", n_max, nrec_max, lds, kUtMaxLdsBytes);
+    ConvVerifyParams CP;
+    CP.V = P;
+    CP.x = static_cast<const bf16_t *>(ca->x);
+    CP.w = static_cast<const bf16_t *>(ca->weight);
+    CP.cstate = ca->conv_state;
+    CP.bank_x[0] = ca->bank_x[0];
+    CP.bank_x[1] = ca->bank_x[1];
+    CP.C = ca->channels;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid(uint32_t(P.n_blocks));
+    if (start == nullptr && stop == nullptr)
+        hipLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), lds, s, CP, P.img, n_max,
+                           nrec_max, nlv_max, nfc);
+    else
+        hipExtLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), uint32_t(lds), s, start, stop,
+                              0, CP, P.img, n_max, nrec_max, nlv_max, nfc);
+    GDN_LAUNCH_CHECK("conv_verify_kernel");
+    return GDN_OK;
+}
+
+}  // namespace
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" gdn_status gdn_tree_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
+                                           const int32_t *host_image, const int32_t *dev_image,
+                                           void *stream) {
+    clear_error();
+    return run_conv_verify(va, ca, host_image, dev_image, stream, nullptr, nullptr);
+}
+
+extern "C" gdn_status gdn_tree_conv_verify_timed(const gdn_verify_args *va,
+                                                 const gdn_conv_args *ca,
+                                                 const int32_t *host_image,
+                                                 const int32_t *dev_image, void *start_event,
+                                                 void *stop_event, void *stream) {
+    clear_error();
+    if (start_event == nullptr || stop_event == nullptr)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify_timed: null event");
+    return run_conv_verify(va, ca, host_image, dev_image, stream,
+                           static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+}

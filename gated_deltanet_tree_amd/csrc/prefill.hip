@@ -26,15 +26,12 @@
 // and columns 16mt + 4(l / 16) + e.
 #include <hip/hip_ext.h>
 
+#include "mfma_common.h"
 #include "ut_common.h"
 
 namespace gdn {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kC = 16;                    // tokens per chunk
@@ -62,43 +59,6 @@ struct PrefillLds {
     float Tm[kC][kC], Cm[kC][kC];    // read as whole rows by every lane (broadcast)
     float W[kC][kRowPad], GR[kC][kRowPad], Ug[kC][kRowPad];
 };
-
-__device__ __forceinline__ void split3(const float *x, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
-    u32x4 h, m, l;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t b0 = __float_as_uint(x[2 * p]), b1 = __float_as_uint(x[2 * p + 1]);
-        const float r0 = x[2 * p] - __uint_as_float(b0 & 0xFFFF0000u);
-        const float r1 = x[2 * p + 1] - __uint_as_float(b1 & 0xFFFF0000u);
-        const uint32_t c0 = __float_as_uint(r0), c1 = __float_as_uint(r1);
-        const float t0 = r0 - __uint_as_float(c0 & 0xFFFF0000u);
-        const float t1 = r1 - __uint_as_float(c1 & 0xFFFF0000u);
-        h[p] = (b0 >> 16) | (b1 & 0xFFFF0000u);
-        m[p] = (c0 >> 16) | (c1 & 0xFFFF0000u);
-        l[p] = (__float_as_uint(t0) >> 16) | (__float_as_uint(t1) & 0xFFFF0000u);
-    }
-    hi = __builtin_bit_cast(bf16x8, h);
-    mid = __builtin_bit_cast(bf16x8, m);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
-
-__device__ __forceinline__ bf16x8 row_operand(const char *row, int c0) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(row + c0 * 2);
-    const uint2 b = *reinterpret_cast<const uint2 *>(row + (c0 + 16) * 2);
-    const u32x4 v = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ float bf16_at(const char *row, int i) {
-    return __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t *>(row + i * 2)) << 16);
-}
-
-// LDS accesses of one wave stay in program order across its lanes.
-__device__ __forceinline__ void wave_order() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 }  // namespace
 

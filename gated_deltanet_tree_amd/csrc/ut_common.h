@@ -30,6 +30,20 @@ template <typename TIn> __device__ __forceinline__ float slot_f32(uint32_t x) {
     return sizeof(TIn) == 2 ? __uint_as_float(x << 16) : __uint_as_float(x);
 }
 
+struct UtUnit {  // (layer, sequence, head) of a workgroup, from its XCD-aware logical id
+    int layer_rel, seq, h;
+};
+__device__ __forceinline__ UtUnit ut_unit(const VerifyParams &P) {
+    // Grids are capped at kMaxBlocks workgroups, so block arithmetic stays in 32 bits.
+    const uint32_t logical = xcd_logical(blockIdx.x, uint32_t(P.n_blocks));
+    const uint32_t per = uint32_t(P.S) * uint32_t(P.H);
+    UtUnit u;
+    u.layer_rel = int(logical / per);
+    u.seq = int((logical % per) / uint32_t(P.H));
+    u.h = int(logical % uint32_t(P.H));
+    return u;
+}
+
 // The matrix-core UT kernel (bf16 inputs, d = 128).
 gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int nrec_max, int nlv_max,
                           int nf_max, hipStream_t stream, hipEvent_t start, hipEvent_t stop);

@@ -249,7 +249,9 @@ static gdn_status dispatch_verify(const VerifyParams &P, int d, int dtype, hipSt
                              : launch_verify<16, float>(P, stream, start, stop);
 }
 
-static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule_inputs) {
+// need_schedule_inputs: beta, gate and out (and q, k, v when need_qkv) are read or written.
+static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule_inputs,
+                                    bool need_qkv = true) {
     if (a == nullptr) return fail(GDN_EINVAL, "verify args: null");
     if (a->head_dim != 16 && a->head_dim != 128)
         return fail(GDN_EINVAL, "verify args: head_dim %d not in {16, 128}", a->head_dim);
@@ -264,9 +266,10 @@ static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule
     for (int i = 0; i < 2; ++i)
         if (!a->bank_k[i] || !a->bank_u[i] || !a->bank_lg[i])
             return fail(GDN_EINVAL, "verify args: null bank pointer");
-    if (need_schedule_inputs &&
-        (!a->q || !a->k || !a->v || !a->beta || !a->gate || !a->out))
-        return fail(GDN_EINVAL, "verify args: null q/k/v/beta/gate/out");
+    if (need_schedule_inputs && (!a->beta || !a->gate || !a->out))
+        return fail(GDN_EINVAL, "verify args: null beta/gate/out");
+    if (need_schedule_inputs && need_qkv && (!a->q || !a->k || !a->v))
+        return fail(GDN_EINVAL, "verify args: null q/k/v");
     // Tiles, rows and vectors are moved in 16-byte pieces.
     const void *aligned[] = {a->q, a->k, a->v, a->state, a->bank_k[0], a->bank_k[1],
                              a->bank_u[0], a->bank_u[1], a->workspace, a->out};
@@ -279,8 +282,8 @@ static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule
 
 gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
                         const int32_t *dev_image, VerifyParams &P, ImageView &v,
-                        bool need_boundary) {
-    gdn_status st = check_verify_args(a, true);
+                        bool need_boundary, bool need_qkv) {
+    gdn_status st = check_verify_args(a, true, need_qkv);
     if (st != GDN_OK) return st;
     if (!image_ok(host_image) || dev_image == nullptr)
         return fail(GDN_EINVAL, "gdn_tree_verify: missing or malformed schedule image");

@@ -25,6 +25,12 @@ struct VerifyParams {
     int32_t fold_only;  // flush: one workgroup per (layer, seq, head), fold + store only
 };
 
+// Host: validates the verify arguments against the schedule image and fills the kernel
+// parameters shared by every verify entry point (q, k, v may be absent when !need_qkv).
+gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
+                        const int32_t *dev_image, VerifyParams &P, ImageView &v,
+                        bool need_boundary, bool need_qkv = true);
+
 template <int D> struct Tile {
     static constexpr int RW = D >= 32 ? 32 : D;       // rows per wave
     static constexpr int NW = D / RW;                 // waves per workgroup

@@ -402,10 +402,6 @@ static gdn_status launch_ut(const VerifyParams &P, int n_max, int np_max, int nf
     return GDN_OK;
 }
 
-gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
-                        const int32_t *dev_image, VerifyParams &P, ImageView &v,
-                        bool need_boundary);
-
 // Largest tree and largest number of (node, strict ancestor) pairs of any tree of a schedule.
 static void ut_tree_bounds(const int32_t *host_image, const ImageView &v, int &n_max,
                            int &np_max) {

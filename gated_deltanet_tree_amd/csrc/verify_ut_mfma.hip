@@ -31,13 +31,10 @@
 // exact and only the fp32 accumulation rounds.
 #include <hip/hip_ext.h>
 
+#include "mfma_common.h"
 #include "ut_common.h"
 
 namespace gdn {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUtD = 128;
 
@@ -76,53 +73,6 @@ struct UtLayout5 {
         total = tabs + (size_t(2) * n + size_t(3) * nrec) * 4;
     }
 };
-
-// Exact split of 8 fp32 values into three bf16 vectors (hi + mid + lo == x for normal x): each
-// term takes the next 8 significant bits by truncation, so every remainder is exact.
-__device__ __forceinline__ void split3(const float *x, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
-    u32x4 h, m, l;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t b0 = __float_as_uint(x[2 * p]), b1 = __float_as_uint(x[2 * p + 1]);
-        const float r0 = x[2 * p] - __uint_as_float(b0 & 0xFFFF0000u);
-        const float r1 = x[2 * p + 1] - __uint_as_float(b1 & 0xFFFF0000u);
-        const uint32_t c0 = __float_as_uint(r0), c1 = __float_as_uint(r1);
-        const float t0 = r0 - __uint_as_float(c0 & 0xFFFF0000u);
-        const float t1 = r1 - __uint_as_float(c1 & 0xFFFF0000u);
-        h[p] = (b0 >> 16) | (b1 & 0xFFFF0000u);
-        m[p] = (c0 >> 16) | (c1 & 0xFFFF0000u);
-        l[p] = (__float_as_uint(t0) >> 16) | (__float_as_uint(t1) & 0xFFFF0000u);
-    }
-    hi = __builtin_bit_cast(bf16x8, h);
-    mid = __builtin_bit_cast(bf16x8, m);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
-
-// Operand of one 32-wide k-step from a bf16 row in LDS: elements c0 .. c0+3 and c0+16 .. c0+19.
-__device__ __forceinline__ bf16x8 row_operand(const char *row, int c0) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(row + c0 * 2);
-    const uint2 b = *reinterpret_cast<const uint2 *>(row + (c0 + 16) * 2);
-    const u32x4 v = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ float bf16_at(const char *row, int i) {
-    return __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t *>(row + i * 2)) << 16);
-}
-
-struct UtUnit {  // (layer, sequence, head) of a workgroup, from its XCD-aware logical id
-    int layer_rel, seq, h;
-};
-__device__ __forceinline__ UtUnit ut_unit(const VerifyParams &P) {
-    // Grids are capped at kMaxBlocks workgroups, so block arithmetic stays in 32 bits.
-    const uint32_t logical = xcd_logical(blockIdx.x, uint32_t(P.n_blocks));
-    const uint32_t per = uint32_t(P.S) * uint32_t(P.H);
-    UtUnit u;
-    u.layer_rel = int(logical / per);
-    u.seq = int((logical % per) / uint32_t(P.H));
-    u.h = int(logical % uint32_t(P.H));
-    return u;
-}
 
 // ------------------------------------------------------------------------------------------
 // one workgroup of 4 waves per (layer, sequence, head)

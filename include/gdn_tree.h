@@ -312,6 +312,40 @@ gdn_status gdn_tree_conv(const gdn_conv_args *args, const int32_t *host_image,
                          const int32_t *dev_image, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Fused conv -> verify (DFlash README, "How it works": the tree-aware conv window is gathered
+ * along the parent chain and feeds the recurrent layer; SpecLA guide, mechanism 1 for the
+ * conv window and the topology-mask verify, mechanisms 3 and 4 for the banks and the fold).
+ * One launch per call does the work of gdn_tree_conv followed by gdn_tree_verify_ut, with q, k
+ * and v taken from the conv instead of from memory:
+ *   y    = the tree conv of gdn_tree_conv (after the same conv-window fold), over channels laid
+ *          out [q heads | k heads | v heads]: C = 3 H d, and head h's q, k and v channels are
+ *          h d + i, H d + h d + i and 2 H d + h d + i (i < d);
+ *   q, k, v = silu(y) of the three blocks, silu(y) = y / (1 + exp(-y));
+ *   q and k of each (node, head) are divided by max(their Euclidean length, 1e-6); v as is;
+ * then the verify, fold, factor banks and outputs of gdn_tree_verify_ut on those q, k, v.  The
+ * banked key is the fp32 unit key; x[n] is banked in bank_x[1 - role] as gdn_tree_conv does,
+ * and the folded conv window is written back to conv_state.  The pages do not spell out the
+ * conv-to-q/k/v wiring; this is the plain reading of a hybrid GDN layer.
+ * Ignored (may be NULL): va->q, va->k, va->v, va->workspace and ca->out (the conv output stays
+ * on chip).  Requirements (GDN_EINVAL otherwise, nothing launched): head_dim 128; bf16 beta,
+ * gate, x and weight; ca->channels = 3 H 128; ca's n_seqs, n_nodes, max_nodes, layer_begin and
+ * n_layers equal va's; ca->role and ca->pending_len are the same device arrays as va's; x and
+ * weight 16-byte aligned; the schedule carries the tree-masked plan and the trees fit one
+ * workgroup's LDS (160 KiB: about 60 nodes).
+ * Work: one workgroup per (layer, sequence, head), 4 waves; the conv, SiLU and normalisation
+ * run in its prologue, the rest as gdn_tree_verify_ut on the matrix cores.
+ * ---------------------------------------------------------------------------------- */
+gdn_status gdn_tree_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
+                                const int32_t *host_image, const int32_t *dev_image,
+                                void *stream);
+
+/* gdn_tree_conv_verify with dispatch-recorded start/stop HIP events (see
+ * gdn_tree_verify_wave_timed). */
+gdn_status gdn_tree_conv_verify_timed(const gdn_verify_args *va, const gdn_conv_args *ca,
+                                      const int32_t *host_image, const int32_t *dev_image,
+                                      void *start_event, void *stop_event, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Accept -> commit (SpecLA guide, mechanism 3). Enqueue after the last layer's verify and
  * conv of the step. For each sequence b with accepted root path P_b of length L_b:
  *   L_b = 0            : pending_len[b] = 0 (nothing to commit)
