@@ -5,10 +5,14 @@ and its upload, then for every GDN layer the tree conv (with the conv-window fol
 verify (with the deferred-commit fold), then accept -> commit of one seeded path per sequence
 (role swap or compaction).  The timed region is K steps plus the final flush.
 
-Both verify paths are timed, one after the other, on the same resident workload:
-  ut     the tree-masked form on the matrix cores, one launch per layer (the headline value);
-  chain  heavy-light chains launched wave by wave (reported under "paths").
-They compute the same outputs, factor banks and committed states.
+Three paths are timed, one after the other, on the same resident workload:
+  ut     the tree conv, then the tree-masked verify of given q/k/v on the matrix cores (the
+         headline by default);
+  fused  conv -> SiLU -> unit-length q/k -> tree-masked verify in one launch per layer: q, k
+         and v come from the conv of the raw inputs x, as in a hybrid GDN layer;
+  chain  the tree conv, then heavy-light chains launched wave by wave.
+ut and chain compute the same outputs, factor banks and committed states; fused computes the
+layer whose q/k/v are the conv's (all three are reported under "paths").
 
 Workload (default): 32 sequences, each with its own seeded 22-node top-4 tree (depth <= 12),
 48 GDN layers x 48 heads x d = 128 with independent fp32 states (4.8 GB), bf16 inputs, conv
@@ -36,13 +40,18 @@ COUNTERS = {
     "chain": os.path.join(ROOT, "profiles", "verify_chain_kernel_batched32x48_counters.json"),
     "ut": os.path.join(ROOT, "profiles", "verify_ut_mfma_kernel_batched32x48_counters.json"),
     "prefill": os.path.join(ROOT, "profiles", "prefill_kernel_8x2048x48_counters.json"),
+    "fused": os.path.join(ROOT, "profiles", "conv_verify_kernel_batched32x48_counters.json"),
 }
 KERNEL_SOURCES = {
     "chain": ["verify.hip", "verify_common.h", "gdn_device.h"],
-    "ut": ["verify_ut_mfma.hip", "ut_common.h", "verify_common.h", "gdn_device.h"],
-    "prefill": ["prefill.hip", "ut_common.h", "verify_common.h", "gdn_device.h"],
+    "ut": ["verify_ut_mfma.hip", "mfma_common.h", "ut_common.h", "verify_common.h",
+           "gdn_device.h"],
+    "prefill": ["prefill.hip", "mfma_common.h", "ut_common.h", "verify_common.h", "gdn_device.h"],
+    "fused": ["conv_verify.hip", "mfma_common.h", "ut_common.h", "verify_common.h",
+              "gdn_device.h"],
 }
-KERNEL = {"chain": "verify_chain_kernel<128, bf16>", "ut": "verify_ut_mfma_kernel"}
+KERNEL = {"chain": "verify_chain_kernel<128, bf16>", "ut": "verify_ut_mfma_kernel",
+          "fused": "conv_verify_kernel"}
 METRIC = "verified tree nodes/sec per GDN layer + achieved HBM GB/s vs peak, 1 MI355X"
 
 
@@ -83,6 +92,25 @@ def ut_bytes(view, pending, H, d, in_bytes, n_layers=1):
         n_b = int(view["seq_offsets"][b + 1] - view["seq_offsets"][b])
         total += H * (tile + (tile + L * (8 * d + 4) if L > 0 else 0) + n_b * per_node)
     return total * n_layers
+
+
+def fused_bytes(view, pending, H, d, in_bytes, n_layers=1):
+    """Bytes one fused conv -> verify launch moves.  Per (sequence, head): the committed tile
+    read, its conv window (3 d channels x 3 taps) read; when folding, the tile write-back, the
+    pending factor rows, the last min(L, 3) pending conv rows and the window write-back.  Per
+    node and head: its 3 d conv inputs, beta and g in, o out, k, u, lg banked and the 3 d conv
+    inputs banked (fp32).  The layer's conv weights once.  No q, k, v or conv output in HBM."""
+    tile = 4 * d * d
+    ch = 3 * d
+    per_node = ch * in_bytes + 2 * in_bytes + 4 * d + (8 * d + 4) + 4 * ch
+    total = 0
+    S = int(view["n_seqs"])
+    for b in range(S):
+        L = int(pending[b])
+        n_b = int(view["seq_offsets"][b + 1] - view["seq_offsets"][b])
+        fold = tile + L * (8 * d + 4) + 4 * ch * min(L, 3) + 12 * ch if L > 0 else 0
+        total += H * (tile + 12 * ch + fold + n_b * per_node)
+    return (total + H * ch * 4 * in_bytes) * n_layers
 
 
 def conv_bytes(view, pending, C, in_bytes, n_layers=1):
@@ -202,10 +230,11 @@ def recorded_traffic(kernel):
 
 
 def _oracle_pair(job):
-    config, seq, layer = job
+    config, seq, layer, fused = job
     from gated_deltanet_tree_amd import synth, workload
     from oracle import conv as oconv
     from oracle import gdn as ogdn
+    from oracle import prologue
     c = synth.CONFIGS[config]
     tree = synth.config_tree(config, seq)
     n = len(tree)
@@ -216,21 +245,27 @@ def _oracle_pair(job):
     S0 = synth.initial_state(config, layer, seq, c["H"], c["d"]).astype(np.float64)
     X0 = synth.initial_conv_state(config, layer, seq, c["Cch"], 4).astype(np.float64)
     path = synth.config_path(config, 0, seq, tree)
-    ogdn.verify(tree, S0, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"],
-                keep_states=False)
-    oconv.tree_conv(tree, X0, x, W)
-    ogdn.replay(S0, inp["k"], inp["v"], inp["beta"], inp["gate"], path)
+    if fused:  # q, k, v from the conv (SiLU, unit length), then verify and commit by replay
+        _, q, k, v = prologue.conv_verify(tree, S0, X0, x, W, inp["beta"], inp["gate"],
+                                          c["H"], c["d"])
+        ogdn.replay(S0, k, v, inp["beta"], inp["gate"], path)
+    else:
+        ogdn.verify(tree, S0, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"],
+                    keep_states=False)
+        oconv.tree_conv(tree, X0, x, W)
+        ogdn.replay(S0, inp["k"], inp["v"], inp["beta"], inp["gate"], path)
     oconv.commit_window(X0, x, path)
     return n
 
 
-def cpu_baseline(config, n_pairs, workers):
+def cpu_baseline(config, n_pairs, workers, fused):
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
     from gated_deltanet_tree_amd import synth
     c = synth.CONFIGS[config]
     rng = np.random.default_rng(1234)
-    jobs = [(config, int(rng.integers(c["Bs"])), int(rng.integers(c["Ly"]))) for _ in range(n_pairs)]
+    jobs = [(config, int(rng.integers(c["Bs"])), int(rng.integers(c["Ly"])), fused)
+            for _ in range(n_pairs)]
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
     ctx = mp.get_context("spawn")
@@ -239,10 +274,12 @@ def cpu_baseline(config, n_pairs, workers):
         t0 = time.perf_counter()
         nodes = sum(ex.map(_oracle_pair, jobs))
         dt = time.perf_counter() - t0
+    work = ("tree conv, SiLU and unit q/k, then fp64 verify of every node by root-path replay"
+            if fused else "fp64 verify of every node by root-path replay, tree conv")
     return dict(value=nodes / dt, unit="node-layers/s", cores=workers, kind="oracle",
-                sample=f"{n_pairs} seeded (sequence, layer) pairs of the workload: fp64 verify of "
-                       f"every node by root-path replay, tree conv, and commit by replay; "
-                       f"{nodes} node-layers in {dt:.1f} s over {workers} processes")
+                sample=f"{n_pairs} seeded (sequence, layer) pairs of the workload: {work}, and "
+                       f"commit by replay; {nodes} node-layers in {dt:.1f} s over {workers} "
+                       f"processes")
 
 
 # ----------------------------------------------------------------------------------------
@@ -254,9 +291,11 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layers-per-call", type=int, default=1)
-    ap.add_argument("--verify", choices=["ut", "chain"], default="ut",
-                    help="headline path (both are timed): ut = tree-masked form on the matrix "
-                         "cores; chain = heavy-light chains in dependency waves")
+    ap.add_argument("--verify", choices=["fused", "ut", "chain"], default="ut",
+                    help="headline path (all are timed): fused = conv -> SiLU -> unit q/k -> "
+                         "tree-masked verify in one launch per layer; ut = tree conv, then the "
+                         "tree-masked verify of given q/k/v on the matrix cores; chain = tree "
+                         "conv, then heavy-light chains in dependency waves")
     ap.add_argument("--only", action="store_true", help="time the headline path only")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill line")
     ap.add_argument("--cpu-pairs", type=int, default=640)
@@ -280,7 +319,7 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         workers = args.cpu_workers or min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(args.config, args.cpu_pairs, workers)
+        cpu = cpu_baseline(args.config, args.cpu_pairs, workers, args.verify == "fused")
 
     import torch
     from gated_deltanet_tree_amd import binding
@@ -317,6 +356,10 @@ def main(argv=None):
                                  workspace, layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
     cargs = [binding.conv_args(image0, lay, inp.x, weights, y, layer_begin=l, n_layers=lpc)
              for l in range(0, Ly, lpc)]
+    fvargs = [binding.verify_args(image0, lay, None, None, None, inp.beta, inp.gate, out, None,
+                                  layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
+    fcargs = [binding.conv_args(image0, lay, inp.x, weights, None, layer_begin=l, n_layers=lpc)
+              for l in range(0, Ly, lpc)]
     va_all = binding.verify_args(image0, lay, None, None, None, None, None, None, None, 0, Ly)
     ca_all = binding.conv_args(image0, lay, None, None, None, 0, Ly)
     stream = torch.cuda.current_stream()
@@ -331,7 +374,7 @@ def main(argv=None):
                    commit_bytes=0)
         # Verify launches are timed by events recorded by the dispatches themselves (no extra
         # packets on the stream); one pair per (step, layer call, launch).
-        launches = 1 if verify == "ut" else n_waves
+        launches = n_waves if verify == "chain" else 1
         ev = [[[(binding.HipEvent(), binding.HipEvent()) for _ in range(launches)]
                for _ in range(len(vargs))] for _ in range(args.steps)]
 
@@ -340,6 +383,14 @@ def main(argv=None):
             dev_image = upload(image)
             pending = [int(L) for L in lay.pending_host]
             for li in range(len(vargs)):
+                if verify == "fused":  # conv, SiLU, unit q/k and verify in one launch
+                    if timed_index is None:
+                        binding.tree_conv_verify(fvargs[li], fcargs[li], image, dev_image)
+                    else:
+                        e0, e1 = ev[timed_index][li][0]
+                        binding.tree_conv_verify_timed(fvargs[li], fcargs[li], image, dev_image,
+                                                       e0, e1)
+                    continue
                 binding.tree_conv(cargs[li], image, dev_image)
                 if verify == "ut":
                     if timed_index is None:
@@ -359,14 +410,17 @@ def main(argv=None):
             binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs))
             if timed_index is not None:  # byte accounting after the launches, off the GPU's path
                 calls = len(vargs)
-                if verify == "ut":
+                if verify == "fused":
+                    acc["verify_bytes"] += calls * fused_bytes(view, pending, H, d, in_bytes, lpc)
+                elif verify == "ut":
                     acc["verify_bytes"] += calls * ut_bytes(view, pending, H, d, in_bytes, lpc)
                 else:
                     acc["verify_bytes"] += calls * sum(
                         verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc)
                         for w in range(n_waves))
                 acc["verify_launches"] += calls * launches
-                acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
+                if verify != "fused":  # the fused launch already counts its conv traffic
+                    acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
                 acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly)
 
         for s in range(args.warmup):
@@ -422,7 +476,8 @@ def main(argv=None):
               "nodes_per_batch": int(sum(len(t["parent"]) for t in built)),
               "note": "host call through the binding (marshalling included), one thread"}
 
-    order = [args.verify] + ([] if args.only else [p for p in ("ut", "chain") if p != args.verify])
+    order = [args.verify] + ([] if args.only else
+                             [p for p in ("fused", "ut", "chain") if p != args.verify])
     runs = {p: run_path(p) for p in order}
     head = runs[args.verify]
     result = {
@@ -441,7 +496,9 @@ def main(argv=None):
         "config": {
             "workload": f"{cfg['name']}: {S} sequences x {Ly} GDN layers x {H} heads x d{d}, "
                         f"{T // S if S else 0}-node trees (top-{cfg['K']}, depth<={cfg['D']}), "
-                        f"bf16 q/k/v/beta/g, fp32 state, conv width 4 over {C} channels",
+                        + ("bf16 conv inputs/beta/g, q/k/v from the conv (SiLU, unit q/k), "
+                           if args.verify == "fused" else "bf16 q/k/v/beta/g, ")
+                        + f"fp32 state, conv width 4 over {C} channels",
             "sequences": S, "layers": Ly, "heads": H, "head_dim": d, "tree_nodes": T,
             "chains": int(view["n_chains"]), "waves": int(view["n_waves"]),
             "boundary_nodes": int(view["n_boundaries"]), "layers_per_call": lpc,

@@ -23,16 +23,18 @@
 //
 // One workgroup of 4 waves per (layer, sequence, head):
 //   0. direct loads of the head's q, k and v conv-input rows of every node, beta, g, parents,
-//      depths and the tree's plan; each of the head's 3 x 128 channels folds its committed conv
-//      window with the pending conv inputs, writes it back once and keeps it in LDS;
-//   1. the state tile loads are issued; prologue: per node, conv of the q and k channels along
-//      the parent chain, SiLU, unit length, fp32 rows to LDS, raw inputs and keys banked; gate
-//      products along every record block;
-//   2. the pending fold rows start loading; pair products [k; q] K^T on the matrix cores;
-//   3. wave 0 forms Y and Z level by level while every wave folds the pending rows into its
-//      part of the tile; the committed state is written back once;
-//   4. [k; q] S0^T on the matrix cores; the epilogue evaluates the v channels' conv and SiLU and
-//      writes w_n and G_n S0 q_n;
+//      depths and the tree's plan; the committed conv windows and the q/k conv weights to
+//      registers;
+//   1. the state tile loads are issued (they land behind phases 1-3); each of the head's
+//      3 x 128 channels folds its conv window, keeps it in LDS and writes it back; per record:
+//      ancestor offsets, distances and gate products;
+//   2. prologue: per node, conv of the q and k channels along the parent chain, SiLU, unit
+//      length; fp32 rows to LDS; raw conv inputs and keys banked;
+//   3. the pending fold rows start loading into the consumed q and k conv-input planes; pair
+//      products [k; q] K^T on the matrix cores;
+//   4. the pending rows are folded into the tile and the committed state is written back once;
+//      wave 0 forms Y and Z level by level; [k; q] S0^T on the matrix cores; the epilogue
+//      evaluates the v channels (conv and SiLU) and writes w_n and G_n S0 q_n;
 //   5. u and o of every (node, row); u banked, o stored.
 // Matrix-core layout as in the bf16 UT kernel (v_mfma_f32_16x16x32_bf16): wave w owns state rows
 // [32w, 32w+32), lane l holds rows 32w + 16nt + (l % 16) and columns 16mt + 4(l/16) + e.  q and k
@@ -60,16 +62,19 @@ struct ConvVerifyParams {
 };
 
 // LDS regions for trees of at most n nodes, nrec records and nlv level entries, with nfc pending
-// rows folded per LDS chunk.  Region 1 holds the bf16 conv-input planes [v | q | k]; once the
-// prologue has consumed q and k, their part takes the fold rows, then G_n S0 q_n.  The v plane
-// lives until the S0 epilogue.  KQ holds the fp32 k and q rows (k_n at row 2n, q_n at 2n + 1);
-// W takes its place after the S0 products when n <= 32 (all M tiles fit one pass).
+// rows folded per chunk.
+//   X:  the bf16 conv-input planes [v | q | k] (n rows of 256 bytes each); once the q and k rows
+//       are consumed, the pending fold rows (k | u | lg) take their place; the v plane lives
+//       until the S0 epilogue.
+//   KQ: the fp32 k and q rows (k_n at row 2n, q_n at 2n + 1, stride KS); after the S0 products,
+//       W (rows 0 .. n-1) and G_n S0 q_n (rows n .. 2n-1) when n <= 32 (all M tiles in one
+//       pass), otherwise W and GR get their own regions.
 struct CvLayout {
     static constexpr int D = kCvD;
     static constexpr int XROW = D * 2;      // bytes of one bf16 conv-input row of one block
     static constexpr int KS = D + 4;        // fp32 row stride (floats): 16 rows hit distinct banks
     static constexpr int CPR = D * 4 / 16;  // 16-byte chunks per fp32 fold row
-    size_t xv, xq, fold_k, fold_u, fold_lg, gr, kq, wu, bg, pd, plan, tabs, x0s, total;
+    size_t xv, xq, kq, fold_k, fold_u, fold_lg, wu, gr, bg, pd, plan, tabs, x0s, total;
     size_t n64, lv64, rec64;
     bool alias_w;
 
@@ -79,16 +84,22 @@ struct CvLayout {
     }
     // direct-load footprint of the three conv-input planes
     __host__ __device__ static size_t xin_bytes(int n) { return round_up(size_t(48) * n, 64) * 16; }
-    __host__ __device__ static size_t gr_bytes(int n) { return size_t(n) * KS * 4; }
-    // Pending rows per fold chunk that fit in region 1 as sized for the planes and GR.
+    __host__ __device__ static size_t rows_bytes(int rows) { return size_t(rows) * KS * 4; }
+    // room after the v plane: the q and k planes (with the direct-load padding), at least
+    // min(nf, 4) fold rows
+    __host__ __device__ static size_t fold_room(int n, int nf) {
+        const size_t a = xin_bytes(n) - size_t(n) * XROW, b = fold_bytes(nf < 4 ? nf : 4);
+        return a > b ? a : b;
+    }
+    // Pending rows per fold chunk: as many as the room holds.
     static int fold_rows(int n, int nf) {
-        const size_t room = std::max(xin_bytes(n) - size_t(n) * XROW, gr_bytes(n));
+        const size_t room = fold_room(n, nf);
         int r = 1;
         while (r < nf && fold_bytes(r + 1) <= room) ++r;
         return r;
     }
 
-    __host__ __device__ CvLayout(int n, int nrec, int nlv, int nfc) {
+    __host__ __device__ CvLayout(int n, int nrec, int nlv, int nf, int nfc) {
         n64 = round_up(size_t(n), 64);
         lv64 = round_up(size_t(nlv), 64);
         rec64 = round_up(size_t(nrec), 64);
@@ -97,38 +108,54 @@ struct CvLayout {
         fold_k = xq;
         fold_u = xq + fold_chunks(nfc) * 16;
         fold_lg = fold_u + fold_chunks(nfc) * 16;
-        gr = xq;
-        size_t r1 = xin_bytes(n);
-        if (xq + fold_bytes(nfc) > r1) r1 = xq + fold_bytes(nfc);
-        if (xq + gr_bytes(n) > r1) r1 = xq + gr_bytes(n);
-        kq = round_up(r1, 16);
-        const size_t kq_bytes = size_t(2) * n * KS * 4;
+        kq = round_up(xq + fold_room(n, nf), 16);
         alias_w = n <= 32;
-        wu = alias_w ? kq : kq + kq_bytes;
-        size_t p = kq + kq_bytes + (alias_w ? 0 : gr_bytes(n));
+        size_t p = kq + rows_bytes(2 * n);
+        if (alias_w) {
+            wu = kq;
+            gr = kq + rows_bytes(n);
+        } else {
+            wu = p;
+            gr = p + rows_bytes(n);
+            p += 2 * rows_bytes(n);
+        }
         bg = p;                   // beta | gate [n64] u32 slots
         p += 2 * n64 * 4;
         pd = p;                   // parent | depth [n64] int (global parent ids)
         p += 2 * n64 * 4;
         plan = p;                 // poff [n64] | lvnode [n64] | lvn [lv64] | recM [rec64]
         p += (2 * n64 + lv64 + rec64) * 4;
-        tabs = p;                 // gam | kqd [n] | recE=recY | recC | recQ | recZ | recP [nrec]
-        p += (size_t(2) * n + size_t(5) * nrec) * 4;
+        tabs = p;                 // gam | kqd [n] | recE=recY | recC | recQ | recZ [nrec] (f32),
+                                  // recP | recT [nrec], anc [n][4] (int)
+        p += (size_t(2) * n + size_t(6) * nrec + size_t(4) * n) * 4;
         x0s = round_up(p, 16);    // folded conv window [3 taps][3 D channels]
         total = x0s + size_t(3) * 3 * D * 4;
     }
 };
 
-__device__ __forceinline__ float silu(float y) { return y / (1.f + expf(-y)); }
+// SiLU with the hardware exp2 and reciprocal (each within about an ulp).
+__device__ __forceinline__ float silu(float y) {
+    return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
+}
 
 // conv of one channel at a node: taps up the parent chain, committed-window entries above the
-// root (w0 oldest); weight tap 3 multiplies the node's own input.
+// root (c0 oldest); weight tap 3 multiplies the node's own input.
 __device__ __forceinline__ float conv4(const float wt[4], float x0, float x1, float x2, float x3,
                                        int dt, float c0, float c1, float c2) {
     const float a1 = dt >= 1 ? x1 : c2;
     const float a2 = dt >= 2 ? x2 : (dt == 1 ? c2 : c1);
     const float a3 = dt >= 3 ? x3 : (dt == 2 ? c2 : (dt == 1 ? c1 : c0));
     return fmaf(wt[3], x0, fmaf(wt[2], a1, fmaf(wt[1], a2, wt[0] * a3)));
+}
+
+// Sum over the 64 lanes with DPP only: octets, the row of 16, then row broadcasts 15 and 31
+// (rows 1 and 3 add the row below, rows 2 and 3 add lanes 0-31); lane 63 holds the total.
+__device__ __forceinline__ float wave_total(float x) {
+    x = octet_sum(x);
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // acc += A B for operands given as three-term splits: the six products above 2^-24 relative,
@@ -145,17 +172,52 @@ __device__ __forceinline__ floatx4 mfma6(const bf16x8 &ah, const bf16x8 &am, con
     return acc;
 }
 
+// Rows n of Y = T^-1 and Z = C' T^-1 from n's own root path: Y T = I and Z T = C' restricted to
+// the ancestor relation give, for the ancestor a_t at distance t + 1 (record q1 + t),
+//   y_t = -(T[n][a_t] + sum_{s<t} y_s T[a_s][a_t])
+//   z_t = C'[n][a_t] - ((q_n.k_n) T[n][a_t] + sum_{s<t} z_s T[a_s][a_t])
+// where T[a_s][a_t] is record rp_s + t - s of a_s's block (rp_s = its start).  Every read is
+// independent of the results, so a lane needs two rounds of loads and then only FMAs.  YD bounds
+// the tree's depth; terms past the node's depth d are computed on clamped indices and dropped.
+template <int YD>
+__device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *recC,
+                                        const float *recQ, const int *recP, float *recY,
+                                        float *recZ) {
+    int rp[YD];
+#pragma unroll
+    for (int s = 0; s < YD; ++s) rp[s] = recP[q1 + min(s, d - 1)];
+    float y[YD], z[YD];
+#pragma unroll
+    for (int t = 0; t < YD; ++t) {
+        const int tc = min(t, d - 1);
+        const float tn = recC[q1 + tc];
+        float ya = tn, za = kq * tn;
+#pragma unroll
+        for (int s = 0; s < t; ++s) {
+            const float ts = recC[rp[s] + (tc - min(s, tc))];
+            ya = fmaf(y[s], ts, ya);
+            za = fmaf(z[s], ts, za);
+        }
+        y[t] = -ya;
+        z[t] = recQ[q1 + tc] - za;
+        if (t < d) {
+            recY[q1 + t] = y[t];
+            recZ[q1 + t] = z[t];
+        }
+    }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
 void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, int n_max,
-                        int nrec_max, int nlv_max, int nfc) {
+                        int nrec_max, int nlv_max, int nf, int nfc) {
     constexpr int D = kCvD, THREADS = 256, NW = 4, JC = 4;
     using LY = CvLayout;
     const VerifyParams &P = CP.V;
     extern __shared__ __align__(16) float dyn[];
     char *lds = reinterpret_cast<char *>(dyn);
-    const LY lay(n_max, nrec_max, nlv_max, nfc);
+    const LY lay(n_max, nrec_max, nlv_max, nf, nfc);
     const size_t n64 = lay.n64;
     const uint32_t *Bl = reinterpret_cast<const uint32_t *>(lds + lay.bg);
     const uint32_t *Gt = Bl + n64;
@@ -176,10 +238,12 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     float *gam = reinterpret_cast<float *>(lds + lay.tabs);
     float *kqd = gam + n_max;
     // recE = E(n, that node), later Y[n][that node]; recC = T, recQ = C', recZ = Z on the
-    // ancestor records; recP = poff of the record's node.
+    // ancestor records; recP = poff of the record's node, recT = its distance - 1 (-1: itself)
     float *recE = kqd + n_max, *recC = recE + nrec_max, *recQ = recC + nrec_max;
     float *recZ = recQ + nrec_max;
     int *recP = reinterpret_cast<int *>(recZ + nrec_max);
+    int *recT = recP + nrec_max;
+    int4 *anc = reinterpret_cast<int4 *>(recT + nrec_max);  // 3 nearest ancestors (local ids)
     float *recY = recE;
     float *X0s = reinterpret_cast<float *>(lds + lay.x0s);
 
@@ -201,12 +265,25 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     const int C = CP.C, HD = P.H * D;
     // node 0's conv inputs, q block of head h; block b adds b H d
     const bf16_t *xrow0 = CP.x + (int64_t(layer) * P.T + seq_off) * C + h * D;
-    // q and k weights of this lane's two channels 2 lane, 2 lane + 1 (8 bf16 each, 16 bytes)
-    const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
-    const uint4 wq = *reinterpret_cast<const uint4 *>(wq_src);
-    const uint4 wk = *reinterpret_cast<const uint4 *>(wq_src + int64_t(HD) * 4);
 
-    // ---- 0. direct loads; conv-window fold ------------------------------------------------
+    const int fk_chunks = int(LY::fold_chunks(nfc));
+    auto issue_fold = [&](int f0, int cnt) {  // pending rows f0 .. f0 + cnt - 1 into LDS
+        const float *pk = P.bank_k[role] + (row0_bank + f0) * D;
+        const float *pu = P.bank_u[role] + (row0_bank + f0) * D;
+        const int rows_chunks = cnt * LY::CPR;
+        for (int base = w * 64; base < 2 * fk_chunks; base += NW * 64) {
+            const int which = base / fk_chunks, b2 = base % fk_chunks;
+            if (b2 >= rows_chunks) continue;
+            const int c = min(b2 + lane, rows_chunks - 1);
+            const float *src = (which == 0 ? pk : pu) + c * 4;
+            to_lds<16>(src, lds + lay.fold_k + size_t(base) * 16);
+        }
+        const float *plg = P.bank_lg[role] + row0_bank + f0;
+        for (int base = w * 64; base < cnt; base += NW * 64)
+            to_lds<4>(plg + min(base + lane, cnt - 1), lds + lay.fold_lg + size_t(base) * 4);
+    };
+
+    // ---- 0. loads ------------------------------------------------------------------------
     {
         const int total = 48 * n;  // planes v | q | k, 16 chunks per node row
         for (int base = w * 64; base < total; base += NW * 64) {
@@ -243,38 +320,30 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 for (int base = w * 64; base < counts[a]; base += NW * 64)
                     to_lds<4>(srcs[a] + min(base + lane, counts[a] - 1), dsts[a] + base);
         }
-        // Fold: only the last three pending inputs survive; one thread owns each channel, reads
-        // its window and writes it back, so no other thread sees a half-updated window.
-        const float *pend = CP.bank_x[role] + ls * P.max_nodes * C;
-        for (int cc = tid; cc < 3 * D; cc += THREADS) {
-            const int64_t ch = int64_t(cc >> 7) * HD + h * D + (cc & (D - 1));
-            float *cs = CP.cstate + (ls * C + ch) * 3;
-            float w0 = cs[0], w1 = cs[1], w2 = cs[2];
-            if (L > 0) {
-                const float *pb = pend + ch;
-                const float r2 = pb[int64_t(L - 1) * C];
-                const float r1 = L >= 2 ? pb[int64_t(L - 2) * C] : 0.f;
-                const float r0 = L >= 3 ? pb[int64_t(L - 3) * C] : 0.f;
-                if (L >= 3) {
-                    w0 = r0; w1 = r1; w2 = r2;
-                } else if (L == 2) {
-                    w0 = w2; w1 = r1; w2 = r2;
-                } else {
-                    w0 = w1; w1 = w2; w2 = r2;
-                }
-                cs[0] = w0;
-                cs[1] = w1;
-                cs[2] = w2;
-            }
-            X0s[cc] = w0;
-            X0s[3 * D + cc] = w1;
-            X0s[6 * D + cc] = w2;
+    }
+    // committed conv windows (thread cc owns channels cc and cc + 256 of the head's 3 x 128)
+    // with their last pending inputs, and the q/k weights of this lane's channels
+    float win[2][3], pend[2][3];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int cc = tid + 256 * j;
+        const int ccl = cc < 3 * D ? cc : tid;  // threads with one channel re-read their first
+        const int64_t ch = int64_t(ccl >> 7) * HD + h * D + (ccl & (D - 1));
+        const float *cs = CP.cstate + (ls * C + ch) * 3;
+        const float *pb = CP.bank_x[role] + ls * P.max_nodes * C + ch;
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+            win[j][e] = cs[e];
+            // pending input L - 3 + e, when it exists
+            pend[j][e] = L >= 3 - e ? pb[int64_t(L - 3 + e) * C] : 0.f;
         }
     }
+    const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
+    const uint4 wq = *reinterpret_cast<const uint4 *>(wq_src);
+    const uint4 wk = *reinterpret_cast<const uint4 *>(wq_src + int64_t(HD) * 4);
     __syncthreads();  // waits for every direct load (the barrier's fence covers them)
 
-    // The state tile is requested now; its latency hides behind the prologue and the pair
-    // products, which need only LDS.
+    // ---- 1. state tile requested; conv-window fold; record tables --------------------------
     float s[2][8][4];  // rows 32w + 16nt + lr, columns 16mt + 4lg + e
     {
         const float *tile = committed + (32 * w + lr) * D + 4 * lg;
@@ -289,8 +358,64 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 s[nt][mt][3] = x.w;
             }
     }
+    // conv window: only the last three pending inputs survive
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int cc = tid + 256 * j;
+        if (cc >= 3 * D) break;
+        float w0 = win[j][0], w1 = win[j][1], w2 = win[j][2];
+        if (L >= 3) {
+            w0 = pend[j][0]; w1 = pend[j][1]; w2 = pend[j][2];
+        } else if (L == 2) {
+            w0 = w2; w1 = pend[j][1]; w2 = pend[j][2];
+        } else if (L == 1) {
+            w0 = w1; w1 = w2; w2 = pend[j][2];
+        }
+        X0s[cc] = w0;
+        X0s[3 * D + cc] = w1;
+        X0s[6 * D + cc] = w2;
+        if (L > 0) {
+            float *cs = CP.cstate + (ls * C + int64_t(cc >> 7) * HD + h * D + (cc & (D - 1))) * 3;
+            cs[0] = w0;
+            cs[1] = w1;
+            cs[2] = w2;
+        }
+    }
+    // Per node t: along its record block, in groups of four records whose reads are independent,
+    //   E(t, anc_0) = g_t, E(t, anc_{s+1}) = E(t, anc_s) g_{anc_s}, G_t = E(t, root) g_root;
+    // recP = the block start of each ancestor, recT its distance - 1; anc = 3 nearest ancestors.
+    for (int t = tid; t < n; t += THREADS) {
+        const int o = poff[t], dt = dep[t];
+        float E = slot_f32<bf16_t>(Gt[t]);
+        recT[o] = -1;
+        for (int s0 = 0; s0 < dt; s0 += 4) {
+            int a[4], pa[4];
+            float ga[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = s0 + j < dt ? recM[o + 1 + s0 + j] : t;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pa[j] = poff[a[j]];
+                ga[j] = slot_f32<bf16_t>(Gt[a[j]]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (s0 + j >= dt) break;
+                const int q = o + 1 + s0 + j;
+                recE[q] = E;
+                recP[q] = pa[j];
+                recT[q] = s0 + j;
+                E *= ga[j];
+            }
+            if (s0 == 0) anc[t] = make_int4(a[0], a[1], a[2], 0);
+        }
+        if (dt == 0) anc[t] = make_int4(t, t, t, 0);
+        gam[t] = E;
+        P.bank_lg[role ^ 1][row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
+    }
+    __syncthreads();  // windows, records and ancestors in LDS
 
-    // ---- 1. prologue: q and k from the conv; raw inputs and keys banked -------------------
+    // ---- 2. prologue: q and k from the conv; raw inputs and keys banked -------------------
     {
         const char *XV = lds + lay.xv;
         const char *XQ = XV + size_t(n) * LY::XROW, *XK = XQ + size_t(n) * LY::XROW;
@@ -314,10 +439,8 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
         float *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D + 2 * lane;
         for (int nd = w; nd < n; nd += NW) {
             const int dt = dep[nd];
-            const int p1 = dt >= 1 ? par[nd] - seq_off : nd;
-            const int p2 = dt >= 2 ? par[p1] - seq_off : p1;
-            const int p3 = dt >= 3 ? par[p2] - seq_off : p2;
-            const int rows[4] = {nd, p1, p2, p3};
+            const int4 an = anc[nd];
+            const int rows[4] = {nd, an.x, an.y, an.z};
             float y[2][2], ss[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -347,9 +470,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 *reinterpret_cast<float2 *>(bx + int64_t(nd) * C + 2 * HD) =
                     make_float2(bf16_lo(xv), bf16_hi(xv));
             }
-            const float sq = wave_sum(ss[0]), sk = wave_sum(ss[1]);
-            const float iq = 1.f / fmaxf(sqrtf(sq), kNormFloor);
-            const float ik = 1.f / fmaxf(sqrtf(sk), kNormFloor);
+            // 1 / max(|y|, floor) as rsqrt(max(|y|^2, floor^2))
+            const float iq = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss[0]), kNormFloor * kNormFloor));
+            const float ik = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss[1]), kNormFloor * kNormFloor));
             const float2 kv = make_float2(y[1][0] * ik, y[1][1] * ik);
             const float2 qv = make_float2(y[0][0] * iq, y[0][1] * iq);
             *reinterpret_cast<float2 *>(KQ + size_t(2 * nd) * LY::KS + 2 * lane) = kv;
@@ -357,41 +480,16 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
             *reinterpret_cast<float2 *>(wk_bank + (row0_bank + nd) * D + 2 * lane) = kv;
         }
     }
-    // gate products along every record block:
-    //   E(n, anc_0) = g_n, E(n, anc_{t+1}) = E(n, anc_t) g_{anc_t}, G_n = E(n, root) g_root.
-    for (int t = tid; t < n; t += THREADS) {
-        const int o = poff[t], dt = dep[t];
-        float E = slot_f32<bf16_t>(Gt[t]);
-        for (int s2 = 0; s2 < dt; ++s2) {
-            const int a = recM[o + 1 + s2];
-            recE[o + 1 + s2] = E;
-            recP[o + 1 + s2] = poff[a];
-            E *= slot_f32<bf16_t>(Gt[a]);
-        }
-        gam[t] = E;
-        P.bank_lg[role ^ 1][row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
-    }
-    __syncthreads();  // q and k rows, gate products, record offsets
+    __syncthreads();  // k and q rows complete; the q and k conv-input planes are consumed
 
-    // ---- 2. pending fold rows (first chunk) start loading; pair products ------------------
-    const int fk_chunks = int(LY::fold_chunks(nfc));
-    auto issue_fold = [&](int f0, int cnt) {
-        const float *pk = P.bank_k[role] + (row0_bank + f0) * D;
-        const float *pu = P.bank_u[role] + (row0_bank + f0) * D;
-        const int rows_chunks = cnt * LY::CPR;
-        for (int base = w * 64; base < 2 * fk_chunks; base += NW * 64) {
-            const int which = base / fk_chunks, b2 = base % fk_chunks;
-            if (b2 >= rows_chunks) continue;
-            const int c = min(b2 + lane, rows_chunks - 1);
-            const float *src = (which == 0 ? pk : pu) + c * 4;
-            to_lds<16>(src, lds + lay.fold_k + size_t(base) * 16);
-        }
-        const float *plg = P.bank_lg[role] + row0_bank + f0;
-        for (int base = w * 64; base < cnt; base += NW * 64)
-            to_lds<4>(plg + min(base + lane, cnt - 1), lds + lay.fold_lg + size_t(base) * 4);
-    };
+    // ---- 3. pending fold rows start loading; pair coefficients on the matrix cores ---------
     if (L > 0) issue_fold(0, min(L, nfc));
-
+    // v-channel taps of this lane's state rows 32w + 16nt + lr, for the S0 epilogue
+    uint2 wvr[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+        wvr[nt] = *reinterpret_cast<const uint2 *>(CP.w + (int64_t(layer) * C + 2 * HD + h * D +
+                                                           32 * w + 16 * nt + lr) * 4);
     // M tile jt stacks k (rows 0-7) and q (rows 8-15) of nodes 8jt .. 8jt+7; N tile at holds the
     // keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: k . k_a for lg < 2 and
     // q . k_a for lg >= 2, of node 8jt + 4(lg & 1) + r, with a = 16at + lr.
@@ -429,43 +527,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 recC[q] = slot_f32<bf16_t>(Bl[nd]) * recE[q] * acc[r];
         }
     }
-    __syncthreads();  // T, C', q.k on the records; the first fold chunk has landed
+    __syncthreads();  // T, C' and q.k on the records; the first fold chunk has landed
 
-    // v-channel taps of this lane's state rows 32w + 16nt + lr, for the S0 epilogue
-    uint2 wvr[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-        wvr[nt] = *reinterpret_cast<const uint2 *>(CP.w + (int64_t(layer) * C + 2 * HD + h * D +
-                                                           32 * w + 16 * nt + lr) * 4);
-
-    // ---- 3. Y = T^-1 and Z = C' Y on the records (wave 0); fold ----------------------------
-    // Record (n, t) = ancestor a_t of n at distance t + 1, at q1 + t with q1 = poff[n] + 1:
-    //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
-    //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
-    // where Y[a_s][a_t] is record poff[a_s] + t - s.  Level by level: every term read belongs to
-    // a shallower node.  Y and Z of a node with itself are 1 and q_n.k_n and are not stored.
-    if (w == 0 && n > 0) {
-        const int dmax = plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2;
-        for (int lv = 1; lv <= dmax; ++lv) {
-            const int j0 = lvn[lv], items = (lvn[lv + 1] - j0) * lv;
-            for (int it = lane; it < items; it += 64) {
-                const int j = j0 + it / lv, t = it % lv;
-                const int nd = lvnode[j];
-                const int q1 = poff[nd] + 1;
-                float ys = recC[q1 + t], zs = recQ[q1 + t];
-                for (int s2 = 0; s2 < t; ++s2) {
-                    const float yv = recY[recP[q1 + s2] + (t - s2)];
-                    ys = fmaf(recC[q1 + s2], yv, ys);
-                    zs = fmaf(recQ[q1 + s2], yv, zs);
-                }
-                recY[q1 + t] = -ys;
-                recZ[q1 + t] = fmaf(kqd[nd], -ys, zs);
-            }
-            wave_order();
-        }
-    }
-
-    // deferred commit: fold the pending rows, write the committed state once
+    // ---- 4. deferred commit: fold the pending rows, write the committed state once --------
     for (int f0 = 0; f0 < L; f0 += nfc) {
         const int cnt = min(L - f0, nfc);
         if (f0 > 0) {  // later chunks (more pending rows than one chunk holds)
@@ -497,14 +561,72 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 *reinterpret_cast<float4 *>(tile + 16 * nt * D + 16 * mt) =
                     make_float4(s[nt][mt][0], s[nt][mt][1], s[nt][mt][2], s[nt][mt][3]);
     }
-    __syncthreads();  // fold rows are dead (their LDS becomes GR); Y and Z are complete
 
-    // ---- 4. p_n = S0 k_n, r_n = S0 q_n on the matrix cores; w_n and G_n r_n to LDS -------
+    // Y = T^-1 and Z = C' Y on the records.  Trees up to depth 12: one lane per node forms its
+    // rows from its own root path (yz_rows).  Deeper trees: wave 0 goes level by level with
+    //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
+    //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
+    // (record (n, t) = ancestor a_t at distance t + 1, at q1 + t with q1 = poff[n] + 1; level
+    // lv's blocks of lv + 1 records are contiguous from record r_lv).  Y and Z of a node with
+    // itself are 1 and q_n.k_n and are not stored.
+    {
+        const int lv0 = n > 0 ? plan[P.off_ut_lv_base + seq] : 0;
+        const int dmax = n > 0 ? plan[P.off_ut_lv_base + seq + 1] - lv0 - 2 : 0;
+        if (dmax <= 12) {
+            for (int nd = tid; nd < n; nd += THREADS) {
+                const int q1 = poff[nd] + 1, d = dep[nd];
+                if (d == 0) continue;
+                const float kq = kqd[nd];
+                if (dmax <= 4)
+                    yz_rows<4>(q1, d, kq, recC, recQ, recP, recY, recZ);
+                else if (dmax <= 8)
+                    yz_rows<8>(q1, d, kq, recC, recQ, recP, recY, recZ);
+                else
+                    yz_rows<12>(q1, d, kq, recC, recQ, recP, recY, recZ);
+            }
+        } else if (w == 0) {
+            int r_lv = lvn[1] - lvn[0];  // level 0: one record per root
+            for (int lv = 1; lv <= dmax; ++lv) {
+                const int nrec_lv = (lvn[lv + 1] - lvn[lv]) * (lv + 1);
+                for (int it = lane; it < nrec_lv; it += 64) {
+                    const int q = r_lv + it, t = recT[q];
+                    if (t < 0) continue;
+                    const int q1 = q - t;
+                    float ys = recC[q], zs = recQ[q];
+                    for (int s0 = 0; s0 < t; s0 += 4) {  // four terms with independent reads
+                        int sp[4];
+                        float cc[4], cq[4], yv[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int s2 = min(s0 + j, t - 1);
+                            sp[j] = recP[q1 + s2] + (t - s2);
+                            cc[j] = recC[q1 + s2];
+                            cq[j] = recQ[q1 + s2];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) yv[j] = recY[sp[j]];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            if (s0 + j >= t) break;
+                            ys = fmaf(cc[j], yv[j], ys);
+                            zs = fmaf(cq[j], yv[j], zs);
+                        }
+                    }
+                    recY[q] = -ys;
+                    recZ[q] = fmaf(kqd[recM[q1 - 1]], -ys, zs);
+                }
+                r_lv += nrec_lv;
+                wave_order();
+            }
+        }
+    }
+
+    // p_n = S0 k_n, r_n = S0 q_n on the matrix cores; then w_n and G_n r_n to LDS.
     {
         const char *XV = lds + lay.xv;
         for (int jt0 = 0; jt0 < JT; jt0 += JC) {
-            // One half of the wave's state rows at a time (nt outer): only that half's split
-            // is live, and the first half's tile registers die before the second half runs.
+            // One half of the wave's state rows at a time (nt outer): only that half's split is
+            // live, and the first half's tile registers die before the second half runs.
             floatx4 acc[JC][2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
@@ -531,9 +653,11 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                     }
                 }
             }
-            if (lay.alias_w) __syncthreads();  // every wave is done with KQ before W replaces it
-            // Lane (lr, lg) holds rows 4lg + r of each M tile: p of node 8jt + 4lg + r for lg < 2,
-            // r of node 8jt + 4(lg - 2) + r for lg >= 2, at state row 32w + 16nt + lr.
+            // When W and GR take KQ's place, every wave must be done reading KQ; Y and Z are
+            // complete past this point too.
+            if (jt0 == 0) __syncthreads();
+            // Lane (lr, lg) holds rows 4lg + r of each M tile: p of node 8jt + 4lg + r for
+            // lg < 2, r of node 8jt + 4(lg - 2) + r for lg >= 2, at state row 32w + 16nt + lr.
 #pragma unroll
             for (int jc = 0; jc < JC; ++jc) {
                 const int jt = jt0 + jc;
@@ -545,9 +669,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                     const float G = gam[nd];
                     if (lg < 2) {
                         const int dt = dep[nd];
-                        const int p1 = dt >= 1 ? par[nd] - seq_off : nd;
-                        const int p2 = dt >= 2 ? par[p1] - seq_off : p1;
-                        const int p3 = dt >= 3 ? par[p2] - seq_off : p2;
+                        const int4 an = anc[nd];
                         const float beta = slot_f32<bf16_t>(Bl[nd]);
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt) {
@@ -557,9 +679,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                             const float *cv = X0s + 2 * D + i;  // v channel i, taps 0..2
                             const float v = silu(conv4(
                                 wv, bf16_at(XV + size_t(nd) * LY::XROW, i),
-                                bf16_at(XV + size_t(p1) * LY::XROW, i),
-                                bf16_at(XV + size_t(p2) * LY::XROW, i),
-                                bf16_at(XV + size_t(p3) * LY::XROW, i), dt, cv[0], cv[3 * D],
+                                bf16_at(XV + size_t(an.x) * LY::XROW, i),
+                                bf16_at(XV + size_t(an.y) * LY::XROW, i),
+                                bf16_at(XV + size_t(an.z) * LY::XROW, i), dt, cv[0], cv[3 * D],
                                 cv[6 * D]));
                             Wm[nd * LY::KS + i] = beta * fmaf(-G, acc[jc][nt][r], v);
                         }
@@ -581,18 +703,53 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
         // row from the wave and lane ids (nothing carried from the kernel start)
         const int i = 64 * (w & 1) + int(__lane_id());
         const int half = w >> 1;
-        for (int nd = half; nd < n; nd += THREADS / D) {
-            const int q1 = poff[nd] + 1, dn = dep[nd];
-            const float wn = Wm[nd * LY::KS + i];
-            float u = wn, o = fmaf(kqd[nd], wn, GR[nd * LY::KS + i]);
-#pragma unroll 4
-            for (int t = 0; t < dn; ++t) {
-                const float x = Wm[recM[q1 + t] * LY::KS + i];
-                u = fmaf(recY[q1 + t], x, u);
-                o = fmaf(recZ[q1 + t], x, o);
+        // nodes half, half + 2, ... two at a time, so the reads of both are in flight together
+        for (int n0 = half; n0 < n; n0 += 2 * (THREADS / D)) {
+            const int n1 = n0 + THREADS / D;
+            const bool has1 = n1 < n;
+            const int q10 = poff[n0] + 1, d0 = dep[n0];
+            const int q11 = has1 ? poff[n1] + 1 : q10, d1 = has1 ? dep[n1] : 0;
+            const float w0 = Wm[n0 * LY::KS + i], w1 = has1 ? Wm[n1 * LY::KS + i] : 0.f;
+            float u0 = w0, o0 = fmaf(kqd[n0], w0, GR[n0 * LY::KS + i]);
+            float u1 = w1, o1 = has1 ? fmaf(kqd[n1], w1, GR[n1 * LY::KS + i]) : 0.f;
+            const int dm = max(d0, d1);
+            for (int t0 = 0; t0 < dm; t0 += 4) {  // four ancestors of each, independent reads
+                int a0[4], a1[4];
+                float y0[4], z0[4], y1[4], z1[4], x0[4], x1[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = t0 + j;
+                    const int ta = min(t, max(d0 - 1, 0)), tb = min(t, max(d1 - 1, 0));
+                    a0[j] = recM[q10 + ta];
+                    y0[j] = recY[q10 + ta];
+                    z0[j] = recZ[q10 + ta];
+                    a1[j] = recM[q11 + tb];
+                    y1[j] = recY[q11 + tb];
+                    z1[j] = recZ[q11 + tb];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x0[j] = Wm[a0[j] * LY::KS + i];
+                    x1[j] = Wm[a1[j] * LY::KS + i];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (t0 + j < d0) {
+                        u0 = fmaf(y0[j], x0[j], u0);
+                        o0 = fmaf(z0[j], x0[j], o0);
+                    }
+                    if (t0 + j < d1) {
+                        u1 = fmaf(y1[j], x1[j], u1);
+                        o1 = fmaf(z1[j], x1[j], o1);
+                    }
+                }
             }
-            wu[(row0_bank + nd) * D + i] = u;
-            out0[int64_t(nd) * P.H * D + i] = o;
+            wu[(row0_bank + n0) * D + i] = u0;
+            out0[int64_t(n0) * P.H * D + i] = o0;
+            if (has1) {
+                wu[(row0_bank + n1) * D + i] = u1;
+                out0[int64_t(n1) * P.H * D + i] = o1;
+            }
         }
     }
 }
@@ -643,8 +800,9 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
     if (P.n_blocks > kMaxBlocks)
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: too many workgroups for one launch");
     const int n_max = v.max_tree, nrec_max = v.ut_max_records, nlv_max = v.ut_max_levels;
-    const int nfc = CvLayout::fold_rows(n_max, va->max_nodes);
-    const size_t lds = CvLayout(n_max, nrec_max, nlv_max, nfc).total;
+    const int nf = va->max_nodes;
+    const int nfc = CvLayout::fold_rows(n_max, nf);
+    const size_t lds = CvLayout(n_max, nrec_max, nlv_max, nf, nfc).total;
     if (lds > kUtMaxLdsBytes)
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: trees of %d nodes with %d records need "
                     "%zu bytes of LDS (limit %zu)", n_max, nrec_max, lds, kUtMaxLdsBytes);
@@ -660,10 +818,10 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
     const dim3 grid(uint32_t(P.n_blocks));
     if (start == nullptr && stop == nullptr)
         hipLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), lds, s, CP, P.img, n_max,
-                           nrec_max, nlv_max, nfc);
+                           nrec_max, nlv_max, nf, nfc);
     else
         hipExtLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), uint32_t(lds), s, start, stop,
-                              0, CP, P.img, n_max, nrec_max, nlv_max, nfc);
+                              0, CP, P.img, n_max, nrec_max, nlv_max, nf, nfc);
     GDN_LAUNCH_CHECK("conv_verify_kernel");
     return GDN_OK;
 }
