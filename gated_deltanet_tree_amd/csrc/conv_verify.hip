@@ -172,41 +172,6 @@ __device__ __forceinline__ floatx4 mfma6(const bf16x8 &ah, const bf16x8 &am, con
     return acc;
 }
 
-// Rows n of Y = T^-1 and Z = C' T^-1 from n's own root path: Y T = I and Z T = C' restricted to
-// the ancestor relation give, for the ancestor a_t at distance t + 1 (record q1 + t),
-//   y_t = -(T[n][a_t] + sum_{s<t} y_s T[a_s][a_t])
-//   z_t = C'[n][a_t] - ((q_n.k_n) T[n][a_t] + sum_{s<t} z_s T[a_s][a_t])
-// where T[a_s][a_t] is record rp_s + t - s of a_s's block (rp_s = its start).  Every read is
-// independent of the results, so a lane needs two rounds of loads and then only FMAs.  YD bounds
-// the tree's depth; terms past the node's depth d are computed on clamped indices and dropped.
-template <int YD>
-__device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *recC,
-                                        const float *recQ, const int *recP, float *recY,
-                                        float *recZ) {
-    int rp[YD];
-#pragma unroll
-    for (int s = 0; s < YD; ++s) rp[s] = recP[q1 + min(s, d - 1)];
-    float y[YD], z[YD];
-#pragma unroll
-    for (int t = 0; t < YD; ++t) {
-        const int tc = min(t, d - 1);
-        const float tn = recC[q1 + tc];
-        float ya = tn, za = kq * tn;
-#pragma unroll
-        for (int s = 0; s < t; ++s) {
-            const float ts = recC[rp[s] + (tc - min(s, tc))];
-            ya = fmaf(y[s], ts, ya);
-            za = fmaf(z[s], ts, za);
-        }
-        y[t] = -ya;
-        z[t] = recQ[q1 + tc] - za;
-        if (t < d) {
-            recY[q1 + t] = y[t];
-            recZ[q1 + t] = z[t];
-        }
-    }
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
@@ -562,64 +527,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                     make_float4(s[nt][mt][0], s[nt][mt][1], s[nt][mt][2], s[nt][mt][3]);
     }
 
-    // Y = T^-1 and Z = C' Y on the records.  Trees up to depth 12: one lane per node forms its
-    // rows from its own root path (yz_rows).  Deeper trees: wave 0 goes level by level with
-    //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
-    //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
-    // (record (n, t) = ancestor a_t at distance t + 1, at q1 + t with q1 = poff[n] + 1; level
-    // lv's blocks of lv + 1 records are contiguous from record r_lv).  Y and Z of a node with
-    // itself are 1 and q_n.k_n and are not stored.
-    {
-        const int lv0 = n > 0 ? plan[P.off_ut_lv_base + seq] : 0;
-        const int dmax = n > 0 ? plan[P.off_ut_lv_base + seq + 1] - lv0 - 2 : 0;
-        if (dmax <= 12) {
-            for (int nd = tid; nd < n; nd += THREADS) {
-                const int q1 = poff[nd] + 1, d = dep[nd];
-                if (d == 0) continue;
-                const float kq = kqd[nd];
-                if (dmax <= 4)
-                    yz_rows<4>(q1, d, kq, recC, recQ, recP, recY, recZ);
-                else if (dmax <= 8)
-                    yz_rows<8>(q1, d, kq, recC, recQ, recP, recY, recZ);
-                else
-                    yz_rows<12>(q1, d, kq, recC, recQ, recP, recY, recZ);
-            }
-        } else if (w == 0) {
-            int r_lv = lvn[1] - lvn[0];  // level 0: one record per root
-            for (int lv = 1; lv <= dmax; ++lv) {
-                const int nrec_lv = (lvn[lv + 1] - lvn[lv]) * (lv + 1);
-                for (int it = lane; it < nrec_lv; it += 64) {
-                    const int q = r_lv + it, t = recT[q];
-                    if (t < 0) continue;
-                    const int q1 = q - t;
-                    float ys = recC[q], zs = recQ[q];
-                    for (int s0 = 0; s0 < t; s0 += 4) {  // four terms with independent reads
-                        int sp[4];
-                        float cc[4], cq[4], yv[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int s2 = min(s0 + j, t - 1);
-                            sp[j] = recP[q1 + s2] + (t - s2);
-                            cc[j] = recC[q1 + s2];
-                            cq[j] = recQ[q1 + s2];
-                        }
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) yv[j] = recY[sp[j]];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            if (s0 + j >= t) break;
-                            ys = fmaf(cc[j], yv[j], ys);
-                            zs = fmaf(cq[j], yv[j], zs);
-                        }
-                    }
-                    recY[q] = -ys;
-                    recZ[q] = fmaf(kqd[recM[q1 - 1]], -ys, zs);
-                }
-                r_lv += nrec_lv;
-                wave_order();
-            }
-        }
-    }
+    // Y = T^-1 and Z = C' Y on the records (every wave; one lane per node up to depth 12)
+    tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
+                 tid, lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ);
 
     // p_n = S0 k_n, r_n = S0 q_n on the matrix cores; then w_n and G_n r_n to LDS.
     {
@@ -697,61 +607,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
-    {
-        float *wu = P.bank_u[role ^ 1];
-        float *out0 = P.out + node_row0 * D;
-        // row from the wave and lane ids (nothing carried from the kernel start)
-        const int i = 64 * (w & 1) + int(__lane_id());
-        const int half = w >> 1;
-        // nodes half, half + 2, ... two at a time, so the reads of both are in flight together
-        for (int n0 = half; n0 < n; n0 += 2 * (THREADS / D)) {
-            const int n1 = n0 + THREADS / D;
-            const bool has1 = n1 < n;
-            const int q10 = poff[n0] + 1, d0 = dep[n0];
-            const int q11 = has1 ? poff[n1] + 1 : q10, d1 = has1 ? dep[n1] : 0;
-            const float w0 = Wm[n0 * LY::KS + i], w1 = has1 ? Wm[n1 * LY::KS + i] : 0.f;
-            float u0 = w0, o0 = fmaf(kqd[n0], w0, GR[n0 * LY::KS + i]);
-            float u1 = w1, o1 = has1 ? fmaf(kqd[n1], w1, GR[n1 * LY::KS + i]) : 0.f;
-            const int dm = max(d0, d1);
-            for (int t0 = 0; t0 < dm; t0 += 4) {  // four ancestors of each, independent reads
-                int a0[4], a1[4];
-                float y0[4], z0[4], y1[4], z1[4], x0[4], x1[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = t0 + j;
-                    const int ta = min(t, max(d0 - 1, 0)), tb = min(t, max(d1 - 1, 0));
-                    a0[j] = recM[q10 + ta];
-                    y0[j] = recY[q10 + ta];
-                    z0[j] = recZ[q10 + ta];
-                    a1[j] = recM[q11 + tb];
-                    y1[j] = recY[q11 + tb];
-                    z1[j] = recZ[q11 + tb];
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x0[j] = Wm[a0[j] * LY::KS + i];
-                    x1[j] = Wm[a1[j] * LY::KS + i];
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (t0 + j < d0) {
-                        u0 = fmaf(y0[j], x0[j], u0);
-                        o0 = fmaf(z0[j], x0[j], o0);
-                    }
-                    if (t0 + j < d1) {
-                        u1 = fmaf(y1[j], x1[j], u1);
-                        o1 = fmaf(z1[j], x1[j], o1);
-                    }
-                }
-            }
-            wu[(row0_bank + n0) * D + i] = u0;
-            out0[int64_t(n0) * P.H * D + i] = o0;
-            if (has1) {
-                wu[(row0_bank + n1) * D + i] = u1;
-                out0[int64_t(n1) * P.H * D + i] = o1;
-            }
-        }
-    }
+    tree_apply(n, 64 * (w & 1) + int(__lane_id()), w >> 1, poff, dep, recM, recY, recZ, kqd, Wm,
+               GR, LY::KS, P.bank_u[role ^ 1] + row0_bank * D, P.out + node_row0 * D,
+               int64_t(P.H) * D);
 }
 
 namespace {

@@ -1,6 +1,7 @@
 // Helpers shared by the tree-masked UT verify kernels (gfx950).
 #pragma once
 
+#include "mfma_common.h"
 #include "verify_common.h"
 
 namespace gdn {
@@ -42,6 +43,151 @@ __device__ __forceinline__ UtUnit ut_unit(const VerifyParams &P) {
     u.seq = int((logical % per) / uint32_t(P.H));
     u.h = int(logical % uint32_t(P.H));
     return u;
+}
+
+// Rows n of Y = T^-1 and Z = C' T^-1 from n's own root path: Y T = I and Z T = C' restricted to
+// the ancestor relation give, for the ancestor a_t at distance t + 1 (record q1 + t),
+//   y_t = -(T[n][a_t] + sum_{s<t} y_s T[a_s][a_t])
+//   z_t = C'[n][a_t] - ((q_n.k_n) T[n][a_t] + sum_{s<t} z_s T[a_s][a_t])
+// where T[a_s][a_t] is record rp_s + t - s of a_s's block (rp_s = its start).  Every read is
+// independent of the results, so a lane needs two rounds of loads and then only FMAs.  YD bounds
+// the tree's depth; terms past the node's depth d are computed on clamped indices and dropped.
+template <int YD>
+__device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *recC,
+                                        const float *recQ, const int *recP, float *recY,
+                                        float *recZ) {
+    int rp[YD];
+#pragma unroll
+    for (int s = 0; s < YD; ++s) rp[s] = recP[q1 + min(s, d - 1)];
+    float y[YD], z[YD];
+#pragma unroll
+    for (int t = 0; t < YD; ++t) {
+        const int tc = min(t, d - 1);
+        const float tn = recC[q1 + tc];
+        float ya = tn, za = kq * tn;
+#pragma unroll
+        for (int s = 0; s < t; ++s) {
+            const float ts = recC[rp[s] + (tc - min(s, tc))];
+            ya = fmaf(y[s], ts, ya);
+            za = fmaf(z[s], ts, za);
+        }
+        y[t] = -ya;
+        z[t] = recQ[q1 + tc] - za;
+        if (t < d) {
+            recY[q1 + t] = y[t];
+            recZ[q1 + t] = z[t];
+        }
+    }
+}
+
+// Y = T^-1 and Z = C' Y on the tree's records (record (n, t) = ancestor a_t of n at distance
+// t + 1, at q1 + t with q1 = poff[n] + 1; recP = block start of the record's node, recT = t,
+// -1 on a node's own record).  Trees up to depth 12: one lane per node (yz_rows), every wave.
+// Deeper trees: wave 0 goes level by level with
+//   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
+//   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
+// (level lv's blocks of lv + 1 records are contiguous from record r_lv; every term read belongs
+// to a shallower level).  Y and Z of a node with itself are 1 and q_n.k_n and are not stored.
+// Needs a barrier before the results are read by other waves.
+__device__ __forceinline__ void tree_inverse(int n, int dmax, int tid, int lane, int w,
+                                             const int *poff, const int *dep, const int *lvn,
+                                             const int *recM, const int *recP, const int *recT,
+                                             const float *recC, const float *recQ,
+                                             const float *kqd, float *recY, float *recZ) {
+    if (dmax <= 12) {
+        for (int nd = tid; nd < n; nd += 256) {
+            const int q1 = poff[nd] + 1, d = dep[nd];
+            if (d == 0) continue;
+            const float kq = kqd[nd];
+            if (dmax <= 4)
+                yz_rows<4>(q1, d, kq, recC, recQ, recP, recY, recZ);
+            else if (dmax <= 8)
+                yz_rows<8>(q1, d, kq, recC, recQ, recP, recY, recZ);
+            else
+                yz_rows<12>(q1, d, kq, recC, recQ, recP, recY, recZ);
+        }
+        return;
+    }
+    if (w != 0) return;
+    int r_lv = lvn[1] - lvn[0];  // level 0: one record per root
+    for (int lv = 1; lv <= dmax; ++lv) {
+        const int nrec_lv = (lvn[lv + 1] - lvn[lv]) * (lv + 1);
+        for (int it = lane; it < nrec_lv; it += 64) {
+            const int q = r_lv + it, t = recT[q];
+            if (t < 0) continue;
+            const int q1 = q - t;
+            float ys = recC[q], zs = recQ[q];
+            for (int s0 = 0; s0 < t; s0 += 4) {  // four terms with independent reads
+                int sp[4];
+                float cc[4], cq[4], yv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s2 = min(s0 + j, t - 1);
+                    sp[j] = recP[q1 + s2] + (t - s2);
+                    cc[j] = recC[q1 + s2];
+                    cq[j] = recQ[q1 + s2];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) yv[j] = recY[sp[j]];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (s0 + j >= t) break;
+                    ys = fmaf(cc[j], yv[j], ys);
+                    zs = fmaf(cq[j], yv[j], zs);
+                }
+            }
+            recY[q] = -ys;
+            recZ[q] = fmaf(kqd[recM[q1 - 1]], -ys, zs);
+        }
+        r_lv += nrec_lv;
+        wave_order();
+    }
+}
+
+// u_n = w_n + sum_{t < d_n} Y[n][a_t] w_{a_t} and o_n = G_n r_n + (q_n.k_n) w_n +
+// sum_t Z[n][a_t] w_{a_t} for state row i = 64 (wave & 1) + lane of nodes half, half + 2, ...
+// A node's records are read once across the wave (lane j takes record j) and handed to every
+// lane with readlane, so each term costs one LDS read of w.  W and GR rows have stride ws floats;
+// u goes to bank row n (stride 128), o to out0 + n * out_stride.
+__device__ __forceinline__ void tree_apply(int n, int i, int half, const int *poff,
+                                           const int *dep, const int *recM, const float *recY,
+                                           const float *recZ, const float *kqd, const float *Wm,
+                                           const float *GR, int ws, float *bank_u0,
+                                           float *out0, int64_t out_stride) {
+    const int lane = int(__lane_id());
+    for (int nd = half; nd < n; nd += 2) {
+        const int q1 = poff[nd] + 1, d = dep[nd];
+        const float wn = Wm[nd * ws + i];
+        float u = wn, o = fmaf(kqd[nd], wn, GR[nd * ws + i]);
+        for (int c0 = 0; c0 < d; c0 += 64) {
+            const int cnt = min(d - c0, 64);
+            const int j = q1 + c0 + min(lane, cnt - 1);
+            const int mj = recM[j];
+            const float yj = recY[j], zj = recZ[j];
+            int t = 0;
+            for (; t + 4 <= cnt; t += 4) {
+                float x[4], yv[4], zv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = Wm[__builtin_amdgcn_readlane(mj, t + e) * ws + i];
+                    yv[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(yj), t + e));
+                    zv[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), t + e));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    u = fmaf(yv[e], x[e], u);
+                    o = fmaf(zv[e], x[e], o);
+                }
+            }
+            for (; t < cnt; ++t) {
+                const float x = Wm[__builtin_amdgcn_readlane(mj, t) * ws + i];
+                u = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(yj), t)), x, u);
+                o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), t)), x, o);
+            }
+        }
+        bank_u0[int64_t(nd) * 128 + i] = u;
+        out0[int64_t(nd) * out_stride + i] = o;
+    }
 }
 
 // The matrix-core UT kernel (bf16 inputs, d = 128).

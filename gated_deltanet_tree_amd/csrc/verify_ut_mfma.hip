@@ -69,8 +69,8 @@ struct UtLayout5 {
         // plan (direct loads): poff [n64] | lvnode [n64] | lvn [lv64] | recM [rec64]
         plan = work + (wg_bytes > fold_bytes ? wg_bytes : fold_bytes);
         tabs = plan + (2 * n64 + lv64 + rec64) * 4;
-        // gam[n] | kq[n] | recE | recC | recQ [nrec]
-        total = tabs + (size_t(2) * n + size_t(3) * nrec) * 4;
+        // gam[n] | kq[n] | recE=recY | recC | recQ | recZ [nrec] (f32) | recP | recT [nrec] (int)
+        total = tabs + (size_t(2) * n + size_t(6) * nrec) * 4;
     }
 };
 
@@ -104,8 +104,11 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     int *recM = lvn + lay.lv64;
     float *gam = reinterpret_cast<float *>(lds + lay.tabs);
     float *kq = gam + n_max;
-    // recE = E(n, that node), recC = T[n][it], recQ = C[n][it]
+    // recE = E(n, that node), later Y[n][that node]; recC = T[n][it], recQ = C[n][it], recZ = Z;
+    // recP = block start of the record's node, recT = its distance - 1 (-1: the node itself)
     float *recE = kq + n_max, *recC = recE + nrec_max, *recQ = recC + nrec_max;
+    float *recZ = recQ + nrec_max, *recY = recE;
+    int *recP = reinterpret_cast<int *>(recZ + nrec_max), *recT = recP + nrec_max;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -198,13 +201,31 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
 
     // ---- 1. gate products along every record block ------------------------------------
-    //   E(n, anc_0) = g_n, E(n, anc_{t+1}) = E(n, anc_t) g_{anc_t}, G_n = E(n, root) g_root.
+    //   E(n, anc_0) = g_n, E(n, anc_{t+1}) = E(n, anc_t) g_{anc_t}, G_n = E(n, root) g_root,
+    // in groups of four records whose reads are independent; recP and recT on the way.
     for (int t = tid; t < n; t += THREADS) {
         const int o = poff[t], dt = dep[t];
         float E = slot_f32<bf16_t>(Gt[t]);
-        for (int s2 = 0; s2 < dt; ++s2) {
-            recE[o + 1 + s2] = E;
-            E *= slot_f32<bf16_t>(Gt[recM[o + 1 + s2]]);
+        recT[o] = -1;
+        for (int s0 = 0; s0 < dt; s0 += 4) {
+            int a[4], pa[4];
+            float ga[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = s0 + j < dt ? recM[o + 1 + s0 + j] : t;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pa[j] = poff[a[j]];
+                ga[j] = slot_f32<bf16_t>(Gt[a[j]]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (s0 + j >= dt) break;
+                const int q = o + 1 + s0 + j;
+                recE[q] = E;
+                recP[q] = pa[j];
+                recT[q] = s0 + j;
+                E *= ga[j];
+            }
         }
         gam[t] = E;
     }
@@ -287,6 +308,11 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
     __syncthreads();  // fold rows are dead: their LDS becomes W and GR; pair terms are done
 
+    // Y = T^-1 and Z = C' Y on the records (every wave; one lane per node up to depth 12); read
+    // only after the barrier that ends the S0 products.
+    tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
+                 tid, lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kq, recY, recZ);
+
     // ---- 4. p_n = S0 k_n, r_n = S0 q_n on the matrix cores; w_n and G_n r_n to LDS -------
     for (int jt0 = 0; jt0 < JT; jt0 += JC) {
         floatx4 acc[JC][2];
@@ -349,45 +375,10 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
     __syncthreads();
 
-    // ---- 5. level by level: u_n = w_n - sum_{a strict ancestor} T[n][a] u_a, then o_n ----
-    //   o_n = G_n r_n + (q_n . k_n) u_n + sum_a C[n][a] u_a.
-    // Nodes of one level depend only on lower levels, so a level's (node, row) items run in
-    // parallel, u overwrites w in place, and one pass over a node's ancestors serves both
-    // sums (roots, level 0, have u = w).
-    // Two waves share one node's 128 rows, so within a wave the node is uniform: its ancestor
-    // ids are read with scalar loads from the plan in the image, and only the rows of u and
-    // the coefficients come from LDS.
-    {
-        float *wu = P.bank_u[role ^ 1];
-        float *out0 = P.out + node_row0 * D;
-        const int i = tid & (D - 1);
-        const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
-        const int lv0 = n > 0 ? plan[P.off_ut_lv_base + seq] : 0;
-        const int dmax = n > 0 ? plan[P.off_ut_lv_base + seq + 1] - lv0 - 2 : -1;
-        // `plan` is the image again, declared read-only and unaliased: uniform reads of it
-        // become scalar loads
-        const int32_t *anc = plan + P.off_ut_rec_anc + (n > 0 ? plan[P.off_ut_rec_base + seq] : 0);
-        const int32_t *lvl = plan + P.off_ut_lvn + lv0;
-        const int32_t *nodes = plan + P.off_ut_lvnode + seq_off;
-        const int32_t *blk = plan + P.off_ut_node_rec + seq_off;
-        for (int lv = 0; lv <= dmax; ++lv) {
-            const int j1 = lvl[lv + 1];
-            for (int j = lvl[lv] + half; j < j1; j += THREADS / D) {
-                const int nd = nodes[j], q1 = blk[nd] + 1;
-                float u = Wm[nd * LY::WS + i], o = 0.f;
-#pragma unroll 4
-                for (int t = 0; t < lv; ++t) {
-                    const float x = Wm[anc[q1 + t] * LY::WS + i];
-                    u = fmaf(-recC[q1 + t], x, u);
-                    o = fmaf(recQ[q1 + t], x, o);
-                }
-                Wm[nd * LY::WS + i] = u;
-                wu[(row0_bank + nd) * D + i] = u;
-                out0[int64_t(nd) * P.H * D + i] = o + fmaf(kq[nd], u, GR[nd * LY::WS + i]);
-            }
-            __syncthreads();
-        }
-    }
+    // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
+    tree_apply(n, 64 * (w & 1) + int(__lane_id()), w >> 1, poff, dep, recM, recY, recZ, kq, Wm, GR,
+               LY::WS, P.bank_u[role ^ 1] + row0_bank * D, P.out + node_row0 * D,
+               int64_t(P.H) * D);
 }
 
 gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int nrec_max, int nlv_max,
