@@ -122,6 +122,18 @@ def test_tiny_tree_and_chain(torch_cuda, mode):
                "f32", 0, 1, 16, 16)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_odd_channel_count_conv(torch_cuda, dtype):
+    """An odd conv channel count (15) takes the one-channel-per-thread conv kernel; the tiny
+    tree and chain over two steps and a flush, conv outputs, banked inputs and windows against
+    the oracle."""
+    trees = [synth.TINY_TREE, synth.TINY_CHAIN]
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, C=15, dtype=dtype, cfg_id=91)
+    paths0 = [synth.deepest_leaf_path(t) for t in trees]
+    _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, [[0, 2, 5], [0, 1, 2]]], dtype, 91, 1,
+               16, 15)
+
+
 def _all_trees(N):
     import itertools
     for choice in itertools.product(*[range(i) for i in range(1, N)]):
