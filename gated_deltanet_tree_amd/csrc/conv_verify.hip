@@ -36,10 +36,11 @@
 //      wave 0 forms Y and Z level by level; [k; q] S0^T on the matrix cores; the epilogue
 //      evaluates the v channels (conv and SiLU) and writes w_n and G_n S0 q_n;
 //   5. u and o of every (node, row); u banked, o stored.
-// Matrix-core layout as in the bf16 UT kernel (v_mfma_f32_16x16x32_bf16): wave w owns state rows
-// [32w, 32w+32), lane l holds rows 32w + 16nt + (l % 16) and columns 16mt + 4(l/16) + e.  q and k
-// are fp32 here, so both operands enter as exact three-term bf16 splits, and each product keeps
-// the six terms that lie above the fp32 rounding level.
+// Matrix-core layout: wave w owns state rows [32w, 32w+32), lane l holds rows 32w + 16nt + (l % 16)
+// and columns 16mt + 4(l/16) + e.  q and k are fp32 here, so the products run on the fp32 matrix
+// cores (v_mfma_f32_16x16x4f32): for the 4-column step {16mt + 4(l/16) + e}, lane l already holds
+// the state element it contributes as B, and one float4 LDS read per mt gives its A elements for
+// the four steps e = 0..3.  Accumulation is fp32, as in a vector dot product.
 #include <hip/hip_ext.h>
 
 #include "mfma_common.h"
@@ -51,6 +52,7 @@ namespace {
 
 constexpr int kCvD = 128;
 constexpr float kNormFloor = 1e-6f;
+constexpr int kFoldRows = 4 * 256 / 64;  // pending rows per stage: 4 chunks per thread, 64 per row
 
 struct ConvVerifyParams {
     VerifyParams V;
@@ -134,6 +136,39 @@ struct CvLayout {
 };
 
 // SiLU with the hardware exp2 and reciprocal (each within about an ulp).
+// Pending rows f0 .. f0 + cnt - 1 (cnt <= kFoldRows) go through registers into LDS: 16-byte chunk
+// c of thread t is c = t + 256 j (j < 4), row c / 64, key half (c % 64 < 32) or residual half.
+// Register loads rather than direct-to-LDS loads: an LDS read after a direct load waits for
+// every older memory operation of the wave.  Four named registers (no array), so nothing of it
+// goes to scratch.
+__device__ __forceinline__ uint4 fold_chunk_load(const float *pk, const float *pu, int f0, int c) {
+    const int r = f0 + (c >> 6), half = (c >> 5) & 1, idx = c & 31;
+    return *reinterpret_cast<const uint4 *>((half ? pu : pk) + r * kCvD + idx * 4);
+}
+__device__ __forceinline__ void fold_chunk_store(float *fk, float *fu, int cnt, int c, uint4 v) {
+    if (c < 64 * cnt) {
+        const int r = c >> 6, half = (c >> 5) & 1, idx = c & 31;
+        *reinterpret_cast<uint4 *>((half ? fu : fk) + r * kCvD + idx * 4) = v;
+    }
+}
+#define GDN_FOLD_LOAD(f0, cnt)                                                          \
+    do {                                                                                \
+        const int lc_ = 64 * (cnt) - 1;                                                 \
+        fv0 = fold_chunk_load(pend_k, pend_u, (f0), min(tid, lc_));                     \
+        fv1 = fold_chunk_load(pend_k, pend_u, (f0), min(tid + 256, lc_));               \
+        fv2 = fold_chunk_load(pend_k, pend_u, (f0), min(tid + 512, lc_));               \
+        fv3 = fold_chunk_load(pend_k, pend_u, (f0), min(tid + 768, lc_));               \
+        flv = pend_lg[(f0) + min(tid, (cnt) - 1)];                                      \
+    } while (0)
+#define GDN_FOLD_STORE(cnt)                                                             \
+    do {                                                                                \
+        fold_chunk_store(fold_k, fold_u, (cnt), tid, fv0);                              \
+        fold_chunk_store(fold_k, fold_u, (cnt), tid + 256, fv1);                        \
+        fold_chunk_store(fold_k, fold_u, (cnt), tid + 512, fv2);                        \
+        fold_chunk_store(fold_k, fold_u, (cnt), tid + 768, fv3);                        \
+        if (tid < (cnt)) fold_lg[tid] = flv;                                            \
+    } while (0)
+
 __device__ __forceinline__ float silu(float y) {
     return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
 }
@@ -156,20 +191,6 @@ __device__ __forceinline__ float wave_total(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
-// acc += A B for operands given as three-term splits: the six products above 2^-24 relative,
-// smallest first.
-__device__ __forceinline__ floatx4 mfma6(const bf16x8 &ah, const bf16x8 &am, const bf16x8 &al,
-                                         const bf16x8 &bh, const bf16x8 &bm, const bf16x8 &bl,
-                                         floatx4 acc) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bm, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bm, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-    return acc;
 }
 
 }  // namespace
@@ -231,22 +252,13 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     // node 0's conv inputs, q block of head h; block b adds b H d
     const bf16_t *xrow0 = CP.x + (int64_t(layer) * P.T + seq_off) * C + h * D;
 
-    const int fk_chunks = int(LY::fold_chunks(nfc));
-    auto issue_fold = [&](int f0, int cnt) {  // pending rows f0 .. f0 + cnt - 1 into LDS
-        const float *pk = P.bank_k[role] + (row0_bank + f0) * D;
-        const float *pu = P.bank_u[role] + (row0_bank + f0) * D;
-        const int rows_chunks = cnt * LY::CPR;
-        for (int base = w * 64; base < 2 * fk_chunks; base += NW * 64) {
-            const int which = base / fk_chunks, b2 = base % fk_chunks;
-            if (b2 >= rows_chunks) continue;
-            const int c = min(b2 + lane, rows_chunks - 1);
-            const float *src = (which == 0 ? pk : pu) + c * 4;
-            to_lds<16>(src, lds + lay.fold_k + size_t(base) * 16);
-        }
-        const float *plg = P.bank_lg[role] + row0_bank + f0;
-        for (int base = w * 64; base < cnt; base += NW * 64)
-            to_lds<4>(plg + min(base + lane, cnt - 1), lds + lay.fold_lg + size_t(base) * 4);
-    };
+    const float *pend_k = P.bank_k[role] + row0_bank * D, *pend_u = P.bank_u[role] + row0_bank * D;
+    const float *pend_lg = P.bank_lg[role] + row0_bank;
+    float *fold_k = reinterpret_cast<float *>(lds + lay.fold_k);
+    float *fold_u = reinterpret_cast<float *>(lds + lay.fold_u);
+    float *fold_lg = reinterpret_cast<float *>(lds + lay.fold_lg);
+    uint4 fv0, fv1, fv2, fv3;
+    float flv;
 
     // ---- 0. loads ------------------------------------------------------------------------
     {
@@ -308,7 +320,20 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     const uint4 wk = *reinterpret_cast<const uint4 *>(wq_src + int64_t(HD) * 4);
     __syncthreads();  // waits for every direct load (the barrier's fence covers them)
 
-    // ---- 1. state tile requested; conv-window fold; record tables --------------------------
+    // ---- 1. raw conv inputs banked; state tile requested; conv-window fold; record tables --
+    // The bank copies go out first, so they have drained long before any later wait on memory.
+    {
+        float *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D;
+        for (int e = tid; e < n * 3 * (D / 4); e += THREADS) {  // (node, block, 4 channels)
+            const int nd = e / (3 * (D / 4)), r = e % (3 * (D / 4));
+            const int p = r / (D / 4), c = (r % (D / 4)) * 4;  // plane v | q | k
+            const int blk = p == 0 ? 2 : p - 1;
+            const uint2 x = *reinterpret_cast<const uint2 *>(
+                lds + lay.xv + (size_t(p) * n + nd) * LY::XROW + c * 2);
+            *reinterpret_cast<float4 *>(bx + int64_t(nd) * C + blk * HD + c) =
+                make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
+        }
+    }
     float s[2][8][4];  // rows 32w + 16nt + lr, columns 16mt + 4lg + e
     {
         const float *tile = committed + (32 * w + lr) * D + 4 * lg;
@@ -380,7 +405,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     }
     __syncthreads();  // windows, records and ancestors in LDS
 
-    // ---- 2. prologue: q and k from the conv; raw inputs and keys banked -------------------
+    // ---- 2. prologue: q and k from the conv ----------------------------------------------
     {
         const char *XV = lds + lay.xv;
         const char *XQ = XV + size_t(n) * LY::XROW, *XK = XQ + size_t(n) * LY::XROW;
@@ -400,8 +425,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 for (int j = 0; j < 3; ++j) cw[b][e][j] = X0s[j * 3 * D + b * D + 2 * lane + e];
             }
         }
-        float *wk_bank = P.bank_k[role ^ 1];
-        float *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D + 2 * lane;
         for (int nd = w; nd < n; nd += NW) {
             const int dt = dep[nd];
             const int4 an = anc[nd];
@@ -426,14 +449,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                     y[b][e] = v;
                     ss[b] = fmaf(v, v, ss[b]);
                 }
-                // raw conv inputs of the q and k blocks to the write bank
-                *reinterpret_cast<float2 *>(bx + int64_t(nd) * C + b * HD) =
-                    make_float2(bf16_lo(xw[0]), bf16_hi(xw[0]));
-            }
-            {  // raw conv inputs of the v block
-                const uint32_t xv = *reinterpret_cast<const uint32_t *>(XV + size_t(nd) * LY::XROW + 4 * lane);
-                *reinterpret_cast<float2 *>(bx + int64_t(nd) * C + 2 * HD) =
-                    make_float2(bf16_lo(xv), bf16_hi(xv));
             }
             // 1 / max(|y|, floor) as rsqrt(max(|y|^2, floor^2))
             const float iq = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss[0]), kNormFloor * kNormFloor));
@@ -442,13 +457,12 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
             const float2 qv = make_float2(y[0][0] * iq, y[0][1] * iq);
             *reinterpret_cast<float2 *>(KQ + size_t(2 * nd) * LY::KS + 2 * lane) = kv;
             *reinterpret_cast<float2 *>(KQ + size_t(2 * nd + 1) * LY::KS + 2 * lane) = qv;
-            *reinterpret_cast<float2 *>(wk_bank + (row0_bank + nd) * D + 2 * lane) = kv;
         }
     }
     __syncthreads();  // k and q rows complete; the q and k conv-input planes are consumed
 
     // ---- 3. pending fold rows start loading; pair coefficients on the matrix cores ---------
-    if (L > 0) issue_fold(0, min(L, nfc));
+    if (L > 0) GDN_FOLD_LOAD(0, min(L, nfc));
     // v-channel taps of this lane's state rows 32w + 16nt + lr, for the S0 epilogue
     uint2 wvr[2];
 #pragma unroll
@@ -462,16 +476,23 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     for (int ti = w; ti < JT * AT; ti += NW) {
         const int jt = ti / AT, at = ti % AT;
         const int xn = 8 * jt + (lr & 7), kn = 16 * at + lr;
-        const float *xrow = KQ + size_t(2 * xn + (lr >> 3)) * LY::KS;
-        const float *krow = KQ + size_t(2 * kn) * LY::KS;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        // fp32 operands straight from LDS: the 4-column step {16mt + 4lg + e} takes A[lr][lg]
+        // and B[lg][lr] from one float4 read per lane and mt; two accumulators halve the chain.
+        const float *xrow = KQ + size_t(2 * min(xn, n - 1) + (lr >> 3)) * LY::KS + 4 * lg;
+        const float *krow = KQ + size_t(2 * min(kn, n - 1)) * LY::KS + 4 * lg;
+        const float amask = xn < n ? 1.f : 0.f, bmask = kn < n ? 1.f : 0.f;
+        floatx4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            bf16x8 ah = {}, am = {}, al = {}, bh = {}, bm = {}, bl = {};
-            if (xn < n) row_operand_split(xrow, 32 * kb + 4 * lg, ah, am, al);
-            if (kn < n) row_operand_split(krow, 32 * kb + 4 * lg, bh, bm, bl);
-            acc = mfma6(ah, am, al, bh, bm, bl, acc);
+        for (int mt = 0; mt < 8; ++mt) {
+            const float4 a4 = *reinterpret_cast<const float4 *>(xrow + 16 * mt);
+            const float4 b4 = *reinterpret_cast<const float4 *>(krow + 16 * mt);
+            const float av[4] = {a4.x * amask, a4.y * amask, a4.z * amask, a4.w * amask};
+            const float bv[4] = {b4.x * bmask, b4.y * bmask, b4.z * bmask, b4.w * bmask};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc2[mt & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc2[mt & 1], 0, 0, 0);
         }
+        const floatx4 acc = acc2[0] + acc2[1];
         const int an = 16 * at + lr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -492,14 +513,23 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 recC[q] = slot_f32<bf16_t>(Bl[nd]) * recE[q] * acc[r];
         }
     }
-    __syncthreads();  // T, C' and q.k on the records; the first fold chunk has landed
+    if (L > 0) GDN_FOLD_STORE(min(L, nfc));
+    __syncthreads();  // T, C' and q.k on the records; the first fold chunk is in LDS
+
+    // keys to the write bank, from their LDS rows (stores issued after the wait above)
+    for (int e = tid; e < n * (D / 4); e += THREADS) {
+        const int nd = e / (D / 4), c = (e % (D / 4)) * 4;
+        *reinterpret_cast<float4 *>(P.bank_k[role ^ 1] + (row0_bank + nd) * D + c) =
+            *reinterpret_cast<const float4 *>(KQ + size_t(2 * nd) * LY::KS + c);
+    }
 
     // ---- 4. deferred commit: fold the pending rows, write the committed state once --------
     for (int f0 = 0; f0 < L; f0 += nfc) {
         const int cnt = min(L - f0, nfc);
         if (f0 > 0) {  // later chunks (more pending rows than one chunk holds)
             __syncthreads();
-            issue_fold(f0, cnt);
+            GDN_FOLD_LOAD(f0, cnt);
+            GDN_FOLD_STORE(cnt);
             __syncthreads();
         }
         for (int f = 0; f < cnt; ++f) {
@@ -535,32 +565,30 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     {
         const char *XV = lds + lay.xv;
         for (int jt0 = 0; jt0 < JT; jt0 += JC) {
-            // One half of the wave's state rows at a time (nt outer): only that half's split is
-            // live, and the first half's tile registers die before the second half runs.
+            // fp32 MFMA 16x16x4 per 4-column step {16mt + 4lg + e}: lane (lr, lg) gives A[lr][lg]
+            // = row lr of the M tile (one float4 read per mt covers e = 0..3) and B[lg][lr] =
+            // its own tile element s[nt][mt][e].
             floatx4 acc[JC][2];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int jc = 0; jc < JC; ++jc)
+                acc[jc][0] = acc[jc][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int jc = 0; jc < JC; ++jc) acc[jc][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    bf16x8 bh, bm, bl;
-                    const float x[8] = {s[nt][2 * kb][0],     s[nt][2 * kb][1],
-                                        s[nt][2 * kb][2],     s[nt][2 * kb][3],
-                                        s[nt][2 * kb + 1][0], s[nt][2 * kb + 1][1],
-                                        s[nt][2 * kb + 1][2], s[nt][2 * kb + 1][3]};
-                    split3(x, bh, bm, bl);
+                for (int jc = 0; jc < JC; ++jc) {
+                    const int jt = jt0 + jc;
+                    if (jt >= JT) break;
+                    const int xn = 8 * jt + (lr & 7);
+                    const float4 a4 = *reinterpret_cast<const float4 *>(
+                        KQ + size_t(2 * min(xn, n - 1) + (lr >> 3)) * LY::KS + 16 * mt + 4 * lg);
+                    const float am = xn < n ? 1.f : 0.f;
+                    const float av[4] = {a4.x * am, a4.y * am, a4.z * am, a4.w * am};
 #pragma unroll
-                    for (int jc = 0; jc < JC; ++jc) {
-                        const int jt = jt0 + jc;
-                        if (jt >= JT) break;
-                        const int xn = 8 * jt + (lr & 7);
-                        bf16x8 ah = {}, am = {}, al = {};
-                        if (xn < n)
-                            row_operand_split(KQ + size_t(2 * xn + (lr >> 3)) * LY::KS,
-                                              32 * kb + 4 * lg, ah, am, al);
-                        acc[jc][nt] = mfma6(ah, am, al, bh, bm, bl, acc[jc][nt]);
-                    }
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt)
+                            acc[jc][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                av[e], s[nt][mt][e], acc[jc][nt], 0, 0, 0);
                 }
             }
             // When W and GR take KQ's place, every wave must be done reading KQ; Y and Z are
@@ -659,7 +687,7 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: too many workgroups for one launch");
     const int n_max = v.max_tree, nrec_max = v.ut_max_records, nlv_max = v.ut_max_levels;
     const int nf = va->max_nodes;
-    const int nfc = CvLayout::fold_rows(n_max, nf);
+    const int nfc = std::min(CvLayout::fold_rows(n_max, nf), kFoldRows);
     const size_t lds = CvLayout(n_max, nrec_max, nlv_max, nf, nfc).total;
     if (lds > kUtMaxLdsBytes)
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: trees of %d nodes with %d records need "
