@@ -6,13 +6,14 @@ verify (with the deferred-commit fold), then accept -> commit of one seeded path
 (role swap or compaction).  The timed region is K steps plus the final flush.
 
 Three paths are timed, one after the other, on the same resident workload:
-  ut     the tree conv, then the tree-masked verify of given q/k/v on the matrix cores (the
-         headline by default);
   fused  conv -> SiLU -> unit-length q/k -> tree-masked verify in one launch per layer: q, k
-         and v come from the conv of the raw inputs x, as in a hybrid GDN layer;
+         and v come from the conv of the raw inputs x, the layer's own data flow (the
+         headline by default);
+  ut     the tree conv, then the tree-masked verify of separately drawn q/k/v on the matrix
+         cores;
   chain  the tree conv, then heavy-light chains launched wave by wave.
-ut and chain compute the same outputs, factor banks and committed states; fused computes the
-layer whose q/k/v are the conv's (all three are reported under "paths").
+ut and chain compute the same outputs, factor banks and committed states from drawn q/k/v; fused
+computes the layer whose q/k/v are the conv's (all three are reported under "paths").
 
 Workload (default): 32 sequences, each with its own seeded 22-node top-4 tree (depth <= 12),
 48 GDN layers x 48 heads x d = 128 with independent fp32 states (4.8 GB), bf16 inputs, conv
@@ -295,7 +296,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layers-per-call", type=int, default=1)
-    ap.add_argument("--verify", choices=["fused", "ut", "chain"], default="ut",
+    ap.add_argument("--verify", choices=["fused", "ut", "chain"], default="fused",
                     help="headline path (all are timed): fused = conv -> SiLU -> unit q/k -> "
                          "tree-masked verify in one launch per layer; ut = tree conv, then the "
                          "tree-masked verify of given q/k/v on the matrix cores; chain = tree "
