@@ -462,7 +462,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     __syncthreads();  // k and q rows complete; the q and k conv-input planes are consumed
 
     // ---- 3. pending fold rows start loading; pair coefficients on the matrix cores ---------
-    if (L > 0) GDN_FOLD_LOAD(0, min(L, nfc));
+    if (L > 0) GDN_FOLD_LOAD(L - min(L, nfc), min(L, nfc));
     // v-channel taps of this lane's state rows 32w + 16nt + lr, for the S0 epilogue
     uint2 wvr[2];
 #pragma unroll
@@ -524,26 +524,42 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     }
 
     // ---- 4. deferred commit: fold the pending rows, write the committed state once --------
-    for (int f0 = 0; f0 < L; f0 += nfc) {
-        const int cnt = min(L - f0, nfc);
-        if (f0 > 0) {  // later chunks (more pending rows than one chunk holds)
-            __syncthreads();
-            GDN_FOLD_LOAD(f0, cnt);
-            GDN_FOLD_STORE(cnt);
-            __syncthreads();
-        }
-        for (int f = 0; f < cnt; ++f) {
-            const float gf = expf(FL[f]);
-            const float u0 = FU[f * D + 32 * w + lr], u1 = FU[f * D + 32 * w + 16 + lr];
+    // S_L = G S0 + sum_i c_i u_i k_i^T with G the product of the L pending gates and c_i that
+    // of the gates after row i: the tile is scaled once and each row costs one FMA per element.
+    // Rows run last to first, so c builds up backward (c_{L-1} = 1, c_{i-1} = c_i g_i); chunks
+    // of nfc rows come last chunk first (the staged one holds rows L - min(L, nfc) .. L - 1).
+    if (L > 0) {
+        float G = 1.f;
+        for (int f = 0; f < L; ++f) G *= expf(pend_lg[f]);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const float4 k4 = *reinterpret_cast<const float4 *>(FK + f * D + 16 * mt + 4 * lg);
-                const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    s[0][mt][e] = fmaf(u0, kk[e], gf * s[0][mt][e]);
-                    s[1][mt][e] = fmaf(u1, kk[e], gf * s[1][mt][e]);
+            for (int e = 0; e < 4; ++e) {
+                s[0][mt][e] *= G;
+                s[1][mt][e] *= G;
+            }
+        float c = 1.f;
+        for (int hi = L; hi > 0; hi -= nfc) {
+            const int lo = max(hi - nfc, 0);
+            if (hi < L) {  // earlier chunks (more pending rows than one chunk holds)
+                __syncthreads();
+                GDN_FOLD_LOAD(lo, hi - lo);
+                GDN_FOLD_STORE(hi - lo);
+                __syncthreads();
+            }
+            for (int f = hi - 1 - lo; f >= 0; --f) {
+                const float u0 = c * FU[f * D + 32 * w + lr], u1 = c * FU[f * D + 32 * w + 16 + lr];
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) {
+                    const float4 k4 = *reinterpret_cast<const float4 *>(FK + f * D + 16 * mt + 4 * lg);
+                    const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        s[0][mt][e] = fmaf(u0, kk[e], s[0][mt][e]);
+                        s[1][mt][e] = fmaf(u1, kk[e], s[1][mt][e]);
+                    }
                 }
+                c *= expf(FL[f]);
             }
         }
     }
@@ -669,8 +685,11 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
                     "role and pending_len arrays");
     if (!ca->x || !ca->weight || !ca->conv_state || !ca->bank_x[0] || !ca->bank_x[1])
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: null x/weight/conv_state/bank_x");
-    if (reinterpret_cast<uintptr_t>(ca->x) % 16 || reinterpret_cast<uintptr_t>(ca->weight) % 16)
-        return fail(GDN_EINVAL, "gdn_tree_conv_verify: x and weight must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(ca->x) % 16 || reinterpret_cast<uintptr_t>(ca->weight) % 16 ||
+        reinterpret_cast<uintptr_t>(ca->bank_x[0]) % 16 ||
+        reinterpret_cast<uintptr_t>(ca->bank_x[1]) % 16)
+        return fail(GDN_EINVAL, "gdn_tree_conv_verify: x, weight and bank_x must be 16-byte "
+                    "aligned");
     if (v.ut_records < 0)
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: the schedule has no tree-masked plan "
                     "(its trees need more than %d records per node)", kUtRecordsPerNode);

@@ -329,8 +329,8 @@ gdn_status gdn_tree_conv(const gdn_conv_args *args, const int32_t *host_image,
  * Ignored (may be NULL): va->q, va->k, va->v, va->workspace and ca->out (the conv output stays
  * on chip).  Requirements (GDN_EINVAL otherwise, nothing launched): head_dim 128; bf16 beta,
  * gate, x and weight; ca->channels = 3 H 128; ca's n_seqs, n_nodes, max_nodes, layer_begin and
- * n_layers equal va's; ca->role and ca->pending_len are the same device arrays as va's; x and
- * weight 16-byte aligned; the schedule carries the tree-masked plan and the trees fit one
+ * n_layers equal va's; ca->role and ca->pending_len are the same device arrays as va's; x,
+ * weight and bank_x 16-byte aligned; the schedule carries the tree-masked plan and the trees fit one
  * workgroup's LDS (160 KiB: about 60 nodes).
  * Work: one workgroup per (layer, sequence, head), 4 waves; the conv, SiLU and normalisation
  * run in its prologue, the rest as gdn_tree_verify_ut on the matrix cores.
