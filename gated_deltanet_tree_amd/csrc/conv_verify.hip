@@ -469,25 +469,25 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     for (int nt = 0; nt < 2; ++nt)
         wvr[nt] = *reinterpret_cast<const uint2 *>(CP.w + (int64_t(layer) * C + 2 * HD + h * D +
                                                            32 * w + 16 * nt + lr) * 4);
-    // M tile jt stacks k (rows 0-7) and q (rows 8-15) of nodes 8jt .. 8jt+7; N tile at holds the
-    // keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: k . k_a for lg < 2 and
-    // q . k_a for lg >= 2, of node 8jt + 4(lg & 1) + r, with a = 16at + lr.
+    // M tile jt is KQ rows 16jt .. 16jt+15, i.e. k and q of nodes 8jt .. 8jt+7 interleaved; N
+    // tile at holds the keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: of
+    // node 8jt + 2lg + r/2, k . k_a for even r and q . k_a for odd r, with a = 16at + lr.  Rows
+    // and keys past the tree are clamped to its last node; their products are never used.
     const int JT = (n + 7) >> 3, AT = (n + 15) >> 4;
     for (int ti = w; ti < JT * AT; ti += NW) {
         const int jt = ti / AT, at = ti % AT;
-        const int xn = 8 * jt + (lr & 7), kn = 16 * at + lr;
+        const int kn = 16 * at + lr;
         // fp32 operands straight from LDS: the 4-column step {16mt + 4lg + e} takes A[lr][lg]
         // and B[lg][lr] from one float4 read per lane and mt; two accumulators halve the chain.
-        const float *xrow = KQ + size_t(2 * min(xn, n - 1) + (lr >> 3)) * LY::KS + 4 * lg;
+        const float *xrow = KQ + size_t(min(16 * jt + lr, 2 * n - 1)) * LY::KS + 4 * lg;
         const float *krow = KQ + size_t(2 * min(kn, n - 1)) * LY::KS + 4 * lg;
-        const float amask = xn < n ? 1.f : 0.f, bmask = kn < n ? 1.f : 0.f;
         floatx4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const float4 a4 = *reinterpret_cast<const float4 *>(xrow + 16 * mt);
             const float4 b4 = *reinterpret_cast<const float4 *>(krow + 16 * mt);
-            const float av[4] = {a4.x * amask, a4.y * amask, a4.z * amask, a4.w * amask};
-            const float bv[4] = {b4.x * bmask, b4.y * bmask, b4.z * bmask, b4.w * bmask};
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+            const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 acc2[mt & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc2[mt & 1], 0, 0, 0);
@@ -496,8 +496,8 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
         const int an = 16 * at + lr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int nd = 8 * jt + 4 * (lg & 1) + r;
-            const bool is_q = lg >= 2;
+            const int nd = 8 * jt + 2 * lg + (r >> 1);
+            const bool is_q = r & 1;
             if (nd >= n || an >= n) continue;
             if (an == nd) {
                 if (is_q) kqd[nd] = acc[r];
@@ -582,8 +582,13 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
         const char *XV = lds + lay.xv;
         for (int jt0 = 0; jt0 < JT; jt0 += JC) {
             // fp32 MFMA 16x16x4 per 4-column step {16mt + 4lg + e}: lane (lr, lg) gives A[lr][lg]
-            // = row lr of the M tile (one float4 read per mt covers e = 0..3) and B[lg][lr] =
-            // its own tile element s[nt][mt][e].
+            // = KQ row 16jt + lr (k and q of node 8jt + lr/2; one float4 read per mt covers
+            // e = 0..3, rows past the tree clamped to its last) and B[lg][lr] = its own tile
+            // element s[nt][mt][e].
+            const float *arow[JC];
+#pragma unroll
+            for (int jc = 0; jc < JC; ++jc)
+                arow[jc] = KQ + size_t(min(16 * (jt0 + jc) + lr, 2 * n - 1)) * LY::KS + 4 * lg;
             floatx4 acc[JC][2];
 #pragma unroll
             for (int jc = 0; jc < JC; ++jc)
@@ -592,13 +597,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
             for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
                 for (int jc = 0; jc < JC; ++jc) {
-                    const int jt = jt0 + jc;
-                    if (jt >= JT) break;
-                    const int xn = 8 * jt + (lr & 7);
-                    const float4 a4 = *reinterpret_cast<const float4 *>(
-                        KQ + size_t(2 * min(xn, n - 1) + (lr >> 3)) * LY::KS + 16 * mt + 4 * lg);
-                    const float am = xn < n ? 1.f : 0.f;
-                    const float av[4] = {a4.x * am, a4.y * am, a4.z * am, a4.w * am};
+                    if (jt0 + jc >= JT) break;
+                    const float4 a4 = *reinterpret_cast<const float4 *>(arow[jc] + 16 * mt);
+                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -610,39 +611,34 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
             // When W and GR take KQ's place, every wave must be done reading KQ; Y and Z are
             // complete past this point too.
             if (jt0 == 0) __syncthreads();
-            // Lane (lr, lg) holds rows 4lg + r of each M tile: p of node 8jt + 4lg + r for
-            // lg < 2, r of node 8jt + 4(lg - 2) + r for lg >= 2, at state row 32w + 16nt + lr.
+            // Lane (lr, lg) holds rows 4lg + r of each M tile: p (even r) and r (odd r) of node
+            // 8jt + 2lg + r/2 at state row 32w + 16nt + lr.
 #pragma unroll
             for (int jc = 0; jc < JC; ++jc) {
                 const int jt = jt0 + jc;
                 if (jt >= JT) break;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int nd = 8 * jt + 4 * (lg & 1) + r;
+                for (int j = 0; j < 2; ++j) {
+                    const int nd = 8 * jt + 2 * lg + j;
                     if (nd >= n) continue;
                     const float G = gam[nd];
-                    if (lg < 2) {
-                        const int dt = dep[nd];
-                        const int4 an = anc[nd];
-                        const float beta = slot_f32<bf16_t>(Bl[nd]);
+                    const int dt = dep[nd];
+                    const int4 an = anc[nd];
+                    const float beta = slot_f32<bf16_t>(Bl[nd]);
 #pragma unroll
-                        for (int nt = 0; nt < 2; ++nt) {
-                            const int i = 32 * w + 16 * nt + lr;
-                            const float wv[4] = {bf16_lo(wvr[nt].x), bf16_hi(wvr[nt].x),
-                                                 bf16_lo(wvr[nt].y), bf16_hi(wvr[nt].y)};
-                            const float *cv = X0s + 2 * D + i;  // v channel i, taps 0..2
-                            const float v = silu(conv4(
-                                wv, bf16_at(XV + size_t(nd) * LY::XROW, i),
-                                bf16_at(XV + size_t(an.x) * LY::XROW, i),
-                                bf16_at(XV + size_t(an.y) * LY::XROW, i),
-                                bf16_at(XV + size_t(an.z) * LY::XROW, i), dt, cv[0], cv[3 * D],
-                                cv[6 * D]));
-                            Wm[nd * LY::KS + i] = beta * fmaf(-G, acc[jc][nt][r], v);
-                        }
-                    } else {
-#pragma unroll
-                        for (int nt = 0; nt < 2; ++nt)
-                            GR[nd * LY::KS + 32 * w + 16 * nt + lr] = G * acc[jc][nt][r];
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const int i = 32 * w + 16 * nt + lr;
+                        const float wv[4] = {bf16_lo(wvr[nt].x), bf16_hi(wvr[nt].x),
+                                             bf16_lo(wvr[nt].y), bf16_hi(wvr[nt].y)};
+                        const float *cv = X0s + 2 * D + i;  // v channel i, taps 0..2
+                        const float v = silu(conv4(
+                            wv, bf16_at(XV + size_t(nd) * LY::XROW, i),
+                            bf16_at(XV + size_t(an.x) * LY::XROW, i),
+                            bf16_at(XV + size_t(an.y) * LY::XROW, i),
+                            bf16_at(XV + size_t(an.z) * LY::XROW, i), dt, cv[0], cv[3 * D],
+                            cv[6 * D]));
+                        Wm[nd * LY::KS + i] = beta * fmaf(-G, acc[jc][nt][2 * j], v);
+                        GR[nd * LY::KS + i] = G * acc[jc][nt][2 * j + 1];
                     }
                 }
             }
