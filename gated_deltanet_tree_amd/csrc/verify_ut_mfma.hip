@@ -244,28 +244,27 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
 
     // ---- 2. pair coefficients: [k; q] K^T on the matrix cores ---------------------------
-    // M tile jt stacks k (rows 0-7) and q (rows 8-15) of nodes 8jt .. 8jt+7; N tile at holds
-    // the keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: k . k_a for
-    // lg < 2 and q . k_a for lg >= 2, of node 8jt + 4(lg & 1) + r, with a = 16at + lr.
+    // M tile jt interleaves k and q of nodes 8jt .. 8jt+7 (row 2j + 0/1 = k/q of node 8jt + j);
+    // N tile at holds the keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r:
+    // of node 8jt + 2lg + r/2, k . k_a for even r and q . k_a for odd r, with a = 16at + lr.
+    // Nodes past the tree are clamped to its last; their products are never used.
     const int JT = (n + 7) >> 3, AT = (n + 15) >> 4;
     for (int ti = w; ti < JT * AT; ti += NW) {
         const int jt = ti / AT, at = ti % AT;
-        const int xn = 8 * jt + (lr & 7), kn = 16 * at + lr;
-        const char *xrow = IN + size_t(xn) * LY::NODE_BYTES + (lr >> 3) * D * 2;
+        const int xn = min(8 * jt + (lr >> 1), n - 1), kn = min(16 * at + lr, n - 1);
+        const char *xrow = IN + size_t(xn) * LY::NODE_BYTES + (lr & 1) * D * 2;
         const char *krow = IN + size_t(kn) * LY::NODE_BYTES;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 z = {};
-            const bf16x8 a = xn < n ? row_operand(xrow, 32 * kb + 4 * lg) : z;
-            const bf16x8 b = kn < n ? row_operand(krow, 32 * kb + 4 * lg) : z;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-        }
+        for (int kb = 0; kb < 4; ++kb)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_operand(xrow, 32 * kb + 4 * lg),
+                                                         row_operand(krow, 32 * kb + 4 * lg), acc,
+                                                         0, 0, 0);
         const int an = 16 * at + lr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int nd = 8 * jt + 4 * (lg & 1) + r;
-            const bool is_q = lg >= 2;
+            const int nd = 8 * jt + 2 * lg + (r >> 1);
+            const bool is_q = r & 1;
             if (nd >= n || an >= n) continue;
             if (an == nd) {
                 if (is_q) kq[nd] = acc[r];
@@ -334,12 +333,10 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
             for (int jc = 0; jc < JC; ++jc) {
                 const int jt = jt0 + jc;
                 if (jt >= JT) break;
-                const int xn = 8 * jt + (lr & 7);
-                const bf16x8 z = {};
-                const bf16x8 a = xn < n
-                    ? row_operand(IN + size_t(xn) * LY::NODE_BYTES + (lr >> 3) * D * 2,
-                                  32 * kb + 4 * lg)
-                    : z;
+                // k (even lr) or q (odd lr) of node 8jt + lr/2, clamped to the tree's last node
+                const int xn = min(8 * jt + (lr >> 1), n - 1);
+                const bf16x8 a =
+                    row_operand(IN + size_t(xn) * LY::NODE_BYTES + (lr & 1) * D * 2, 32 * kb + 4 * lg);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     acc[jc][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[nt], acc[jc][nt], 0, 0, 0);
@@ -348,27 +345,23 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
                 }
             }
         }
-        // Lane (lr, lg) holds rows 4lg + r of each M tile: p of node 8jt + 4lg + r for lg < 2,
-        // r of node 8jt + 4(lg - 2) + r for lg >= 2, at state row 32w + 16nt + lr.
+        // Lane (lr, lg) holds rows 4lg + r of each M tile: p (even r) and r (odd r) of node
+        // 8jt + 2lg + r/2 at state row 32w + 16nt + lr.
 #pragma unroll
         for (int jc = 0; jc < JC; ++jc) {
             const int jt = jt0 + jc;
             if (jt >= JT) break;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int nd = 8 * jt + 4 * (lg & 1) + r;
+            for (int j = 0; j < 2; ++j) {
+                const int nd = 8 * jt + 2 * lg + j;
                 if (nd >= n) continue;
-                const float G = gam[nd];
+                const float G = gam[nd], beta = slot_f32<bf16_t>(Bl[nd]);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int i = 32 * w + 16 * nt + lr;
-                    if (lg < 2) {
-                        const float v = bf16_at(IN + size_t(nd) * LY::NODE_BYTES + 2 * D * 2, i);
-                        Wm[nd * LY::WS + i] =
-                            slot_f32<bf16_t>(Bl[nd]) * fmaf(-G, acc[jc][nt][r], v);
-                    } else {
-                        GR[nd * LY::WS + i] = G * acc[jc][nt][r];
-                    }
+                    const float v = bf16_at(IN + size_t(nd) * LY::NODE_BYTES + 2 * D * 2, i);
+                    Wm[nd * LY::WS + i] = beta * fmaf(-G, acc[jc][nt][2 * j], v);
+                    GR[nd * LY::WS + i] = G * acc[jc][nt][2 * j + 1];
                 }
             }
         }
