@@ -51,14 +51,17 @@ __device__ __forceinline__ UtUnit ut_unit(const VerifyParams &P) {
 //   z_t = C'[n][a_t] - ((q_n.k_n) T[n][a_t] + sum_{s<t} z_s T[a_s][a_t])
 // where T[a_s][a_t] is record rp_s + t - s of a_s's block (rp_s = its start).  Every read is
 // independent of the results, so a lane needs two rounds of loads and then only FMAs.  YD bounds
-// the tree's depth; terms past the node's depth d are computed on clamped indices and dropped.
+// the tree's depth; terms past the node's depth d are computed and dropped.  Their inner reads
+// (records bs_s + t with bs_s = rp_s - s, a compile-time offset from one base per s) may run up
+// to YD - 2 records past the node's block: into the next node's records or the table after recC,
+// never past the tables, and only into dropped terms.
 template <int YD>
 __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *recC,
                                         const float *recQ, const int *recP, float *recY,
                                         float *recZ) {
-    int rp[YD];
+    const float *tb[YD];  // recC + rp_s - s
 #pragma unroll
-    for (int s = 0; s < YD; ++s) rp[s] = recP[q1 + min(s, d - 1)];
+    for (int s = 0; s < YD; ++s) tb[s] = recC + recP[q1 + min(s, d - 1)] - s;
     float y[YD], z[YD];
 #pragma unroll
     for (int t = 0; t < YD; ++t) {
@@ -67,7 +70,7 @@ __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *re
         float ya = tn, za = kq * tn;
 #pragma unroll
         for (int s = 0; s < t; ++s) {
-            const float ts = recC[rp[s] + (tc - min(s, tc))];
+            const float ts = tb[s][t];
             ya = fmaf(y[s], ts, ya);
             za = fmaf(z[s], ts, za);
         }

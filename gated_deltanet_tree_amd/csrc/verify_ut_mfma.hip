@@ -282,18 +282,33 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
 
     // ---- 3. deferred commit: fold the pending rows, write the committed state once --------
-    for (int f = 0; f < L; ++f) {
-        const float gf = expf(FL[f]);
-        const float u0 = FU[f * D + 32 * w + lr], u1 = FU[f * D + 32 * w + 16 + lr];
+    // S_L = G S0 + sum_f c_f u_f k_f^T with G the product of the L pending gates and c_f that of
+    // the gates after row f: the tile is scaled once, then each row costs one FMA per element.
+    // Rows run last to first so that c builds up backward (c_{L-1} = 1, c_{f-1} = c_f g_f).
+    if (L > 0) {
+        float G = 1.f;
+        for (int f = 0; f < L; ++f) G *= expf(FL[f]);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const float4 k4 = *reinterpret_cast<const float4 *>(FK + f * D + 16 * mt + 4 * lg);
-            const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                s[0][mt][e] = fmaf(u0, kk[e], gf * s[0][mt][e]);
-                s[1][mt][e] = fmaf(u1, kk[e], gf * s[1][mt][e]);
+                s[0][mt][e] *= G;
+                s[1][mt][e] *= G;
             }
+        float c = 1.f;
+        for (int f = L - 1; f >= 0; --f) {
+            const float u0 = c * FU[f * D + 32 * w + lr], u1 = c * FU[f * D + 32 * w + 16 + lr];
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const float4 k4 = *reinterpret_cast<const float4 *>(FK + f * D + 16 * mt + 4 * lg);
+                const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s[0][mt][e] = fmaf(u0, kk[e], s[0][mt][e]);
+                    s[1][mt][e] = fmaf(u1, kk[e], s[1][mt][e]);
+                }
+            }
+            c *= expf(FL[f]);
         }
     }
     if (L > 0) {
