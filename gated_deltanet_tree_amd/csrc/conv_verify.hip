@@ -473,9 +473,14 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     // tile at holds the keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: of
     // node 8jt + 2lg + r/2, k . k_a for even r and q . k_a for odd r, with a = 16at + lr.  Rows
     // and keys past the tree are clamped to its last node; their products are never used.
-    const int JT = (n + 7) >> 3, AT = (n + 15) >> 4;
-    for (int ti = w; ti < JT * AT; ti += NW) {
-        const int jt = ti / AT, at = ti % AT;
+    // A key a pairs with node n only if a <= n (an ancestor, or n itself), so M tile jt (nodes
+    // up to 8jt + 7) needs the key tiles at <= jt / 2 only: (jt / 2) + 1 tiles per M tile.
+    const int JT = (n + 7) >> 3;
+    int n_tiles = 0;
+    for (int j = 0; j < JT; ++j) n_tiles += (j >> 1) + 1;
+    for (int ti = w; ti < n_tiles; ti += NW) {
+        int jt = 0, at = ti;
+        while (at > (jt >> 1)) at -= (jt++ >> 1) + 1;
         const int kn = 16 * at + lr;
         // fp32 operands straight from LDS: the 4-column step {16mt + 4lg + e} takes A[lr][lg]
         // and B[lg][lr] from one float4 read per lane and mt; two accumulators halve the chain.
