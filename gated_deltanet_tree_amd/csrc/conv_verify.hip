@@ -66,8 +66,8 @@ struct ConvVerifyParams {
 // LDS regions for trees of at most n nodes, nrec records and nlv level entries, with nfc pending
 // rows folded per chunk.
 //   X:  the bf16 conv-input planes [v | q | k] (n rows of 256 bytes each); once the q and k rows
-//       are consumed, the pending fold rows (k | u | lg) take their place; the v plane lives
-//       until the S0 epilogue.
+//       are consumed, the pending fold rows (k | u | lg) take their place, and after the fold the
+//       dense Y and Z rows; the v plane lives until the S0 epilogue.
 //   KQ: the fp32 k and q rows (k_n at row 2n, q_n at 2n + 1, stride KS); after the S0 products,
 //       W (rows 0 .. n-1) and G_n S0 q_n (rows n .. 2n-1) when n <= 32 (all M tiles in one
 //       pass), otherwise W and GR get their own regions.
@@ -87,11 +87,16 @@ struct CvLayout {
     // direct-load footprint of the three conv-input planes
     __host__ __device__ static size_t xin_bytes(int n) { return round_up(size_t(48) * n, 64) * 16; }
     __host__ __device__ static size_t rows_bytes(int rows) { return size_t(rows) * KS * 4; }
+    // dense Y and Z rows of the u/o pass: round16(n) rows of round4(n) floats each
+    __host__ __device__ static size_t dense_bytes(int n) {
+        return 2 * round_up(size_t(n), 16) * round_up(size_t(n), 4) * 4;
+    }
     // room after the v plane: the q and k planes (with the direct-load padding), at least
-    // min(nf, 4) fold rows
+    // min(nf, 4) fold rows and the dense Y and Z rows
     __host__ __device__ static size_t fold_room(int n, int nf) {
         const size_t a = xin_bytes(n) - size_t(n) * XROW, b = fold_bytes(nf < 4 ? nf : 4);
-        return a > b ? a : b;
+        const size_t c = dense_bytes(n), ab = a > b ? a : b;
+        return ab > c ? ab : c;
     }
     // Pending rows per fold chunk: as many as the room holds.
     static int fold_rows(int n, int nf) {
@@ -240,6 +245,10 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     const int layer = P.layer_begin + un.layer_rel, seq = un.seq, h = un.h;
     const int seq_off = P.img[P.off_seq + seq];
     const int n = P.img[P.off_seq + seq + 1] - seq_off;
+    // dense Y and Z rows of the u/o pass, over the fold rows once the fold is done
+    const int ys = (n + 3) & ~3;
+    float *Yd = reinterpret_cast<float *>(lds + lay.xq);
+    float *Zd = Yd + ((n + 15) & ~15) * ys;
     // pending counts come from the commit call, which bounds them by the bank rows; the clamp
     // keeps a corrupted count from reading past the banks.
     const int role = P.role[seq], L = min(max(P.pending[seq], 0), P.max_nodes);
@@ -578,10 +587,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                     make_float4(s[nt][mt][0], s[nt][mt][1], s[nt][mt][2], s[nt][mt][3]);
     }
 
-    // Y = T^-1 and Z = C' Y on the records (every wave; one lane per node up to depth 12)
-    tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
-                 tid, lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ);
-
     // p_n = S0 k_n, r_n = S0 q_n on the matrix cores; then w_n and G_n r_n to LDS.
     {
         const char *XV = lds + lay.xv;
@@ -613,8 +618,8 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                                 av[e], s[nt][mt][e], acc[jc][nt], 0, 0, 0);
                 }
             }
-            // When W and GR take KQ's place, every wave must be done reading KQ; Y and Z are
-            // complete past this point too.
+            // When W and GR take KQ's place, every wave must be done reading KQ; the fold rows
+            // are dead past this point too.
             if (jt0 == 0) __syncthreads();
             // Lane (lr, lg) holds rows 4lg + r of each M tile: p (even r) and r (odd r) of node
             // 8jt + 2lg + r/2 at state row 32w + 16nt + lr.
@@ -649,12 +654,16 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
             }
         }
     }
+    // Y = T^-1 and Z = C' Y on the records and their dense rows (over the dead fold rows), on
+    // wave 0 while the other waves finish their epilogue.
+    tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
+                 tid, lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ);
+    tree_dense(n, ys, w, lane, poff, dep, recM, recY, recZ, kqd, Yd, Zd);
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
-    tree_apply(n, 64 * (w & 1) + int(__lane_id()), w >> 1, poff, dep, recM, recY, recZ, kqd, Wm,
-               GR, LY::KS, P.bank_u[role ^ 1] + row0_bank * D, P.out + node_row0 * D,
-               int64_t(P.H) * D);
+    tree_apply_mfma(n, ys, w, lane, Yd, Zd, Wm, GR, LY::KS, P.bank_u[role ^ 1] + row0_bank * D,
+                    P.out + node_row0 * D, int64_t(P.H) * D);
 }
 
 namespace {

@@ -85,8 +85,8 @@ __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *re
 
 // Y = T^-1 and Z = C' Y on the tree's records (record (n, t) = ancestor a_t of n at distance
 // t + 1, at q1 + t with q1 = poff[n] + 1; recP = block start of the record's node, recT = t,
-// -1 on a node's own record).  Trees up to depth 12: one lane per node (yz_rows), every wave.
-// Deeper trees: wave 0 goes level by level with
+// -1 on a node's own record), all on wave 0.  Trees up to depth 12: one lane per node
+// (yz_rows).  Deeper trees: level by level with
 //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
 //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
 // (level lv's blocks of lv + 1 records are contiguous from record r_lv; every term read belongs
@@ -97,8 +97,9 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int tid, int lane,
                                              const int *recM, const int *recP, const int *recT,
                                              const float *recC, const float *recQ,
                                              const float *kqd, float *recY, float *recZ) {
+    if (w != 0) return;
     if (dmax <= 12) {
-        for (int nd = tid; nd < n; nd += 256) {
+        for (int nd = lane; nd < n; nd += 64) {
             const int q1 = poff[nd] + 1, d = dep[nd];
             if (d == 0) continue;
             const float kq = kqd[nd];
@@ -111,7 +112,6 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int tid, int lane,
         }
         return;
     }
-    if (w != 0) return;
     int r_lv = lvn[1] - lvn[0];  // level 0: one record per root
     for (int lv = 1; lv <= dmax; ++lv) {
         const int nrec_lv = (lvn[lv + 1] - lvn[lv]) * (lv + 1);
@@ -190,6 +190,81 @@ __device__ __forceinline__ void tree_apply(int n, int i, int half, const int *po
         }
         bank_u0[int64_t(nd) * 128 + i] = u;
         out0[int64_t(nd) * out_stride + i] = o;
+    }
+}
+
+// Dense rows of Y and Z for the matrix-core u/o pass, on wave 0 after tree_inverse (whose records
+// it reads): Yd[m][k] = Y[m][k] on m's ancestor records, 1 on the diagonal and 0 elsewhere; Zd
+// likewise with q_m.k_m on the diagonal.  Rows are ys = round4(n) floats (16-byte aligned);
+// rows past n are left as they are, since their products are never stored.
+__device__ __forceinline__ void tree_dense(int n, int ys, int w, int lane, const int *poff,
+                                           const int *dep, const int *recM, const float *recY,
+                                           const float *recZ, const float *kqd, float *Yd,
+                                           float *Zd) {
+    if (w != 0) return;
+    for (int m = lane; m < n; m += 64) {
+        float *yr = Yd + m * ys, *zr = Zd + m * ys;
+        for (int k = 0; k < ys; k += 4) {
+            *reinterpret_cast<float4 *>(yr + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<float4 *>(zr + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        yr[m] = 1.f;
+        zr[m] = kqd[m];
+        const int q1 = poff[m] + 1, d = dep[m];
+        for (int t = 0; t < d; ++t) {
+            const int a = recM[q1 + t];
+            yr[a] = recY[q1 + t];
+            zr[a] = recZ[q1 + t];
+        }
+    }
+}
+
+// u and o of every (node, state row) on the fp32 matrix cores: U = Yd W and O = GR + Zd W over
+// the wave's state rows 32w .. 32w + 31, which makes
+//   u_n = w_n + sum_{t < d_n} Y[n][a_t] w_{a_t},  o_n = G_n r_n + (q_n.k_n) w_n + sum_t Z[n][a_t] w_{a_t}.
+// M tiles of 16 nodes, N tiles of 16 state rows, K steps of 4 nodes; ancestors precede their
+// descendants, so node tile mt needs the K steps below node 16mt + 16 only.  W row k (stride ws
+// floats) past the tree is read clamped to row n - 1, where Yd and Zd hold 0.  u goes to bank row
+// n (stride 128), o to out0 + n * out_stride.  Needs Yd, Zd, W and GR complete (a barrier after
+// tree_dense and the epilogue).
+__device__ __forceinline__ void tree_apply_mfma(int n, int ys, int w, int lane, const float *Yd,
+                                                const float *Zd, const float *Wm,
+                                                const float *GR, int ws, float *bank_u0,
+                                                float *out0, int64_t out_stride) {
+    const int lr = lane & 15, lg = lane >> 4;
+    const int MT = (n + 15) >> 4, KT = (n + 3) >> 2;
+    for (int mt = 0; mt < MT; ++mt) {
+        const int ksn = min(4 * mt + 4, KT);
+        const float *ya = Yd + (16 * mt + lr) * ys + lg, *za = Zd + (16 * mt + lr) * ys + lg;
+        floatx4 au[2], ao[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int i = 32 * w + 16 * nt + lr;
+            au[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ao[nt][r] = GR[min(16 * mt + 4 * lg + r, n - 1) * ws + i];
+        }
+        for (int ks = 0; ks < ksn; ++ks) {
+            const float yv = ya[4 * ks], zv = za[4 * ks];
+            const float *wr = Wm + min(4 * ks + lg, n - 1) * ws + 32 * w + lr;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const float b = wr[16 * nt];
+                au[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(yv, b, au[nt], 0, 0, 0);
+                ao[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv, b, ao[nt], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int nd = 16 * mt + 4 * lg + r;
+            if (nd >= n) break;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int i = 32 * w + 16 * nt + lr;
+                bank_u0[int64_t(nd) * 128 + i] = au[nt][r];
+                out0[int64_t(nd) * out_stride + i] = ao[nt][r];
+            }
+        }
     }
 }
 
