@@ -147,52 +147,6 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int tid, int lane,
     }
 }
 
-// u_n = w_n + sum_{t < d_n} Y[n][a_t] w_{a_t} and o_n = G_n r_n + (q_n.k_n) w_n +
-// sum_t Z[n][a_t] w_{a_t} for state row i = 64 (wave & 1) + lane of nodes half, half + 2, ...
-// A node's records are read once across the wave (lane j takes record j) and handed to every
-// lane with readlane, so each term costs one LDS read of w.  W and GR rows have stride ws floats;
-// u goes to bank row n (stride 128), o to out0 + n * out_stride.
-__device__ __forceinline__ void tree_apply(int n, int i, int half, const int *poff,
-                                           const int *dep, const int *recM, const float *recY,
-                                           const float *recZ, const float *kqd, const float *Wm,
-                                           const float *GR, int ws, float *bank_u0,
-                                           float *out0, int64_t out_stride) {
-    const int lane = int(__lane_id());
-    for (int nd = half; nd < n; nd += 2) {
-        const int q1 = poff[nd] + 1, d = dep[nd];
-        const float wn = Wm[nd * ws + i];
-        float u = wn, o = fmaf(kqd[nd], wn, GR[nd * ws + i]);
-        for (int c0 = 0; c0 < d; c0 += 64) {
-            const int cnt = min(d - c0, 64);
-            const int j = q1 + c0 + min(lane, cnt - 1);
-            const int mj = recM[j];
-            const float yj = recY[j], zj = recZ[j];
-            int t = 0;
-            for (; t + 4 <= cnt; t += 4) {
-                float x[4], yv[4], zv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = Wm[__builtin_amdgcn_readlane(mj, t + e) * ws + i];
-                    yv[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(yj), t + e));
-                    zv[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), t + e));
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    u = fmaf(yv[e], x[e], u);
-                    o = fmaf(zv[e], x[e], o);
-                }
-            }
-            for (; t < cnt; ++t) {
-                const float x = Wm[__builtin_amdgcn_readlane(mj, t) * ws + i];
-                u = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(yj), t)), x, u);
-                o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), t)), x, o);
-            }
-        }
-        bank_u0[int64_t(nd) * 128 + i] = u;
-        out0[int64_t(nd) * out_stride + i] = o;
-    }
-}
-
 // Dense rows of Y and Z for the matrix-core u/o pass, on wave 0 after tree_inverse (whose records
 // it reads): Yd[m][k] = Y[m][k] on m's ancestor records, 1 on the diagonal and 0 elsewhere; Zd
 // likewise with q_m.k_m on the diagonal.  Rows are ys = round4(n) floats (16-byte aligned);

@@ -56,7 +56,11 @@ struct UtLayout5 {
         lv64 = round_up(size_t(nlv), 64);
         rec64 = round_up(size_t(nrec), 64);
         in = 0;
-        bg = in + round_up(size_t(n) * CPN, 64) * 16;  // beta | gate  [n64] x u32
+        // node rows; after the S0 epilogue, the dense Y and Z rows of the u/o pass (round16(n)
+        // rows of round4(n) floats each)
+        const size_t rows = round_up(size_t(n) * CPN, 64) * 16;
+        const size_t dense = 2 * round_up(size_t(n), 16) * round_up(size_t(n), 4) * 4;
+        bg = in + (rows > dense ? rows : dense);  // beta | gate  [n64] x u32
         pd = bg + 2 * n64 * 4;                         // parent | depth [n64] int
         work = pd + 2 * n64 * 4;                       // W [n][WS] | GR [n][WS], after the fold
         const size_t fk = round_up(size_t(nf) * CPR, 64) * 16;
@@ -117,6 +121,10 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     const int layer = P.layer_begin + un.layer_rel, seq = un.seq, h = un.h;
     const int seq_off = P.img[P.off_seq + seq];
     const int n = P.img[P.off_seq + seq + 1] - seq_off;
+    // dense Y and Z rows of the u/o pass, over the node rows once the epilogue is done
+    const int ys = (n + 3) & ~3;
+    float *Yd = reinterpret_cast<float *>(lds + lay.in);
+    float *Zd = Yd + ((n + 15) & ~15) * ys;
     // pending counts come from the commit call, which bounds them by the bank rows; the clamp
     // keeps a corrupted count from reading past the bank.
     const int role = P.role[seq], L = min(max(P.pending[seq], 0), P.max_nodes);
@@ -327,8 +335,8 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
     __syncthreads();  // fold rows are dead: their LDS becomes W and GR; pair terms are done
 
-    // Y = T^-1 and Z = C' Y on the records (every wave; one lane per node up to depth 12); read
-    // only after the barrier that ends the S0 products.
+    // Y = T^-1 and Z = C' Y on the records (wave 0; one lane per node up to depth 12); their
+    // dense rows are formed after the S0 epilogue.
     tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
                  tid, lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kq, recY, recZ);
 
@@ -389,9 +397,10 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
-    tree_apply(n, 64 * (w & 1) + int(__lane_id()), w >> 1, poff, dep, recM, recY, recZ, kq, Wm, GR,
-               LY::WS, P.bank_u[role ^ 1] + row0_bank * D, P.out + node_row0 * D,
-               int64_t(P.H) * D);
+    tree_dense(n, ys, w, lane, poff, dep, recM, recY, recZ, kq, Yd, Zd);  // over the node rows
+    __syncthreads();
+    tree_apply_mfma(n, ys, w, lane, Yd, Zd, Wm, GR, LY::WS, P.bank_u[role ^ 1] + row0_bank * D,
+                    P.out + node_row0 * D, int64_t(P.H) * D);
 }
 
 gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int nrec_max, int nlv_max,
