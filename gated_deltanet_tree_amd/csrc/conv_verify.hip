@@ -657,8 +657,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     // Y = T^-1 and Z = C' Y on the records and their dense rows (over the dead fold rows), on
     // wave 0 while the other waves finish their epilogue.
     tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
-                 tid, lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ);
-    tree_dense(n, ys, w, lane, poff, dep, recM, recY, recZ, kqd, Yd, Zd);
+                 lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ, Yd, Zd, ys);
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---

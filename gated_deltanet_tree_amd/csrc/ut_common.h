@@ -45,23 +45,39 @@ __device__ __forceinline__ UtUnit ut_unit(const VerifyParams &P) {
     return u;
 }
 
+// Row m of the dense Y and Z (ys floats each, 16-byte aligned): zeros, then 1 and q_m.k_m on the
+// diagonal; the ancestor entries are written after.
+__device__ __forceinline__ void dense_row_init(float *yr, float *zr, int ys, int m, float kq) {
+    for (int k = 0; k < ys; k += 4) {
+        *reinterpret_cast<float4 *>(yr + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(zr + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    yr[m] = 1.f;
+    zr[m] = kq;
+}
+
 // Rows n of Y = T^-1 and Z = C' T^-1 from n's own root path: Y T = I and Z T = C' restricted to
 // the ancestor relation give, for the ancestor a_t at distance t + 1 (record q1 + t),
 //   y_t = -(T[n][a_t] + sum_{s<t} y_s T[a_s][a_t])
 //   z_t = C'[n][a_t] - ((q_n.k_n) T[n][a_t] + sum_{s<t} z_s T[a_s][a_t])
 // where T[a_s][a_t] is record rp_s + t - s of a_s's block (rp_s = its start).  Every read is
-// independent of the results, so a lane needs two rounds of loads and then only FMAs.  YD bounds
-// the tree's depth; terms past the node's depth d are computed and dropped.  Their inner reads
-// (records bs_s + t with bs_s = rp_s - s, a compile-time offset from one base per s) may run up
-// to YD - 2 records past the node's block: into the next node's records or the table after recC,
-// never past the tables, and only into dropped terms.
+// independent of the results, so a lane needs two rounds of loads and then only FMAs; y_t and z_t
+// go to column a_t of the node's dense rows yr, zr.  YD bounds the tree's depth; terms past the
+// node's depth d are computed and dropped.  Their inner reads (records bs_s + t with
+// bs_s = rp_s - s, a compile-time offset from one base per s) may run up to YD - 2 records past
+// the node's block: into the next node's records or the table after recC, never past the tables,
+// and only into dropped terms.
 template <int YD>
 __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *recC,
-                                        const float *recQ, const int *recP, float *recY,
-                                        float *recZ) {
+                                        const float *recQ, const int *recP, const int *recM,
+                                        float *yr, float *zr) {
     const float *tb[YD];  // recC + rp_s - s
+    int am[YD];           // a_t
 #pragma unroll
-    for (int s = 0; s < YD; ++s) tb[s] = recC + recP[q1 + min(s, d - 1)] - s;
+    for (int s = 0; s < YD; ++s) {
+        tb[s] = recC + recP[q1 + min(s, d - 1)] - s;
+        am[s] = recM[q1 + min(s, d - 1)];
+    }
     float y[YD], z[YD];
 #pragma unroll
     for (int t = 0; t < YD; ++t) {
@@ -77,38 +93,44 @@ __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *re
         y[t] = -ya;
         z[t] = recQ[q1 + tc] - za;
         if (t < d) {
-            recY[q1 + t] = y[t];
-            recZ[q1 + t] = z[t];
+            yr[am[t]] = y[t];
+            zr[am[t]] = z[t];
         }
     }
 }
 
-// Y = T^-1 and Z = C' Y on the tree's records (record (n, t) = ancestor a_t of n at distance
-// t + 1, at q1 + t with q1 = poff[n] + 1; recP = block start of the record's node, recT = t,
-// -1 on a node's own record), all on wave 0.  Trees up to depth 12: one lane per node
-// (yz_rows).  Deeper trees: level by level with
+// Y = T^-1 and Z = C' Y of the tree (record (n, t) = ancestor a_t of n at distance t + 1, at
+// q1 + t with q1 = poff[n] + 1; recP = block start of the record's node, recT = t, -1 on a node's
+// own record), all on wave 0, as dense rows for the matrix-core u/o pass: Yd[m][k] = Y[m][k] on
+// m's ancestors, 1 on the diagonal and 0 elsewhere; Zd likewise with q_m.k_m on the diagonal.
+// Rows are ys = round4(n) floats; rows past n are left as they are (their products are never
+// stored).  Trees up to depth 12: one lane per node (yz_rows).  Deeper trees: level by level on
+// the records (recY, recZ) with
 //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
 //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
 // (level lv's blocks of lv + 1 records are contiguous from record r_lv; every term read belongs
-// to a shallower level).  Y and Z of a node with itself are 1 and q_n.k_n and are not stored.
-// Needs a barrier before the results are read by other waves.
-__device__ __forceinline__ void tree_inverse(int n, int dmax, int tid, int lane, int w,
-                                             const int *poff, const int *dep, const int *lvn,
-                                             const int *recM, const int *recP, const int *recT,
+// to a shallower level), then spread into the dense rows.  Needs a barrier before the results are
+// read by other waves.
+__device__ __forceinline__ void tree_inverse(int n, int dmax, int lane, int w, const int *poff,
+                                             const int *dep, const int *lvn, const int *recM,
+                                             const int *recP, const int *recT,
                                              const float *recC, const float *recQ,
-                                             const float *kqd, float *recY, float *recZ) {
+                                             const float *kqd, float *recY, float *recZ,
+                                             float *Yd, float *Zd, int ys) {
     if (w != 0) return;
     if (dmax <= 12) {
         for (int nd = lane; nd < n; nd += 64) {
             const int q1 = poff[nd] + 1, d = dep[nd];
-            if (d == 0) continue;
             const float kq = kqd[nd];
+            float *yr = Yd + nd * ys, *zr = Zd + nd * ys;
+            dense_row_init(yr, zr, ys, nd, kq);
+            if (d == 0) continue;
             if (dmax <= 4)
-                yz_rows<4>(q1, d, kq, recC, recQ, recP, recY, recZ);
+                yz_rows<4>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
             else if (dmax <= 8)
-                yz_rows<8>(q1, d, kq, recC, recQ, recP, recY, recZ);
+                yz_rows<8>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
             else
-                yz_rows<12>(q1, d, kq, recC, recQ, recP, recY, recZ);
+                yz_rows<12>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
         }
         return;
     }
@@ -119,7 +141,7 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int tid, int lane,
             const int q = r_lv + it, t = recT[q];
             if (t < 0) continue;
             const int q1 = q - t;
-            float ys = recC[q], zs = recQ[q];
+            float ya = recC[q], za = recQ[q];
             for (int s0 = 0; s0 < t; s0 += 4) {  // four terms with independent reads
                 int sp[4];
                 float cc[4], cq[4], yv[4];
@@ -135,40 +157,23 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int tid, int lane,
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (s0 + j >= t) break;
-                    ys = fmaf(cc[j], yv[j], ys);
-                    zs = fmaf(cq[j], yv[j], zs);
+                    ya = fmaf(cc[j], yv[j], ya);
+                    za = fmaf(cq[j], yv[j], za);
                 }
             }
-            recY[q] = -ys;
-            recZ[q] = fmaf(kqd[recM[q1 - 1]], -ys, zs);
+            recY[q] = -ya;
+            recZ[q] = fmaf(kqd[recM[q1 - 1]], -ya, za);
         }
         r_lv += nrec_lv;
         wave_order();
     }
-}
-
-// Dense rows of Y and Z for the matrix-core u/o pass, on wave 0 after tree_inverse (whose records
-// it reads): Yd[m][k] = Y[m][k] on m's ancestor records, 1 on the diagonal and 0 elsewhere; Zd
-// likewise with q_m.k_m on the diagonal.  Rows are ys = round4(n) floats (16-byte aligned);
-// rows past n are left as they are, since their products are never stored.
-__device__ __forceinline__ void tree_dense(int n, int ys, int w, int lane, const int *poff,
-                                           const int *dep, const int *recM, const float *recY,
-                                           const float *recZ, const float *kqd, float *Yd,
-                                           float *Zd) {
-    if (w != 0) return;
     for (int m = lane; m < n; m += 64) {
         float *yr = Yd + m * ys, *zr = Zd + m * ys;
-        for (int k = 0; k < ys; k += 4) {
-            *reinterpret_cast<float4 *>(yr + k) = make_float4(0.f, 0.f, 0.f, 0.f);
-            *reinterpret_cast<float4 *>(zr + k) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        yr[m] = 1.f;
-        zr[m] = kqd[m];
+        dense_row_init(yr, zr, ys, m, kqd[m]);
         const int q1 = poff[m] + 1, d = dep[m];
         for (int t = 0; t < d; ++t) {
-            const int a = recM[q1 + t];
-            yr[a] = recY[q1 + t];
-            zr[a] = recZ[q1 + t];
+            yr[recM[q1 + t]] = recY[q1 + t];
+            zr[recM[q1 + t]] = recZ[q1 + t];
         }
     }
 }
@@ -180,7 +185,7 @@ __device__ __forceinline__ void tree_dense(int n, int ys, int w, int lane, const
 // descendants, so node tile mt needs the K steps below node 16mt + 16 only.  W row k (stride ws
 // floats) past the tree is read clamped to row n - 1, where Yd and Zd hold 0.  u goes to bank row
 // n (stride 128), o to out0 + n * out_stride.  Needs Yd, Zd, W and GR complete (a barrier after
-// tree_dense and the epilogue).
+// tree_inverse and the epilogue).
 __device__ __forceinline__ void tree_apply_mfma(int n, int ys, int w, int lane, const float *Yd,
                                                 const float *Zd, const float *Wm,
                                                 const float *GR, int ws, float *bank_u0,

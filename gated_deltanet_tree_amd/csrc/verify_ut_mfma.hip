@@ -335,10 +335,6 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
     __syncthreads();  // fold rows are dead: their LDS becomes W and GR; pair terms are done
 
-    // Y = T^-1 and Z = C' Y on the records (wave 0; one lane per node up to depth 12); their
-    // dense rows are formed after the S0 epilogue.
-    tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
-                 tid, lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kq, recY, recZ);
 
     // ---- 4. p_n = S0 k_n, r_n = S0 q_n on the matrix cores; w_n and G_n r_n to LDS -------
     for (int jt0 = 0; jt0 < JT; jt0 += JC) {
@@ -397,7 +393,10 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
-    tree_dense(n, ys, w, lane, poff, dep, recM, recY, recZ, kq, Yd, Zd);  // over the node rows
+    // Y = T^-1 and Z = C' Y as dense rows over the consumed node rows (wave 0; one lane per node
+    // up to depth 12)
+    tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
+                 lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kq, recY, recZ, Yd, Zd, ys);
     __syncthreads();
     tree_apply_mfma(n, ys, w, lane, Yd, Zd, Wm, GR, LY::WS, P.bank_u[role ^ 1] + row0_bank * D,
                     P.out + node_row0 * D, int64_t(P.H) * D);
