@@ -188,16 +188,6 @@ __device__ __forceinline__ float conv4(const float wt[4], float x0, float x1, fl
     return fmaf(wt[3], x0, fmaf(wt[2], a1, fmaf(wt[1], a2, wt[0] * a3)));
 }
 
-// Sum over the 64 lanes with DPP only: octets, the row of 16, then row broadcasts 15 and 31
-// (rows 1 and 3 add the row below, rows 2 and 3 add lanes 0-31); lane 63 holds the total.
-__device__ __forceinline__ float wave_total(float x) {
-    x = octet_sum(x);
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
@@ -324,6 +314,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
             pend[j][e] = L >= 3 - e ? pb[int64_t(L - 3 + e) * C] : 0.f;
         }
     }
+    // this lane's share of the pending log gates: their sum gives the fold's gate product
+    float lg_part = 0.f;
+    for (int f = lane; f < L; f += 64) lg_part += pend_lg[f];
     const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
     const uint4 wq = *reinterpret_cast<const uint4 *>(wq_src);
     const uint4 wk = *reinterpret_cast<const uint4 *>(wq_src + int64_t(HD) * 4);
@@ -538,13 +531,13 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     }
 
     // ---- 4. deferred commit: fold the pending rows, write the committed state once --------
-    // S_L = G S0 + sum_i c_i u_i k_i^T with G the product of the L pending gates and c_i that
-    // of the gates after row i: the tile is scaled once and each row costs one FMA per element.
+    // S_L = G S0 + sum_i c_i u_i k_i^T with G the product of the L pending gates (exp of the sum
+    // of their logs, loaded in phase 0) and c_i that of the gates after row i: the tile is scaled
+    // once and each row costs one FMA per element.
     // Rows run last to first, so c builds up backward (c_{L-1} = 1, c_{i-1} = c_i g_i); chunks
     // of nfc rows come last chunk first (the staged one holds rows L - min(L, nfc) .. L - 1).
     if (L > 0) {
-        float G = 1.f;
-        for (int f = 0; f < L; ++f) G *= expf(pend_lg[f]);
+        const float G = expf(wave_total(lg_part));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll

@@ -78,14 +78,15 @@ __device__ __forceinline__ float bf16_at(const char *row, int i) {
     return __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t *>(row + i * 2)) << 16);
 }
 
-// Sum over the 64 lanes of a wave; every lane gets the total.  DPP inside each row of 16
-// (lane octets, then the other octet of the row), then two cross-row exchanges.
-__device__ __forceinline__ float wave_sum(float x) {
+// Sum over the 64 lanes with DPP only: octets, the row of 16, then row broadcasts 15 and 31
+// (rows 1 and 3 add the row below, rows 2 and 3 add lanes 0-31); lane 63 holds the total, which
+// every lane receives.
+__device__ __forceinline__ float wave_total(float x) {
     x = octet_sum(x);
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // LDS accesses of one wave stay in program order across its lanes.

@@ -295,12 +295,14 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     }
 
     // ---- 3. deferred commit: fold the pending rows, write the committed state once --------
-    // S_L = G S0 + sum_f c_f u_f k_f^T with G the product of the L pending gates and c_f that of
-    // the gates after row f: the tile is scaled once, then each row costs one FMA per element.
+    // S_L = G S0 + sum_f c_f u_f k_f^T with G the product of the L pending gates (exp of the sum
+    // of their logs) and c_f that of the gates after row f: the tile is scaled once, then each
+    // row costs one FMA per element.
     // Rows run last to first so that c builds up backward (c_{L-1} = 1, c_{f-1} = c_f g_f).
     if (L > 0) {
-        float G = 1.f;
-        for (int f = 0; f < L; ++f) G *= expf(FL[f]);
+        float lg_part = 0.f;  // this lane's share of the pending log gates
+        for (int f = lane; f < L; f += 64) lg_part += FL[f];
+        const float G = expf(wave_total(lg_part));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
