@@ -66,7 +66,7 @@ struct ConvVerifyParams {
 // LDS regions for trees of at most n nodes, nrec records and nlv level entries, with nfc pending
 // rows folded per chunk.
 //   X:  the bf16 conv-input planes [v | q | k] (n rows of 256 bytes each); once the q and k rows
-//       are consumed, the pending fold rows (k | u | lg) take their place, and after the fold the
+//       are consumed, the pending fold rows (k | u | c) take their place, and after the fold the
 //       dense Y and Z rows; the v plane lives until the S0 epilogue.
 //   KQ: the fp32 k and q rows (k_n at row 2n, q_n at 2n + 1, stride KS); after the S0 products,
 //       W (rows 0 .. n-1) and G_n S0 q_n (rows n .. 2n-1) when n <= 32 (all M tiles in one
@@ -76,7 +76,7 @@ struct CvLayout {
     static constexpr int XROW = D * 2;      // bytes of one bf16 conv-input row of one block
     static constexpr int KS = D + 4;        // fp32 row stride (floats): 16 rows hit distinct banks
     static constexpr int CPR = D * 4 / 16;  // 16-byte chunks per fp32 fold row
-    size_t xv, xq, kq, fold_k, fold_u, fold_lg, wu, gr, bg, pd, plan, tabs, x0s, total;
+    size_t xv, xq, kq, fold_k, fold_u, fold_c, wu, gr, bg, pd, plan, tabs, x0s, total;
     size_t n64, lv64, rec64;
     bool alias_w;
 
@@ -114,7 +114,7 @@ struct CvLayout {
         xq = size_t(n) * XROW;
         fold_k = xq;
         fold_u = xq + fold_chunks(nfc) * 16;
-        fold_lg = fold_u + fold_chunks(nfc) * 16;
+        fold_c = fold_u + fold_chunks(nfc) * 16;
         kq = round_up(xq + fold_room(n, nf), 16);
         alias_w = n <= 32;
         size_t p = kq + rows_bytes(2 * n);
@@ -141,11 +141,25 @@ struct CvLayout {
 };
 
 // SiLU with the hardware exp2 and reciprocal (each within about an ulp).
+// Inclusive suffix sum over lanes 0-15 (lane l gets the sum of lanes l .. 15); other lanes get
+// partial sums that are not used.
+__device__ __forceinline__ float chunk_suffix_sum(float x) {
+    const int lane = int(__lane_id());
+#pragma unroll
+    for (int d = 1; d < 16; d *= 2) {
+        const float y = __shfl_down(x, d);
+        x += lane + d < 16 ? y : 0.f;
+    }
+    return x;
+}
+
 // Pending rows f0 .. f0 + cnt - 1 (cnt <= kFoldRows) go through registers into LDS: 16-byte chunk
 // c of thread t is c = t + 256 j (j < 4), row c / 64, key half (c % 64 < 32) or residual half.
-// Register loads rather than direct-to-LDS loads: an LDS read after a direct load waits for
-// every older memory operation of the wave.  Four named registers (no array), so nothing of it
-// goes to scratch.
+// With the rows, wave 0 stages each row's fold coefficient c_f = exp(sum of the log gates of the
+// pending rows after f): a suffix scan over the chunk plus fold_carry, the sum over the chunks
+// already staged (they hold later rows).  Register loads rather than direct-to-LDS loads: an LDS
+// read after a direct load waits for every older memory operation of the wave.  Four named
+// registers (no array), so nothing of it goes to scratch.
 __device__ __forceinline__ uint4 fold_chunk_load(const float *pk, const float *pu, int f0, int c) {
     const int r = f0 + (c >> 6), half = (c >> 5) & 1, idx = c & 31;
     return *reinterpret_cast<const uint4 *>((half ? pu : pk) + r * kCvD + idx * 4);
@@ -171,7 +185,12 @@ __device__ __forceinline__ void fold_chunk_store(float *fk, float *fu, int cnt, 
         fold_chunk_store(fold_k, fold_u, (cnt), tid + 256, fv1);                        \
         fold_chunk_store(fold_k, fold_u, (cnt), tid + 512, fv2);                        \
         fold_chunk_store(fold_k, fold_u, (cnt), tid + 768, fv3);                        \
-        if (tid < (cnt)) fold_lg[tid] = flv;                                            \
+        if (w == 0) {                                                                   \
+            const float v_ = lane < (cnt) ? flv : 0.f;                                  \
+            const float x_ = chunk_suffix_sum(v_);                                      \
+            if (lane < (cnt)) fold_c[lane] = expf(fold_carry + (x_ - v_));             \
+            fold_carry += __shfl(x_, 0);                                                \
+        }                                                                               \
     } while (0)
 
 __device__ __forceinline__ float silu(float y) {
@@ -209,7 +228,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     float *GR = reinterpret_cast<float *>(lds + lay.gr);
     const float *FK = reinterpret_cast<const float *>(lds + lay.fold_k);
     const float *FU = reinterpret_cast<const float *>(lds + lay.fold_u);
-    const float *FL = reinterpret_cast<const float *>(lds + lay.fold_lg);
+    const float *FC = reinterpret_cast<const float *>(lds + lay.fold_c);
     // Plan of this tree (from the schedule image): record poff[n] is n itself, poff[n] + d its
     // ancestor at distance d; recM = that node.
     int *poff = reinterpret_cast<int *>(lds + lay.plan);
@@ -255,9 +274,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     const float *pend_lg = P.bank_lg[role] + row0_bank;
     float *fold_k = reinterpret_cast<float *>(lds + lay.fold_k);
     float *fold_u = reinterpret_cast<float *>(lds + lay.fold_u);
-    float *fold_lg = reinterpret_cast<float *>(lds + lay.fold_lg);
+    float *fold_c = reinterpret_cast<float *>(lds + lay.fold_c);
     uint4 fv0, fv1, fv2, fv3;
-    float flv;
+    float flv, fold_carry = 0.f;
 
     // ---- 0. loads ------------------------------------------------------------------------
     {
@@ -532,9 +551,8 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
 
     // ---- 4. deferred commit: fold the pending rows, write the committed state once --------
     // S_L = G S0 + sum_i c_i u_i k_i^T with G the product of the L pending gates (exp of the sum
-    // of their logs, loaded in phase 0) and c_i that of the gates after row i: the tile is scaled
-    // once and each row costs one FMA per element.
-    // Rows run last to first, so c builds up backward (c_{L-1} = 1, c_{i-1} = c_i g_i); chunks
+    // of their logs, loaded in phase 0) and c_i that of the gates after row i (staged with the
+    // rows): the tile is scaled once, then the rank-L update runs on the matrix cores.  Chunks
     // of nfc rows come last chunk first (the staged one holds rows L - min(L, nfc) .. L - 1).
     if (L > 0) {
         const float G = expf(wave_total(lg_part));
@@ -545,28 +563,36 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                 s[0][mt][e] *= G;
                 s[1][mt][e] *= G;
             }
-        float c = 1.f;
         for (int hi = L; hi > 0; hi -= nfc) {
-            const int lo = max(hi - nfc, 0);
+            const int lo = max(hi - nfc, 0), cnt = hi - lo;
             if (hi < L) {  // earlier chunks (more pending rows than one chunk holds)
                 __syncthreads();
-                GDN_FOLD_LOAD(lo, hi - lo);
-                GDN_FOLD_STORE(hi - lo);
+                GDN_FOLD_LOAD(lo, cnt);
+                GDN_FOLD_STORE(cnt);
                 __syncthreads();
             }
-            for (int f = hi - 1 - lo; f >= 0; --f) {
-                const float u0 = c * FU[f * D + 32 * w + lr], u1 = c * FU[f * D + 32 * w + 16 + lr];
+            // S^T += K^T (c u)^T on the fp32 matrix cores: s[nt][mt] is the D tile of columns
+            // 16mt.. and rows 32w + 16nt..; the 4-row step from row k0 takes A[lr][lg] =
+            // k_{k0+lg}[16mt + lr] and B[lg][lr] = c_{k0+lg} u_{k0+lg}[32w + 16nt + lr].  Rows
+            // past the chunk read its last row with c = 0.
+            for (int k0 = 0; k0 < cnt; k0 += 4) {
+                const int f = k0 + lg, fr = min(f, cnt - 1);
+                const float cf = f < cnt ? FC[f] : 0.f;
+                const float b0 = cf * FU[fr * D + 32 * w + lr];
+                const float b1 = cf * FU[fr * D + 32 * w + 16 + lr];
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt) {
-                    const float4 k4 = *reinterpret_cast<const float4 *>(FK + f * D + 16 * mt + 4 * lg);
-                    const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+                    const float a = FK[fr * D + 16 * mt + lr];
+                    floatx4 t0 = {s[0][mt][0], s[0][mt][1], s[0][mt][2], s[0][mt][3]};
+                    floatx4 t1 = {s[1][mt][0], s[1][mt][1], s[1][mt][2], s[1][mt][3]};
+                    t0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b0, t0, 0, 0, 0);
+                    t1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b1, t1, 0, 0, 0);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        s[0][mt][e] = fmaf(u0, kk[e], s[0][mt][e]);
-                        s[1][mt][e] = fmaf(u1, kk[e], s[1][mt][e]);
+                        s[0][mt][e] = t0[e];
+                        s[1][mt][e] = t1[e];
                     }
                 }
-                c *= expf(FL[f]);
             }
         }
     }
