@@ -17,8 +17,9 @@
 //   T[n][a] = beta_n E(n,a) (k_n . k_a)  (a a strict ancestor; T[n][n] = 1),
 //   w_n = beta_n (v_n - G_n S0 k_n),   T u = w,
 //   o_n = G_n S0 q_n + sum_{a in A(n)} C'[n][a] u_a,  C'[n][a] = E(n,a) (q_n . k_a), C'[n][n] = q_n . k_n.
-// The system is not solved level by level here: one wave forms Y = T^-1 and Z = C' Y on the
-// tree's records, after which every (node, state row) is independent:
+// The system is not solved level by level here: one wave forms Y = T^-1 and Z = C' Y as dense
+// rows, after which every (node, state row) is independent and all of them are two small
+// matrix products:
 //   u_n = sum_{a in A(n)} Y[n][a] w_a,   o_n = G_n S0 q_n + sum_{a in A(n)} Z[n][a] w_a.
 //
 // One workgroup of 4 waves per (layer, sequence, head):
@@ -32,10 +33,10 @@
 //      length; fp32 rows to LDS; raw conv inputs and keys banked;
 //   3. the pending fold rows start loading into the consumed q and k conv-input planes; pair
 //      products [k; q] K^T on the matrix cores;
-//   4. the pending rows are folded into the tile and the committed state is written back once;
-//      wave 0 forms Y and Z level by level; [k; q] S0^T on the matrix cores; the epilogue
-//      evaluates the v channels (conv and SiLU) and writes w_n and G_n S0 q_n;
-//   5. u and o of every (node, row); u banked, o stored.
+//   4. the pending rows are folded into the tile on the matrix cores and the committed state is
+//      written back once; [k; q] S0^T on the matrix cores; the epilogue evaluates the v channels
+//      (conv and SiLU) and writes w_n and G_n S0 q_n; wave 0 forms Y and Z as dense rows;
+//   5. U = Y W and O = G r + Z W on the matrix cores; u banked, o stored.
 // Matrix-core layout: wave w owns state rows [32w, 32w+32), lane l holds rows 32w + 16nt + (l % 16)
 // and columns 16mt + 4(l/16) + e.  q and k are fp32 here, so the products run on the fp32 matrix
 // cores (v_mfma_f32_16x16x4f32): for the 4-column step {16mt + 4(l/16) + e}, lane l already holds

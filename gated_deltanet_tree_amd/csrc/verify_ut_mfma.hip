@@ -16,11 +16,11 @@
 //      records per node, itself then its ancestors nearest first) gets the gate products E
 //      and G_n; keys and log-gates are banked;
 //   2. the pair products [k; q] K^T run on the matrix cores and give T and C on the records;
-//   3. the pending rows are folded, S <- exp(lg) S + u k^T, and S is written back once;
+//   3. the pending rows are folded in closed form, S = G S0 + sum_f c_f u_f k_f^T (G the product
+//      of the pending gates, c_f that of the gates after row f), and S is written back once;
 //   4. [k; q] S0^T runs on the matrix cores; its epilogue writes w_n and G_n r_n to LDS;
-//   5. T U = W is solved level by level, o_n formed in the same pass over each node's
-//      ancestors: the (node, row) items of one level are independent and u overwrites w in
-//      place; u is banked.
+//   5. wave 0 forms Y = T^-1 and Z = C' Y as dense rows over the consumed node rows, and
+//      U = Y W, O = G r + Z W run on the matrix cores; u is banked, o stored.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16, fp32 accumulate): wave w owns state rows
 // [32w, 32w+32); lane l holds rows 32w + 16nt + (l % 16) and columns 16mt + 4(l / 16) + e
