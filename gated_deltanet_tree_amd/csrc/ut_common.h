@@ -118,7 +118,7 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int lane, int w, c
                                              const float *kqd, float *recY, float *recZ,
                                              float *Yd, float *Zd, int ys) {
     if (w != 0) return;
-    if (dmax <= 12) {
+    if (dmax <= 16) {
         for (int nd = lane; nd < n; nd += 64) {
             const int q1 = poff[nd] + 1, d = dep[nd];
             const float kq = kqd[nd];
@@ -129,8 +129,10 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int lane, int w, c
                 yz_rows<4>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
             else if (dmax <= 8)
                 yz_rows<8>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
-            else
+            else if (dmax <= 12)
                 yz_rows<12>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
+            else
+                yz_rows<16>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
         }
         return;
     }

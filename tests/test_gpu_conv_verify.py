@@ -198,6 +198,17 @@ def test_forty_node_tree(torch_cuda):
     _steps(torch_cuda, [tree, synth.TINY_TREE], H=1, n_layers=1, steps_paths=steps, cfg_id=13)
 
 
+def test_deep_chain_level_inverse(torch_cuda):
+    """A 24-node chain (depth 23: past the per-lane register form of the tree inverse, which
+    stops at depth 16, so the level-by-level form runs) next to a branched tree."""
+    rng = synth.rng_for(16, 0, 0, 0, "tree")
+    tree = synth.make_tree(rng, 30, 4, 10)
+    chain = np.arange(-1, 23, dtype=np.int32)
+    steps = [[list(range(20)), synth.deepest_leaf_path(tree)],
+             [list(range(24)), [0]]]
+    _steps(torch_cuda, [chain, tree], H=1, n_layers=1, steps_paths=steps, cfg_id=16)
+
+
 def test_batched_workload_sampled(torch_cuda):
     """The batched workload's trees (32 sequences, 22 nodes, top-4, depth <= 12) at 48 heads,
     one layer, two steps (the second folds the first's accepted paths); every head of sampled

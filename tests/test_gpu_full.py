@@ -265,6 +265,17 @@ def test_ut_largest_fitting_tree_64_nodes_d128(torch_cuda):
     _edge_run(torch_cuda, trees, 2, 128, 16, steps, 96, dtype="bf16", mode="ut")
 
 
+def test_ut_deep_chain_level_inverse(torch_cuda):
+    """A 24-node chain (depth 23: past the per-lane register form of the tree inverse, which
+    stops at depth 16, so the level-by-level form runs) next to a branched tree, d = 128,
+    bf16."""
+    rng = np.random.default_rng(13)
+    trees = [np.arange(-1, 23, dtype=np.int32), synth.make_tree(rng, 30, 4, 10)]
+    steps = [[np.arange(20), synth.random_path(rng, trees[1], 6)],
+             [np.arange(24), synth.random_path(rng, trees[1], 3)]]
+    _edge_run(torch_cuda, trees, 2, 128, 16, steps, 97, dtype="bf16", mode="ut")
+
+
 def test_empty_batch_is_a_no_op(torch_cuda):
     import ctypes
     image = binding.hld_schedule([])
