@@ -104,7 +104,7 @@ __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *re
 // own record), all on wave 0, as dense rows for the matrix-core u/o pass: Yd[m][k] = Y[m][k] on
 // m's ancestors, 1 on the diagonal and 0 elsewhere; Zd likewise with q_m.k_m on the diagonal.
 // Rows are ys = round4(n) floats; rows past n are left as they are (their products are never
-// stored).  Trees up to depth 12: one lane per node (yz_rows).  Deeper trees: level by level on
+// stored).  Trees up to depth 16: one lane per node (yz_rows).  Deeper trees: level by level on
 // the records (recY, recZ) with
 //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
 //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]

@@ -396,7 +396,7 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
     // Y = T^-1 and Z = C' Y as dense rows over the consumed node rows (wave 0; one lane per node
-    // up to depth 12)
+    // up to depth 16)
     tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
                  lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kq, recY, recZ, Yd, Zd, ys);
     __syncthreads();
