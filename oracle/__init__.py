@@ -21,9 +21,12 @@ Modules:
   conv   -- tree-aware causal depthwise conv and the committed conv window.
   hld    -- heavy-light chain schedule (iterative and recursive formulations).
   banks  -- factor-bank compaction and role/pending bookkeeping.
+  prologue -- conv -> SiLU -> unit-length q/k prologue feeding the tree verify (the reading
+            of the q/k/v wiring the pages leave open, stated in its header).
+  ddtree -- best-first draft-tree builder with budget, tau pruning and chain pre-seed.
 
 Every function is pinned by tests/test_oracle_*.py against closed forms, invariants,
-brute force or the hand-worked schedule examples under tests/golden/. None is "parity
-unpinned".
+brute force, library routines of the plain definitions, or the hand-worked schedule and
+draft-tree examples under tests/golden/. None is "parity unpinned".
 """
 from . import banks, conv, gdn, hld  # noqa: F401
