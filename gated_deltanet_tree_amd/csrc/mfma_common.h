@@ -34,44 +34,12 @@ __device__ __forceinline__ void split3(const float *x, bf16x8 &hi, bf16x8 &mid, 
     lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// Exact split with round-to-nearest-even terms (the hardware conversion): hi = rne(x),
-// mid = rne(x - hi), lo = x - hi - mid.  x - hi carries at most 16 significant bits and the
-// last remainder at most 8, so every step is exact; terms shrink by 2^-9 and 2^-17 relative
-// to x, which lets a product of two split operands drop its mid*lo and lo*lo terms at the
-// fp32 rounding level.
-__device__ __forceinline__ void split3_rne(const float *x, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
-    u32x4 h, m, l;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float a = x[2 * p], b = x[2 * p + 1];
-        const uint32_t hw = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
-        const float ra = a - __uint_as_float(hw << 16), rb = b - __uint_as_float(hw & 0xFFFF0000u);
-        const uint32_t mw = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)ra, (__bf16)rb});
-        const float sa = ra - __uint_as_float(mw << 16), sb = rb - __uint_as_float(mw & 0xFFFF0000u);
-        h[p] = hw;
-        m[p] = mw;
-        l[p] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sa, (__bf16)sb});
-    }
-    hi = __builtin_bit_cast(bf16x8, h);
-    mid = __builtin_bit_cast(bf16x8, m);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
-
 // Operand of one 32-wide k-step from a bf16 row in LDS: elements c0 .. c0+3 and c0+16 .. c0+19.
 __device__ __forceinline__ bf16x8 row_operand(const char *row, int c0) {
     const uint2 a = *reinterpret_cast<const uint2 *>(row + c0 * 2);
     const uint2 b = *reinterpret_cast<const uint2 *>(row + (c0 + 16) * 2);
     const u32x4 v = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, v);
-}
-
-// The same eight elements from an fp32 row in LDS, as an exact three-term split.
-__device__ __forceinline__ void row_operand_split(const float *row, int c0, bf16x8 &hi,
-                                                  bf16x8 &mid, bf16x8 &lo) {
-    const float4 a = *reinterpret_cast<const float4 *>(row + c0);
-    const float4 b = *reinterpret_cast<const float4 *>(row + c0 + 16);
-    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    split3_rne(x, hi, mid, lo);
 }
 
 __device__ __forceinline__ float bf16_at(const char *row, int i) {
