@@ -4,8 +4,9 @@ C ABI, on seeded bf16 inputs: per-node outputs, banked keys, residual vectors, l
 inputs, the folded conv window and the committed state, over several verify + commit steps and
 a flush.  Cases: ragged small trees (a 7-node tree, an 8-node chain, single nodes), a 16-node
 chain whose pending path outgrows one LDS fold chunk, a 40-node tree (the layout without the
-W/KQ overlap), and the batched workload (32 sequences x 22-node trees x 48 heads) on sampled
-sequences.
+W/KQ overlap), a 48-node top-8 tree of depth 16 close to the LDS budget, a 24-node chain (the
+level-by-level inverse), and the batched workload (32 sequences x 22-node trees x 48 heads) on
+sampled sequences.
 
 Tolerances: o per (node, head) vector <= 1e-3 normwise max relative error; committed state <= 1e-5
 relative Frobenius per (layer, seq, head) tile; banked u <= 1e-4 relative 2-norm per row; ln g
@@ -207,6 +208,17 @@ def test_deep_chain_level_inverse(torch_cuda):
     steps = [[list(range(20)), synth.deepest_leaf_path(tree)],
              [list(range(24)), [0]]]
     _steps(torch_cuda, [chain, tree], H=1, n_layers=1, steps_paths=steps, cfg_id=16)
+
+
+def test_largest_fitting_tree(torch_cuda):
+    """A 48-node top-8 tree of depth <= 16: close to the fused kernel's LDS budget (W and GR in
+    their own regions, two passes of S0 products, the depth-16 per-lane inverse), next to a
+    7-node tree."""
+    rng = synth.rng_for(17, 0, 0, 0, "tree")
+    tree = synth.make_tree(rng, 48, 8, 16)
+    steps = [[synth.random_path(rng, tree, 11), [0, 1, 3]],
+             [synth.deepest_leaf_path(tree), [0, 2, 5]]]
+    _steps(torch_cuda, [tree, synth.TINY_TREE], H=1, n_layers=1, steps_paths=steps, cfg_id=17)
 
 
 def test_batched_workload_sampled(torch_cuda):
