@@ -69,17 +69,16 @@ struct ConvVerifyParams {
 //   X:  the bf16 conv-input planes [v | q | k] (n rows of 256 bytes each); once the q and k rows
 //       are consumed, the pending fold rows (k | u | c) take their place, and after the fold the
 //       dense Y and Z rows; the v plane lives until the S0 epilogue.
-//   KQ: the fp32 k and q rows (k_n at row 2n, q_n at 2n + 1, stride KS); after the S0 products,
-//       W (rows 0 .. n-1) and G_n S0 q_n (rows n .. 2n-1) when n <= 32 (all M tiles in one
-//       pass), otherwise W and GR get their own regions.
+//   KQ: the fp32 k and q rows (k_n at row 2n, q_n at 2n + 1, stride KS); each pass of S0
+//       products consumes the rows of its nodes, after which w_n takes row 2n and G_n S0 q_n
+//       row 2n + 1.
 struct CvLayout {
     static constexpr int D = kCvD;
     static constexpr int XROW = D * 2;      // bytes of one bf16 conv-input row of one block
     static constexpr int KS = D + 4;        // fp32 row stride (floats): 16 rows hit distinct banks
     static constexpr int CPR = D * 4 / 16;  // 16-byte chunks per fp32 fold row
-    size_t xv, xq, kq, fold_k, fold_u, fold_c, wu, gr, bg, pd, plan, tabs, x0s, total;
+    size_t xv, xq, kq, fold_k, fold_u, fold_c, bg, pd, plan, tabs, x0s, total;
     size_t n64, lv64, rec64;
-    bool alias_w;
 
     __host__ __device__ static size_t fold_chunks(int r) { return round_up(size_t(r) * CPR, 64); }
     __host__ __device__ static size_t fold_bytes(int r) {
@@ -117,16 +116,7 @@ struct CvLayout {
         fold_u = xq + fold_chunks(nfc) * 16;
         fold_c = fold_u + fold_chunks(nfc) * 16;
         kq = round_up(xq + fold_room(n, nf), 16);
-        alias_w = n <= 32;
         size_t p = kq + rows_bytes(2 * n);
-        if (alias_w) {
-            wu = kq;
-            gr = kq + rows_bytes(n);
-        } else {
-            wu = p;
-            gr = p + rows_bytes(n);
-            p += 2 * rows_bytes(n);
-        }
         bg = p;                   // beta | gate [n64] u32 slots
         p += 2 * n64 * 4;
         pd = p;                   // parent | depth [n64] int (global parent ids)
@@ -225,8 +215,8 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     const int *par = reinterpret_cast<const int *>(lds + lay.pd);
     const int *dep = par + n64;
     float *KQ = reinterpret_cast<float *>(lds + lay.kq);
-    float *Wm = reinterpret_cast<float *>(lds + lay.wu);
-    float *GR = reinterpret_cast<float *>(lds + lay.gr);
+    float *Wm = KQ, *GR = KQ + LY::KS;  // row n at 2 n KS: over k_n and q_n once consumed
+    constexpr int WS = 2 * LY::KS;      // row stride of W and GR
     const float *FK = reinterpret_cast<const float *>(lds + lay.fold_k);
     const float *FU = reinterpret_cast<const float *>(lds + lay.fold_u);
     const float *FC = reinterpret_cast<const float *>(lds + lay.fold_c);
@@ -638,9 +628,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                                 av[e], s[nt][mt][e], acc[jc][nt], 0, 0, 0);
                 }
             }
-            // When W and GR take KQ's place, every wave must be done reading KQ; the fold rows
-            // are dead past this point too.
-            if (jt0 == 0) __syncthreads();
+            // W and GR of this pass's nodes take their k and q rows: every wave must be done
+            // reading them.  The fold rows are dead past the first pass too.
+            __syncthreads();
             // Lane (lr, lg) holds rows 4lg + r of each M tile: p (even r) and r (odd r) of node
             // 8jt + 2lg + r/2 at state row 32w + 16nt + lr.
 #pragma unroll
@@ -667,8 +657,8 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
                             bf16_at(XV + size_t(an.y) * LY::XROW, i),
                             bf16_at(XV + size_t(an.z) * LY::XROW, i), dt, cv[0], cv[3 * D],
                             cv[6 * D]));
-                        Wm[nd * LY::KS + i] = beta * fmaf(-G, acc[jc][nt][2 * j], v);
-                        GR[nd * LY::KS + i] = G * acc[jc][nt][2 * j + 1];
+                        Wm[nd * WS + i] = beta * fmaf(-G, acc[jc][nt][2 * j], v);
+                        GR[nd * WS + i] = G * acc[jc][nt][2 * j + 1];
                     }
                 }
             }
@@ -681,7 +671,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
-    tree_apply_mfma(n, ys, w, lane, Yd, Zd, Wm, GR, LY::KS, P.bank_u[role ^ 1] + row0_bank * D,
+    tree_apply_mfma(n, ys, w, lane, Yd, Zd, Wm, GR, WS, P.bank_u[role ^ 1] + row0_bank * D,
                     P.out + node_row0 * D, int64_t(P.H) * D);
 }
 

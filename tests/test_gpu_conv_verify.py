@@ -3,10 +3,10 @@
 C ABI, on seeded bf16 inputs: per-node outputs, banked keys, residual vectors, log gates and conv
 inputs, the folded conv window and the committed state, over several verify + commit steps and
 a flush.  Cases: ragged small trees (a 7-node tree, an 8-node chain, single nodes), a 16-node
-chain whose pending path outgrows one LDS fold chunk, a 40-node tree (the layout without the
-W/KQ overlap), a 48-node top-8 tree of depth 16 close to the LDS budget, a 24-node chain (the
-level-by-level inverse), and the batched workload (32 sequences x 22-node trees x 48 heads) on
-sampled sequences.
+chain whose pending path outgrows one LDS fold chunk, a 40-node tree (two passes of S0
+products), a 48-node top-8 tree of depth 16, a 64-node top-8 tree next to a 16-node chain
+(the wide/deep workload's shapes), a 24-node chain (the level-by-level inverse), and the batched
+workload (32 sequences x 22-node trees x 48 heads) on sampled sequences.
 
 Tolerances: o per (node, head) vector <= 1e-3 normwise max relative error; committed state <= 1e-5
 relative Frobenius per (layer, seq, head) tile; banked u <= 1e-4 relative 2-norm per row; ln g
@@ -210,15 +210,24 @@ def test_deep_chain_level_inverse(torch_cuda):
     _steps(torch_cuda, [chain, tree], H=1, n_layers=1, steps_paths=steps, cfg_id=16)
 
 
-def test_largest_fitting_tree(torch_cuda):
-    """A 48-node top-8 tree of depth <= 16: close to the fused kernel's LDS budget (W and GR in
-    their own regions, two passes of S0 products, the depth-16 per-lane inverse), next to a
-    7-node tree."""
+def test_48_node_tree(torch_cuda):
+    """A 48-node top-8 tree of depth <= 16 (two passes of S0 products, the depth-16 per-lane
+    inverse), next to a 7-node tree."""
     rng = synth.rng_for(17, 0, 0, 0, "tree")
     tree = synth.make_tree(rng, 48, 8, 16)
     steps = [[synth.random_path(rng, tree, 11), [0, 1, 3]],
              [synth.deepest_leaf_path(tree), [0, 2, 5]]]
     _steps(torch_cuda, [tree, synth.TINY_TREE], H=1, n_layers=1, steps_paths=steps, cfg_id=17)
+
+
+def test_wide_deep_64_node_tree_and_chain(torch_cuda):
+    """The wide/deep workload's shapes: a 64-node top-8 tree of depth <= 16 (two passes of S0
+    products, each handing its nodes' k and q rows to w and G r) next to a 16-node chain."""
+    rng = synth.rng_for(18, 0, 0, 0, "tree")
+    tree, chain = synth.make_tree(rng, 64, 8, 16), np.arange(-1, 15, dtype=np.int32)
+    steps = [[synth.random_path(rng, tree, 9), list(range(12))],
+             [synth.deepest_leaf_path(tree), list(range(16))]]
+    _steps(torch_cuda, [tree, chain], H=2, n_layers=1, steps_paths=steps, cfg_id=18)
 
 
 def test_batched_workload_sampled(torch_cuda):
@@ -282,8 +291,8 @@ def test_rejects_bad_arguments(torch_cuda):
         binding.tree_conv_verify(va, ca, big, b.dev_image)
     torch_cuda.cuda.synchronize()
     assert np.array_equal(gh.to_np(b.out), before)
-    # a 64-node top-8 tree needs more LDS than one workgroup has: refused, nothing launched
-    wide = FusedRun(torch_cuda, [synth.make_tree(synth.rng_for(15, 0, 0, 1, "tree"), 64, 8, 16)],
+    # a 96-node top-8 tree needs more LDS than one workgroup has: refused, nothing launched
+    wide = FusedRun(torch_cuda, [synth.make_tree(synth.rng_for(15, 0, 0, 1, "tree"), 96, 8, 16)],
                     1, 1, cfg_id=15)
     with pytest.raises(binding.GdnError, match="LDS"):
         wide.verify(0)
