@@ -331,7 +331,7 @@ gdn_status gdn_tree_conv(const gdn_conv_args *args, const int32_t *host_image,
  * gate, x and weight; ca->channels = 3 H 128; ca's n_seqs, n_nodes, max_nodes, layer_begin and
  * n_layers equal va's; ca->role and ca->pending_len are the same device arrays as va's; x,
  * weight and bank_x 16-byte aligned; the schedule carries the tree-masked plan and the trees fit one
- * workgroup's LDS (160 KiB: about 60 nodes).
+ * workgroup's LDS (160 KiB: a 64-node top-8 tree of depth 16 takes about 144 KiB).
  * Work: one workgroup per (layer, sequence, head), 4 waves; the conv, SiLU and normalisation
  * run in its prologue, the rest as gdn_tree_verify_ut on the matrix cores.
  * ---------------------------------------------------------------------------------- */
