@@ -20,7 +20,7 @@ Workload (default): 32 sequences, each with its own seeded 22-node top-4 tree (d
 width 4 over 3*48*128 channels, accepted lengths uniform in 1..9.  Inputs are resident in HBM
 before timing starts.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--layers-per-call 1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched] [--layers-per-call 1]
 """
 from __future__ import annotations
 
@@ -215,10 +215,10 @@ def kernel_source_sha256(verify):
     return h.hexdigest()
 
 
-def measured_traffic(config, lpc, verify):
+def measured_traffic(name, lpc, verify):
     """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     or None when the kernel's sources changed since they were taken (or another workload)."""
-    if config != 3 or lpc != 1:
+    if name != "batched" or lpc != 1:
         return None
     return recorded_traffic(verify)
 
@@ -235,21 +235,22 @@ def recorded_traffic(kernel):
 
 
 def _oracle_pair(job):
-    config, seq, layer, fused = job
+    name, seq, layer, fused = job
     from gated_deltanet_tree_amd import synth, workload
     from oracle import conv as oconv
     from oracle import gdn as ogdn
     from oracle import prologue
-    c = synth.CONFIGS[config]
-    tree = synth.config_tree(config, seq)
+    c = synth.WORKLOADS[name]
+    seed = c["seed"]
+    tree = synth.workload_tree(name, seq)
     n = len(tree)
-    inp = synth.node_inputs(config, 0, layer, seq, n, c["H"], c["d"], c["dtype"])
+    inp = synth.node_inputs(seed, 0, layer, seq, n, c["H"], c["d"], c["dtype"])
     inp = {k: workload.widen(v, c["dtype"]) for k, v in inp.items()}
-    x = workload.widen(synth.conv_inputs(config, 0, layer, seq, n, c["Cch"], c["dtype"]), c["dtype"])
-    W = workload.widen(synth.conv_weight(config, layer, c["Cch"], 4, c["dtype"]), c["dtype"])
-    S0 = synth.initial_state(config, layer, seq, c["H"], c["d"]).astype(np.float64)
-    X0 = synth.initial_conv_state(config, layer, seq, c["Cch"], 4).astype(np.float64)
-    path = synth.config_path(config, 0, seq, tree)
+    x = workload.widen(synth.conv_inputs(seed, 0, layer, seq, n, c["Cch"], c["dtype"]), c["dtype"])
+    W = workload.widen(synth.conv_weight(seed, layer, c["Cch"], 4, c["dtype"]), c["dtype"])
+    S0 = synth.initial_state(seed, layer, seq, c["H"], c["d"]).astype(np.float64)
+    X0 = synth.initial_conv_state(seed, layer, seq, c["Cch"], 4).astype(np.float64)
+    path = synth.workload_path(name, 0, seq, tree)
     if fused:  # q, k, v from the conv (SiLU, unit length), then verify and commit by replay
         _, q, k, v = prologue.conv_verify(tree, S0, X0, x, W, inp["beta"], inp["gate"],
                                           c["H"], c["d"])
@@ -263,13 +264,13 @@ def _oracle_pair(job):
     return n
 
 
-def cpu_baseline(config, n_pairs, workers, fused):
+def cpu_baseline(name, n_pairs, workers, fused):
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
     from gated_deltanet_tree_amd import synth
-    c = synth.CONFIGS[config]
+    c = synth.WORKLOADS[name]
     rng = np.random.default_rng(1234)
-    jobs = [(config, int(rng.integers(c["Bs"])), int(rng.integers(c["Ly"])), fused)
+    jobs = [(name, int(rng.integers(c["Bs"])), int(rng.integers(c["Ly"])), fused)
             for _ in range(n_pairs)]
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
@@ -294,7 +295,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", default="batched",
+                    choices=["one-layer", "48-layer", "batched", "wide-deep", "chain16"])
     ap.add_argument("--layers-per-call", type=int, default=1)
     ap.add_argument("--verify", choices=["fused", "ut", "chain"], default="fused",
                     help="headline path (all are timed): fused = conv -> SiLU -> unit q/k -> "
@@ -316,7 +318,7 @@ def main(argv=None):
         return 2
 
     from gated_deltanet_tree_amd import synth, workload
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.WORKLOADS[args.workload]
     H, d, C, Ly, dtype = cfg["H"], cfg["d"], cfg["Cch"], cfg["Ly"], cfg["dtype"]
     in_bytes = 2 if dtype == "bf16" else 4
 
@@ -324,14 +326,14 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         workers = args.cpu_workers or min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(args.config, args.cpu_pairs, workers, args.verify == "fused")
+        cpu = cpu_baseline(args.workload, args.cpu_pairs, workers, args.verify == "fused")
 
     import torch
     from gated_deltanet_tree_amd import binding
     binding.lib()
     dev = torch.device("cuda:0")
 
-    trees = workload.config_trees(args.config)
+    trees = workload.workload_trees(args.workload)
     S = len(trees)
     image0 = binding.hld_schedule(trees)
     view = binding.schedule_view(image0)
@@ -341,9 +343,9 @@ def main(argv=None):
     assert Ly % lpc == 0
 
     t_gen = time.perf_counter()
-    state0, conv0 = workload.host_initial_state(args.config, range(Ly), S)
-    weights = workload._to_torch(workload.host_weights(args.config, range(Ly)), dtype, dev)
-    inp = workload.device_step_inputs(args.config, 0, trees, range(Ly), dev)
+    state0, conv0 = workload.host_initial_state(args.workload, range(Ly), S)
+    weights = workload._to_torch(workload.host_weights(args.workload, range(Ly)), dtype, dev)
+    inp = workload.device_step_inputs(args.workload, 0, trees, range(Ly), dev)
     lay = binding.alloc_layers(Ly, S, H, d, max_nodes, C, dev)
     lay.state.copy_(torch.from_numpy(state0))
     lay.conv_state.copy_(torch.from_numpy(conv0))
@@ -355,7 +357,7 @@ def main(argv=None):
     gen_s = time.perf_counter() - t_gen
 
     n_total = args.warmup + args.steps
-    all_paths = [[synth.config_path(args.config, s, b, trees[b]) for b in range(S)]
+    all_paths = [[synth.workload_path(args.workload, s, b, trees[b]) for b in range(S)]
                  for s in range(n_total)]
     vargs = [binding.verify_args(image0, lay, inp.q, inp.k, inp.v, inp.beta, inp.gate, out,
                                  workspace, layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
@@ -453,7 +455,7 @@ def main(argv=None):
         v_launch_bytes = acc["stamped_bytes"] / max(acc["verify_launches"], 1)
         calls_total = args.steps * len(vargs)
         achieved = v_launch_bytes / v_launch_s / 1e9
-        traffic_bytes = measured_traffic(args.config, lpc, verify)
+        traffic_bytes = measured_traffic(args.workload, lpc, verify)
         return {
             "value": args.steps * T * Ly / wall,
             "ms_per_step": wall * 1e3 / args.steps,
@@ -475,7 +477,7 @@ def main(argv=None):
 
     # Draft-tree builder (host): the batch's trees from seeded synthetic drafts, budget 22,
     # top-4, tau 6, chain pre-seed, 15 draft positions.
-    drafts = [synth.draft_scores(args.config, 0, b, 15, 4) for b in range(S)]
+    drafts = [synth.draft_scores(cfg["seed"], 0, b, 15, 4) for b in range(S)]
     d_lp = np.stack([x[0] for x in drafts])
     d_tok = np.stack([x[1] for x in drafts])
     binding.ddtree_build(d_lp, d_tok, None, budget=22, tau=6.0)
@@ -507,7 +509,7 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg['name']}: {S} sequences x {Ly} GDN layers x {H} heads x d{d}, "
+            "workload": f"{args.workload}: {S} sequences x {Ly} GDN layers x {H} heads x d{d}, "
                         f"{T // S if S else 0}-node trees (top-{cfg['K']}, depth<={cfg['D']}), "
                         + ("bf16 conv inputs/beta/g, q/k/v from the conv (SiLU, unit q/k), "
                            if args.verify == "fused" else "bf16 q/k/v/beta/g, ")

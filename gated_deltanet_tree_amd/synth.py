@@ -12,7 +12,8 @@ SpecLA): best-first trees of up to 22 nodes with at most K children per node, gr
 main chain (the chain pre-seed), labelled so that every parent index is lower than its child's.
 
 Every stream is a PCG64 generator seeded by
-``SeedSequence([20261202, config, step, layer, seq, stream])``.
+``SeedSequence([20261202, seed, step, layer, seq, stream])``, where ``seed`` is the workload
+preset's number (or a test's own number).
 bf16 values are produced by round-to-nearest-even from the float32 draws and are kept as
 raw ``uint16`` bit patterns; ``bf16_to_f32`` widens them exactly.
 """
@@ -26,29 +27,30 @@ STREAMS = {
     "x": 7, "weight": 8, "conv_state": 9, "path": 10, "draft": 11,
 }
 
-# Workload presets. d = head dim (d_k = d_v), H = heads, N = nodes per tree, K = top-k,
-# D = max edge depth, Bs = sequences, Ly = GDN layers, Kc = conv width, Cch = conv channels.
-CONFIGS = {
-    0: dict(name="tiny", H=1, d=16, N=None, K=None, D=None, Bs=1, Ly=1, Kc=4, Cch=16,
-            dtype="f32"),
-    1: dict(name="one-layer", H=48, d=128, N=22, K=4, D=12, Bs=1, Ly=1, Kc=4,
-            Cch=3 * 48 * 128, dtype="bf16"),
-    2: dict(name="48-layer", H=48, d=128, N=22, K=4, D=12, Bs=1, Ly=48, Kc=4,
-            Cch=3 * 48 * 128, dtype="bf16", steps=10, accept_len=6),
-    3: dict(name="batched", H=48, d=128, N=22, K=4, D=12, Bs=32, Ly=48, Kc=4,
-            Cch=3 * 48 * 128, dtype="bf16", accept_max=9),
-    4: dict(name="wide-deep", H=48, d=128, N=64, K=8, D=16, Bs=8, Ly=48, Kc=4,
-            Cch=3 * 48 * 128, dtype="bf16"),
-    5: dict(name="chain16", H=48, d=128, N=16, K=1, D=15, Bs=8, Ly=48, Kc=4,
-            Cch=3 * 48 * 128, dtype="bf16"),
+# Workload presets, by name.  d = head dim (d_k = d_v), H = heads, N = nodes per tree, K = top-k,
+# D = max edge depth, Bs = sequences, Ly = GDN layers, Kc = conv width, Cch = conv channels;
+# seed = the preset's number in every seed sequence below.
+WORKLOADS = {
+    "tiny": dict(seed=0, H=1, d=16, N=None, K=None, D=None, Bs=1, Ly=1, Kc=4, Cch=16,
+                 dtype="f32"),
+    "one-layer": dict(seed=1, H=48, d=128, N=22, K=4, D=12, Bs=1, Ly=1, Kc=4,
+                      Cch=3 * 48 * 128, dtype="bf16", accept_len=6),
+    "48-layer": dict(seed=2, H=48, d=128, N=22, K=4, D=12, Bs=1, Ly=48, Kc=4,
+                     Cch=3 * 48 * 128, dtype="bf16", steps=10, accept_len=6),
+    "batched": dict(seed=3, H=48, d=128, N=22, K=4, D=12, Bs=32, Ly=48, Kc=4,
+                    Cch=3 * 48 * 128, dtype="bf16", accept_max=9),
+    "wide-deep": dict(seed=4, H=48, d=128, N=64, K=8, D=16, Bs=8, Ly=48, Kc=4,
+                      Cch=3 * 48 * 128, dtype="bf16"),
+    "chain16": dict(seed=5, H=48, d=128, N=16, K=1, D=15, Bs=8, Ly=48, Kc=4,
+                    Cch=3 * 48 * 128, dtype="bf16"),
 }
 
 TINY_TREE = np.array([-1, 0, 0, 1, 1, 2, 3], dtype=np.int32)
 TINY_CHAIN = np.arange(-1, 7, dtype=np.int32)
 
 
-def rng_for(config: int, step: int, layer: int, seq: int, stream: str) -> np.random.Generator:
-    ss = np.random.SeedSequence([ROOT_SEED, config, step, layer, seq, STREAMS[stream]])
+def rng_for(seed: int, step: int, layer: int, seq: int, stream: str) -> np.random.Generator:
+    ss = np.random.SeedSequence([ROOT_SEED, seed, step, layer, seq, STREAMS[stream]])
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -132,35 +134,39 @@ def random_path(rng: np.random.Generator, parent: np.ndarray, length: int) -> np
     return root_path(parent, int(cands[int(rng.integers(len(cands)))]))
 
 
-def config_tree(config: int, seq: int) -> np.ndarray:
-    c = CONFIGS[config]
-    if config == 0:
+def workload_tree(name: str, seq: int) -> np.ndarray:
+    """Candidate tree of sequence `seq` of a preset (the 48-layer stack reuses the one-layer
+    workload's tree)."""
+    c = WORKLOADS[name]
+    if name == "tiny":
         return TINY_TREE.copy() if seq == 0 else TINY_CHAIN.copy()
-    tree_config = 1 if config == 2 else config
-    return make_tree(rng_for(tree_config, 0, 0, seq, "tree"), c["N"], c["K"], c["D"])
+    tree_seed = WORKLOADS["one-layer"]["seed"] if name == "48-layer" else c["seed"]
+    return make_tree(rng_for(tree_seed, 0, 0, seq, "tree"), c["N"], c["K"], c["D"])
 
 
-def config_path(config: int, step: int, seq: int, parent: np.ndarray) -> np.ndarray:
-    """Accepted root path for (config, step, seq)."""
-    if config == 0:
+def workload_path(name: str, step: int, seq: int, parent: np.ndarray) -> np.ndarray:
+    """Accepted root path for (preset, step, seq): the deepest leaf for the tiny cases, a fixed
+    length for the one-layer and 48-layer presets, a uniform length otherwise."""
+    c = WORKLOADS[name]
+    if name == "tiny":
         return deepest_leaf_path(parent)
-    rng = rng_for(config, step, 0, seq, "path")
-    if config in (1, 2):
-        length = CONFIGS[2]["accept_len"]
-    elif config == 3:
-        length = int(rng.integers(1, CONFIGS[3]["accept_max"] + 1))
+    rng = rng_for(c["seed"], step, 0, seq, "path")
+    if "accept_len" in c:
+        length = c["accept_len"]
+    elif "accept_max" in c:
+        length = int(rng.integers(1, c["accept_max"] + 1))
     else:
         length = int(rng.integers(1, int(node_depths(parent).max()) + 2))
     return random_path(rng, parent, length)
 
 
-def draft_scores(config: int, step: int, seq: int, positions: int, top_k: int,
+def draft_scores(seed: int, step: int, seq: int, positions: int, top_k: int,
                  vocab: int = 64) -> tuple[np.ndarray, np.ndarray]:
     """Synthetic draft of one sequence: for each of `positions` tokens after the root, the
     top-k candidates (ids, fp32 log-probabilities sorted descending) of a softmax over `vocab`
     logits ~ N(0, s^2), with s falling from 4 to 1.5 along the block (later positions are less
     certain).  Returns (logp [positions][top_k], tokens [positions][top_k])."""
-    rng = rng_for(config, step, 0, seq, "draft")
+    rng = rng_for(seed, step, 0, seq, "draft")
     scale = np.linspace(4.0, 1.5, max(positions, 1))[:positions, None]
     logits = rng.normal(size=(positions, vocab)) * scale
     logp = logits - np.log(np.exp(logits - logits.max(axis=1, keepdims=True)).sum(
@@ -198,7 +204,7 @@ def _cast(x, dtype):
     return f32_to_bf16(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
 
-def node_inputs(config: int, step: int, layer: int, seq: int, n_nodes: int, heads: int,
+def node_inputs(seed: int, step: int, layer: int, seq: int, n_nodes: int, heads: int,
                 d: int, dtype: str) -> dict:
     """q, k, v [N,H,d]; beta, gate [N,H] in `dtype` (uint16 bits for bf16).
 
@@ -207,31 +213,31 @@ def node_inputs(config: int, step: int, layer: int, seq: int, n_nodes: int, head
     """
     sh = (n_nodes, heads, d)
     out = {
-        "q": _unit_rows(_normal(rng_for(config, step, layer, seq, "q"), sh)),
-        "k": _unit_rows(_normal(rng_for(config, step, layer, seq, "k"), sh)),
-        "v": _normal(rng_for(config, step, layer, seq, "v"), sh),
-        "beta": _sigmoid(_normal(rng_for(config, step, layer, seq, "beta"), sh[:2])),
-        "gate": _exp_neg_softplus(_normal(rng_for(config, step, layer, seq, "gate"), sh[:2])),
+        "q": _unit_rows(_normal(rng_for(seed, step, layer, seq, "q"), sh)),
+        "k": _unit_rows(_normal(rng_for(seed, step, layer, seq, "k"), sh)),
+        "v": _normal(rng_for(seed, step, layer, seq, "v"), sh),
+        "beta": _sigmoid(_normal(rng_for(seed, step, layer, seq, "beta"), sh[:2])),
+        "gate": _exp_neg_softplus(_normal(rng_for(seed, step, layer, seq, "gate"), sh[:2])),
     }
     return {key: _cast(val, dtype) for key, val in out.items()}
 
 
-def initial_state(config: int, layer: int, seq: int, heads: int, d: int) -> np.ndarray:
+def initial_state(seed: int, layer: int, seq: int, heads: int, d: int) -> np.ndarray:
     """Committed recurrent state [H, d_v, d_k], float32, N(0, 0.02^2)."""
-    return _normal(rng_for(config, 0, layer, seq, "state"), (heads, d, d), 0.02)
+    return _normal(rng_for(seed, 0, layer, seq, "state"), (heads, d, d), 0.02)
 
 
-def conv_inputs(config: int, step: int, layer: int, seq: int, n_nodes: int, channels: int,
+def conv_inputs(seed: int, step: int, layer: int, seq: int, n_nodes: int, channels: int,
                 dtype: str) -> np.ndarray:
     """Raw (pre-conv) per-node channel inputs [N, Cch] in `dtype`."""
-    return _cast(_normal(rng_for(config, step, layer, seq, "x"), (n_nodes, channels)), dtype)
+    return _cast(_normal(rng_for(seed, step, layer, seq, "x"), (n_nodes, channels)), dtype)
 
 
-def conv_weight(config: int, layer: int, channels: int, width: int, dtype: str) -> np.ndarray:
+def conv_weight(seed: int, layer: int, channels: int, width: int, dtype: str) -> np.ndarray:
     """Depthwise conv weight [Cch, Kc]; column Kc-1 multiplies the current token."""
-    return _cast(_normal(rng_for(config, 0, layer, 0, "weight"), (channels, width), 0.5), dtype)
+    return _cast(_normal(rng_for(seed, 0, layer, 0, "weight"), (channels, width), 0.5), dtype)
 
 
-def initial_conv_state(config: int, layer: int, seq: int, channels: int, width: int) -> np.ndarray:
+def initial_conv_state(seed: int, layer: int, seq: int, channels: int, width: int) -> np.ndarray:
     """Committed conv window [Cch, Kc-1], float32, oldest input first."""
-    return _normal(rng_for(config, 0, layer, seq, "conv_state"), (channels, width - 1))
+    return _normal(rng_for(seed, 0, layer, seq, "conv_state"), (channels, width - 1))

@@ -26,8 +26,9 @@ class StepInputs:
     x: object
 
 
-def config_trees(config: int) -> list:
-    return [synth.config_tree(config, b) for b in range(synth.CONFIGS[config]["Bs"])]
+def workload_trees(name: str) -> list:
+    """The candidate trees of a preset's sequences."""
+    return [synth.workload_tree(name, b) for b in range(synth.WORKLOADS[name]["Bs"])]
 
 
 def _to_torch(a: np.ndarray, dtype: str, device):
@@ -37,10 +38,12 @@ def _to_torch(a: np.ndarray, dtype: str, device):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
-def host_step_inputs(config: int, step: int, trees: list, layers: range, cfg=None,
+def host_step_inputs(name: str, step: int, trees: list, layers: range, cfg=None,
                      threads: int = 8) -> dict:
-    """numpy arrays of one step's node inputs for the given layers (all sequences)."""
-    c = dict(synth.CONFIGS[config], **(cfg or {}))
+    """numpy arrays of one step's node inputs for the given layers (all sequences) of a
+    preset (`cfg` overrides its fields)."""
+    c = dict(synth.WORKLOADS[name], **(cfg or {}))
+    seed = c["seed"]
     H, d, C, dtype = c["H"], c["d"], c["Cch"], c["dtype"]
     sizes = [len(t) for t in trees]
     T = int(sum(sizes))
@@ -55,10 +58,10 @@ def host_step_inputs(config: int, step: int, trees: list, layers: range, cfg=Non
         li, layer, b = job
         n = sizes[b]
         sl = slice(offs[b], offs[b] + n)
-        vals = synth.node_inputs(config, step, layer, b, n, H, d, dtype)
+        vals = synth.node_inputs(seed, step, layer, b, n, H, d, dtype)
         for name, arr in vals.items():
             out[name][li, sl] = arr
-        out["x"][li, sl] = synth.conv_inputs(config, step, layer, b, n, C, dtype)
+        out["x"][li, sl] = synth.conv_inputs(seed, step, layer, b, n, C, dtype)
 
     jobs = [(li, layer, b) for li, layer in enumerate(layers) for b in range(len(trees))]
     with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -66,23 +69,23 @@ def host_step_inputs(config: int, step: int, trees: list, layers: range, cfg=Non
     return out
 
 
-def device_step_inputs(config: int, step: int, trees: list, layers: range, device="cuda",
+def device_step_inputs(name: str, step: int, trees: list, layers: range, device="cuda",
                        cfg=None) -> StepInputs:
-    c = dict(synth.CONFIGS[config], **(cfg or {}))
-    h = host_step_inputs(config, step, trees, layers, cfg)
+    c = dict(synth.WORKLOADS[name], **(cfg or {}))
+    h = host_step_inputs(name, step, trees, layers, cfg)
     return StepInputs(**{k: _to_torch(v, c["dtype"], device) for k, v in h.items()})
 
 
-def host_initial_state(config: int, layers: range, n_seqs: int, cfg=None, threads: int = 8):
-    c = dict(synth.CONFIGS[config], **(cfg or {}))
-    H, d, C = c["H"], c["d"], c["Cch"]
+def host_initial_state(name: str, layers: range, n_seqs: int, cfg=None, threads: int = 8):
+    c = dict(synth.WORKLOADS[name], **(cfg or {}))
+    H, d, C, seed = c["H"], c["d"], c["Cch"], c["seed"]
     state = np.empty((len(layers), n_seqs, H, d, d), dtype=np.float32)
     conv = np.empty((len(layers), n_seqs, C, 3), dtype=np.float32)
 
     def fill(job):
         li, layer, b = job
-        state[li, b] = synth.initial_state(config, layer, b, H, d)
-        conv[li, b] = synth.initial_conv_state(config, layer, b, C, 4)
+        state[li, b] = synth.initial_state(seed, layer, b, H, d)
+        conv[li, b] = synth.initial_conv_state(seed, layer, b, C, 4)
 
     jobs = [(li, layer, b) for li, layer in enumerate(layers) for b in range(n_seqs)]
     with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -90,9 +93,9 @@ def host_initial_state(config: int, layers: range, n_seqs: int, cfg=None, thread
     return state, conv
 
 
-def host_weights(config: int, layers: range, cfg=None) -> np.ndarray:
-    c = dict(synth.CONFIGS[config], **(cfg or {}))
-    return np.stack([synth.conv_weight(config, layer, c["Cch"], 4, c["dtype"]) for layer in layers])
+def host_weights(name: str, layers: range, cfg=None) -> np.ndarray:
+    c = dict(synth.WORKLOADS[name], **(cfg or {}))
+    return np.stack([synth.conv_weight(c["seed"], layer, c["Cch"], 4, c["dtype"]) for layer in layers])
 
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:

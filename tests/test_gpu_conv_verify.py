@@ -234,12 +234,12 @@ def test_batched_workload_sampled(torch_cuda):
     """The batched workload's trees (32 sequences, 22 nodes, top-4, depth <= 12) at 48 heads,
     one layer, two steps (the second folds the first's accepted paths); every head of sampled
     sequences against the oracle."""
-    trees = workload.config_trees(3)
-    run = FusedRun(torch_cuda, trees, 48, 1, cfg_id=3)
+    trees = workload.workload_trees("batched")
+    run = FusedRun(torch_cuda, trees, 48, 1, cfg_id=synth.WORKLOADS["batched"]["seed"])
     seqs = [0, 7, 31]
     run.verify(0)
     refs = run.check_outputs(seqs=seqs)
-    paths = [synth.config_path(3, 0, s, t) for s, t in enumerate(trees)]
+    paths = [synth.workload_path("batched", 0, s, t) for s, t in enumerate(trees)]
     run.commit(paths, refs)
     run.verify(1)
     S = gh.to_np(run.b.layers.state[0][seqs])

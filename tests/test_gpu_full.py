@@ -26,14 +26,14 @@ def torch_cuda():
 MODES = ["chain", "ut"]
 
 
-def _full_case(torch, config, steps, n_samples, seed, mode="chain"):
-    """Run `steps` verify+commit steps of a full config, then flush; check sampled pairs."""
-    c = synth.CONFIGS[config]
+def _full_case(torch, name, steps, n_samples, seed, mode="chain"):
+    """Run `steps` verify+commit steps of a full-size preset, then flush; check sampled pairs."""
+    c = synth.WORKLOADS[name]
     H, d, C, dtype, Ly = c["H"], c["d"], c["Cch"], c["dtype"], c["Ly"]
-    trees = workload.config_trees(config)
+    trees = workload.workload_trees(name)
     b = gh.Batch(trees, Ly, H, d, C, mode=mode)
-    S0, X0 = workload.host_initial_state(config, range(Ly), b.S)
-    W = workload.host_weights(config, range(Ly))
+    S0, X0 = workload.host_initial_state(name, range(Ly), b.S)
+    W = workload.host_weights(name, range(Ly))
     b.set_state(S0, X0)
     Wd = workload._to_torch(W, dtype, "cuda")
     rng = np.random.default_rng(seed)
@@ -41,7 +41,7 @@ def _full_case(torch, config, steps, n_samples, seed, mode="chain"):
     committed = {p: S0[p[0], p[1]].astype(np.float64) for p in pairs}
     window = {p: X0[p[0], p[1]].astype(np.float64) for p in pairs}
     for step in range(steps):
-        h = workload.host_step_inputs(config, step, trees, range(Ly))
+        h = workload.host_step_inputs(name, step, trees, range(Ly))
         inp = workload.StepInputs(**{k: workload._to_torch(v, dtype, "cuda") for k, v in h.items()})
         role_before = b.layers.role_host.copy()
         b.step(inp, Wd)
@@ -61,7 +61,7 @@ def _full_case(torch, config, steps, n_samples, seed, mode="chain"):
             y = oconv.tree_conv(trees[s], window[(l, s)], h64["x"], workload.widen(W[l], dtype))
             gh.assert_outputs(gh.to_np(b.y[l, sl]), y, what=f"y layer {l} seq {s}")
             gh.assert_bank_rows(b, l, s, 1 - role_before[s], range(len(trees[s])), kf, uf, lg)
-        paths = [synth.config_path(config, step, s, trees[s]) for s in range(b.S)]
+        paths = [synth.workload_path(name, step, s, trees[s]) for s in range(b.S)]
         b.commit(inp, paths, Wd)
         for (l, s) in pairs:
             sl = slice(b.offs[s], b.offs[s + 1])
@@ -80,21 +80,21 @@ def _full_case(torch, config, steps, n_samples, seed, mode="chain"):
 def test_batched_32x48_full_size(torch_cuda, mode):
     """The benchmarked workload: 32 sequences x 48 layers x 48 heads x 128, 22-node top-4
     trees, two verify+commit steps (the second folds the first's accepted paths), flush."""
-    _full_case(torch_cuda, 3, steps=2, n_samples=6, seed=31, mode=mode)
+    _full_case(torch_cuda, "batched", steps=2, n_samples=6, seed=31, mode=mode)
 
 
 @pytest.mark.parametrize("mode", MODES)
 def test_wide_deep_64_node_trees_full_size(torch_cuda, mode):
     """64-node top-8 trees of depth up to 16, batch 8, 48 layers: long heavy chains and
     many sibling boundaries."""
-    _full_case(torch_cuda, 4, steps=2, n_samples=4, seed=41, mode=mode)
+    _full_case(torch_cuda, "wide-deep", steps=2, n_samples=4, seed=41, mode=mode)
 
 
 @pytest.mark.parametrize("mode", MODES)
 def test_pure_16_node_chains_full_size(torch_cuda, mode):
     """Batch 8 of 16-node pure chains (block-diffusion draft blocks), 48 layers: every
     acceptance is in order, so commits only swap bank roles."""
-    _full_case(torch_cuda, 5, steps=2, n_samples=4, seed=51, mode=mode)
+    _full_case(torch_cuda, "chain16", steps=2, n_samples=4, seed=51, mode=mode)
 
 
 # ---------------------------------------------------------------------------------------
@@ -111,11 +111,11 @@ def _one_layer(torch, h, S0, trees, dtype="bf16", mode="chain"):
     return b
 
 
-def _config1_inputs():
-    trees = workload.config_trees(1)
-    h = workload.host_step_inputs(1, 0, trees, range(1))
+def _one_layer_inputs():
+    trees = workload.workload_trees("one-layer")
+    h = workload.host_step_inputs("one-layer", 0, trees, range(1))
     h.pop("x")
-    S0 = synth.initial_state(1, 0, 0, 48, 128)
+    S0 = synth.initial_state(synth.WORKLOADS["one-layer"]["seed"], 0, 0, 48, 128)
     return trees, h, S0
 
 
@@ -123,7 +123,7 @@ def _config1_inputs():
 def test_sibling_isolation_bit_identical(torch_cuda, mode):
     """Changing every input of one node changes its subtree's outputs and leaves every other
     node's output bit-identical (same schedule, same inputs elsewhere)."""
-    trees, h, S0 = _config1_inputs()
+    trees, h, S0 = _one_layer_inputs()
     parent = trees[0]
     base = gh.to_np(_one_layer(torch_cuda, h, S0, trees, mode=mode).out[0])
     for m in (3, 13, 17):
@@ -144,7 +144,7 @@ def test_sibling_isolation_bit_identical(torch_cuda, mode):
 def test_power_of_two_scaling_bit_exact(torch_cuda, mode):
     """Scaling the committed state and every v by 2 scales outputs, residual vectors and
     boundary-derived states by exactly 2 (no rounding difference anywhere)."""
-    trees, h, S0 = _config1_inputs()
+    trees, h, S0 = _one_layer_inputs()
     b1 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
     h2 = {k: v.copy() for k, v in h.items()}
     h2["v"] = synth.f32_to_bf16(2 * synth.bf16_to_f32(h2["v"]))
@@ -156,7 +156,7 @@ def test_power_of_two_scaling_bit_exact(torch_cuda, mode):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_run_to_run_deterministic(torch_cuda, mode):
-    trees, h, S0 = _config1_inputs()
+    trees, h, S0 = _one_layer_inputs()
     b1 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
     b2 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
     assert torch_cuda.equal(b1.out, b2.out)

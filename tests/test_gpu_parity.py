@@ -111,8 +111,8 @@ def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d,
 
 @pytest.mark.parametrize("mode", MODES)
 def test_tiny_tree_and_chain(torch_cuda, mode):
-    """Config 0: the 7-node tree [-1,0,0,1,1,2,3] and an 8-node chain, batched, fp32, d = 16.
-    Step 0 accepts the deepest leaves ([0,1,3,6] is branched -> compaction; the chain is in
+    """The tiny workload: the 7-node tree [-1,0,0,1,1,2,3] and an 8-node chain, batched, fp32,
+    d = 16.  Step 0 accepts the deepest leaves ([0,1,3,6] is branched -> compaction; the chain is in
     order -> role swap); step 1 accepts [0,2,5] and [0,1,2]; then flush."""
     trees = [synth.TINY_TREE, synth.TINY_CHAIN]
     b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, mode=mode)
@@ -169,21 +169,21 @@ def test_bf16_inputs_small(torch_cuda, mode):
     _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps, "bf16", 91, 3, 16, 24)
 
 
-def _layer_case(torch_cuda, config, n_layers, trees, steps, sample_layers, check_outputs_at,
+def _layer_case(torch_cuda, name, n_layers, trees, steps, sample_layers, check_outputs_at,
                 mode="chain"):
-    c = synth.CONFIGS[config]
+    c = synth.WORKLOADS[name]
     H, d, C, dtype = c["H"], c["d"], c["Cch"], c["dtype"]
     b = gh.Batch(trees, n_layers, H, d, C, mode=mode)
     layers = range(n_layers)
-    S0, X0 = workload.host_initial_state(config, layers, b.S)
-    W = workload.host_weights(config, layers)
+    S0, X0 = workload.host_initial_state(name, layers, b.S)
+    W = workload.host_weights(name, layers)
     b.set_state(S0, X0)
     Wd = workload._to_torch(W, dtype, "cuda")
     committed = {l: [S0[l, s].astype(np.float64) for s in range(b.S)] for l in sample_layers}
     window = {l: [X0[l, s].astype(np.float64) for s in range(b.S)] for l in sample_layers}
     W64 = {l: workload.widen(W[l], dtype) for l in sample_layers}
     for step in range(steps):
-        h = workload.host_step_inputs(config, step, trees, layers)
+        h = workload.host_step_inputs(name, step, trees, layers)
         inp = workload.StepInputs(**{k: workload._to_torch(v, dtype, "cuda") for k, v in h.items()})
         role_before = b.layers.role_host.copy()
         b.step(inp, Wd)
@@ -195,7 +195,7 @@ def _layer_case(torch_cuda, config, n_layers, trees, steps, sample_layers, check
             if step in check_outputs_at:
                 _check_step(b, h64, committed[l], window[l], W64[l], l,
                             write_bank=1 - role_before, host_layer=li)
-        paths = [synth.config_path(config, step, s, trees[s]) for s in range(b.S)]
+        paths = [synth.workload_path(name, step, s, trees[s]) for s in range(b.S)]
         b.commit(inp, paths, Wd)
         for li, l in enumerate(sample_layers):
             for s, path in enumerate(paths):
@@ -213,18 +213,18 @@ def _layer_case(torch_cuda, config, n_layers, trees, steps, sample_layers, check
 
 @pytest.mark.parametrize("mode", MODES)
 def test_one_layer_bf16_48_heads(torch_cuda, mode):
-    """Config 1: one layer, 48 heads x 128, bf16 inputs, the seeded 22-node top-4 tree; verify,
+    """The one-layer workload: 48 heads x 128, bf16 inputs, the seeded 22-node top-4 tree; verify,
     conv and banks for every node and head, then commit of a length-6 path and flush."""
-    trees = workload.config_trees(1)
-    _layer_case(torch_cuda, 1, 1, trees, steps=2, sample_layers=[0], check_outputs_at={0, 1},
+    trees = workload.workload_trees("one-layer")
+    _layer_case(torch_cuda, "one-layer", 1, trees, steps=2, sample_layers=[0], check_outputs_at={0, 1},
                 mode=mode)
 
 
 @pytest.mark.parametrize("mode", MODES)
 def test_48_layers_ten_steps(torch_cuda, mode):
-    """Config 2: 48 independent layers, 10 verify steps each folding the previous step's
-    accepted length-6 path, then flush; oracle on three sampled layers (states every step,
+    """The 48-layer workload: 48 independent layers, 10 verify steps each folding the previous
+    step's accepted length-6 path, then flush; oracle on three sampled layers (states every step,
     outputs and banks at steps 0, 4 and 9)."""
-    trees = workload.config_trees(2)
-    _layer_case(torch_cuda, 2, 48, trees, steps=10, sample_layers=[0, 23, 47],
+    trees = workload.workload_trees("48-layer")
+    _layer_case(torch_cuda, "48-layer", 48, trees, steps=10, sample_layers=[0, 23, 47],
                 check_outputs_at={0, 4, 9}, mode=mode)

@@ -72,9 +72,9 @@ def test_random_batches_bit_exact():
         _check_same(binding.hld_schedule(parents), hld.schedule(parents))
 
 
-@pytest.mark.parametrize("config", [1, 3, 4, 5])
-def test_config_trees_bit_exact(config):
-    parents = [synth.config_tree(config, b) for b in range(synth.CONFIGS[config]["Bs"])]
+@pytest.mark.parametrize("name", ["one-layer", "batched", "wide-deep", "chain16"])
+def test_workload_trees_bit_exact(name):
+    parents = [synth.workload_tree(name, b) for b in range(synth.WORKLOADS[name]["Bs"])]
     _check_same(binding.hld_schedule(parents), hld.schedule(parents))
 
 
