@@ -3,7 +3,9 @@
 One step = the whole hot path over one batch: heavy-light schedule of the batch's trees (host)
 and its upload, then for every GDN layer the tree conv (with the conv-window fold) and the tree
 verify (with the deferred-commit fold), then accept -> commit of one seeded path per sequence
-(role swap or compaction).  The timed region is K steps plus the final flush.
+(by default the row-map form: the next fold reads the accepted rows where the verify wrote them;
+--commit compact gathers branched paths into path order first).  The timed region is K steps
+plus the final flush.
 
 Three paths are timed, one after the other, on the same resident workload:
   fused  conv -> SiLU -> unit-length q/k -> tree-masked verify in one launch per layer: q, k
@@ -127,8 +129,11 @@ def conv_bytes(view, pending, C, in_bytes, n_layers=1):
     return (T * per_node + seqs + C * 4 * in_bytes) * n_layers
 
 
-def commit_bytes(paths, H, d, C, n_layers):
-    """Compaction of branched paths: L rows of (k, u, lg per head + conv input) read + written."""
+def commit_bytes(paths, H, d, C, n_layers, compact=True):
+    """Compaction of branched paths: L rows of (k, u, lg per head + conv input) read + written.
+    The row-map commit copies no rows (its map is L int32 per sequence: counted as 0)."""
+    if not compact:
+        return 0
     row = H * (8 * d + 4) + 4 * C
     total = 0
     for p in paths:
@@ -303,6 +308,10 @@ def main(argv=None):
                          "tree-masked verify in one launch per layer; ut = tree conv, then the "
                          "tree-masked verify of given q/k/v on the matrix cores; chain = tree "
                          "conv, then heavy-light chains in dependency waves")
+    ap.add_argument("--commit", choices=["row-map", "compact"], default="row-map",
+                    help="accept -> commit form: row-map = the next fold reads the accepted rows "
+                         "where the verify wrote them (no copy); compact = branched paths are "
+                         "gathered into path order first")
     ap.add_argument("--only", action="store_true", help="time the headline path only")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill line")
     ap.add_argument("--cpu-pairs", type=int, default=640)
@@ -375,6 +384,7 @@ def main(argv=None):
         return torch.from_numpy(a).pin_memory().to(dev, non_blocking=True)
 
     n_waves = int(view["n_waves"])
+    commit_mode = {"row-map": binding.COMMIT_ROW_MAP, "compact": binding.COMMIT_COMPACT}[args.commit]
 
     def run_path(verify):
         acc = dict(verify_ms=0.0, verify_launches=0, verify_bytes=0, stamped_bytes=0,
@@ -417,7 +427,8 @@ def main(argv=None):
                         binding.tree_verify_wave_timed(vargs[li], image, dev_image, w, e0, e1)
             paths = all_paths[s]
             flat, offs = binding.pack_paths(paths)
-            binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs))
+            binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs),
+                                mode=commit_mode)
             if timed_index is not None:  # byte accounting after the launches, off the GPU's path
                 calls = len(vargs)
                 if verify == "fused":
@@ -433,7 +444,8 @@ def main(argv=None):
                     acc["verify_launches"] += calls * launches
                 if verify != "fused":  # the fused launch already counts its conv traffic
                     acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
-                acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly)
+                acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly,
+                                                    commit_mode == binding.COMMIT_COMPACT)
 
         for s in range(args.warmup):
             step(s, None)
@@ -517,7 +529,7 @@ def main(argv=None):
             "sequences": S, "layers": Ly, "heads": H, "head_dim": d, "tree_nodes": T,
             "chains": int(view["n_chains"]), "waves": int(view["n_waves"]),
             "boundary_nodes": int(view["n_boundaries"]), "layers_per_call": lpc,
-            "verify": args.verify,
+            "verify": args.verify, "commit": args.commit,
         },
         "roofline": head["roofline"],
         "cpu_baseline": cpu,

@@ -50,7 +50,7 @@ class VerifyArgs(ctypes.Structure):
         ("max_nodes", _I32), ("layer_begin", _I32), ("n_layers", _I32), ("in_dtype", _I32),
         ("q", _P), ("k", _P), ("v", _P), ("beta", _P), ("gate", _P), ("state", _P),
         ("bank_k", _P * 2), ("bank_u", _P * 2), ("bank_lg", _P * 2),
-        ("role", _P), ("pending_len", _P), ("workspace", _P), ("out", _P),
+        ("role", _P), ("pending_len", _P), ("pending_rows", _P), ("workspace", _P), ("out", _P),
     ]
 
 
@@ -68,7 +68,7 @@ class ConvArgs(ctypes.Structure):
         ("n_seqs", _I32), ("channels", _I32), ("width", _I32), ("n_nodes", _I32),
         ("max_nodes", _I32), ("layer_begin", _I32), ("n_layers", _I32), ("in_dtype", _I32),
         ("x", _P), ("weight", _P), ("conv_state", _P), ("bank_x", _P * 2),
-        ("role", _P), ("pending_len", _P), ("out", _P),
+        ("role", _P), ("pending_len", _P), ("pending_rows", _P), ("out", _P),
     ]
 
 
@@ -120,7 +120,7 @@ def lib() -> ctypes.CDLL:
     L.gdn_tree_conv.argtypes = [ctypes.POINTER(ConvArgs), _I32P, _P, _P]
     L.gdn_commit_path.restype = _I32
     L.gdn_commit_path.argtypes = [_I32P, _I32P, _I32P, _P, _P, ctypes.POINTER(VerifyArgs),
-                                  ctypes.POINTER(ConvArgs), _I32P, _I32P, _P]
+                                  ctypes.POINTER(ConvArgs), _I32P, _I32P, _I32, _P]
     L.gdn_compact_factors.restype = _I32
     L.gdn_compact_factors.argtypes = [_P, _P, ctypes.c_int64, _P, _P, _I32, _P]
     L.gdn_flush.restype = _I32
@@ -260,7 +260,8 @@ class Layers:
 
     Shapes: state [Ly,S,H,d,d]; bank_k/bank_u [2][Ly,S,H,max_nodes,d]; bank_lg
     [2][Ly,S,H,max_nodes]; conv_state [Ly,S,Cch,3]; bank_x [2][Ly,S,max_nodes,Cch];
-    role, pending [S] int32 (device) with host mirrors role_host, pending_host.
+    role, pending [S] int32 (device) with host mirrors role_host, pending_host;
+    pending_rows [S,max_nodes] int32 (device): the bank row of each pending factor.
     """
     state: object
     bank_k: list
@@ -270,6 +271,7 @@ class Layers:
     pending: object
     role_host: np.ndarray
     pending_host: np.ndarray
+    pending_rows: object = None
     conv_state: object = None
     bank_x: list = None
 
@@ -302,6 +304,7 @@ def verify_args(image, layers: Layers, q, k, v, beta, gate, out, workspace,
         _need(layers.bank_lg[i], Ly_end * S * H * Nm, "bank_lg")
     _need(layers.role, S, "role")
     _need(layers.pending, S, "pending")
+    _need(layers.pending_rows, S * Nm, "pending_rows")
     _need(workspace, 0, "workspace")
     a = VerifyArgs()
     # kept for the size check of the chain entry points
@@ -320,6 +323,7 @@ def verify_args(image, layers: Layers, q, k, v, beta, gate, out, workspace,
         a.bank_u[i] = _dev(layers.bank_u[i])
         a.bank_lg[i] = _dev(layers.bank_lg[i])
     a.role, a.pending_len = _dev(layers.role), _dev(layers.pending)
+    a.pending_rows = _dev(layers.pending_rows)
     a.workspace, a.out = _dev(workspace), _dev(out)
     return a
 
@@ -346,7 +350,9 @@ def conv_args(image, layers: Layers, x, weight, out, layer_begin=0, n_layers=1,
     a.x, a.weight, a.out = _dev(x), _dev(weight), _dev(out)
     a.conv_state = _dev(layers.conv_state)
     a.bank_x[0], a.bank_x[1] = _dev(layers.bank_x[0]), _dev(layers.bank_x[1])
+    _need(layers.pending_rows, S * Nm, "pending_rows")
     a.role, a.pending_len = _dev(layers.role), _dev(layers.pending)
+    a.pending_rows = _dev(layers.pending_rows)
     return a
 
 
@@ -489,10 +495,15 @@ def pack_paths(paths):
     return flat, offsets
 
 
+COMMIT_COMPACT, COMMIT_ROW_MAP = 0, 1
+
+
 def commit_path(image, paths, layers: Layers, vargs: VerifyArgs, cargs: ConvArgs | None,
-                dev_paths=None, dev_offsets=None, stream=None):
-    """Accept one root path per sequence (local ids); updates layers.role/pending (device
-    on the stream, host mirrors now).  dev_paths/dev_offsets default to fresh uploads."""
+                dev_paths=None, dev_offsets=None, stream=None, mode=COMMIT_ROW_MAP):
+    """Accept one root path per sequence (local ids); updates layers.role/pending/pending_rows
+    (device on the stream, host mirrors now).  dev_paths/dev_offsets default to fresh
+    uploads.  mode: COMMIT_ROW_MAP (no copy) or COMMIT_COMPACT (branched paths gathered into
+    path order)."""
     import torch
     flat, offsets = pack_paths(paths)
     if dev_paths is None:
@@ -501,7 +512,8 @@ def commit_path(image, paths, layers: Layers, vargs: VerifyArgs, cargs: ConvArgs
     _check(lib().gdn_commit_path(
         _ptr(image), _ptr(flat), _ptr(offsets), _dev(dev_paths), _dev(dev_offsets),
         ctypes.byref(vargs), ctypes.byref(cargs) if cargs is not None else None,
-        _ptr(layers.role_host), _ptr(layers.pending_host), _stream(stream)), "gdn_commit_path")
+        _ptr(layers.role_host), _ptr(layers.pending_host), int(mode), _stream(stream)),
+        "gdn_commit_path")
     return dev_paths, dev_offsets
 
 
@@ -530,6 +542,7 @@ def alloc_layers(n_layers, n_seqs, n_heads, head_dim, max_nodes, channels=0, dev
         pending=torch.zeros(S, device=device, dtype=torch.int32),
         role_host=np.zeros(S, dtype=np.int32),
         pending_host=np.zeros(S, dtype=np.int32),
+        pending_rows=torch.zeros((S, Nm), device=device, dtype=torch.int32),
     )
     if channels:
         lay.conv_state = torch.zeros((Ly, S, channels, 3), **f)

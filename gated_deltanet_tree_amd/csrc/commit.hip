@@ -11,6 +11,12 @@
 // bank that the last verify consumed (the pending one) and leaves the roles as they are.
 // The kernels re-derive the per-sequence decision from the device copy of the paths, so no
 // host-to-device copy happens inside the library.
+//
+// Every fold reads pending factor i from bank row pending_rows[b][i].  The guide's mode
+// (compaction) keeps that map the identity.  The row-map mode never copies: the written bank
+// always becomes pending and the map holds the accepted path itself.  A factor row is 512
+// contiguous bytes per head at d = 128, so a gathered row costs the fold what a compacted one
+// does, and the gather kernel's read + write of every branched row (all layers) disappears.
 #include <algorithm>
 #include <vector>
 
@@ -68,14 +74,22 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams P) {
     }
 }
 
-// Runs after compact_kernel on the same stream: role flip for in-order paths, new pending.
-__global__ void commit_bookkeeping_kernel(int32_t *role, int32_t *pending, const int32_t *paths,
-                                          const int32_t *path_off, int S) {
-    const int seq = blockIdx.x * blockDim.x + threadIdx.x;
-    if (seq >= S) return;
+// Runs after compact_kernel on the same stream, one workgroup per sequence: the row map, the
+// role flip (row-map mode: every non-empty path; compaction: in-order paths) and the pending
+// length.
+__global__ __launch_bounds__(64) void commit_bookkeeping_kernel(
+    int32_t *role, int32_t *pending, int32_t *rows, const int32_t *paths, const int32_t *path_off,
+    int max_nodes, int mode) {
+    const int seq = blockIdx.x;
     const int beg = path_off[seq], L = path_off[seq + 1] - beg;
-    if (L > 0 && path_in_order(paths + beg, L)) role[seq] ^= 1;
-    pending[seq] = L;
+    int32_t *rm = rows + int64_t(seq) * max_nodes;
+    for (int i = threadIdx.x; i < L; i += blockDim.x)
+        rm[i] = mode == GDN_COMMIT_ROW_MAP ? paths[beg + i] : i;
+    if (threadIdx.x == 0) {
+        if (L > 0 && (mode == GDN_COMMIT_ROW_MAP || path_in_order(paths + beg, L)))
+            role[seq] ^= 1;
+        pending[seq] = L;
+    }
 }
 
 __global__ void clear_pending_kernel(int32_t *pending, int S) {
@@ -102,21 +116,25 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
                                       const int32_t *path_offsets, const int32_t *dev_paths,
                                       const int32_t *dev_path_offsets,
                                       const gdn_verify_args *va, const gdn_conv_args *ca,
-                                      int32_t *role_host, int32_t *pending_host, void *stream) {
+                                      int32_t *role_host, int32_t *pending_host, int32_t mode,
+                                      void *stream) {
     clear_error();
     if (!image_ok(host_image) || !path_offsets || !dev_path_offsets || !role_host ||
         !pending_host)
         return fail(GDN_EINVAL, "gdn_commit_path: null argument or malformed schedule image");
+    if (mode != GDN_COMMIT_COMPACT && mode != GDN_COMMIT_ROW_MAP)
+        return fail(GDN_EINVAL, "gdn_commit_path: unknown mode %d", mode);
     gdn_status st = check_flush_verify_args(va);
     if (st != GDN_OK) return st;
     if (ca != nullptr) {
         st = check_flush_conv_args(ca);
         if (st != GDN_OK) return st;
         if (ca->role != va->role || ca->pending_len != va->pending_len ||
-            ca->n_seqs != va->n_seqs || ca->layer_begin != va->layer_begin ||
-            ca->n_layers != va->n_layers || ca->max_nodes != va->max_nodes)
+            ca->pending_rows != va->pending_rows || ca->n_seqs != va->n_seqs ||
+            ca->layer_begin != va->layer_begin || ca->n_layers != va->n_layers ||
+            ca->max_nodes != va->max_nodes)
             return fail(GDN_EINVAL, "gdn_commit_path: conv args disagree with verify args on "
-                        "role/pending_len/n_seqs/layers/max_nodes");
+                        "role/pending_len/pending_rows/n_seqs/layers/max_nodes");
     }
     const ImageView v = view_image(host_image);
     if (v.n_seqs != va->n_seqs)
@@ -127,7 +145,7 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
     if (S == 0) return GDN_OK;
     if (path_offsets[0] != 0) return fail(GDN_EPATH, "gdn_commit_path: path_offsets[0] != 0");
     const int32_t *seq_off = host_image + v.off_seq, *npar = host_image + v.off_parent;
-    bool any_compaction = false;
+    bool any_compaction = false, any_path = false;
     int32_t max_len = 0;
     std::vector<int32_t> new_role(role_host, role_host + S), new_pending(S);
     for (int32_t b = 0; b < S; ++b) {
@@ -151,14 +169,19 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
                             "follow its parent", b, i, node);
             in_order = in_order && node == i;
         }
-        if (L > 0 && in_order) new_role[b] ^= 1;
-        if (L > 0 && !in_order) any_compaction = true;
-        if (!in_order) max_len = std::max(max_len, L);
+        any_path = any_path || L > 0;
+        if (mode == GDN_COMMIT_ROW_MAP) {
+            if (L > 0) new_role[b] ^= 1;
+        } else {
+            if (L > 0 && in_order) new_role[b] ^= 1;
+            if (L > 0 && !in_order) any_compaction = true;
+            if (!in_order) max_len = std::max(max_len, L);
+        }
         new_pending[b] = L;
     }
     if (S > 65535 || va->n_layers > 65535)
         return fail(GDN_EINVAL, "gdn_commit_path: n_seqs and n_layers must be <= 65535");
-    if (any_compaction && dev_paths == nullptr)
+    if (any_path && dev_paths == nullptr)
         return fail(GDN_EINVAL, "gdn_commit_path: null dev_paths");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (any_compaction) {
@@ -181,9 +204,10 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
         hipLaunchKernelGGL(compact_kernel, dim3(max_len, S, va->n_layers), dim3(256), 0, s, P);
         GDN_LAUNCH_CHECK("compact_kernel");
     }
-    hipLaunchKernelGGL(commit_bookkeeping_kernel, dim3((S + 255) / 256), dim3(256), 0, s,
+    hipLaunchKernelGGL(commit_bookkeeping_kernel, dim3(S), dim3(64), 0, s,
                        const_cast<int32_t *>(va->role), const_cast<int32_t *>(va->pending_len),
-                       dev_paths, dev_path_offsets, S);
+                       const_cast<int32_t *>(va->pending_rows), dev_paths, dev_path_offsets,
+                       va->max_nodes, mode);
     GDN_LAUNCH_CHECK("commit_bookkeeping_kernel");
     for (int32_t b = 0; b < S; ++b) {
         role_host[b] = new_role[b];
@@ -218,8 +242,9 @@ extern "C" gdn_status gdn_flush(const gdn_verify_args *va, const gdn_conv_args *
         st = check_flush_conv_args(ca);
         if (st != GDN_OK) return st;
         if (ca->role != va->role || ca->pending_len != va->pending_len ||
-            ca->n_seqs != va->n_seqs || ca->layer_begin != va->layer_begin ||
-            ca->n_layers != va->n_layers)
+            ca->pending_rows != va->pending_rows || ca->n_seqs != va->n_seqs ||
+            ca->layer_begin != va->layer_begin || ca->n_layers != va->n_layers ||
+            ca->max_nodes != va->max_nodes)
             return fail(GDN_EINVAL, "gdn_flush: conv args disagree with verify args");
     }
     if (pending_host == nullptr) return fail(GDN_EINVAL, "gdn_flush: null pending_host");

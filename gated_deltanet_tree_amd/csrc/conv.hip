@@ -9,8 +9,8 @@
 //
 // One thread per (layer, sequence, channel); consecutive threads take consecutive channels,
 // so every access to x, the banks and the output is a coalesced row segment.  The thread
-// keeps the committed window in registers, folds the pending bank rows into it (only the
-// last three can survive), writes it back once, then walks its tree in index order in blocks
+// keeps the committed window in registers, folds the pending bank rows (found through the
+// pending row map) into it (only the last three can survive), writes it back once, then walks its tree in index order in blocks
 // of nodes whose loads are all issued before any is used.  A node's window is read along its
 // parent chain: the node's own input, up to three ancestors' inputs, then committed-window
 // entries above the root.  Ancestor inputs were read moments earlier by the same thread, so
@@ -24,6 +24,7 @@ struct ConvParams {
     float *cstate;
     float *bank[2];
     const int32_t *role, *pending;
+    const int32_t *rows;  // [S][max_nodes] pending row map
     float *out;
     const int32_t *img;
     int64_t off_seq, off_parent, off_depth;
@@ -36,7 +37,8 @@ struct ConvParams {
 #endif
 
 template <typename TIn>
-__global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P) {
+__global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P,
+                                                        const int32_t *__restrict__ rows) {
     const int c = blockIdx.x * blockDim.x + threadIdx.x;
     const int seq = blockIdx.y;
     const int layer = P.layer_begin + blockIdx.z;
@@ -46,11 +48,17 @@ __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P) {
     float *cs = P.cstate + (ls * P.C + c) * 3;
     float w0 = cs[0], w1 = cs[1], w2 = cs[2];  // committed window, oldest first
     if (L > 0) {
-        // Only the last three pending inputs survive the fold.
+        // Only the last three pending inputs survive the fold; the row map (uniform, scalar
+        // loads) says where they sit in the bank, clamped to its rows.
+        const int32_t *rm = rows + int64_t(seq) * P.max_nodes;
+        const int m = P.max_nodes - 1;
+        const int i0 = L >= 3 ? min(max(rm[L - 3], 0), m) : 0;
+        const int i1 = L >= 2 ? min(max(rm[L - 2], 0), m) : 0;
+        const int i2 = min(max(rm[L - 1], 0), m);
         const float *pb = P.bank[role] + ls * P.max_nodes * P.C + c;
-        const float r0 = L >= 3 ? pb[int64_t(L - 3) * P.C] : 0.f;
-        const float r1 = L >= 2 ? pb[int64_t(L - 2) * P.C] : 0.f;
-        const float r2 = pb[int64_t(L - 1) * P.C];
+        const float r0 = L >= 3 ? pb[int64_t(i0) * P.C] : 0.f;
+        const float r1 = L >= 2 ? pb[int64_t(i1) * P.C] : 0.f;
+        const float r2 = pb[int64_t(i2) * P.C];
         if (L >= 3) {
             w0 = r0; w1 = r1; w2 = r2;
         } else if (L == 2) {
@@ -112,8 +120,9 @@ static gdn_status check_conv_args(const gdn_conv_args *a, bool need_inputs) {
     if (a->in_dtype != GDN_F32 && a->in_dtype != GDN_BF16)
         return fail(GDN_EINVAL, "conv args: in_dtype %d", a->in_dtype);
     if (a->n_seqs == 0) return GDN_OK;  // empty batch: nothing is read or written
-    if (!a->conv_state || !a->bank_x[0] || !a->bank_x[1] || !a->role || !a->pending_len)
-        return fail(GDN_EINVAL, "conv args: null conv_state/bank/role/pending_len");
+    if (!a->conv_state || !a->bank_x[0] || !a->bank_x[1] || !a->role || !a->pending_len ||
+        !a->pending_rows)
+        return fail(GDN_EINVAL, "conv args: null conv_state/bank/role/pending_len/pending_rows");
     if (need_inputs && (!a->x || !a->weight || !a->out))
         return fail(GDN_EINVAL, "conv args: null x/weight/out");
     if (a->n_seqs > 65535 || a->n_layers > 65535)
@@ -125,9 +134,9 @@ static gdn_status launch_conv(const ConvParams &P, int n_layers, int dtype, hipS
     if (P.S == 0) return GDN_OK;
     dim3 grid((P.C + 255) / 256, P.S, n_layers);
     if (dtype == GDN_BF16)
-        hipLaunchKernelGGL(tree_conv_kernel<bf16_t>, grid, dim3(256), 0, stream, P);
+        hipLaunchKernelGGL(tree_conv_kernel<bf16_t>, grid, dim3(256), 0, stream, P, P.rows);
     else
-        hipLaunchKernelGGL(tree_conv_kernel<float>, grid, dim3(256), 0, stream, P);
+        hipLaunchKernelGGL(tree_conv_kernel<float>, grid, dim3(256), 0, stream, P, P.rows);
     GDN_LAUNCH_CHECK("tree_conv_kernel");
     return GDN_OK;
 }
@@ -141,6 +150,7 @@ static ConvParams conv_params(const gdn_conv_args *a) {
     P.bank[1] = a->bank_x[1];
     P.role = a->role;
     P.pending = a->pending_len;
+    P.rows = a->pending_rows;
     P.out = a->out;
     P.S = a->n_seqs;
     P.C = a->channels;

@@ -145,15 +145,17 @@ __device__ __forceinline__ float chunk_suffix_sum(float x) {
 }
 
 // Pending rows f0 .. f0 + cnt - 1 (cnt <= kFoldRows) go through registers into LDS: 16-byte chunk
-// c of thread t is c = t + 256 j (j < 4), row c / 64, key half (c % 64 < 32) or residual half.
+// c of thread t is c = t + 256 j (j < 4), row c / 64, key half (c % 64 < 32) or residual half;
+// the row is uniform over a wave (w + 4 j), its bank row comes from the pending row map.
 // With the rows, wave 0 stages each row's fold coefficient c_f = exp(sum of the log gates of the
 // pending rows after f): a suffix scan over the chunk plus fold_carry, the sum over the chunks
 // already staged (they hold later rows).  Register loads rather than direct-to-LDS loads: an LDS
 // read after a direct load waits for every older memory operation of the wave.  Four named
 // registers (no array), so nothing of it goes to scratch.
-__device__ __forceinline__ uint4 fold_chunk_load(const float *pk, const float *pu, int f0, int c) {
-    const int r = f0 + (c >> 6), half = (c >> 5) & 1, idx = c & 31;
-    return *reinterpret_cast<const uint4 *>((half ? pu : pk) + r * kCvD + idx * 4);
+__device__ __forceinline__ uint4 fold_chunk_load(const float *pk, const float *pu, int row,
+                                                 int lane) {
+    const int half = (lane >> 5) & 1, idx = lane & 31;
+    return *reinterpret_cast<const uint4 *>((half ? pu : pk) + row * kCvD + idx * 4);
 }
 __device__ __forceinline__ void fold_chunk_store(float *fk, float *fu, int cnt, int c, uint4 v) {
     if (c < 64 * cnt) {
@@ -163,12 +165,13 @@ __device__ __forceinline__ void fold_chunk_store(float *fk, float *fu, int cnt, 
 }
 #define GDN_FOLD_LOAD(f0, cnt)                                                          \
     do {                                                                                \
-        const int lc_ = 64 * (cnt) - 1;                                                 \
-        fv0 = fold_chunk_load(pend_k, pend_u, (f0), min(tid, lc_));                     \
-        fv1 = fold_chunk_load(pend_k, pend_u, (f0), min(tid + 256, lc_));               \
-        fv2 = fold_chunk_load(pend_k, pend_u, (f0), min(tid + 512, lc_));               \
-        fv3 = fold_chunk_load(pend_k, pend_u, (f0), min(tid + 768, lc_));               \
-        flv = pend_lg[(f0) + min(tid, (cnt) - 1)];                                      \
+        const int lc_ = (cnt) - 1;                                                      \
+        fv0 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w, lc_)), lane);      \
+        fv1 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w + 4, lc_)), lane);  \
+        fv2 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w + 8, lc_)), lane);  \
+        fv3 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w + 12, lc_)), lane); \
+        const int fl_ = (f0) + min(lane, lc_), rl_ = __shfl(rml, min(fl_, 63));         \
+        flv = pend_lg[fl_ < 64 ? rl_ : min(max(rm[fl_], 0), mrow)];                     \
     } while (0)
 #define GDN_FOLD_STORE(cnt)                                                             \
     do {                                                                                \
@@ -201,8 +204,9 @@ __device__ __forceinline__ float conv4(const float wt[4], float x0, float x1, fl
 }  // namespace
 
 __global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
-void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, int n_max,
-                        int nrec_max, int nlv_max, int nf, int nfc) {
+void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
+                        const int32_t *__restrict__ rows, int n_max, int nrec_max, int nlv_max,
+                        int nf, int nfc) {
     constexpr int D = kCvD, THREADS = 256, NW = 4, JC = 4;
     using LY = CvLayout;
     const VerifyParams &P = CP.V;
@@ -263,6 +267,20 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
 
     const float *pend_k = P.bank_k[role] + row0_bank * D, *pend_u = P.bank_u[role] + row0_bank * D;
     const float *pend_lg = P.bank_lg[role] + row0_bank;
+    // Pending factor f sits in bank row rm[f] (the commit's row map; clamped to the bank).  Lane
+    // f < 64 keeps the row of factor f (read now, used after the first barrier); the three
+    // rows of the conv window's inputs are uniform, scalar loads.
+    const int32_t *rm = rows + int64_t(seq) * P.max_nodes;
+    const int mrow = P.max_nodes - 1;
+    int rml = 0;
+    if (L > 0) rml = min(max(rm[min(lane, L - 1)], 0), mrow);
+    int wrow[3];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) wrow[e] = L >= 3 - e ? min(max(rm[L - 3 + e], 0), mrow) : 0;
+    // bank row of pending factor f, f uniform
+    auto pend_row = [&](int f) {
+        return f < 64 ? __builtin_amdgcn_readlane(rml, f) : min(max(rm[f], 0), mrow);
+    };
     float *fold_k = reinterpret_cast<float *>(lds + lay.fold_k);
     float *fold_u = reinterpret_cast<float *>(lds + lay.fold_u);
     float *fold_c = reinterpret_cast<float *>(lds + lay.fold_c);
@@ -321,16 +339,19 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan, i
         for (int e = 0; e < 3; ++e) {
             win[j][e] = cs[e];
             // pending input L - 3 + e, when it exists
-            pend[j][e] = L >= 3 - e ? pb[int64_t(L - 3 + e) * C] : 0.f;
+            pend[j][e] = L >= 3 - e ? pb[int64_t(wrow[e]) * C] : 0.f;
         }
     }
-    // this lane's share of the pending log gates: their sum gives the fold's gate product
-    float lg_part = 0.f;
-    for (int f = lane; f < L; f += 64) lg_part += pend_lg[f];
     const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
     const uint4 wq = *reinterpret_cast<const uint4 *>(wq_src);
     const uint4 wk = *reinterpret_cast<const uint4 *>(wq_src + int64_t(HD) * 4);
     __syncthreads();  // waits for every direct load (the barrier's fence covers them)
+
+    // this lane's share of the pending log gates (factor `lane`, then every 64th): their sum
+    // gives the fold's gate product; requested ahead of the tile, so waiting for the tile
+    // covers them
+    float lg_part = lane < L ? pend_lg[rml] : 0.f;
+    for (int f = 64 + lane; f < L; f += 64) lg_part += pend_lg[min(max(rm[f], 0), mrow)];
 
     // ---- 1. raw conv inputs banked; state tile requested; conv-window fold; record tables --
     // The bank copies go out first, so they have drained long before any later wait on memory.
@@ -699,9 +720,10 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: conv and verify args disagree on "
                     "n_seqs/n_nodes/max_nodes/layer_begin/n_layers");
     if (va->n_seqs == 0) return GDN_OK;  // empty batch: nothing is read or written
-    if (ca->role != va->role || ca->pending_len != va->pending_len)
+    if (ca->role != va->role || ca->pending_len != va->pending_len ||
+        ca->pending_rows != va->pending_rows)
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: conv and verify args must share the "
-                    "role and pending_len arrays");
+                    "role, pending_len and pending_rows arrays");
     if (!ca->x || !ca->weight || !ca->conv_state || !ca->bank_x[0] || !ca->bank_x[1])
         return fail(GDN_EINVAL, "gdn_tree_conv_verify: null x/weight/conv_state/bank_x");
     if (reinterpret_cast<uintptr_t>(ca->x) % 16 || reinterpret_cast<uintptr_t>(ca->weight) % 16 ||
@@ -741,11 +763,11 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(uint32_t(P.n_blocks));
     if (start == nullptr && stop == nullptr)
-        hipLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), lds, s, CP, P.img, n_max,
-                           nrec_max, nlv_max, nf, nfc);
+        hipLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), lds, s, CP, P.img, P.rows,
+                           n_max, nrec_max, nlv_max, nf, nfc);
     else
         hipExtLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), uint32_t(lds), s, start, stop,
-                              0, CP, P.img, n_max, nrec_max, nlv_max, nf, nfc);
+                              0, CP, P.img, P.rows, n_max, nrec_max, nlv_max, nf, nfc);
     GDN_LAUNCH_CHECK("conv_verify_kernel");
     return GDN_OK;
 }

@@ -37,7 +37,7 @@ namespace gdn {
 // fp32 inputs need twice the staging registers; they get a 2-wave budget to avoid spills.
 template <int D, typename TIn>
 __global__ __launch_bounds__(Tile<D>::THREADS, sizeof(TIn) == 2 ? GDN_VERIFY_MIN_WAVES : 2)
-void verify_chain_kernel(VerifyParams P) {
+void verify_chain_kernel(VerifyParams P, const int32_t *__restrict__ rows) {
     using TL = Tile<D>;
     using SG = Stager<D, TIn>;
     constexpr int M = TL::M, NP = TL::NP, VEC = TL::VEC;
@@ -95,6 +95,8 @@ void verify_chain_kernel(VerifyParams P) {
     c.pk = P.bank_k[role];
     c.pu = P.bank_u[role];
     c.plg = P.bank_lg[role];
+    c.prow = rows + int64_t(seq) * P.max_nodes;  // a separate no-alias argument: scalar loads
+    c.max_nodes = P.max_nodes;
     float *wk = P.bank_k[role ^ 1], *wu = P.bank_u[role ^ 1], *wlg = P.bank_lg[role ^ 1];
     c.bank_row0 = sh * P.max_nodes;  // row index of (layer, seq, head, 0)
 
@@ -231,10 +233,10 @@ static gdn_status launch_verify(const VerifyParams &P, hipStream_t stream, hipEv
     if (P.n_blocks <= 0) return GDN_OK;
     if (start == nullptr && stop == nullptr) {
         hipLaunchKernelGGL((verify_chain_kernel<D, TIn>), dim3(uint32_t(P.n_blocks)),
-                           dim3(Tile<D>::THREADS), 0, stream, P);
+                           dim3(Tile<D>::THREADS), 0, stream, P, P.rows);
     } else {  // timestamps taken by the dispatch itself: no extra packets on the stream
         hipExtLaunchKernelGGL((verify_chain_kernel<D, TIn>), dim3(uint32_t(P.n_blocks)),
-                              dim3(Tile<D>::THREADS), 0, stream, start, stop, 0, P);
+                              dim3(Tile<D>::THREADS), 0, stream, start, stop, 0, P, P.rows);
     }
     GDN_LAUNCH_CHECK("verify_chain_kernel");
     return GDN_OK;
@@ -261,8 +263,8 @@ static gdn_status check_verify_args(const gdn_verify_args *a, bool need_schedule
     if (a->in_dtype != GDN_F32 && a->in_dtype != GDN_BF16)
         return fail(GDN_EINVAL, "verify args: in_dtype %d", a->in_dtype);
     if (a->n_seqs == 0) return GDN_OK;  // empty batch: nothing is read or written
-    if (!a->state || !a->role || !a->pending_len)
-        return fail(GDN_EINVAL, "verify args: null state/role/pending_len");
+    if (!a->state || !a->role || !a->pending_len || !a->pending_rows)
+        return fail(GDN_EINVAL, "verify args: null state/role/pending_len/pending_rows");
     for (int i = 0; i < 2; ++i)
         if (!a->bank_k[i] || !a->bank_u[i] || !a->bank_lg[i])
             return fail(GDN_EINVAL, "verify args: null bank pointer");
@@ -305,7 +307,7 @@ gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
         P.bank_u[i] = a->bank_u[i];
         P.bank_lg[i] = a->bank_lg[i];
     }
-    P.role = a->role; P.pending = a->pending_len; P.boundary = a->workspace; P.out = a->out;
+    P.role = a->role; P.pending = a->pending_len; P.rows = a->pending_rows; P.boundary = a->workspace; P.out = a->out;
     P.img = dev_image;
     P.off_seq = v.off_seq; P.off_chain = v.off_chain; P.off_cnodes = v.off_cnodes;
     P.off_cseq = v.off_cseq; P.off_csrc = v.off_csrc; P.off_store = v.off_store;
@@ -399,6 +401,7 @@ gdn_status flush_state(const gdn_verify_args *a, hipStream_t stream) {
     }
     P.role = a->role;
     P.pending = a->pending_len;
+    P.rows = a->pending_rows;
     P.S = a->n_seqs;
     P.H = a->n_heads;
     P.max_nodes = a->max_nodes;

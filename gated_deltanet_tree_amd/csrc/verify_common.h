@@ -12,6 +12,7 @@ struct VerifyParams {
     float *state;
     float *bank_k[2], *bank_u[2], *bank_lg[2];
     const int32_t *role, *pending;
+    const int32_t *rows;  // [S][max_nodes]: bank row of each pending factor, in path order
     float *boundary;
     float *out;
     const int32_t *img;
@@ -77,7 +78,8 @@ template <> struct VecT<2> {
 // Staging of a block of items into LDS.  An item is a pending fold row (fp32 k, u, lg) or a
 // node (k, q, v, beta, g in the input dtype).  Its LDS slot holds fp32 [k | q | v-or-u |
 // scalar0 | scalar1 | pad]: scalar0 = beta or lg, scalar1 = g.
-//   - The block's node ids are uniform: they are read with scalar loads and stay in SGPRs.
+//   - The block's node ids (for a fold row: its bank row, from the pending row map) are
+//     uniform: they are read with scalar loads and stay in SGPRs.
 //   - Every thread owns NCH 16-byte vector chunks of the block's vectors; the first 2 PB
 //     threads also fetch one per-item scalar each.
 // Loads keep their raw bits until stage_commit, so issuing them never waits on memory; the
@@ -93,14 +95,15 @@ template <int D, typename TIn, int PB_ = GDN_STAGE_ITEMS> struct Stager {
     static constexpr int SLOT = 3 * D + 4;
     uint4 v[NCH];     // per thread: raw vector chunks
     uint32_t sc;      // per thread: raw bits of one per-item scalar (thread < 2 PB)
-    int node[PB];     // uniform: global node id of each node item
+    int node[PB];     // uniform: global node id of each node item, bank row of each fold row
 };
 
 // Per-workgroup context of the staging helpers.  Passed by value and unpacked into scalars
 // before any pointer is selected, so that no private (scratch) copy is ever needed.
 struct ChainCtx {
-    int L, n_items, nbeg, h, layer, T, H;
+    int L, n_items, nbeg, h, layer, T, H, max_nodes;
     int64_t bank_row0, off_cnodes;
+    const int32_t *prow;  // the sequence's pending row map
     const float *pk, *pu, *plg;
     const void *k, *q, *v, *beta, *gate;
     const int32_t *img;
@@ -118,9 +121,14 @@ __device__ __forceinline__ void stage_issue(Stager<D, TIn, PB> &st, const ChainC
     using SG = Stager<D, TIn, PB>;
     const int it1 = min(c.n_items, it0 + SG::PB);
 #pragma unroll
-    for (int jj = 0; jj < SG::PB; ++jj) {  // uniform: node ids of the block
+    for (int jj = 0; jj < SG::PB; ++jj) {  // uniform: node ids / bank rows of the block
         const int item = it0 + jj;
-        st.node[jj] = (item >= c.L && item < it1) ? c.img[c.off_cnodes + c.nbeg + (item - c.L)] : 0;
+        int id = 0;
+        if (item < c.L)  // the map comes from the commit call; the clamp keeps a bad entry in the bank
+            id = min(max(c.prow[item], 0), c.max_nodes - 1);
+        else if (item < it1)
+            id = c.img[c.off_cnodes + c.nbeg + (item - c.L)];
+        st.node[jj] = id;
     }
     // Thread t < 2 PB fetches scalar t / PB (0: beta or lg, 1: g) of item it0 + t % PB; the
     // raw bits are converted only in stage_commit, so nothing here waits for memory.
@@ -128,13 +136,13 @@ __device__ __forceinline__ void stage_issue(Stager<D, TIn, PB> &st, const ChainC
     if (tid < 2 * SG::PB) {
         const int rel = tid % SG::PB, which = tid / SG::PB, item = it0 + rel;
         if (item < it1) {
-            if (item < c.L) {
-                if (which == 0) st.sc = __float_as_uint(c.plg[c.bank_row0 + item]);
-            } else {
-                int node = st.node[0];
+            int node = st.node[0];
 #pragma unroll
-                for (int jj = 1; jj < SG::PB; ++jj)
-                    if (rel == jj) node = st.node[jj];
+            for (int jj = 1; jj < SG::PB; ++jj)
+                if (rel == jj) node = st.node[jj];
+            if (item < c.L) {
+                if (which == 0) st.sc = __float_as_uint(c.plg[c.bank_row0 + node]);
+            } else {
                 const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;
                 const TIn *src = static_cast<const TIn *>(which == 0 ? c.beta : c.gate) + row;
                 if (sizeof(TIn) == 2)
@@ -150,17 +158,17 @@ __device__ __forceinline__ void stage_issue(Stager<D, TIn, PB> &st, const ChainC
         const int rel = j / SG::VCH, item = it0 + rel, ch = j % SG::VCH;
         st.v[i] = make_uint4(0, 0, 0, 0);
         if (j >= SG::PB * SG::VCH || item >= it1) continue;
+        int node = st.node[0];
+#pragma unroll
+        for (int jj = 1; jj < SG::PB; ++jj)
+            if (rel == jj) node = st.node[jj];
         if (item < c.L) {
             if (ch < 2 * SG::FOLD_CV) {
                 const float *src = static_cast<const float *>(pick3(ch < SG::FOLD_CV ? 0 : 1, c.pk, c.pu, c.pu)) +
-                                   (c.bank_row0 + item) * D;
+                                   (c.bank_row0 + node) * D;
                 st.v[i] = reinterpret_cast<const uint4 *>(src)[ch % SG::FOLD_CV];
             }
         } else if (ch < 3 * SG::NODE_CV) {
-            int node = st.node[0];
-#pragma unroll
-            for (int jj = 1; jj < SG::PB; ++jj)
-                if (rel == jj) node = st.node[jj];
             const int vec = ch / SG::NODE_CV;
             const void *base = pick3(vec, c.k, c.q, c.v);
             const int64_t row = (int64_t(c.layer) * c.T + node) * c.H + c.h;

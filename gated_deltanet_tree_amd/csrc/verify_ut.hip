@@ -183,6 +183,9 @@ void verify_ut_kernel(VerifyParams P, int n_max, int np_max, int nf_max) {
             }
         }
         if (L > 0) {
+            // pending factor f sits in bank row rm[f] (the commit's row map, clamped to the bank)
+            const int32_t *rm = P.rows + int64_t(seq) * P.max_nodes;
+            const int mrow = P.max_nodes - 1;
             const float *pk = P.bank_k[role] + row0_bank * D, *pu = P.bank_u[role] + row0_bank * D;
             const int rows_chunks = L * LY::CPR;
             const int fk_chunks = int(round_up(size_t(nf_max) * LY::CPR, 64));
@@ -190,12 +193,14 @@ void verify_ut_kernel(VerifyParams P, int n_max, int np_max, int nf_max) {
                 const int which = base / fk_chunks, b2 = base % fk_chunks;
                 if (b2 >= rows_chunks) continue;
                 const int c = min(b2 + lane, rows_chunks - 1);
-                const float *src = (which == 0 ? pk : pu) + c * 4;
+                const int br = min(max(rm[c / LY::CPR], 0), mrow);
+                const float *src = (which == 0 ? pk : pu) + int64_t(br) * D + (c % LY::CPR) * 4;
                 to_lds<16>(src, lds + lay.fold_k + size_t(base) * 16);
             }
             const float *plg = P.bank_lg[role] + row0_bank;
             for (int base = w * 64; base < L; base += NW * 64)
-                to_lds<4>(plg + min(base + lane, L - 1), lds + lay.fold_lg + size_t(base) * 4);
+                to_lds<4>(plg + min(max(rm[min(base + lane, L - 1)], 0), mrow),
+                          lds + lay.fold_lg + size_t(base) * 4);
         }
     }
     __builtin_amdgcn_s_waitcnt(0);

@@ -49,7 +49,7 @@ struct UtLayout5 {
     static constexpr int NODE_BYTES = CPN * 16;
     static constexpr int WS = D + 4;        // row stride of W and GR in floats (same reason)
     static constexpr int CPR = D * 4 / 16;  // 16-byte chunks per fp32 fold row
-    size_t in, bg, pd, work, fold_k, fold_u, fold_lg, gr, plan, tabs, total;
+    size_t in, bg, pd, work, fold_k, fold_u, gr, plan, tabs, total;
     size_t n64, lv64, rec64;
     __host__ __device__ UtLayout5(int n, int nrec, int nlv, int nf) {
         n64 = round_up(size_t(n), 64);
@@ -66,8 +66,7 @@ struct UtLayout5 {
         const size_t fk = round_up(size_t(nf) * CPR, 64) * 16;
         fold_k = work;
         fold_u = work + fk;
-        fold_lg = work + 2 * fk;
-        const size_t fold_bytes = 2 * fk + round_up(size_t(nf), 64) * 4;
+        const size_t fold_bytes = 2 * fk;
         gr = work + size_t(n) * WS * 4;
         const size_t wg_bytes = size_t(2) * n * WS * 4;
         // plan (direct loads): poff [n64] | lvnode [n64] | lvn [lv64] | recM [rec64]
@@ -82,8 +81,9 @@ struct UtLayout5 {
 // one workgroup of 4 waves per (layer, sequence, head)
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
-void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int n_max,
-                           int nrec_max, int nlv_max, int nf_max) {
+void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
+                           const int32_t *__restrict__ rows, int n_max, int nrec_max, int nlv_max,
+                           int nf_max) {
     constexpr int D = kUtD, THREADS = 256, NW = 4, JC = 4;
     using LY = UtLayout5;
     extern __shared__ __align__(16) float dyn[];
@@ -99,7 +99,6 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     float *GR = reinterpret_cast<float *>(lds + lay.gr);
     const float *FK = reinterpret_cast<const float *>(lds + lay.fold_k);
     const float *FU = reinterpret_cast<const float *>(lds + lay.fold_u);
-    const float *FL = reinterpret_cast<const float *>(lds + lay.fold_lg);
     // Plan of this tree (from the schedule image): record q of node n is q = poff[n] for n
     // itself and poff[n] + 1 + t for its ancestor at distance t + 1; recM = that node.
     int *poff = reinterpret_cast<int *>(lds + lay.plan);
@@ -132,6 +131,12 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     float *committed = P.state + sh * D * D;
     const int64_t row0_bank = sh * P.max_nodes;
     const int64_t node_row0 = (int64_t(layer) * P.T + seq_off) * P.H + h;  // node 0's row
+    // Pending factor f sits in bank row rm[f] (the commit's row map; clamped to the bank).
+    // Lane f < 64 keeps its factor's row: it is read now and used after the first barrier.
+    const int32_t *rm = rows + int64_t(seq) * P.max_nodes;
+    const int mrow = P.max_nodes - 1;
+    int rml = 0;
+    if (L > 0) rml = min(max(rm[min(lane, L - 1)], 0), mrow);
 
     // ---- 0. direct loads: k, q, v, beta, g, parents, depths, pending fold rows ----------
     {
@@ -177,19 +182,27 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
             const float *pk = P.bank_k[role] + row0_bank * D, *pu = P.bank_u[role] + row0_bank * D;
             const int rows_chunks = L * LY::CPR;
             const int fk_chunks = int(round_up(size_t(nf_max) * LY::CPR, 64));
+            static_assert(64 == 2 * LY::CPR, "one load instruction covers two fold rows");
             for (int base = w * 64; base < 2 * fk_chunks; base += NW * 64) {
                 const int which = base / fk_chunks, b2 = base % fk_chunks;
                 if (b2 >= rows_chunks) continue;
                 const int c = min(b2 + lane, rows_chunks - 1);
-                const float *src = (which == 0 ? pk : pu) + c * 4;
+                // the instruction's two factors and their bank rows (uniform: scalar loads)
+                const int fa = b2 / LY::CPR, fb = min(fa + 1, L - 1);
+                const int ra = min(max(rm[fa], 0), mrow), rb = min(max(rm[fb], 0), mrow);
+                const float *src = (which == 0 ? pk : pu) +
+                                   int64_t(c / LY::CPR == fa ? ra : rb) * D + (c % LY::CPR) * 4;
                 to_lds<16>(src, lds + lay.fold_k + size_t(base) * 16);
             }
-            const float *plg = P.bank_lg[role] + row0_bank;
-            for (int base = w * 64; base < L; base += NW * 64)
-                to_lds<4>(plg + min(base + lane, L - 1), lds + lay.fold_lg + size_t(base) * 4);
         }
     }
     __syncthreads();  // waits for every direct load (the barrier's fence covers them)
+
+    // ln g of pending factor `lane` (lanes < L), for the fold; requested before the tile so
+    // that waiting for the tile covers it
+    const float *plg = P.bank_lg[role] + row0_bank;
+    float lgr = 0.f;
+    if (lane < L) lgr = plg[rml];
 
     // The state tile is requested now; its latency hides behind the table and pair phases,
     // which need only LDS.
@@ -300,8 +313,8 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
     // row costs one FMA per element.
     // Rows run last to first so that c builds up backward (c_{L-1} = 1, c_{f-1} = c_f g_f).
     if (L > 0) {
-        float lg_part = 0.f;  // this lane's share of the pending log gates
-        for (int f = lane; f < L; f += 64) lg_part += FL[f];
+        float lg_part = lgr;  // this lane's share of the pending log gates
+        for (int f = 64 + lane; f < L; f += 64) lg_part += plg[min(max(rm[f], 0), mrow)];
         const float G = expf(wave_total(lg_part));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
@@ -323,7 +336,8 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan, int
                     s[1][mt][e] = fmaf(u1, kk[e], s[1][mt][e]);
                 }
             }
-            c *= expf(FL[f]);
+            c *= expf(f < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lgr), f))
+                             : plg[min(max(rm[f], 0), mrow)]);
         }
     }
     if (L > 0) {
@@ -414,11 +428,11 @@ gdn_status launch_ut_mfma(const VerifyParams &P, int n_max, int nrec_max, int nl
     if (P.n_blocks <= 0) return GDN_OK;
     const dim3 grid(uint32_t(P.n_blocks));
     if (start == nullptr && stop == nullptr)
-        hipLaunchKernelGGL(verify_ut_mfma_kernel, grid, dim3(256), lds, stream, P, P.img, n_max,
-                           nrec_max, nlv_max, nf_max);
+        hipLaunchKernelGGL(verify_ut_mfma_kernel, grid, dim3(256), lds, stream, P, P.img, P.rows,
+                           n_max, nrec_max, nlv_max, nf_max);
     else
         hipExtLaunchKernelGGL(verify_ut_mfma_kernel, grid, dim3(256), uint32_t(lds), stream,
-                              start, stop, 0, P, P.img, n_max, nrec_max, nlv_max, nf_max);
+                              start, stop, 0, P, P.img, P.rows, n_max, nrec_max, nlv_max, nf_max);
     GDN_LAUNCH_CHECK("verify_ut_mfma_kernel");
     return GDN_OK;
 }

@@ -163,8 +163,9 @@ gdn_status gdn_ddtree_build(const float *logp, const int32_t *tokens,
  *       (= g_n S_parent (I - beta_n k_n k_n^T) + beta_n v_n k_n^T)
  *   out[n] = S_n q_n
  * where S_parent of a root is the committed state AFTER the deferred fold:
- *   if pending_len[b] = L > 0:  S <- exp(lg_i) S + u_i k_i^T for pending rows i = 0..L-1,
- *   and the folded state is written back to `state` (once, by the root chain).
+ *   if pending_len[b] = L > 0:  S <- exp(lg_i) S + u_i k_i^T for pending factors i = 0..L-1,
+ *   where factor i is row pending_rows[b][i] of the pending bank, and the folded state is
+ *   written back to `state` (once, by the root chain).
  * Factors (k_n, u_n, lg_n = ln g_n) are written to row n (local id) of the write bank
  * 1 - role[b]. Rows of the pending bank role[b] are only read.
  *
@@ -191,6 +192,10 @@ typedef struct {
     float *bank_lg[2];   /* [Ly][S][H][max_nodes]     log decay gates                      */
     const int32_t *role;        /* device [S]: index (0/1) of the pending bank             */
     const int32_t *pending_len; /* device [S]: pending rows to fold, 0 = none              */
+    const int32_t *pending_rows; /* device [S][max_nodes]: bank row of pending factor i of   */
+                                 /* sequence b, in path order; written by gdn_commit_path,   */
+                                 /* entries i < pending_len[b] read by the fold; each within */
+                                 /* [0, max_nodes) (out-of-range entries are clamped)        */
     float *workspace;    /* device scratch of gdn_tree_verify*: gdn_verify_workspace_bytes() */
                          /* bytes of boundary states; not used by gdn_tree_verify_ut*       */
     float *out;          /* [Ly][T][H][d] fp32 outputs                                     */
@@ -283,7 +288,7 @@ gdn_status gdn_prefill_timed(const gdn_prefill_args *args, const int32_t *host_s
  * works", tree-aware conv gather; SpecLA guide, mechanisms 1, 3 and 4).
  *
  * Fold first: if pending_len[b] = L > 0, conv_state[b] <- last 3 of
- *   (conv_state[b] columns, bank_x[role[b]] rows 0..L-1), written back.
+ *   (conv_state[b] columns, bank_x[role[b]] rows pending_rows[b][0..L-1]), written back.
  * Then for node n, channel c:
  *   out[n][c] = sum_{j<4} weight[c][j] * win_n[j],  win_n = last 4 of
  *   (conv_state[b][c][0..2], x along n's root path ending with x[n][c]);
@@ -303,8 +308,9 @@ typedef struct {
     const void *weight;  /* [Ly][Cch][4]                                                   */
     float *conv_state;   /* [Ly][S][Cch][3] committed window, oldest first, in/out         */
     float *bank_x[2];    /* [Ly][S][max_nodes][Cch]                                        */
-    const int32_t *role;
+    const int32_t *role;         /* the same device arrays as the verify's                 */
     const int32_t *pending_len;
+    const int32_t *pending_rows;
     float *out;          /* [Ly][T][Cch] fp32                                              */
 } gdn_conv_args;
 
@@ -329,7 +335,7 @@ gdn_status gdn_tree_conv(const gdn_conv_args *args, const int32_t *host_image,
  * Ignored (may be NULL): va->q, va->k, va->v, va->workspace and ca->out (the conv output stays
  * on chip).  Requirements (GDN_EINVAL otherwise, nothing launched): head_dim 128; bf16 beta,
  * gate, x and weight; ca->channels = 3 H 128; ca's n_seqs, n_nodes, max_nodes, layer_begin and
- * n_layers equal va's; ca->role and ca->pending_len are the same device arrays as va's; x,
+ * n_layers equal va's; ca->role, ca->pending_len and ca->pending_rows are va's arrays; x,
  * weight and bank_x 16-byte aligned; the schedule carries the tree-masked plan and the trees fit one
  * workgroup's LDS (160 KiB: a 64-node top-8 tree of depth 16 takes about 144 KiB).
  * Work: one workgroup per (layer, sequence, head), 4 waves; the conv, SiLU and normalisation
@@ -349,22 +355,32 @@ gdn_status gdn_tree_conv_verify_timed(const gdn_verify_args *va, const gdn_conv_
  * Accept -> commit (SpecLA guide, mechanism 3). Enqueue after the last layer's verify and
  * conv of the step. For each sequence b with accepted root path P_b of length L_b:
  *   L_b = 0            : pending_len[b] = 0 (nothing to commit)
- *   P_b = [0..L_b-1]   : role[b] ^= 1 (the written bank becomes pending; no device copy)
- *   otherwise          : row P_b[i] of every write bank (k, u, lg for every head, x) is
- *                        copied to row i of the pending bank, for all n_layers layers
- *   and pending_len[b] = L_b.
+ *   mode GDN_COMMIT_COMPACT (the guide's accepted-factor cache):
+ *     P_b = [0..L_b-1] : role[b] ^= 1 (the written bank becomes pending; no device copy)
+ *     otherwise        : row P_b[i] of every write bank (k, u, lg for every head, x) is
+ *                        copied to row i of the pending bank, for all n_layers layers;
+ *     pending_rows[b][i] = i
+ *   mode GDN_COMMIT_ROW_MAP (no copy in either case):
+ *     role[b] ^= 1 and pending_rows[b][i] = P_b[i]: the next fold reads the accepted rows
+ *     where the verify wrote them
+ *   and pending_len[b] = L_b.  Both modes fold the same factors in the same order, so the
+ *   committed states they lead to are bit-identical; only the bank rows differ.
  * paths: host, concatenated local ids; path_offsets: host [S+1].
- * dev_paths / dev_path_offsets: the same arrays in device memory (read by the kernels).
+ * dev_paths / dev_path_offsets: the same arrays in device memory, read by the enqueued
+ * kernels (keep them until those have run).
  * role_host / pending_host: host mirrors [S], read and updated by the call.
- * va->role and va->pending_len (device) are updated on the stream; ca may be NULL when no
- * conv banks are kept, otherwise its bank_x, role and pending_len must match va's.
- * GDN_EPATH if some P_b is not a root path of tree b (nothing is enqueued then).
+ * va->role, va->pending_len and va->pending_rows (device) are updated on the stream; ca may
+ * be NULL when no conv banks are kept, otherwise its role, pending_len and pending_rows
+ * must be va's.  GDN_EPATH if some P_b is not a root path of tree b, GDN_EINVAL for an unknown
+ * mode (nothing is enqueued then).
  * ---------------------------------------------------------------------------------- */
+#define GDN_COMMIT_COMPACT 0
+#define GDN_COMMIT_ROW_MAP 1
 gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *paths,
                            const int32_t *path_offsets, const int32_t *dev_paths,
                            const int32_t *dev_path_offsets, const gdn_verify_args *va,
                            const gdn_conv_args *ca, int32_t *role_host, int32_t *pending_host,
-                           void *stream);
+                           int32_t mode, void *stream);
 
 /* Raw row gather used by gdn_commit_path, exported for direct use:
  * for r in [0, n_rows): dst[dst_rows[r] * row_elems ..] = src[src_rows[r] * row_elems ..]

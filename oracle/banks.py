@@ -8,6 +8,11 @@ order.
 
 Readings: "already in order" means path == [0, 1, ..., L-1]; compaction writes into the
 consumed pending bank and leaves the roles unchanged; pending length becomes L either way.
+
+A second commit form (not on the pages, a design of this library) never copies: the written
+bank always becomes pending, and a row map records where each pending factor sits, i.e. the
+accepted path itself.  Reading the written rows through that map gives exactly the rows the
+compaction would have produced, so the fold that follows is the same.
 """
 from __future__ import annotations
 
@@ -47,3 +52,17 @@ def commit_bookkeeping(role: int, path) -> tuple[int, int, bool]:
     if is_in_order(path):
         return role ^ 1, L, False
     return role, L, True
+
+
+def commit_row_map(role: int, path) -> tuple[int, int, list[int]]:
+    """(new role, new pending length, row map) of the no-copy commit: pending factor i is row
+    path[i] of the bank the verify wrote, which becomes the pending bank."""
+    L = len(path)
+    if L == 0:
+        return role, 0, []
+    return role ^ 1, L, [int(p) for p in path]
+
+
+def pending_rows_after_compaction(path) -> list[int]:
+    """Row map after the guide's commit: compacted (or already in-order) rows sit at 0..L-1."""
+    return list(range(len(path)))

@@ -49,11 +49,14 @@ def to_np(t):
 class Batch:
     """One batch of trees on the device with its schedule and layer buffers."""
 
-    def __init__(self, trees, n_layers, H, d, C, max_nodes=None, device="cuda", mode="chain"):
+    def __init__(self, trees, n_layers, H, d, C, max_nodes=None, device="cuda", mode="chain",
+                 commit_mode="row-map"):
         """mode: "chain" = heavy-light chains in dependency waves (gdn_tree_verify),
-        "ut" = tree-masked UT form in one launch (gdn_tree_verify_ut)."""
+        "ut" = tree-masked UT form in one launch (gdn_tree_verify_ut).
+        commit_mode: "row-map" (no copy) or "compact" (the guide's compaction)."""
         import torch
         self.mode = mode
+        self.commit_mode = commit_mode
         self.trees = [np.asarray(t, dtype=np.int32) for t in trees]
         self.image = binding.hld_schedule(self.trees)
         self.view = binding.schedule_view(self.image)
@@ -100,7 +103,7 @@ class Batch:
                                  None, 0, self.Ly)
         ca = binding.conv_args(self.image, self.layers, None, None, None, 0, self.Ly) \
             if self.C else None
-        binding.commit_path(self.image, paths, self.layers, va, ca)
+        binding.commit_path(self.image, paths, self.layers, va, ca, mode=COMMIT_MODES[self.commit_mode])
 
     def flush(self):
         va = binding.verify_args(self.image, self.layers, None, None, None, None, None, None,
@@ -149,9 +152,18 @@ def assert_bank_rows(b: Batch, layer: int, seq: int, bank: int, rows, ref_k, ref
     assert np.all(np.abs(lgg - ref_lg) <= 4 * ulp32(ref_lg)), "banked ln g beyond 4 ulp"
 
 
-def role_pending_expect(role, paths):
-    new = [obanks.commit_bookkeeping(int(r), p) for r, p in zip(role, paths)]
-    return np.array([n[0] for n in new]), np.array([n[1] for n in new])
+COMMIT_MODES = {"row-map": binding.COMMIT_ROW_MAP, "compact": binding.COMMIT_COMPACT}
+
+
+def role_pending_expect(role, paths, commit_mode="row-map"):
+    """Oracle bookkeeping of a commit: new roles, pending lengths and row maps."""
+    if commit_mode == "row-map":
+        new = [obanks.commit_row_map(int(r), p) for r, p in zip(role, paths)]
+        rows = [n[2] for n in new]
+    else:
+        new = [obanks.commit_bookkeeping(int(r), p) for r, p in zip(role, paths)]
+        rows = [obanks.pending_rows_after_compaction(p) for p in paths]
+    return np.array([n[0] for n in new]), np.array([n[1] for n in new]), rows
 
 
 def tiny_inputs(trees, step, H=1, d=16, C=16, dtype="f32", cfg_id=0):

@@ -62,11 +62,13 @@ class FusedRun:
     """A batch of trees on the device, driven through gdn_tree_conv_verify, with the oracle's
     committed states and windows carried alongside."""
 
-    def __init__(self, torch_cuda, trees, H, n_layers, cfg_id, max_nodes=None):
+    def __init__(self, torch_cuda, trees, H, n_layers, cfg_id, max_nodes=None,
+                 commit_mode="row-map"):
         self.torch = torch_cuda
         self.H, self.Ly, self.cfg = H, n_layers, cfg_id
         self.C = 3 * H * D
-        self.b = gh.Batch(trees, n_layers, H, D, self.C, max_nodes=max_nodes, mode="ut")
+        self.b = gh.Batch(trees, n_layers, H, D, self.C, max_nodes=max_nodes, mode="ut",
+                          commit_mode=commit_mode)
         b = self.b
         S0 = np.stack([np.stack([synth.initial_state(cfg_id, l, s, H, D) for s in range(b.S)])
                        for l in range(n_layers)])
@@ -140,9 +142,13 @@ class FusedRun:
         b = self.b
         b.commit(None, paths)
         self.torch.cuda.synchronize()
-        exp_role, exp_pend = gh.role_pending_expect(self.role_before, paths)
+        exp_role, exp_pend, exp_rows = gh.role_pending_expect(self.role_before, paths,
+                                                              b.commit_mode)
         assert np.array_equal(b.layers.role_host, exp_role)
         assert np.array_equal(b.layers.pending_host, exp_pend)
+        row_map = b.layers.pending_rows.cpu().numpy()
+        for s, rows in enumerate(exp_rows):
+            assert list(row_map[s, :len(rows)]) == rows, f"row map seq {s}"
         for (layer, s), r in refs.items():
             p = [int(i) for i in paths[s]]
             self.committed[layer, s] = ogdn.replay(self.committed[layer, s], r["k"], r["v"],
@@ -154,8 +160,9 @@ class FusedRun:
         self.torch.cuda.synchronize()
 
 
-def _steps(torch_cuda, trees, H, n_layers, steps_paths, cfg_id, max_nodes=None):
-    run = FusedRun(torch_cuda, trees, H, n_layers, cfg_id, max_nodes)
+def _steps(torch_cuda, trees, H, n_layers, steps_paths, cfg_id, max_nodes=None,
+           commit_mode="row-map"):
+    run = FusedRun(torch_cuda, trees, H, n_layers, cfg_id, max_nodes, commit_mode)
     for step, paths in enumerate(steps_paths):
         run.verify(step)
         run.check_fold(f"fold before step {step}")
@@ -166,9 +173,10 @@ def _steps(torch_cuda, trees, H, n_layers, steps_paths, cfg_id, max_nodes=None):
     return run
 
 
-def test_small_trees_steps_and_flush(torch_cuda):
+@pytest.mark.parametrize("commit_mode", ["row-map", "compact"])
+def test_small_trees_steps_and_flush(torch_cuda, commit_mode):
     """7-node tree, 8-node chain and a single node; branched, in-order, single-node and empty
-    paths over three steps, then a flush."""
+    paths over three steps, then a flush; both commit forms."""
     tiny, chain, single = synth.TINY_TREE, synth.TINY_CHAIN, np.array([-1])
     trees = [tiny, chain, single]
     steps = [
@@ -176,18 +184,21 @@ def test_small_trees_steps_and_flush(torch_cuda):
         [[0, 2, 5], [0, 1, 2], []],               # branched, short prefix, nothing committed
         [[0, 1, 4], list(range(5)), [0]],
     ]
-    _steps(torch_cuda, trees, H=2, n_layers=2, steps_paths=steps, cfg_id=11)
+    _steps(torch_cuda, trees, H=2, n_layers=2, steps_paths=steps, cfg_id=11,
+           commit_mode=commit_mode)
 
 
-def test_pending_path_longer_than_one_fold_chunk(torch_cuda):
+@pytest.mark.parametrize("commit_mode", ["row-map", "compact"])
+def test_pending_path_longer_than_one_fold_chunk(torch_cuda, commit_mode):
     """A 16-node chain: the LDS fold chunk holds 8 rows at this size, so a pending path of 16
-    (then 9) rows folds in two chunks."""
+    (then 9) rows folds in two chunks; both commit forms."""
     chain = np.arange(-1, 15)
     tree = np.array([-1, 0, 0, 1, 2, 3, 4, 5, 6, 7])
     steps = [[list(range(16)), [0, 1, 3, 5, 7, 9]],
              [list(range(9)), [0, 2, 4, 6, 8]],
              [list(range(16)), [0]]]
-    _steps(torch_cuda, [chain, tree], H=1, n_layers=1, steps_paths=steps, cfg_id=12)
+    _steps(torch_cuda, [chain, tree], H=1, n_layers=1, steps_paths=steps, cfg_id=12,
+           commit_mode=commit_mode)
 
 
 def test_forty_node_tree(torch_cuda):
@@ -279,6 +290,10 @@ def test_rejects_bad_arguments(torch_cuda):
         binding.tree_conv_verify(va, ca, b.image, b.dev_image)
     va, ca = args()
     ca.pending_len = 0
+    with pytest.raises(binding.GdnError):
+        binding.tree_conv_verify(va, ca, b.image, b.dev_image)
+    va, ca = args()
+    ca.pending_rows = 0
     with pytest.raises(binding.GdnError):
         binding.tree_conv_verify(va, ca, b.image, b.dev_image)
     va, ca = args()

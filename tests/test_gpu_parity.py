@@ -45,10 +45,12 @@ def _check_step(b: gh.Batch, h64, S0s, X0s, W, layer=0, write_bank=None, conv=Tr
 
 
 MODES = ["chain", "ut"]
+COMMITS = ["row-map", "compact"]
 
 
-def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0, mode="chain"):
-    b = gh.Batch(trees, 1, H, d, C, mode=mode)
+def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0, mode="chain",
+                commit_mode="row-map"):
+    b = gh.Batch(trees, 1, H, d, C, mode=mode, commit_mode=commit_mode)
     S0 = np.stack([synth.initial_state(cfg_id, 0, s, H, d) for s in range(b.S)])[None]
     X0 = np.stack([synth.initial_conv_state(cfg_id, 0, s, C, 4) for s in range(b.S)])[None]
     W = synth.conv_weight(cfg_id, 0, C, 4, dtype)[None]
@@ -77,20 +79,24 @@ def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d,
                    for name in ("bank_k", "bank_u", "bank_lg", "bank_x")}
         b.commit(inp, paths, Wd)
         torch_cuda.cuda.synchronize()
-        exp_role, exp_pend = gh.role_pending_expect(role_before, paths)
+        exp_role, exp_pend, exp_rows = gh.role_pending_expect(role_before, paths, b.commit_mode)
         assert np.array_equal(b.layers.role_host, exp_role)
         assert np.array_equal(b.layers.pending_host, exp_pend)
         assert np.array_equal(b.layers.role.cpu().numpy(), exp_role)
         assert np.array_equal(b.layers.pending.cpu().numpy(), exp_pend)
+        row_map = b.layers.pending_rows.cpu().numpy()
         for s, path in enumerate(paths):
             wb, pb = 1 - role_before[s], exp_role[s]
+            rows = list(row_map[s, :len(path)])
+            assert rows == exp_rows[s], f"row map seq {s}"
             for name in ("bank_k", "bank_u", "bank_lg", "bank_x"):
                 src = written[name][wb][0, s]
                 dst = getattr(b.layers, name)[pb][0, s]
+                # pending factor i, read where the fold reads it: row rows[i] of the pending bank
                 if name == "bank_x":
-                    got, ref = dst[:len(path)], src[list(path)]
+                    got, ref = dst[rows], src[list(path)]
                 else:
-                    got, ref = dst[:, :len(path)], src[:, list(path)]
+                    got, ref = dst[:, rows], src[:, list(path)]
                 assert torch_cuda.equal(got, ref), f"pending {name} rows seq {s}"
             sl = slice(b.offs[s], b.offs[s + 1])
             seq = {k: h64[k][0, sl] for k in h64}
@@ -109,13 +115,14 @@ def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d,
     assert torch_cuda.equal(before[1], b.layers.conv_state)
 
 
+@pytest.mark.parametrize("commit_mode", COMMITS)
 @pytest.mark.parametrize("mode", MODES)
-def test_tiny_tree_and_chain(torch_cuda, mode):
+def test_tiny_tree_and_chain(torch_cuda, mode, commit_mode):
     """The tiny workload: the 7-node tree [-1,0,0,1,1,2,3] and an 8-node chain, batched, fp32,
-    d = 16.  Step 0 accepts the deepest leaves ([0,1,3,6] is branched -> compaction; the chain is in
-    order -> role swap); step 1 accepts [0,2,5] and [0,1,2]; then flush."""
+    d = 16.  Step 0 accepts the deepest leaves ([0,1,3,6] is branched -> compaction or a row map;
+    the chain is in order -> role swap); step 1 accepts [0,2,5] and [0,1,2]; then flush."""
     trees = [synth.TINY_TREE, synth.TINY_CHAIN]
-    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, mode=mode)
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, mode=mode, commit_mode=commit_mode)
     paths0 = [synth.deepest_leaf_path(t) for t in trees]
     assert list(paths0[0]) == [0, 1, 3, 6] and list(paths0[1]) == list(range(8))
     _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, [[0, 2, 5], [0, 1, 2]], [[0], []]],
@@ -140,13 +147,15 @@ def _all_trees(N):
         yield np.array((-1,) + choice, dtype=np.int32)
 
 
+@pytest.mark.parametrize("commit_mode", COMMITS)
 @pytest.mark.parametrize("mode", MODES)
-def test_every_small_tree_batched(torch_cuda, mode):
+def test_every_small_tree_batched(torch_cuda, mode, commit_mode):
     """All 154 labelled trees with N <= 6 in one batch (d = 16, 2 heads, fp32): three steps of
     verify + commit with seeded random paths of every length (0 included), then flush."""
     trees = [t for N in range(1, 7) for t in _all_trees(N)]
     assert len(trees) == 154
-    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=2, C=8, cfg_id=90, mode=mode)
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, H=2, C=8, cfg_id=90, mode=mode,
+                                     commit_mode=commit_mode)
     rng = np.random.default_rng(4)
     steps = []
     for _ in range(3):
@@ -170,10 +179,10 @@ def test_bf16_inputs_small(torch_cuda, mode):
 
 
 def _layer_case(torch_cuda, name, n_layers, trees, steps, sample_layers, check_outputs_at,
-                mode="chain"):
+                mode="chain", commit_mode="row-map"):
     c = synth.WORKLOADS[name]
     H, d, C, dtype = c["H"], c["d"], c["Cch"], c["dtype"]
-    b = gh.Batch(trees, n_layers, H, d, C, mode=mode)
+    b = gh.Batch(trees, n_layers, H, d, C, mode=mode, commit_mode=commit_mode)
     layers = range(n_layers)
     S0, X0 = workload.host_initial_state(name, layers, b.S)
     W = workload.host_weights(name, layers)
@@ -220,11 +229,11 @@ def test_one_layer_bf16_48_heads(torch_cuda, mode):
                 mode=mode)
 
 
-@pytest.mark.parametrize("mode", MODES)
-def test_48_layers_ten_steps(torch_cuda, mode):
+@pytest.mark.parametrize("mode,commit_mode", [("chain", "compact"), ("ut", "row-map")])
+def test_48_layers_ten_steps(torch_cuda, mode, commit_mode):
     """The 48-layer workload: 48 independent layers, 10 verify steps each folding the previous
     step's accepted length-6 path, then flush; oracle on three sampled layers (states every step,
-    outputs and banks at steps 0, 4 and 9)."""
+    outputs and banks at steps 0, 4 and 9).  Each verify form runs with one commit form."""
     trees = workload.workload_trees("48-layer")
     _layer_case(torch_cuda, "48-layer", 48, trees, steps=10, sample_layers=[0, 23, 47],
-                check_outputs_at={0, 4, 9}, mode=mode)
+                check_outputs_at={0, 4, 9}, mode=mode, commit_mode=commit_mode)

@@ -49,3 +49,24 @@ def test_rotation_and_compaction_hold_the_same_rows():
         path = np.arange(L)
         assert banks.check_path(parent, path)
         assert np.array_equal(banks.compact(written, path), written[:L])
+
+
+def test_row_map_commit_reads_the_compacted_rows():
+    """The no-copy commit: for every root path of a tree, the written rows read through the row
+    map are the rows compaction would produce, the written bank becomes pending whenever
+    something was accepted, and an empty path changes nothing."""
+    rng = np.random.default_rng(13)
+    parent = synth.make_tree(rng, 22, 4, 12)
+    written = rng.standard_normal((22, 5))
+    for node in range(22):
+        path = gdn.root_path(parent, node)
+        role, L, rows = banks.commit_row_map(1, path)
+        assert (role, L) == (0, len(path))
+        assert np.array_equal(written[rows], banks.compact(written, path))
+        old_role, _, compacted = banks.commit_bookkeeping(1, path)
+        # the guide's commit: the rows sit at 0..L-1 of the pending bank either way
+        assert banks.pending_rows_after_compaction(path) == list(range(L))
+        assert old_role == (0 if banks.is_in_order(path) else 1) and compacted != \
+            banks.is_in_order(path)
+    assert banks.commit_row_map(0, []) == (0, 0, [])
+    assert banks.commit_row_map(1, [0]) == (0, 1, [0])

@@ -125,6 +125,9 @@ def test_device_calls_validate_before_launch():
         setattr(args, name, 16)
     for i in range(2):
         args.bank_k[i] = args.bank_u[i] = args.bank_lg[i] = 16
+    assert L.gdn_tree_verify(ctypes.byref(args), binding._ptr(image), 1, None) == -1
+    assert b"pending_rows" in L.gdn_last_error()  # the row map is required
+    args.pending_rows = 16
     args.max_nodes = 3  # smaller than the tree
     assert L.gdn_tree_verify(ctypes.byref(args), binding._ptr(image), 1, None) == -4
     args.max_nodes, args.n_nodes = 4, 5  # disagrees with the schedule
@@ -148,18 +151,29 @@ def test_commit_rejects_bad_paths_before_launch():
     args = binding.VerifyArgs()
     args.n_seqs, args.n_nodes, args.n_heads, args.head_dim = 1, 7, 1, 16
     args.max_nodes, args.n_layers = 7, 1
-    for name in ("state", "role", "pending_len"):
+    for name in ("state", "role", "pending_len", "pending_rows"):
         setattr(args, name, 16)
     for i in range(2):
         args.bank_k[i] = args.bank_u[i] = args.bank_lg[i] = 16
     role, pend = np.array([0], dtype=np.int32), np.array([3], dtype=np.int32)
-    for bad in ([1], [0, 2, 3], [0, 1, 5], [0, 7], [0, 1, 3, 6, 6], [0, -1]):
-        flat, offs = binding.pack_paths([bad])
-        rc = L.gdn_commit_path(binding._ptr(image), binding._ptr(flat), binding._ptr(offs), 16, 16,
-                               ctypes.byref(args), None, binding._ptr(role), binding._ptr(pend),
-                               None)
-        assert rc == -3, bad
-        assert role[0] == 0 and pend[0] == 3
+
+    def commit(path, mode=binding.COMMIT_ROW_MAP, dev_paths=16):
+        flat, offs = binding.pack_paths([path])
+        return L.gdn_commit_path(binding._ptr(image), binding._ptr(flat), binding._ptr(offs),
+                                 dev_paths, 16, ctypes.byref(args), None, binding._ptr(role),
+                                 binding._ptr(pend), mode, None)
+
+    for mode in (binding.COMMIT_COMPACT, binding.COMMIT_ROW_MAP):
+        for bad in ([1], [0, 2, 3], [0, 1, 5], [0, 7], [0, 1, 3, 6, 6], [0, -1]):
+            assert commit(bad, mode) == -3, (bad, mode)
+            assert role[0] == 0 and pend[0] == 3
+    assert commit([0, 1, 3], mode=2) == -1  # unknown mode
+    assert b"mode" in L.gdn_last_error()
+    assert commit([0, 1, 3], dev_paths=None) == -1  # a non-empty path needs its device copy
+    assert b"dev_paths" in L.gdn_last_error()
+    args.pending_rows = None
+    assert commit([0, 1, 3]) == -1
+    assert role[0] == 0 and pend[0] == 3
 
 
 def test_ut_plan_matches_oracle_bit_exact():
