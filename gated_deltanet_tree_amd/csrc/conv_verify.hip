@@ -247,8 +247,13 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     const int lr = lane & 15, lg = lane >> 4;
     const UtUnit un = ut_unit(P);
     const int layer = P.layer_begin + un.layer_rel, seq = un.seq, h = un.h;
-    const int seq_off = P.img[P.off_seq + seq];
-    const int n = P.img[P.off_seq + seq + 1] - seq_off;
+    // Image words are read through `plan` (a no-alias argument) and before any direct load, so
+    // that they are scalar loads: a vector load here would make the wave wait for every direct
+    // load issued before it.
+    const int seq_off = plan[P.off_seq + seq];
+    const int n = plan[P.off_seq + seq + 1] - seq_off;
+    const int r0 = plan[P.off_ut_rec_base + seq], nrec = plan[P.off_ut_rec_base + seq + 1] - r0;
+    const int l0 = plan[P.off_ut_lv_base + seq], nlv = plan[P.off_ut_lv_base + seq + 1] - l0;
     // dense Y and Z rows of the u/o pass, over the fold rows once the fold is done
     const int ys = (n + 3) & ~3;
     float *Yd = reinterpret_cast<float *>(lds + lay.xq);
@@ -268,15 +273,16 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     const float *pend_k = P.bank_k[role] + row0_bank * D, *pend_u = P.bank_u[role] + row0_bank * D;
     const float *pend_lg = P.bank_lg[role] + row0_bank;
     // Pending factor f sits in bank row rm[f] (the commit's row map; clamped to the bank).  Lane
-    // f < 64 keeps the row of factor f (read now, used after the first barrier); the three
-    // rows of the conv window's inputs are uniform, scalar loads.
+    // f < 64 requests the row of factor f now and uses it after the first barrier (touching it
+    // earlier would wait for the load); the three rows of the conv window's inputs are uniform,
+    // scalar loads.  Indices stay in the sequence's map for any L.
     const int32_t *rm = rows + int64_t(seq) * P.max_nodes;
     const int mrow = P.max_nodes - 1;
-    int rml = 0;
-    if (L > 0) rml = min(max(rm[min(lane, L - 1)], 0), mrow);
+    const int rml_raw = rm[min(lane, max(L - 1, 0))];
     int wrow[3];
 #pragma unroll
-    for (int e = 0; e < 3; ++e) wrow[e] = L >= 3 - e ? min(max(rm[L - 3 + e], 0), mrow) : 0;
+    for (int e = 0; e < 3; ++e) wrow[e] = rm[max(L - 3 + e, 0)];
+    int rml = 0;  // set after the first barrier
     // bank row of pending factor f, f uniform
     auto pend_row = [&](int f) {
         return f < 64 ? __builtin_amdgcn_readlane(rml, f) : min(max(rm[f], 0), mrow);
@@ -312,8 +318,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
             }
         }
         if (n > 0) {  // the tree's plan: node blocks, level lists, ancestor records
-            const int r0 = P.img[P.off_ut_rec_base + seq], nrec = P.img[P.off_ut_rec_base + seq + 1] - r0;
-            const int l0 = P.img[P.off_ut_lv_base + seq], nlv = P.img[P.off_ut_lv_base + seq + 1] - l0;
             const int32_t *srcs[4] = {P.img + P.off_ut_node_rec + seq_off,
                                       P.img + P.off_ut_lvnode + seq_off, P.img + P.off_ut_lvn + l0,
                                       P.img + P.off_ut_rec_anc + r0};
@@ -339,7 +343,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
         for (int e = 0; e < 3; ++e) {
             win[j][e] = cs[e];
             // pending input L - 3 + e, when it exists
-            pend[j][e] = L >= 3 - e ? pb[int64_t(wrow[e]) * C] : 0.f;
+            pend[j][e] = L >= 3 - e ? pb[int64_t(min(max(wrow[e], 0), mrow)) * C] : 0.f;
         }
     }
     const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
@@ -350,6 +354,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     // this lane's share of the pending log gates (factor `lane`, then every 64th): their sum
     // gives the fold's gate product; requested ahead of the tile, so waiting for the tile
     // covers them
+    rml = min(max(rml_raw, 0), mrow);
     float lg_part = lane < L ? pend_lg[rml] : 0.f;
     for (int f = 64 + lane; f < L; f += 64) lg_part += pend_lg[min(max(rm[f], 0), mrow)];
 

@@ -118,8 +118,13 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
     const int lr = lane & 15, lg = lane >> 4;
     const UtUnit un = ut_unit(P);
     const int layer = P.layer_begin + un.layer_rel, seq = un.seq, h = un.h;
-    const int seq_off = P.img[P.off_seq + seq];
-    const int n = P.img[P.off_seq + seq + 1] - seq_off;
+    // Image words are read through `plan` (a no-alias argument) and before any direct load, so
+    // that they are scalar loads: a vector load here would make the wave wait for every direct
+    // load issued before it.
+    const int seq_off = plan[P.off_seq + seq];
+    const int n = plan[P.off_seq + seq + 1] - seq_off;
+    const int r0 = plan[P.off_ut_rec_base + seq], nrec = plan[P.off_ut_rec_base + seq + 1] - r0;
+    const int l0 = plan[P.off_ut_lv_base + seq], nlv = plan[P.off_ut_lv_base + seq + 1] - l0;
     // dense Y and Z rows of the u/o pass, over the node rows once the epilogue is done
     const int ys = (n + 3) & ~3;
     float *Yd = reinterpret_cast<float *>(lds + lay.in);
@@ -132,11 +137,11 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
     const int64_t row0_bank = sh * P.max_nodes;
     const int64_t node_row0 = (int64_t(layer) * P.T + seq_off) * P.H + h;  // node 0's row
     // Pending factor f sits in bank row rm[f] (the commit's row map; clamped to the bank).
-    // Lane f < 64 keeps its factor's row: it is read now and used after the first barrier.
+    // Lane f < 64 requests its factor's row now and uses it after the first barrier (touching
+    // it earlier would wait for the load); the index stays in the sequence's map for any L.
     const int32_t *rm = rows + int64_t(seq) * P.max_nodes;
     const int mrow = P.max_nodes - 1;
-    int rml = 0;
-    if (L > 0) rml = min(max(rm[min(lane, L - 1)], 0), mrow);
+    const int rml_raw = rm[min(lane, max(L - 1, 0))];
 
     // ---- 0. direct loads: k, q, v, beta, g, parents, depths, pending fold rows ----------
     {
@@ -166,8 +171,6 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
             }
         }
         if (n > 0) {  // the tree's plan: node blocks, level lists, ancestor records
-            const int r0 = P.img[P.off_ut_rec_base + seq], nrec = P.img[P.off_ut_rec_base + seq + 1] - r0;
-            const int l0 = P.img[P.off_ut_lv_base + seq], nlv = P.img[P.off_ut_lv_base + seq + 1] - l0;
             const int32_t *srcs[4] = {P.img + P.off_ut_node_rec + seq_off,
                                       P.img + P.off_ut_lvnode + seq_off, P.img + P.off_ut_lvn + l0,
                                       P.img + P.off_ut_rec_anc + r0};
@@ -202,7 +205,7 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
     // that waiting for the tile covers it
     const float *plg = P.bank_lg[role] + row0_bank;
     float lgr = 0.f;
-    if (lane < L) lgr = plg[rml];
+    if (lane < L) lgr = plg[min(max(rml_raw, 0), mrow)];
 
     // The state tile is requested now; its latency hides behind the table and pair phases,
     // which need only LDS.
