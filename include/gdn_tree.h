@@ -18,7 +18,8 @@
  *     mechanism 3 (accepted-factor cache): per node the key, the delta-rule residual
  *       update vector, the log decay gate and the conv raw input are kept in two FP32
  *       double-buffered banks; in-order acceptance swaps the banks, branched acceptance
- *       compacts rows back into path order;
+ *       compacts rows back into path order (this library also offers a commit that copies
+ *       nothing and records where the accepted rows sit: see gdn_commit_path);
  *     mechanism 4 (deferred fused commit): the next verify folds the pending factors into
  *       the committed state before verifying; a final flush materialises the last path.
  *   "Luce DFlash server README", section "How it works": DDTree verifies a parent-indexed
