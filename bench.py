@@ -106,35 +106,36 @@ def fused_bytes(view, pending, H, d, in_bytes, n_layers=1):
     read, its conv window (3 d channels x 3 taps) read; when folding, the tile write-back, the
     pending factor rows, the last min(L, 3) pending conv rows and the window write-back.  Per
     node and head: its 3 d conv inputs, beta and g in, o out, k, u, lg banked and the 3 d conv
-    inputs banked (fp32).  The layer's conv weights once.  No q, k, v or conv output in HBM."""
+    inputs banked (raw, in their input dtype).  The layer's conv weights once.  No q, k, v or
+    conv output in HBM."""
     tile = 4 * d * d
     ch = 3 * d
-    per_node = ch * in_bytes + 2 * in_bytes + 4 * d + (8 * d + 4) + 4 * ch
+    per_node = ch * in_bytes + 2 * in_bytes + 4 * d + (8 * d + 4) + in_bytes * ch
     total = 0
     S = int(view["n_seqs"])
     for b in range(S):
         L = int(pending[b])
         n_b = int(view["seq_offsets"][b + 1] - view["seq_offsets"][b])
-        fold = tile + L * (8 * d + 4) + 4 * ch * min(L, 3) + 12 * ch if L > 0 else 0
+        fold = tile + L * (8 * d + 4) + in_bytes * ch * min(L, 3) + 12 * ch if L > 0 else 0
         total += H * (tile + 12 * ch + fold + n_b * per_node)
     return (total + H * ch * 4 * in_bytes) * n_layers
 
 
 def conv_bytes(view, pending, C, in_bytes, n_layers=1):
-    """Per layer: x in, y out, x banked per node; window read (+ write and pending rows read
-    when folding) per sequence; the weights once."""
+    """Per layer: x in, y out (fp32), x banked raw per node; window read (+ write and the last
+    min(L, 3) pending inputs read when folding) per sequence; the weights once."""
     T, S = int(view["n_nodes"]), int(view["n_seqs"])
-    per_node = C * (in_bytes + 4 + 4)
-    seqs = sum(C * (12 + (12 + 4 * int(L) if L > 0 else 0)) for L in pending[:S])
+    per_node = C * (2 * in_bytes + 4)
+    seqs = sum(C * (12 + (12 + in_bytes * min(int(L), 3) if L > 0 else 0)) for L in pending[:S])
     return (T * per_node + seqs + C * 4 * in_bytes) * n_layers
 
 
-def commit_bytes(paths, H, d, C, n_layers, compact=True):
+def commit_bytes(paths, H, d, C, n_layers, compact=True, in_bytes=4):
     """Compaction of branched paths: L rows of (k, u, lg per head + conv input) read + written.
     The row-map commit copies no rows (its map is L int32 per sequence: counted as 0)."""
     if not compact:
         return 0
-    row = H * (8 * d + 4) + 4 * C
+    row = H * (8 * d + 4) + in_bytes * C
     total = 0
     for p in paths:
         L = len(p)
@@ -143,10 +144,10 @@ def commit_bytes(paths, H, d, C, n_layers, compact=True):
     return total * n_layers
 
 
-def fold_bytes(pending, H, d, C, n_layers):
+def fold_bytes(pending, H, d, C, n_layers, in_bytes=4):
     tile = 4 * d * d
-    return n_layers * sum(H * (2 * tile + int(L) * (8 * d + 4)) + C * (24 + 4 * int(L))
-                          for L in pending if L > 0)
+    return n_layers * sum(H * (2 * tile + int(L) * (8 * d + 4)) +
+                          C * (24 + in_bytes * min(int(L), 3)) for L in pending if L > 0)
 
 
 def prefill_bytes(T, S, H, d):
@@ -355,7 +356,7 @@ def main(argv=None):
     state0, conv0 = workload.host_initial_state(args.workload, range(Ly), S)
     weights = workload._to_torch(workload.host_weights(args.workload, range(Ly)), dtype, dev)
     inp = workload.device_step_inputs(args.workload, 0, trees, range(Ly), dev)
-    lay = binding.alloc_layers(Ly, S, H, d, max_nodes, C, dev)
+    lay = binding.alloc_layers(Ly, S, H, d, max_nodes, C, dev, conv_dtype=dtype)
     lay.state.copy_(torch.from_numpy(state0))
     lay.conv_state.copy_(torch.from_numpy(conv0))
     del state0, conv0
@@ -445,7 +446,8 @@ def main(argv=None):
                 if verify != "fused":  # the fused launch already counts its conv traffic
                     acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
                 acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly,
-                                                    commit_mode == binding.COMMIT_COMPACT)
+                                                    commit_mode == binding.COMMIT_COMPACT,
+                                                    in_bytes)
 
         for s in range(args.warmup):
             step(s, None)
@@ -462,7 +464,7 @@ def main(argv=None):
                 for e0, e1 in per_call:
                     acc["verify_ms"] += e0.elapsed_ms(e1)
         total_bytes = acc["verify_bytes"] + acc["conv_bytes"] + acc["commit_bytes"] + \
-            fold_bytes(flush_pending, H, d, C, Ly)
+            fold_bytes(flush_pending, H, d, C, Ly, in_bytes)
         v_launch_s = acc["verify_ms"] / 1e3 / max(acc["verify_launches"], 1)
         v_launch_bytes = acc["stamped_bytes"] / max(acc["verify_launches"], 1)
         calls_total = args.steps * len(vargs)

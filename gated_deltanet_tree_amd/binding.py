@@ -260,6 +260,7 @@ class Layers:
 
     Shapes: state [Ly,S,H,d,d]; bank_k/bank_u [2][Ly,S,H,max_nodes,d]; bank_lg
     [2][Ly,S,H,max_nodes]; conv_state [Ly,S,Cch,3]; bank_x [2][Ly,S,max_nodes,Cch];
+    bank_x holds the raw conv inputs in their own dtype (bf16 or fp32);
     role, pending [S] int32 (device) with host mirrors role_host, pending_host;
     pending_rows [S,max_nodes] int32 (device): the bank row of each pending factor.
     """
@@ -346,7 +347,12 @@ def conv_args(image, layers: Layers, x, weight, out, layer_begin=0, n_layers=1,
     a.channels, a.width = int(layers.conv_state.shape[2]), 4
     a.max_nodes = int(layers.bank_x[0].shape[2]) if max_nodes is None else max_nodes
     a.layer_begin, a.n_layers = layer_begin, n_layers
-    a.in_dtype = GDN_BF16 if (x is not None and x.dtype == torch.bfloat16) else GDN_F32
+    # the conv bank keeps the raw inputs in their own dtype: x (when given) must match it
+    bank_bf16 = layers.bank_x[0].dtype == torch.bfloat16
+    if x is not None and (x.dtype == torch.bfloat16) != bank_bf16:
+        raise ValueError(f"x is {x.dtype} but the conv bank holds {layers.bank_x[0].dtype}: "
+                         "allocate the layers with conv_dtype matching the conv inputs")
+    a.in_dtype = GDN_BF16 if bank_bf16 else GDN_F32
     a.x, a.weight, a.out = _dev(x), _dev(weight), _dev(out)
     a.conv_state = _dev(layers.conv_state)
     a.bank_x[0], a.bank_x[1] = _dev(layers.bank_x[0]), _dev(layers.bank_x[1])
@@ -528,8 +534,10 @@ def flush(vargs: VerifyArgs, cargs: ConvArgs | None, layers: Layers, stream=None
                            _ptr(layers.pending_host), _stream(stream)), "gdn_flush")
 
 
-def alloc_layers(n_layers, n_seqs, n_heads, head_dim, max_nodes, channels=0, device="cuda"):
-    """Zero-initialised device buffers for `n_layers` layers (torch.empty/zeros on device)."""
+def alloc_layers(n_layers, n_seqs, n_heads, head_dim, max_nodes, channels=0, device="cuda",
+                 conv_dtype="f32"):
+    """Zero-initialised device buffers for `n_layers` layers (torch.empty/zeros on device);
+    conv_dtype ("f32" or "bf16") is the dtype of the conv inputs, which the conv bank keeps."""
     import torch
     f = dict(device=device, dtype=torch.float32)
     Ly, S, H, d, Nm = n_layers, n_seqs, n_heads, head_dim, max_nodes
@@ -546,5 +554,7 @@ def alloc_layers(n_layers, n_seqs, n_heads, head_dim, max_nodes, channels=0, dev
     )
     if channels:
         lay.conv_state = torch.zeros((Ly, S, channels, 3), **f)
-        lay.bank_x = [torch.zeros((Ly, S, Nm, channels), **f) for _ in range(2)]
+        xdt = torch.bfloat16 if conv_dtype == "bf16" else torch.float32
+        lay.bank_x = [torch.zeros((Ly, S, Nm, channels), device=device, dtype=xdt)
+                      for _ in range(2)]
     return lay

@@ -30,7 +30,9 @@ gdn_status check_flush_verify_args(const gdn_verify_args *a);
 gdn_status check_flush_conv_args(const gdn_conv_args *a);
 
 struct CompactParams {
-    float *bk[2], *bu[2], *blg[2], *bx[2];
+    float *bk[2], *bu[2], *blg[2];
+    char *bx[2];  // conv-input banks, elements of xbytes bytes (the conv's input dtype)
+    int32_t xbytes;
     const int32_t *role, *paths, *path_off;
     int32_t S, H, D, C, max_nodes, layer_begin;
 };
@@ -67,10 +69,11 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams P) {
     for (int h = tid; h < P.H; h += blockDim.x)
         P.blg[dst][ls * hrows + int64_t(h) * P.max_nodes + i] =
             P.blg[src][ls * hrows + int64_t(h) * P.max_nodes + from];
-    if (P.bx[0] != nullptr) {
-        const float *xs = P.bx[src] + (ls * P.max_nodes + from) * P.C;
-        float *xd = P.bx[dst] + (ls * P.max_nodes + i) * P.C;
-        for (int c = tid; c < P.C; c += blockDim.x) xd[c] = xs[c];
+    if (P.bx[0] != nullptr) {  // raw bit copy of the row, in 2-byte units (C x xbytes is even)
+        const int64_t rb = int64_t(P.C) * P.xbytes;
+        const uint16_t *xs = reinterpret_cast<const uint16_t *>(P.bx[src] + (ls * P.max_nodes + from) * rb);
+        uint16_t *xd = reinterpret_cast<uint16_t *>(P.bx[dst] + (ls * P.max_nodes + i) * rb);
+        for (int64_t c = tid; c < rb / 2; c += blockDim.x) xd[c] = xs[c];
     }
 }
 
@@ -190,7 +193,7 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
             P.bk[i] = va->bank_k[i];
             P.bu[i] = va->bank_u[i];
             P.blg[i] = va->bank_lg[i];
-            P.bx[i] = ca ? ca->bank_x[i] : nullptr;
+            P.bx[i] = ca ? static_cast<char *>(ca->bank_x[i]) : nullptr;
         }
         P.role = va->role;
         P.paths = dev_paths;
@@ -199,6 +202,7 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
         P.H = va->n_heads;
         P.D = va->head_dim;
         P.C = ca ? ca->channels : 0;
+        P.xbytes = ca && ca->in_dtype == GDN_BF16 ? 2 : 4;
         P.max_nodes = va->max_nodes;
         P.layer_begin = va->layer_begin;
         hipLaunchKernelGGL(compact_kernel, dim3(max_len, S, va->n_layers), dim3(256), 0, s, P);

@@ -22,7 +22,7 @@ namespace gdn {
 struct ConvParams {
     const void *x, *w;
     float *cstate;
-    float *bank[2];
+    void *bank[2];  // raw conv inputs, in the input dtype
     const int32_t *role, *pending;
     const int32_t *rows;  // [S][max_nodes] pending row map
     float *out;
@@ -55,10 +55,10 @@ __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P,
         const int i0 = L >= 3 ? min(max(rm[L - 3], 0), m) : 0;
         const int i1 = L >= 2 ? min(max(rm[L - 2], 0), m) : 0;
         const int i2 = min(max(rm[L - 1], 0), m);
-        const float *pb = P.bank[role] + ls * P.max_nodes * P.C + c;
-        const float r0 = L >= 3 ? pb[int64_t(i0) * P.C] : 0.f;
-        const float r1 = L >= 2 ? pb[int64_t(i1) * P.C] : 0.f;
-        const float r2 = pb[int64_t(i2) * P.C];
+        const TIn *pb = static_cast<const TIn *>(P.bank[role]) + ls * P.max_nodes * P.C + c;
+        const float r0 = L >= 3 ? to_f32(pb[int64_t(i0) * P.C]) : 0.f;
+        const float r1 = L >= 2 ? to_f32(pb[int64_t(i1) * P.C]) : 0.f;
+        const float r2 = to_f32(pb[int64_t(i2) * P.C]);
         if (L >= 3) {
             w0 = r0; w1 = r1; w2 = r2;
         } else if (L == 2) {
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P,
     const float k0 = to_f32(wt[0]), k1 = to_f32(wt[1]), k2 = to_f32(wt[2]), k3 = to_f32(wt[3]);
     const int off = P.img[P.off_seq + seq], n = P.img[P.off_seq + seq + 1] - off;
     const TIn *x = static_cast<const TIn *>(P.x) + int64_t(layer) * P.T * P.C + c;
-    float *wb = P.bank[role ^ 1] + ls * P.max_nodes * P.C + c;
+    TIn *wb = static_cast<TIn *>(P.bank[role ^ 1]) + ls * P.max_nodes * P.C + c;
     float *y = P.out + int64_t(layer) * P.T * P.C + c;
     const int32_t *par = P.img + P.off_parent, *dep = P.img + P.off_depth;
     for (int i0 = 0; i0 < n; i0 += GDN_CONV_BLOCK) {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void tree_conv_kernel(ConvParams P,
             const float x1 = depth >= 1 ? xv[j][1] : w2;
             const float x2 = depth >= 2 ? xv[j][2] : (depth == 1 ? w2 : w1);
             const float x3 = depth >= 3 ? xv[j][3] : (depth == 2 ? w2 : (depth == 1 ? w1 : w0));
-            wb[int64_t(i) * P.C] = xv[j][0];
+            wb[int64_t(i) * P.C] = from_exact_f32<TIn>(xv[j][0]);  // the raw input, bit-exact
             y[int64_t(off + i) * P.C] = fmaf(k3, xv[j][0], fmaf(k2, x1, fmaf(k1, x2, k0 * x3)));
         }
     }

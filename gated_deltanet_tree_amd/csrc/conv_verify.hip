@@ -60,7 +60,7 @@ struct ConvVerifyParams {
     const bf16_t *x;     // [Ly][T][C] conv inputs
     const bf16_t *w;     // [Ly][C][4] conv weights, tap 3 multiplies the node's own input
     float *cstate;       // [Ly][S][C][3] committed conv window, oldest first
-    float *bank_x[2];    // [Ly][S][max_nodes][C] conv-input banks
+    bf16_t *bank_x[2];   // [Ly][S][max_nodes][C] conv-input banks (the raw bf16 inputs)
     int32_t C;           // 3 H d
 };
 
@@ -338,12 +338,12 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
         const int ccl = cc < 3 * D ? cc : tid;  // threads with one channel re-read their first
         const int64_t ch = int64_t(ccl >> 7) * HD + h * D + (ccl & (D - 1));
         const float *cs = CP.cstate + (ls * C + ch) * 3;
-        const float *pb = CP.bank_x[role] + ls * P.max_nodes * C + ch;
+        const bf16_t *pb = CP.bank_x[role] + ls * P.max_nodes * C + ch;
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
             win[j][e] = cs[e];
             // pending input L - 3 + e, when it exists
-            pend[j][e] = L >= 3 - e ? pb[int64_t(min(max(wrow[e], 0), mrow)) * C] : 0.f;
+            pend[j][e] = L >= 3 - e ? to_f32(pb[int64_t(min(max(wrow[e], 0), mrow)) * C]) : 0.f;
         }
     }
     const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
@@ -361,15 +361,14 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     // ---- 1. raw conv inputs banked; state tile requested; conv-window fold; record tables --
     // The bank copies go out first, so they have drained long before any later wait on memory.
     {
-        float *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D;
-        for (int e = tid; e < n * 3 * (D / 4); e += THREADS) {  // (node, block, 4 channels)
-            const int nd = e / (3 * (D / 4)), r = e % (3 * (D / 4));
-            const int p = r / (D / 4), c = (r % (D / 4)) * 4;  // plane v | q | k
+        bf16_t *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D;
+        for (int e = tid; e < n * 3 * (D / 8); e += THREADS) {  // (node, block, 8 channels)
+            const int nd = e / (3 * (D / 8)), r = e % (3 * (D / 8));
+            const int p = r / (D / 8), c = (r % (D / 8)) * 8;  // plane v | q | k
             const int blk = p == 0 ? 2 : p - 1;
-            const uint2 x = *reinterpret_cast<const uint2 *>(
-                lds + lay.xv + (size_t(p) * n + nd) * LY::XROW + c * 2);
-            *reinterpret_cast<float4 *>(bx + int64_t(nd) * C + blk * HD + c) =
-                make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
+            *reinterpret_cast<uint4 *>(bx + int64_t(nd) * C + blk * HD + c) =
+                *reinterpret_cast<const uint4 *>(lds + lay.xv + (size_t(p) * n + nd) * LY::XROW +
+                                                 c * 2);
         }
     }
     float s[2][8][4];  // rows 32w + 16nt + lr, columns 16mt + 4lg + e
@@ -762,8 +761,8 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
     CP.x = static_cast<const bf16_t *>(ca->x);
     CP.w = static_cast<const bf16_t *>(ca->weight);
     CP.cstate = ca->conv_state;
-    CP.bank_x[0] = ca->bank_x[0];
-    CP.bank_x[1] = ca->bank_x[1];
+    CP.bank_x[0] = static_cast<bf16_t *>(ca->bank_x[0]);
+    CP.bank_x[1] = static_cast<bf16_t *>(ca->bank_x[1]);
     CP.C = ca->channels;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(uint32_t(P.n_blocks));

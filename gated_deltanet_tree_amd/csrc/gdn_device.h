@@ -19,6 +19,12 @@ template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; 
 template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t x) {
     return __uint_as_float(uint32_t(x) << 16);
 }
+// Inverse of to_f32 for a value that came from T (exact: a widened bf16 has zero low bits).
+template <typename T> __device__ __forceinline__ T from_exact_f32(float x);
+template <> __device__ __forceinline__ float from_exact_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_exact_f32<bf16_t>(float x) {
+    return bf16_t(__float_as_uint(x) >> 16);
+}
 
 // Sum over the 8 consecutive lanes of an aligned lane octet; every lane of the octet gets
 // the total. Two quad permutations (xor 1, xor 2) then the half-row mirror (lane i <-> 7-i),

@@ -294,7 +294,9 @@ gdn_status gdn_prefill_timed(const gdn_prefill_args *args, const int32_t *host_s
  *   out[n][c] = sum_{j<4} weight[c][j] * win_n[j],  win_n = last 4 of
  *   (conv_state[b][c][0..2], x along n's root path ending with x[n][c]);
  * weight[c][3] multiplies the current token; no bias, no activation.
- * Raw inputs x[n] (as fp32) go to row n (local id) of bank_x[1 - role[b]].
+ * Raw inputs x[n] go to row n (local id) of bank_x[1 - role[b]], in in_dtype: the bank keeps
+ * every raw input bit-exact, as the guide's FP32 bank does; for bf16 inputs the bf16 bits are
+ * that exact value in half the bytes.
  * ---------------------------------------------------------------------------------- */
 typedef struct {
     int32_t n_seqs;      /* S                                                              */
@@ -304,11 +306,11 @@ typedef struct {
     int32_t max_nodes;   /* bank rows per (layer, seq); >= every N_b                       */
     int32_t layer_begin;
     int32_t n_layers;
-    int32_t in_dtype;    /* gdn_dtype of x and weight                                      */
+    int32_t in_dtype;    /* gdn_dtype of x, weight and bank_x (fold-only calls: of bank_x) */
     const void *x;       /* [Ly][T][Cch]                                                   */
     const void *weight;  /* [Ly][Cch][4]                                                   */
     float *conv_state;   /* [Ly][S][Cch][3] committed window, oldest first, in/out         */
-    float *bank_x[2];    /* [Ly][S][max_nodes][Cch]                                        */
+    void *bank_x[2];     /* [Ly][S][max_nodes][Cch] raw inputs, in in_dtype                */
     const int32_t *role;         /* the same device arrays as the verify's                 */
     const int32_t *pending_len;
     const int32_t *pending_rows;

@@ -50,7 +50,7 @@ class Batch:
     """One batch of trees on the device with its schedule and layer buffers."""
 
     def __init__(self, trees, n_layers, H, d, C, max_nodes=None, device="cuda", mode="chain",
-                 commit_mode="row-map"):
+                 commit_mode="row-map", conv_dtype="f32"):
         """mode: "chain" = heavy-light chains in dependency waves (gdn_tree_verify),
         "ut" = tree-masked UT form in one launch (gdn_tree_verify_ut).
         commit_mode: "row-map" (no copy) or "compact" (the guide's compaction)."""
@@ -65,7 +65,8 @@ class Batch:
         self.offs = self.view["seq_offsets"].astype(int)
         self.Ly, self.H, self.d, self.C = n_layers, H, d, C
         self.max_nodes = max_nodes or max(len(t) for t in trees)
-        self.layers = binding.alloc_layers(n_layers, self.S, H, d, self.max_nodes, C, device)
+        self.layers = binding.alloc_layers(n_layers, self.S, H, d, self.max_nodes, C, device,
+                                           conv_dtype=conv_dtype)
         ws = binding.verify_workspace_bytes(self.image, H, d, 1)
         self.workspace = torch.zeros(max(ws // 4, 1), device=device, dtype=torch.float32)
         self.out = torch.zeros((n_layers, self.T, H, d), device=device, dtype=torch.float32)

@@ -68,7 +68,7 @@ class FusedRun:
         self.H, self.Ly, self.cfg = H, n_layers, cfg_id
         self.C = 3 * H * D
         self.b = gh.Batch(trees, n_layers, H, D, self.C, max_nodes=max_nodes, mode="ut",
-                          commit_mode=commit_mode)
+                          commit_mode=commit_mode, conv_dtype="bf16")
         b = self.b
         S0 = np.stack([np.stack([synth.initial_state(cfg_id, l, s, H, D) for s in range(b.S)])
                        for l in range(n_layers)])

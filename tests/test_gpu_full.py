@@ -31,7 +31,7 @@ def _full_case(torch, name, steps, n_samples, seed, mode="chain"):
     c = synth.WORKLOADS[name]
     H, d, C, dtype, Ly = c["H"], c["d"], c["Cch"], c["dtype"], c["Ly"]
     trees = workload.workload_trees(name)
-    b = gh.Batch(trees, Ly, H, d, C, mode=mode)
+    b = gh.Batch(trees, Ly, H, d, C, mode=mode, conv_dtype=dtype)
     S0, X0 = workload.host_initial_state(name, range(Ly), b.S)
     W = workload.host_weights(name, range(Ly))
     b.set_state(S0, X0)
@@ -170,7 +170,7 @@ def test_run_to_run_deterministic(torch_cuda, mode):
 
 def _edge_run(torch, trees, H, d, C, steps_paths, cfg_id, max_nodes=None, dtype="f32",
               mode="chain"):
-    b = gh.Batch(trees, 1, H, d, C, max_nodes=max_nodes, mode=mode)
+    b = gh.Batch(trees, 1, H, d, C, max_nodes=max_nodes, mode=mode, conv_dtype=dtype)
     S0 = np.stack([synth.initial_state(cfg_id, 0, s, H, d) for s in range(b.S)])
     X0 = np.stack([synth.initial_conv_state(cfg_id, 0, s, C, 4) for s in range(b.S)])
     W = synth.conv_weight(cfg_id, 0, C, 4, dtype)

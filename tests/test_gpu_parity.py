@@ -50,7 +50,7 @@ COMMITS = ["row-map", "compact"]
 
 def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0, mode="chain",
                 commit_mode="row-map"):
-    b = gh.Batch(trees, 1, H, d, C, mode=mode, commit_mode=commit_mode)
+    b = gh.Batch(trees, 1, H, d, C, mode=mode, commit_mode=commit_mode, conv_dtype=dtype)
     S0 = np.stack([synth.initial_state(cfg_id, 0, s, H, d) for s in range(b.S)])[None]
     X0 = np.stack([synth.initial_conv_state(cfg_id, 0, s, C, 4) for s in range(b.S)])[None]
     W = synth.conv_weight(cfg_id, 0, C, 4, dtype)[None]
@@ -182,7 +182,7 @@ def _layer_case(torch_cuda, name, n_layers, trees, steps, sample_layers, check_o
                 mode="chain", commit_mode="row-map"):
     c = synth.WORKLOADS[name]
     H, d, C, dtype = c["H"], c["d"], c["Cch"], c["dtype"]
-    b = gh.Batch(trees, n_layers, H, d, C, mode=mode, commit_mode=commit_mode)
+    b = gh.Batch(trees, n_layers, H, d, C, mode=mode, commit_mode=commit_mode, conv_dtype=dtype)
     layers = range(n_layers)
     S0, X0 = workload.host_initial_state(name, layers, b.S)
     W = workload.host_weights(name, layers)
