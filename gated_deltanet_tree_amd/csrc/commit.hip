@@ -10,7 +10,8 @@
 // Readings: "in order" = the path is [0, 1, ..., L-1]; compaction writes rows 0..L-1 of the
 // bank that the last verify consumed (the pending one) and leaves the roles as they are.
 // The kernels re-derive the per-sequence decision from the device copy of the paths, so no
-// host-to-device copy happens inside the library.
+// host-to-device copy happens inside the library.  The conv-input bank keeps the raw inputs in
+// their own dtype (exact, like an FP32 copy), so its rows are copied as raw bits.
 //
 // Every fold reads pending factor i from bank row pending_rows[b][i].  The guide's mode
 // (compaction) keeps that map the identity.  The row-map mode never copies: the written bank
