@@ -59,7 +59,8 @@ def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0, mode=
     return b, S0[0].astype(np.float64), X0[0].astype(np.float64), workload.widen(W[0], dtype), Wd
 
 
-def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d, C):
+def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d, C,
+               commit_modes=None):
     """Several verify+commit steps then a flush, each checked against the oracle carrying the
     exact committed state (replay of the accepted paths)."""
     committed, window = [s.copy() for s in S0], [x.copy() for x in X0]
@@ -77,6 +78,8 @@ def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d,
         _check_step(b, h64, committed, window, W64, 0, write_bank=1 - role_before)
         written = {name: [t.clone() for t in getattr(b.layers, name)]
                    for name in ("bank_k", "bank_u", "bank_lg", "bank_x")}
+        if commit_modes is not None:
+            b.commit_mode = commit_modes[step]
         b.commit(inp, paths, Wd)
         torch_cuda.cuda.synchronize()
         exp_role, exp_pend, exp_rows = gh.role_pending_expect(role_before, paths, b.commit_mode)
@@ -127,6 +130,19 @@ def test_tiny_tree_and_chain(torch_cuda, mode, commit_mode):
     assert list(paths0[0]) == [0, 1, 3, 6] and list(paths0[1]) == list(range(8))
     _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, [[0, 2, 5], [0, 1, 2]], [[0], []]],
                "f32", 0, 1, 16, 16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_commit_modes_alternate(torch_cuda, mode):
+    """A caller may switch commit forms between steps: row map, compaction, row map, compaction
+    over four steps of the tiny tree and chain (branched, in-order and empty paths), then flush;
+    every fold reads the rows the last commit recorded."""
+    trees = [synth.TINY_TREE, synth.TINY_CHAIN]
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, mode=mode)
+    steps = [[[0, 1, 3, 6], list(range(8))], [[0, 2, 5], [0, 1, 2]], [[0, 1, 4], []],
+             [[0, 2], list(range(6))]]
+    _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps, "f32", 0, 1, 16, 16,
+               commit_modes=["row-map", "compact", "row-map", "compact"])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
