@@ -131,7 +131,6 @@ struct CvLayout {
     }
 };
 
-// SiLU with the hardware exp2 and reciprocal (each within about an ulp).
 // Inclusive suffix sum over lanes 0-15 (lane l gets the sum of lanes l .. 15); other lanes get
 // partial sums that are not used.
 __device__ __forceinline__ float chunk_suffix_sum(float x) {
@@ -148,8 +147,10 @@ __device__ __forceinline__ float chunk_suffix_sum(float x) {
 // c of thread t is c = t + 256 j (j < 4), row c / 64, key half (c % 64 < 32) or residual half;
 // the row is uniform over a wave (w + 4 j), its bank row comes from the pending row map.
 // With the rows, wave 0 stages each row's fold coefficient c_f = exp(sum of the log gates of the
-// pending rows after f): a suffix scan over the chunk plus fold_carry, the sum over the chunks
-// already staged (they hold later rows).  Register loads rather than direct-to-LDS loads: an LDS
+// pending rows after f): an exclusive suffix scan over the chunk (lane f sums the log gates of
+// lanes f + 1 .. 15, never its own, so a zero gate's -inf is only ever added, and c_f = 0 for
+// every row before it) plus fold_carry, the sum over the chunks already staged (they hold later
+// rows).  Register loads rather than direct-to-LDS loads: an LDS
 // read after a direct load waits for every older memory operation of the wave.  Four named
 // registers (no array), so nothing of it goes to scratch.
 __device__ __forceinline__ uint4 fold_chunk_load(const float *pk, const float *pu, int row,
@@ -181,12 +182,14 @@ __device__ __forceinline__ void fold_chunk_store(float *fk, float *fu, int cnt, 
         fold_chunk_store(fold_k, fold_u, (cnt), tid + 768, fv3);                        \
         if (w == 0) {                                                                   \
             const float v_ = lane < (cnt) ? flv : 0.f;                                  \
-            const float x_ = chunk_suffix_sum(v_);                                      \
-            if (lane < (cnt)) fold_c[lane] = expf(fold_carry + (x_ - v_));             \
-            fold_carry += __shfl(x_, 0);                                                \
+            const float n_ = __shfl_down(v_, 1);                                        \
+            const float x_ = chunk_suffix_sum(lane + 1 < 16 ? n_ : 0.f);                \
+            if (lane < (cnt)) fold_c[lane] = expf(fold_carry + x_);                     \
+            fold_carry += __shfl(x_ + v_, 0);                                           \
         }                                                                               \
     } while (0)
 
+// SiLU, y / (1 + e^-y), with the hardware exp and reciprocal (each within about an ulp).
 __device__ __forceinline__ float silu(float y) {
     return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
 }

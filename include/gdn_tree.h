@@ -186,7 +186,9 @@ typedef struct {
     const void *q, *k;   /* [Ly][T][H][d]     (per-layer block T*H*d)                      */
     const void *v;       /* [Ly][T][H][d]                                                  */
     const void *beta;    /* [Ly][T][H]        (per-layer block T*H)                        */
-    const void *gate;    /* [Ly][T][H]        g in (0, 1], linear (not log)                */
+    const void *gate;    /* [Ly][T][H]        g in [0, 1], linear (not log); g = 0 banks    */
+                         /* ln g = -inf, whose fold coefficient is exactly 0 (the state    */
+                         /* before that token is erased, as the recurrence says)           */
     float *state;        /* [Ly][S][H][d][d]  committed state, row = d_v index, in/out     */
     float *bank_k[2];    /* [Ly][S][H][max_nodes][d]  keys                                 */
     float *bank_u[2];    /* [Ly][S][H][max_nodes][d]  residual update vectors              */
@@ -268,7 +270,7 @@ typedef struct {
     int32_t in_dtype;    /* must be GDN_BF16                                                */
     int32_t reserved;
     const void *q, *k, *v;      /* [Ly][T][H][d] bf16, 16-byte aligned                       */
-    const void *beta, *gate;    /* [Ly][T][H] bf16, gate = g in (0, 1] (linear)              */
+    const void *beta, *gate;    /* [Ly][T][H] bf16, gate = g in [0, 1] (linear)              */
     const int32_t *seq_offsets; /* device [S+1]: sequence b holds tokens [off[b], off[b+1])  */
     float *state;        /* [Ly][S][H][d][d] fp32 committed states, in/out, 16-byte aligned */
     float *out;          /* [Ly][T][H][d] fp32 outputs, 16-byte aligned                     */

@@ -16,7 +16,7 @@ chain mode is the same tree with no branching.
 Conventions of the arrays (one layer, one sequence):
     parent [N] int, parent[0] == -1, 0 <= parent[i] < i
     S0     [H, d_v, d_k]            committed state
-    q, k   [N, H, d_k];  v [N, H, d_v];  beta, gate [N, H]  (gate = g in (0, 1], linear)
+    q, k   [N, H, d_k];  v [N, H, d_v];  beta, gate [N, H]  (gate = g in [0, 1], linear)
 All arithmetic is float64; callers pass the exact values the device reads (bf16 widened).
 """
 from __future__ import annotations

@@ -15,3 +15,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Largest parity errors the GPU tests measured, per quantity and verify form."""
+    gh = sys.modules.get("gpu_harness")
+    if gh is None or not gh.MAX_ERR:
+        return
+    terminalreporter.write_sep("-", "largest parity errors measured (quantity, verify form)")
+    for (what, mode), err in sorted(gh.MAX_ERR.items()):
+        terminalreporter.write_line(f"{what:>10s} {mode:>6s}  {err:.3e}")

@@ -9,7 +9,7 @@ products), a 48-node top-8 tree of depth 16, a 64-node top-8 tree next to a 16-n
 workload (32 sequences x 22-node trees x 48 heads) on sampled sequences.
 
 Tolerances: o per (node, head) vector <= 1e-3 normwise max relative error; committed state <= 1e-5
-relative Frobenius per (layer, seq, head) tile; banked u <= 1e-4 relative 2-norm per row; ln g
+relative Frobenius per (layer, seq, head) tile; banked u <= 1e-5 relative 2-norm per row; ln g
 within 4 fp32 ulp; conv inputs and folded windows bit-exact (copies of bf16 / fp32 values).
 The banked key is the kernel's fp32 unit key: conv (4 fused multiply-adds of exact products),
 SiLU (exp and a division) and the normalisation (a sum of squares, a square root and a
@@ -28,7 +28,7 @@ import gpu_harness as gh
 pytestmark = pytest.mark.gpu
 
 D = 128
-K_TOL = 1e-5
+K_TOL = gh.K_TOL
 
 
 @pytest.fixture(scope="module")
@@ -67,7 +67,7 @@ class FusedRun:
         self.torch = torch_cuda
         self.H, self.Ly, self.cfg = H, n_layers, cfg_id
         self.C = 3 * H * D
-        self.b = gh.Batch(trees, n_layers, H, D, self.C, max_nodes=max_nodes, mode="ut",
+        self.b = gh.Batch(trees, n_layers, H, D, self.C, max_nodes=max_nodes, mode="fused",
                           commit_mode=commit_mode, conv_dtype="bf16")
         b = self.b
         S0 = np.stack([np.stack([synth.initial_state(cfg_id, l, s, H, D) for s in range(b.S)])
@@ -97,7 +97,7 @@ class FusedRun:
                     "gate": workload.widen(gate, "bf16")}
 
     def check_fold(self, what):
-        gh.assert_state(gh.to_np(self.b.layers.state), self.committed, what=what)
+        gh.assert_state(gh.to_np(self.b.layers.state), self.committed, what=what, mode="fused")
         cs = gh.to_np(self.b.layers.conv_state)
         assert np.array_equal(cs, self.window.astype(np.float32)), f"conv window after {what}"
 
@@ -108,7 +108,8 @@ class FusedRun:
         o, q, k, v = prologue.conv_verify(b.trees[s], self.committed[layer, s],
                                           self.window[layer, s], x, self.W64[layer], beta, gate,
                                           self.H, D)
-        kf, uf, lg = ogdn.factors(b.trees[s], self.committed[layer, s], k, v, beta, gate)
+        with np.errstate(divide="ignore"):  # a zero gate banks ln g = -inf
+            kf, uf, lg = ogdn.factors(b.trees[s], self.committed[layer, s], k, v, beta, gate)
         return dict(o=o, k=kf, u=uf, lg=lg, v=v, beta=beta, gate=gate, x=x)
 
     def check_outputs(self, seqs=None, layers=None):
@@ -121,16 +122,10 @@ class FusedRun:
                 r = self.oracle(layer, s)
                 sl = slice(b.offs[s], b.offs[s + 1])
                 n = len(b.trees[s])
-                gh.assert_outputs(o_gpu[sl], r["o"], what=f"o layer {layer} seq {s}")
+                gh.assert_outputs(o_gpu[sl], r["o"], what=f"o layer {layer} seq {s}",
+                                  mode="fused")
                 wb = 1 - int(self.role_before[s])
-                kg = gh.to_np(b.layers.bank_k[wb][layer, s][:, :n]).transpose(1, 0, 2)
-                kerr = np.linalg.norm(kg - r["k"], axis=-1) / np.linalg.norm(r["k"], axis=-1)
-                assert np.max(kerr) <= K_TOL, f"banked k: rel error {np.max(kerr):.3e}"
-                ug = gh.to_np(b.layers.bank_u[wb][layer, s][:, :n]).transpose(1, 0, 2)
-                uerr = np.linalg.norm(ug - r["u"], axis=-1) / np.linalg.norm(r["u"], axis=-1)
-                assert np.max(uerr) <= gh.U_TOL, f"banked u: rel error {np.max(uerr):.3e}"
-                lgg = gh.to_np(b.layers.bank_lg[wb][layer, s][:, :n]).T
-                assert np.all(np.abs(lgg - r["lg"]) <= 4 * gh.ulp32(r["lg"])), "banked ln g"
+                gh.assert_bank_rows(b, layer, s, wb, range(n), r["k"], r["u"], r["lg"])
                 xb = gh.to_np(b.layers.bank_x[wb][layer, s][:n])
                 assert np.array_equal(xb, r["x"]), "banked conv inputs not exact"
                 refs[(layer, s)] = r
@@ -161,9 +156,13 @@ class FusedRun:
 
 
 def _steps(torch_cuda, trees, H, n_layers, steps_paths, cfg_id, max_nodes=None,
-           commit_mode="row-map"):
+           commit_mode="row-map", commit_modes=None):
+    """Verify + check + commit per step, then flush; commit_modes switches the commit form
+    step by step."""
     run = FusedRun(torch_cuda, trees, H, n_layers, cfg_id, max_nodes, commit_mode)
     for step, paths in enumerate(steps_paths):
+        if commit_modes is not None:
+            run.b.commit_mode = commit_modes[step]
         run.verify(step)
         run.check_fold(f"fold before step {step}")
         refs = run.check_outputs()
@@ -190,8 +189,9 @@ def test_small_trees_steps_and_flush(torch_cuda, commit_mode):
 
 @pytest.mark.parametrize("commit_mode", ["row-map", "compact"])
 def test_pending_path_longer_than_one_fold_chunk(torch_cuda, commit_mode):
-    """A 16-node chain: the LDS fold chunk holds 8 rows at this size, so a pending path of 16
-    (then 9) rows folds in two chunks; both commit forms."""
+    """A 16-node chain next to a 10-node tree: at 16 nodes and 16 bank rows the LDS room after
+    the v plane holds 6 fold rows (7 would need 8448 bytes of its 8192), so a pending path of
+    16 rows folds in three chunks (6, 6, 4) and one of 9 in two; both commit forms."""
     chain = np.arange(-1, 15)
     tree = np.array([-1, 0, 0, 1, 2, 3, 4, 5, 6, 7])
     steps = [[list(range(16)), [0, 1, 3, 5, 7, 9]],
@@ -199,6 +199,20 @@ def test_pending_path_longer_than_one_fold_chunk(torch_cuda, commit_mode):
              [list(range(16)), [0]]]
     _steps(torch_cuda, [chain, tree], H=1, n_layers=1, steps_paths=steps, cfg_id=12,
            commit_mode=commit_mode)
+
+
+def test_commit_modes_alternate(torch_cuda):
+    """A caller may switch commit forms between steps: row map, compaction, row map,
+    compaction over four steps of the tiny tree, the 8-node chain and a single node (branched,
+    in-order, root-only and empty paths), then flush; every fused fold reads the rows the last
+    commit recorded."""
+    trees = [synth.TINY_TREE, synth.TINY_CHAIN, np.array([-1])]
+    steps = [[[0, 1, 3, 6], list(range(8)), [0]],
+             [[0, 2, 5], [0, 1, 2], []],
+             [[0, 1, 4], [], [0]],
+             [[0, 2], list(range(6)), [0]]]
+    _steps(torch_cuda, trees, H=2, n_layers=1, steps_paths=steps, cfg_id=19,
+           commit_modes=["row-map", "compact", "row-map", "compact"])
 
 
 def test_forty_node_tree(torch_cuda):

@@ -23,11 +23,13 @@ def torch_cuda():
     return torch
 
 
-MODES = ["chain", "ut"]
+MODES = ["chain", "ut", "fused"]
 
 
 def _full_case(torch, name, steps, n_samples, seed, mode="chain"):
-    """Run `steps` verify+commit steps of a full-size preset, then flush; check sampled pairs."""
+    """Run `steps` verify+commit steps of a full-size preset, then flush; check sampled pairs.
+    In the fused form q, k and v come from the conv of the preset's x (3 H d channels), and
+    the oracle is the prologue followed by the tree verify."""
     c = synth.WORKLOADS[name]
     H, d, C, dtype, Ly = c["H"], c["d"], c["Cch"], c["dtype"], c["Ly"]
     trees = workload.workload_trees(name)
@@ -46,33 +48,39 @@ def _full_case(torch, name, steps, n_samples, seed, mode="chain"):
         role_before = b.layers.role_host.copy()
         b.step(inp, Wd)
         torch.cuda.synchronize()
+        refs = {}
         for (l, s) in pairs:
             sl = slice(b.offs[s], b.offs[s + 1])
             h64 = {k: workload.widen(v[l, sl], dtype) for k, v in h.items()}
-            gh.assert_state(gh.to_np(b.layers.state[l, s]), committed[(l, s)],
+            gh.assert_state(gh.to_np(b.layers.state[l, s]), committed[(l, s)], mode=mode,
                             what=f"committed layer {l} seq {s} step {step}")
             assert np.array_equal(gh.to_np(b.layers.conv_state[l, s]),
                                   window[(l, s)].astype(np.float32))
-            o, states = ogdn.verify(trees[s], committed[(l, s)], h64["q"], h64["k"], h64["v"],
-                                    h64["beta"], h64["gate"])
-            kf, uf, lg = ogdn.factors(trees[s], committed[(l, s)], h64["k"], h64["v"],
-                                      h64["beta"], h64["gate"], states)
-            gh.assert_outputs(gh.to_np(b.out[l, sl]), o, what=f"o layer {l} seq {s}")
-            y = oconv.tree_conv(trees[s], window[(l, s)], h64["x"], workload.widen(W[l], dtype))
-            gh.assert_outputs(gh.to_np(b.y[l, sl]), y, what=f"y layer {l} seq {s}")
-            gh.assert_bank_rows(b, l, s, 1 - role_before[s], range(len(trees[s])), kf, uf, lg)
+            r = gh.oracle_pair(trees[s], committed[(l, s)], window[(l, s)],
+                               workload.widen(W[l], dtype), h64, mode, H, d)
+            gh.assert_outputs(gh.to_np(b.out[l, sl]), r["o"], mode=mode,
+                              what=f"o layer {l} seq {s}")
+            if r["y"] is not None:
+                gh.assert_outputs(gh.to_np(b.y[l, sl]), r["y"], mode=mode, quantity="conv y",
+                                  what=f"y layer {l} seq {s}")
+            gh.assert_bank_rows(b, l, s, 1 - role_before[s], range(len(trees[s])), r["k"],
+                                r["u"], r["lg"])
+            xb = gh.to_np(b.layers.bank_x[1 - role_before[s]][l, s][:len(trees[s])])
+            assert np.array_equal(xb, h64["x"]), f"banked conv inputs layer {l} seq {s}"
+            refs[(l, s)] = (r, h64)
         paths = [synth.workload_path(name, step, s, trees[s]) for s in range(b.S)]
         b.commit(inp, paths, Wd)
         for (l, s) in pairs:
-            sl = slice(b.offs[s], b.offs[s + 1])
-            h64 = {k: workload.widen(v[l, sl], dtype) for k, v in h.items()}
-            committed[(l, s)] = ogdn.replay(committed[(l, s)], h64["k"], h64["v"], h64["beta"],
-                                            h64["gate"], paths[s])
+            r, h64 = refs[(l, s)]
+            k, v = r["kv"]
+            committed[(l, s)] = ogdn.replay(committed[(l, s)], k, v, h64["beta"], h64["gate"],
+                                            paths[s])
             window[(l, s)] = oconv.commit_window(window[(l, s)], h64["x"], paths[s])
     b.flush()
     torch.cuda.synchronize()
     for (l, s) in pairs:
-        gh.assert_state(gh.to_np(b.layers.state[l, s]), committed[(l, s)], what=f"flush {l} {s}")
+        gh.assert_state(gh.to_np(b.layers.state[l, s]), committed[(l, s)], mode=mode,
+                        what=f"flush {l} {s}")
         assert np.array_equal(gh.to_np(b.layers.conv_state[l, s]), window[(l, s)].astype(np.float32))
 
 
@@ -101,37 +109,50 @@ def test_pure_16_node_chains_full_size(torch_cuda, mode):
 # invariants at the one-layer 48-head shape
 # ---------------------------------------------------------------------------------------
 
-def _one_layer(torch, h, S0, trees, dtype="bf16", mode="chain"):
-    b = gh.Batch(trees, 1, 48, 128, 0, mode=mode)
-    b.set_state(S0[None])
-    inp = workload.StepInputs(**{k: workload._to_torch(v, dtype, "cuda") for k, v in h.items()},
-                              x=None)
-    b.step(inp)
+def _one_layer(torch, h, S0, trees, dtype="bf16", mode="chain", X0=None, W=None):
+    """One verify of the one-layer workload.  The q/k/v forms read h's q, k, v; the fused form
+    reads its conv inputs x (3 H d channels) with the window X0 and weights W."""
+    fused = mode == "fused"
+    C = 3 * 48 * 128 if fused else 0
+    b = gh.Batch(trees, 1, 48, 128, C, mode=mode, conv_dtype=dtype)
+    b.set_state(S0[None], X0[None] if fused else None)
+    keep = ("beta", "gate", "x") if fused else ("q", "k", "v", "beta", "gate")
+    dev = {k: workload._to_torch(v, dtype, "cuda") for k, v in h.items() if k in keep}
+    inp = workload.StepInputs(**{k: dev.get(k) for k in ("q", "k", "v", "beta", "gate", "x")})
+    b.step(inp, workload._to_torch(W[None], dtype, "cuda") if fused else None)
     torch.cuda.synchronize()
     return b
 
 
 def _one_layer_inputs():
+    """Trees, step-0 inputs (q, k, v, beta, gate, x), S0, X0 and W of the one-layer workload."""
+    c = synth.WORKLOADS["one-layer"]
     trees = workload.workload_trees("one-layer")
     h = workload.host_step_inputs("one-layer", 0, trees, range(1))
-    h.pop("x")
-    S0 = synth.initial_state(synth.WORKLOADS["one-layer"]["seed"], 0, 0, 48, 128)
-    return trees, h, S0
+    S0 = synth.initial_state(c["seed"], 0, 0, 48, 128)
+    X0 = synth.initial_conv_state(c["seed"], 0, 0, c["Cch"], 4)
+    W = synth.conv_weight(c["seed"], 0, c["Cch"], 4, c["dtype"])
+    return trees, h, S0, X0, W
 
 
 @pytest.mark.parametrize("mode", MODES)
 def test_sibling_isolation_bit_identical(torch_cuda, mode):
     """Changing every input of one node changes its subtree's outputs and leaves every other
-    node's output bit-identical (same schedule, same inputs elsewhere)."""
-    trees, h, S0 = _one_layer_inputs()
+    node's output bit-identical (same schedule, same inputs elsewhere).  The q/k/v forms get a
+    new q, k, v and beta at the node; the fused form a new raw conv input row x (all 3 H d
+    channels) and beta, which reaches the node's subtree through both the conv window and the
+    state."""
+    trees, h, S0, X0, W = _one_layer_inputs()
     parent = trees[0]
-    base = gh.to_np(_one_layer(torch_cuda, h, S0, trees, mode=mode).out[0])
+    run = lambda hh: gh.to_np(_one_layer(torch_cuda, hh, S0, trees, mode=mode, X0=X0,
+                                         W=W).out[0])
+    base = run(h)
     for m in (3, 13, 17):
         h2 = {k: v.copy() for k, v in h.items()}
-        for k in ("q", "k", "v"):
+        for k in ("x",) if mode == "fused" else ("q", "k", "v"):
             h2[k][0, m] = synth.f32_to_bf16(-synth.bf16_to_f32(h2[k][0, m]))
         h2["beta"][0, m] = synth.f32_to_bf16(0.5 * synth.bf16_to_f32(h2["beta"][0, m]))
-        out = gh.to_np(_one_layer(torch_cuda, h2, S0, trees, mode=mode).out[0])
+        out = run(h2)
         sub = {n for n in range(len(parent)) if m in ogdn.root_path(parent, n)}
         for n in range(len(parent)):
             if n in sub:
@@ -140,11 +161,16 @@ def test_sibling_isolation_bit_identical(torch_cuda, mode):
                 assert np.array_equal(out[n], base[n]), (m, n)
 
 
-@pytest.mark.parametrize("mode", MODES)
+# forms that take q, k, v as inputs (the fused form's v = SiLU(conv) is not linear in x, and
+# it needs d = 128 and bf16)
+QKV_MODES = ["chain", "ut"]
+
+
+@pytest.mark.parametrize("mode", QKV_MODES)
 def test_power_of_two_scaling_bit_exact(torch_cuda, mode):
     """Scaling the committed state and every v by 2 scales outputs, residual vectors and
     boundary-derived states by exactly 2 (no rounding difference anywhere)."""
-    trees, h, S0 = _one_layer_inputs()
+    trees, h, S0, _, _ = _one_layer_inputs()
     b1 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
     h2 = {k: v.copy() for k, v in h.items()}
     h2["v"] = synth.f32_to_bf16(2 * synth.bf16_to_f32(h2["v"]))
@@ -156,9 +182,9 @@ def test_power_of_two_scaling_bit_exact(torch_cuda, mode):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_run_to_run_deterministic(torch_cuda, mode):
-    trees, h, S0 = _one_layer_inputs()
-    b1 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
-    b2 = _one_layer(torch_cuda, h, S0, trees, mode=mode)
+    trees, h, S0, X0, W = _one_layer_inputs()
+    b1 = _one_layer(torch_cuda, h, S0, trees, mode=mode, X0=X0, W=W)
+    b2 = _one_layer(torch_cuda, h, S0, trees, mode=mode, X0=X0, W=W)
     assert torch_cuda.equal(b1.out, b2.out)
     for name in ("bank_k", "bank_u", "bank_lg"):
         assert torch_cuda.equal(getattr(b1.layers, name)[1], getattr(b2.layers, name)[1])
@@ -203,7 +229,7 @@ def _edge_run(torch, trees, H, d, C, steps_paths, cfg_id, max_nodes=None, dtype=
     assert np.array_equal(gh.to_np(b.layers.conv_state[0]), np.stack(window).astype(np.float32))
 
 
-@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("mode", QKV_MODES)
 def test_single_node_trees(torch_cuda, mode):
     """Trees of one node (the root only), with accept-nothing and accept-root steps."""
     trees = [np.array([-1], dtype=np.int32)] * 5

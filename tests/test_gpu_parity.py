@@ -24,20 +24,25 @@ def torch_cuda():
 def _check_step(b: gh.Batch, h64, S0s, X0s, W, layer=0, write_bank=None, conv=True, host_layer=None):
     """Compare one layer's outputs, conv outputs and written banks with the oracle.
     S0s/X0s: per sequence committed state/window used by this verify; `host_layer` indexes
-    the host input arrays (defaults to `layer`)."""
+    the host input arrays (defaults to `layer`).  Returns the oracle record of each sequence
+    (its "kv" are the k and v a commit replays)."""
     hl = layer if host_layer is None else host_layer
     o_gpu = gh.to_np(b.out[layer])
-    y_gpu = gh.to_np(b.y[layer]) if conv else None
+    y_gpu = gh.to_np(b.y[layer]) if conv and b.mode != "fused" else None
     refs = []
     for s in range(b.S):
-        r = gh.oracle_seq(b.trees[s], S0s[s], X0s[s] if conv else None, W, h64, hl, s, b.offs)
         sl = slice(b.offs[s], b.offs[s + 1])
-        gh.assert_outputs(o_gpu[sl], r["o"], what=f"o seq {s}")
+        seq = {k: v[hl, sl] for k, v in h64.items()}
+        r = gh.oracle_pair(b.trees[s], S0s[s], X0s[s] if conv else None, W, seq, b.mode, b.H,
+                           b.d)
+        gh.assert_outputs(o_gpu[sl], r["o"], what=f"o seq {s}", mode=b.mode)
+        if y_gpu is not None:
+            gh.assert_outputs(y_gpu[sl], r["y"], what=f"conv y seq {s}", mode=b.mode,
+                              quantity="conv y")
         if conv:
-            gh.assert_outputs(y_gpu[sl], r["y"], what=f"conv y seq {s}")
             wb = write_bank[s]
             xb = gh.to_np(b.layers.bank_x[wb][layer, s][:len(b.trees[s]), :b.C])
-            assert np.array_equal(xb, h64["x"][hl, sl]), "banked conv input not exact"
+            assert np.array_equal(xb, seq["x"]), "banked conv input not exact"
         gh.assert_bank_rows(b, layer, s, write_bank[s], range(len(b.trees[s])),
                             r["k"], r["u"], r["lg"])
         refs.append(r)
@@ -72,7 +77,8 @@ def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d,
         b.step(inp, Wd)
         torch_cuda.cuda.synchronize()
         # the fold of the previous step's path happened inside this verify
-        gh.assert_state(gh.to_np(b.layers.state[0]), np.stack(committed), what=f"fold @ {step}")
+        gh.assert_state(gh.to_np(b.layers.state[0]), np.stack(committed), what=f"fold @ {step}",
+                        mode=b.mode)
         cs = gh.to_np(b.layers.conv_state[0])
         assert np.array_equal(cs, np.stack(window).astype(np.float32)), "conv window fold"
         _check_step(b, h64, committed, window, W64, 0, write_bank=1 - role_before)
@@ -108,7 +114,7 @@ def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d,
             window[s] = oconv.commit_window(window[s], seq["x"], path)
     b.flush()
     torch_cuda.cuda.synchronize()
-    gh.assert_state(gh.to_np(b.layers.state[0]), np.stack(committed), what="flush")
+    gh.assert_state(gh.to_np(b.layers.state[0]), np.stack(committed), what="flush", mode=b.mode)
     assert np.array_equal(gh.to_np(b.layers.conv_state[0]), np.stack(window).astype(np.float32))
     assert np.all(b.layers.pending.cpu().numpy() == 0) and np.all(b.layers.pending_host == 0)
     before = b.layers.state.clone(), b.layers.conv_state.clone()
@@ -214,29 +220,34 @@ def _layer_case(torch_cuda, name, n_layers, trees, steps, sample_layers, check_o
         b.step(inp, Wd)
         torch_cuda.cuda.synchronize()
         h64 = {k: workload.widen(v[list(sample_layers)], dtype) for k, v in h.items()}
+        kv = {}
         for li, l in enumerate(sample_layers):
-            gh.assert_state(gh.to_np(b.layers.state[l]), np.stack(committed[l]),
+            gh.assert_state(gh.to_np(b.layers.state[l]), np.stack(committed[l]), mode=mode,
                             what=f"committed layer {l} step {step}")
-            if step in check_outputs_at:
-                _check_step(b, h64, committed[l], window[l], W64[l], l,
-                            write_bank=1 - role_before, host_layer=li)
+            if step in check_outputs_at or mode == "fused":
+                # the fused form's k and v come from the conv: the oracle computes them here
+                refs = _check_step(b, h64, committed[l], window[l], W64[l], l,
+                                   write_bank=1 - role_before, host_layer=li)
+                kv[l] = [r["kv"] for r in refs]
         paths = [synth.workload_path(name, step, s, trees[s]) for s in range(b.S)]
         b.commit(inp, paths, Wd)
         for li, l in enumerate(sample_layers):
             for s, path in enumerate(paths):
                 sl = slice(b.offs[s], b.offs[s + 1])
-                committed[l][s] = ogdn.replay(committed[l][s], h64["k"][li, sl], h64["v"][li, sl],
-                                              h64["beta"][li, sl], h64["gate"][li, sl], path)
+                k, v = kv[l][s] if l in kv else (h64["k"][li, sl], h64["v"][li, sl])
+                committed[l][s] = ogdn.replay(committed[l][s], k, v, h64["beta"][li, sl],
+                                              h64["gate"][li, sl], path)
                 window[l][s] = oconv.commit_window(window[l][s], h64["x"][li, sl], path)
     b.flush()
     torch_cuda.cuda.synchronize()
     for l in sample_layers:
-        gh.assert_state(gh.to_np(b.layers.state[l]), np.stack(committed[l]), what=f"flush {l}")
+        gh.assert_state(gh.to_np(b.layers.state[l]), np.stack(committed[l]), what=f"flush {l}",
+                        mode=mode)
         assert np.array_equal(gh.to_np(b.layers.conv_state[l]),
                               np.stack(window[l]).astype(np.float32))
 
 
-@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("mode", MODES + ["fused"])
 def test_one_layer_bf16_48_heads(torch_cuda, mode):
     """The one-layer workload: 48 heads x 128, bf16 inputs, the seeded 22-node top-4 tree; verify,
     conv and banks for every node and head, then commit of a length-6 path and flush."""
@@ -245,11 +256,13 @@ def test_one_layer_bf16_48_heads(torch_cuda, mode):
                 mode=mode)
 
 
-@pytest.mark.parametrize("mode,commit_mode", [("chain", "compact"), ("ut", "row-map")])
+@pytest.mark.parametrize("mode,commit_mode", [("chain", "compact"), ("ut", "row-map"),
+                                              ("fused", "row-map"), ("fused", "compact")])
 def test_48_layers_ten_steps(torch_cuda, mode, commit_mode):
     """The 48-layer workload: 48 independent layers, 10 verify steps each folding the previous
     step's accepted length-6 path, then flush; oracle on three sampled layers (states every step,
-    outputs and banks at steps 0, 4 and 9).  Each verify form runs with one commit form."""
+    outputs and banks at steps 0, 4 and 9; every step in the fused form, whose replayed k and v
+    are the conv's).  Each verify form runs with one commit form, the fused form with both."""
     trees = workload.workload_trees("48-layer")
     _layer_case(torch_cuda, "48-layer", 48, trees, steps=10, sample_layers=[0, 23, 47],
                 check_outputs_at={0, 4, 9}, mode=mode, commit_mode=commit_mode)

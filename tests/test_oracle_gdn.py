@@ -228,6 +228,36 @@ def test_v11_fold_of_factors_equals_replay(name):
         np.testing.assert_allclose(F, R, rtol=0, atol=1e-13)
 
 
+def test_v11_zero_and_tiny_gates_fold_closed_form():
+    """A zero gate erases everything before its token: after it, the state is u k^T of that
+    token (u = beta v, since g S k vanishes) and the later tokens' updates, whatever S0 was.
+    Its banked ln g is -inf, and the fold (exp(-inf) = 0) gives the same finite state as the
+    replay.  A 1e-30 gate keeps a 1e-30 trace of the past, which the fold keeps too."""
+    parent = TREES["chain"]
+    rng = np.random.default_rng(11)
+    S0, q, k, v, beta, gate = _inputs(len(parent), 2, 16, rng)
+    gate = gate.copy()
+    gate[3] = 0.0
+    gate[5, 0] = 1e-30
+    path = list(range(len(parent)))
+    with np.errstate(divide="ignore"):
+        kf, uf, lg = gdn.factors(parent, S0, k, v, beta, gate)
+    assert np.all(np.isneginf(lg[3]))
+    R = gdn.replay(S0, k, v, beta, gate, path)
+    F = gdn.fold(S0, kf, uf, lg)
+    assert np.all(np.isfinite(F))
+    np.testing.assert_allclose(F, R, rtol=0, atol=1e-13)
+    # independent of S0 once the zero gate has passed
+    R2 = gdn.replay(5.0 * S0 + 1.0, k, v, beta, gate, path)
+    np.testing.assert_allclose(R2, R, rtol=0, atol=1e-13)
+    # from the zero gate on: the replay from a zero state with g = 1 at that token
+    g1 = gate.copy()
+    g1[3] = 1.0
+    R3 = gdn.replay(np.zeros_like(S0), k, v, beta, g1, path[3:])
+    np.testing.assert_allclose(R3, R, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(uf[3], beta[3][:, None] * v[3], rtol=0, atol=1e-15)
+
+
 def test_v12_multi_step_commit_is_sequential_replay():
     """Carrying the committed state over several verify+accept steps equals one sequential
     replay of all accepted tokens (accepted paths may branch off the main chain)."""
