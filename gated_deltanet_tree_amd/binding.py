@@ -22,7 +22,8 @@ STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_ETREE", -3: "GDN_EPATH",
 EXPORTS = [
     "gdn_last_error", "gdn_schedule_words", "gdn_hld_schedule", "gdn_ddtree_build",
     "gdn_verify_workspace_bytes",
-    "gdn_tree_verify", "gdn_tree_verify_wave", "gdn_tree_verify_wave_timed",
+    "gdn_tree_verify", "gdn_tree_verify_noalloc", "gdn_tree_verify_wave",
+    "gdn_tree_verify_wave_timed",
     "gdn_tree_verify_ut", "gdn_tree_verify_ut_timed", "gdn_tree_conv",
     "gdn_tree_conv_verify", "gdn_tree_conv_verify_timed",
     "gdn_commit_path", "gdn_prefill", "gdn_prefill_timed",
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_verify_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32]
     L.gdn_tree_verify.restype = _I32
     L.gdn_tree_verify.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
+    L.gdn_tree_verify_noalloc.restype = _I32
+    L.gdn_tree_verify_noalloc.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
     L.gdn_tree_verify_wave.restype = _I32
     L.gdn_tree_verify_wave.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _I32, _P]
     L.gdn_tree_verify_wave_timed.restype = _I32
@@ -376,6 +379,13 @@ def tree_verify(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
     _need_ws(args, image)
     _check(lib().gdn_tree_verify(ctypes.byref(args), _ptr(image), _dev(dev_image),
                                  _stream(stream)), "gdn_tree_verify")
+
+
+def tree_verify_noalloc(args: VerifyArgs, image: np.ndarray, dev_image, stream=None):
+    """gdn_tree_verify with the boundary states in the library's fixed device scratch
+    (args.workspace is ignored); allocates nothing."""
+    _check(lib().gdn_tree_verify_noalloc(ctypes.byref(args), _ptr(image), _dev(dev_image),
+                                         _stream(stream)), "gdn_tree_verify_noalloc")
 
 
 def tree_verify_wave(args: VerifyArgs, image: np.ndarray, dev_image, wave: int, stream=None):

@@ -30,6 +30,8 @@
 // in the other slot afterwards, so their latency hides behind a node of work.
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "verify_common.h"
 
 namespace gdn {
@@ -316,6 +318,47 @@ gdn_status verify_setup(const gdn_verify_args *a, const int32_t *host_image,
     return GDN_OK;
 }
 
+// ---- boundary-state scratch of gdn_tree_verify_noalloc ------------------------------------
+// For callers that cannot allocate (HIP graph capture, tight serving loops): the boundary
+// states live in a fixed array in device memory that the library holds on every GPU it runs
+// on until the process ends.  In host code `scratch` names a host-side stand-in, not a device
+// address: kernels receive the address that hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.  Calls that overlap on one GPU share the array
+// and race; nothing in it needs to start at zero (every boundary slot is written by its chain
+// before a later wave reads it).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace gdn
+
+static __device__ __align__(256) float scratch[gdn::kNoAllocScratchBytes / sizeof(float)];
+
+namespace gdn {
+
+static std::mutex g_scratch_mu;
+static float *g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+static gdn_status scratch_address(float **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GDN_EINVAL, "device %d beyond the %d devices the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(GDN_EDEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return GDN_OK;
+}
+
 static gdn_status run_wave(VerifyParams P, const int32_t *host_image, const ImageView &v,
                            const gdn_verify_args *a, int wave, hipStream_t stream,
                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
@@ -350,6 +393,37 @@ extern "C" gdn_status gdn_tree_verify(const gdn_verify_args *a, const int32_t *h
     if (st != GDN_OK || a->n_seqs == 0) return st;
     for (int w = 0; w < v.n_waves; ++w) {
         st = run_wave(P, host_image, v, a, w, static_cast<hipStream_t>(stream));
+        if (st != GDN_OK) return st;
+    }
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_tree_verify_noalloc(const gdn_verify_args *a,
+                                              const int32_t *host_image,
+                                              const int32_t *dev_image, void *stream) {
+    clear_error();
+    if (a == nullptr) return fail(GDN_EINVAL, "gdn_tree_verify_noalloc: null args");
+    gdn_verify_args b = *a;
+    b.workspace = nullptr;  // not used: the boundary states go to the library's scratch
+    VerifyParams P;
+    ImageView v;
+    gdn_status st = verify_setup(&b, host_image, dev_image, P, v, false);
+    if (st != GDN_OK || b.n_seqs == 0) return st;
+    const size_t need = size_t(b.n_layers) * size_t(v.n_boundaries) * size_t(b.n_heads) *
+                        size_t(b.head_dim) * size_t(b.head_dim) * sizeof(float);
+    if (need > kNoAllocScratchBytes)
+        return fail(GDN_ECAPACITY, "gdn_tree_verify_noalloc: %zu bytes of boundary states "
+                    "(%d boundary nodes x %d heads x %d layers) exceed the fixed scratch of %zu "
+                    "bytes; use gdn_tree_verify with a workspace", need, v.n_boundaries,
+                    b.n_heads, b.n_layers, kNoAllocScratchBytes);
+    if (need > 0) {
+        float *scr = nullptr;
+        st = scratch_address(&scr);
+        if (st != GDN_OK) return st;
+        P.boundary = scr;
+    }
+    for (int w = 0; w < v.n_waves; ++w) {
+        st = run_wave(P, host_image, v, &b, w, static_cast<hipStream_t>(stream));
         if (st != GDN_OK) return st;
     }
     return GDN_OK;

@@ -30,7 +30,8 @@
  *   - Ownership: the caller allocates every buffer. Host arrays are plain memory; device
  *     arrays are device pointers (e.g. from torch on ROCm). The library allocates nothing,
  *     keeps no pointer after a call returns and has no global state except a per-thread
- *     error string (gdn_last_error).
+ *     error string (gdn_last_error) and the fixed device scratch of gdn_tree_verify_noalloc
+ *     (with its per-device address, looked up once).
  *   - Streams: device calls take a hipStream_t as `void *stream` (NULL = default stream),
  *     only enqueue work and return. Host calls (schedule, sizes) are synchronous.
  *   - Errors: every call returns a gdn_status. All arguments are validated before anything
@@ -213,6 +214,18 @@ size_t gdn_verify_workspace_bytes(const int32_t *host_image, int32_t n_heads, in
  * dev_image: the same words in device memory (read by the kernels). */
 gdn_status gdn_tree_verify(const gdn_verify_args *args, const int32_t *host_image,
                            const int32_t *dev_image, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same work and results as gdn_tree_verify,
+ * bit-identical, with the boundary states kept in a fixed 32 MiB array of device memory that
+ * the library holds on every GPU it runs on until the process ends, instead of `workspace`
+ * (ignored; may be NULL).  The call allocates nothing.  GDN_ECAPACITY (nothing launched) when
+ * gdn_verify_workspace_bytes for the call exceeds 32 MiB = 33554432 bytes (512 boundary tiles
+ * at d = 128: e.g. one 22-node tree's ~6 boundary nodes x 48 heads fits, a 32-tree batch does
+ * not).  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, two threads) race and must be serialised by the caller. */
+gdn_status gdn_tree_verify_noalloc(const gdn_verify_args *args, const int32_t *host_image,
+                                   const int32_t *dev_image, void *stream);
 
 /* Same work as gdn_tree_verify restricted to dependency wave `wave` (0 <= wave < n_waves):
  * calling it for waves 0, 1, ... in order on one stream equals gdn_tree_verify. */
