@@ -32,7 +32,7 @@ def torch_cuda():
 
 def _set_gate(h, node, head, value):
     """gate[0, node, head] = value, as the bf16 (or fp32) the device reads."""
-    h["gate"][0, node, head] = synth.f32_to_bf16(np.float32(value))
+    h["gate"][0, node, head] = synth.f32_to_bf16(np.array([value], np.float32))[0]
 
 
 @pytest.mark.parametrize("mode", ["chain", "ut", "fused"])
