@@ -116,36 +116,3 @@ def test_random_batches_two_formulations():
         b = hld.schedule_recursive(parents)
         _same(a, b)
         check_properties(parents, a)
-
-
-# ---------------------------------------------------------------------------------------
-# tree-masked verify plan (records by depth level)
-# ---------------------------------------------------------------------------------------
-
-def test_ut_plan_records_are_root_paths_by_level():
-    rng = np.random.default_rng(77)
-    trees = [np.array([-1, 0, 0, 1, 1, 2, 3]), np.arange(-1, 7), np.array([-1]),
-             synth.make_tree(rng, 22, 4, 12), synth.make_tree(rng, 40, 8, 16)]
-    plan = hld.ut_plan(trees)
-    for b, parent in enumerate(trees):
-        n = len(parent)
-        depth = synth.node_depths(parent)
-        r0, r1 = plan["rec_base"][b], plan["rec_base"][b + 1]
-        recs = plan["rec_anc"][r0:r1]
-        assert r1 - r0 == int(np.sum(depth + 1))
-        off = sum(len(t) for t in trees[:b])
-        poff = plan["node_rec"][off:off + n]
-        for t in range(n):  # block = t, then its root path upward
-            block = recs[poff[t]:poff[t] + depth[t] + 1]
-            assert block.tolist() == list(reversed(synth.root_path(parent, t)))
-        order = plan["lvnode"][off:off + n]
-        assert sorted(order.tolist()) == list(range(n))
-        keys = [(depth[t], t) for t in order]
-        assert keys == sorted(keys)
-        lvn = plan["lvn"][plan["lv_base"][b]:plan["lv_base"][b + 1]]
-        assert len(lvn) == depth.max() + 2 and lvn[0] == 0 and lvn[-1] == n
-        for d in range(depth.max() + 1):  # level d = positions lvn[d] .. lvn[d+1]
-            assert all(depth[t] == d for t in order[lvn[d]:lvn[d + 1]])
-        # blocks laid out in level order, back to back
-        assert [poff[t] for t in order] == np.concatenate(
-            [[0], np.cumsum([depth[t] + 1 for t in order])[:-1]]).tolist()

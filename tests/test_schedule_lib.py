@@ -12,6 +12,8 @@ import pytest
 from gated_deltanet_tree_amd import binding, synth
 from oracle import hld
 
+import plan_layout
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KEYS = ["seq_offsets", "wave_offsets", "chain_offsets", "chain_nodes", "chain_seq",
         "chain_src", "node_store", "node_parent", "node_depth"]
@@ -176,8 +178,8 @@ def test_commit_rejects_bad_paths_before_launch():
     assert role[0] == 0 and pend[0] == 3
 
 
-def test_ut_plan_matches_oracle_bit_exact():
-    """The tree-masked verify plan in the image equals the oracle's construction."""
+def test_ut_plan_matches_layout_checker_bit_exact():
+    """The tree-masked verify plan in the image equals the layout checker's construction."""
     rng = np.random.default_rng(31)
     batches = [[np.array([-1, 0, 0, 1, 1, 2, 3])],
                [synth.make_tree(rng, 22, 4, 12) for _ in range(32)],
@@ -186,7 +188,7 @@ def test_ut_plan_matches_oracle_bit_exact():
     for trees in batches:
         image = binding.hld_schedule(trees)
         got = binding.schedule_view(image)["ut_plan"]
-        want = hld.ut_plan(trees)
+        want = plan_layout.ut_plan(trees)
         for key in ("rec_base", "node_rec", "lv_base", "lvn", "lvnode", "rec_anc"):
             assert np.array_equal(got[key], want[key]), key
         assert got["records"] == int(want["rec_base"][-1])
