@@ -76,58 +76,65 @@ class ConvArgs(ctypes.Structure):
 _lib = None
 
 
+# A host-only build of the library's plain C++ parts (schedule, draft-tree builder, commit
+# bookkeeping) with AddressSanitizer and UndefinedBehaviorSanitizer (build_host_san.py): when
+# this variable names it, lib() loads it instead, for host-side tests; device entry points are
+# then absent and torch is not imported.
+HOST_LIB_ENV = "GDN_TREE_HOST_LIB"
+
+
+def host_only() -> bool:
+    return bool(os.environ.get(HOST_LIB_ENV))
+
+
+def _prototypes():
+    VA, CA, PA = ctypes.POINTER(VerifyArgs), ctypes.POINTER(ConvArgs), ctypes.POINTER(PrefillArgs)
+    return {
+        "gdn_last_error": (ctypes.c_char_p, []),
+        "gdn_schedule_words": (ctypes.c_size_t, [_I32, _I32]),
+        "gdn_hld_schedule": (_I32, [_I32P, _I32P, _I32, _I32P, ctypes.c_size_t]),
+        "gdn_ddtree_build": (_I32, [_FP, _I32P, _I32P, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                    _I32, _I32P, _I32P, _I32P, _I32P, _FP, _I32P]),
+        "gdn_verify_workspace_bytes": (ctypes.c_size_t, [_I32P, _I32, _I32, _I32]),
+        "gdn_tree_verify": (_I32, [VA, _I32P, _P, _P]),
+        "gdn_tree_verify_noalloc": (_I32, [VA, _I32P, _P, _P]),
+        "gdn_tree_verify_wave": (_I32, [VA, _I32P, _P, _I32, _P]),
+        "gdn_tree_verify_wave_timed": (_I32, [VA, _I32P, _P, _I32, _P, _P, _P]),
+        "gdn_tree_verify_ut": (_I32, [VA, _I32P, _P, _P]),
+        "gdn_tree_verify_ut_timed": (_I32, [VA, _I32P, _P, _P, _P, _P]),
+        "gdn_prefill": (_I32, [PA, _I32P, _P]),
+        "gdn_prefill_timed": (_I32, [PA, _I32P, _P, _P, _P]),
+        "gdn_tree_conv_verify": (_I32, [VA, CA, _I32P, _P, _P]),
+        "gdn_tree_conv_verify_timed": (_I32, [VA, CA, _I32P, _P, _P, _P, _P]),
+        "gdn_tree_conv": (_I32, [CA, _I32P, _P, _P]),
+        "gdn_commit_path": (_I32, [_I32P, _I32P, _I32P, _P, _P, VA, CA, _I32P, _I32P, _I32, _P]),
+        "gdn_compact_factors": (_I32, [_P, _P, ctypes.c_int64, _P, _P, _I32, _P]),
+        "gdn_flush": (_I32, [VA, CA, _I32P, _P]),
+    }
+
+
 def lib() -> ctypes.CDLL:
-    """Load the HIP library (after torch, so the HIP runtime is shared)."""
+    """Load the HIP library (after torch, so the HIP runtime is shared), or the sanitized
+    host-only build named by GDN_TREE_HOST_LIB."""
     global _lib
     if _lib is not None:
         return _lib
-    import torch  # noqa: F401  -- must precede the library: one HIP runtime per process
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                           "`python -m gated_deltanet_tree_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
-    L.gdn_last_error.restype = ctypes.c_char_p
-    L.gdn_schedule_words.restype = ctypes.c_size_t
-    L.gdn_schedule_words.argtypes = [_I32, _I32]
-    L.gdn_hld_schedule.restype = _I32
-    L.gdn_hld_schedule.argtypes = [_I32P, _I32P, _I32, _I32P, ctypes.c_size_t]
-    L.gdn_ddtree_build.restype = _I32
-    L.gdn_ddtree_build.argtypes = [_FP, _I32P, _I32P, _I32, _I32, _I32, _I32, ctypes.c_float,
-                                   _I32, _I32P, _I32P, _I32P, _I32P, _FP, _I32P]
-    L.gdn_verify_workspace_bytes.restype = ctypes.c_size_t
-    L.gdn_verify_workspace_bytes.argtypes = [_I32P, _I32, _I32, _I32]
-    L.gdn_tree_verify.restype = _I32
-    L.gdn_tree_verify.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
-    L.gdn_tree_verify_noalloc.restype = _I32
-    L.gdn_tree_verify_noalloc.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
-    L.gdn_tree_verify_wave.restype = _I32
-    L.gdn_tree_verify_wave.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _I32, _P]
-    L.gdn_tree_verify_wave_timed.restype = _I32
-    L.gdn_tree_verify_wave_timed.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _I32, _P, _P,
-                                             _P]
-    L.gdn_tree_verify_ut.restype = _I32
-    L.gdn_tree_verify_ut.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P]
-    L.gdn_tree_verify_ut_timed.restype = _I32
-    L.gdn_tree_verify_ut_timed.argtypes = [ctypes.POINTER(VerifyArgs), _I32P, _P, _P, _P, _P]
-    L.gdn_prefill.restype = _I32
-    L.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _I32P, _P]
-    L.gdn_prefill_timed.restype = _I32
-    L.gdn_prefill_timed.argtypes = [ctypes.POINTER(PrefillArgs), _I32P, _P, _P, _P]
-    L.gdn_tree_conv_verify.restype = _I32
-    L.gdn_tree_conv_verify.argtypes = [ctypes.POINTER(VerifyArgs), ctypes.POINTER(ConvArgs),
-                                       _I32P, _P, _P]
-    L.gdn_tree_conv_verify_timed.restype = _I32
-    L.gdn_tree_conv_verify_timed.argtypes = [ctypes.POINTER(VerifyArgs),
-                                             ctypes.POINTER(ConvArgs), _I32P, _P, _P, _P, _P]
-    L.gdn_tree_conv.restype = _I32
-    L.gdn_tree_conv.argtypes = [ctypes.POINTER(ConvArgs), _I32P, _P, _P]
-    L.gdn_commit_path.restype = _I32
-    L.gdn_commit_path.argtypes = [_I32P, _I32P, _I32P, _P, _P, ctypes.POINTER(VerifyArgs),
-                                  ctypes.POINTER(ConvArgs), _I32P, _I32P, _I32, _P]
-    L.gdn_compact_factors.restype = _I32
-    L.gdn_compact_factors.argtypes = [_P, _P, ctypes.c_int64, _P, _P, _I32, _P]
-    L.gdn_flush.restype = _I32
-    L.gdn_flush.argtypes = [ctypes.POINTER(VerifyArgs), ctypes.POINTER(ConvArgs), _I32P, _P]
+    host = os.environ.get(HOST_LIB_ENV)
+    if host:
+        L = ctypes.CDLL(host)
+    else:
+        import torch  # noqa: F401  -- must precede the library: one HIP runtime per process
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m gated_deltanet_tree_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _prototypes().items():
+        if host and not hasattr(L, name):
+            continue  # device entry points are not in the host-only build
+        fn = getattr(L, name)
+        fn.restype = res
+        if args:
+            fn.argtypes = args
     _lib = L
     return L
 

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn_tree.so")
 ARCH = "gfx950"
 
-SOURCES = ["errors.cpp", "schedule.cpp", "ddtree.cpp", "verify.hip", "verify_ut.hip", "verify_ut_mfma.hip", "conv_verify.hip", "conv.hip", "prefill.hip", "commit.hip"]
+SOURCES = ["errors.cpp", "schedule.cpp", "ddtree.cpp", "commit_host.cpp", "verify.hip", "verify_ut.hip", "verify_ut_mfma.hip", "conv_verify.hip", "conv.hip", "prefill.hip", "commit.hip"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -123,11 +123,9 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
                                       int32_t *role_host, int32_t *pending_host, int32_t mode,
                                       void *stream) {
     clear_error();
-    if (!image_ok(host_image) || !path_offsets || !dev_path_offsets || !role_host ||
-        !pending_host)
+    if (!image_ok(host_image) || !dev_path_offsets || !pending_host)
         return fail(GDN_EINVAL, "gdn_commit_path: null argument or malformed schedule image");
-    if (mode != GDN_COMMIT_COMPACT && mode != GDN_COMMIT_ROW_MAP)
-        return fail(GDN_EINVAL, "gdn_commit_path: unknown mode %d", mode);
+    if (va == nullptr) return fail(GDN_EINVAL, "gdn_commit_path: null verify args");
     gdn_status st = check_flush_verify_args(va);
     if (st != GDN_OK) return st;
     if (ca != nullptr) {
@@ -145,44 +143,13 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
         return fail(GDN_EINVAL, "gdn_commit_path: n_seqs differs from the schedule's");
     if (v.max_tree > va->max_nodes)
         return fail(GDN_ECAPACITY, "gdn_commit_path: max_nodes smaller than the largest tree");
+    CommitPlan plan;
+    st = plan_commit(host_image, paths, path_offsets, role_host, mode, plan);
+    if (st != GDN_OK) return st;
     const int32_t S = v.n_seqs;
     if (S == 0) return GDN_OK;
-    if (path_offsets[0] != 0) return fail(GDN_EPATH, "gdn_commit_path: path_offsets[0] != 0");
-    const int32_t *seq_off = host_image + v.off_seq, *npar = host_image + v.off_parent;
-    bool any_compaction = false, any_path = false;
-    int32_t max_len = 0;
-    std::vector<int32_t> new_role(role_host, role_host + S), new_pending(S);
-    for (int32_t b = 0; b < S; ++b) {
-        const int32_t beg = path_offsets[b], L = path_offsets[b + 1] - beg;
-        const int32_t n_b = seq_off[b + 1] - seq_off[b];
-        if (L < 0 || L > n_b)
-            return fail(GDN_EPATH, "gdn_commit_path: sequence %d: path length %d not in [0, %d]",
-                        b, L, n_b);
-        if (L > 0 && paths == nullptr) return fail(GDN_EINVAL, "gdn_commit_path: null paths");
-        if (role_host[b] != 0 && role_host[b] != 1)
-            return fail(GDN_EINVAL, "gdn_commit_path: role[%d] = %d", b, role_host[b]);
-        bool in_order = true;
-        for (int32_t i = 0; i < L; ++i) {
-            const int32_t node = paths[beg + i];
-            if (node < 0 || node >= n_b)
-                return fail(GDN_EPATH, "gdn_commit_path: sequence %d: node %d out of range", b,
-                            node);
-            const int32_t expect_parent = i == 0 ? -1 : seq_off[b] + paths[beg + i - 1];
-            if (npar[seq_off[b] + node] != expect_parent)
-                return fail(GDN_EPATH, "gdn_commit_path: sequence %d: path[%d] = %d does not "
-                            "follow its parent", b, i, node);
-            in_order = in_order && node == i;
-        }
-        any_path = any_path || L > 0;
-        if (mode == GDN_COMMIT_ROW_MAP) {
-            if (L > 0) new_role[b] ^= 1;
-        } else {
-            if (L > 0 && in_order) new_role[b] ^= 1;
-            if (L > 0 && !in_order) any_compaction = true;
-            if (!in_order) max_len = std::max(max_len, L);
-        }
-        new_pending[b] = L;
-    }
+    const bool any_compaction = plan.any_compaction, any_path = plan.any_path;
+    const int32_t max_len = plan.max_len;
     if (S > 65535 || va->n_layers > 65535)
         return fail(GDN_EINVAL, "gdn_commit_path: n_seqs and n_layers must be <= 65535");
     if (any_path && dev_paths == nullptr)
@@ -215,8 +182,8 @@ extern "C" gdn_status gdn_commit_path(const int32_t *host_image, const int32_t *
                        va->max_nodes, mode);
     GDN_LAUNCH_CHECK("commit_bookkeeping_kernel");
     for (int32_t b = 0; b < S; ++b) {
-        role_host[b] = new_role[b];
-        pending_host[b] = new_pending[b];
+        role_host[b] = plan.role[size_t(b)];
+        pending_host[b] = plan.pending[size_t(b)];
     }
     return GDN_OK;
 }

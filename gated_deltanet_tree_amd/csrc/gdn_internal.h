@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/gdn_tree.h"
 
@@ -36,6 +37,19 @@ struct ImageView {
 size_t schedule_words(int32_t n_seqs, int32_t n_nodes);
 ImageView view_image(const int32_t *img);
 bool image_ok(const int32_t *img);
+
+// Host bookkeeping of one commit (commit_host.cpp): new roles and pending lengths per
+// sequence, whether any branched path needs the compacting gather, and its longest path.
+struct CommitPlan {
+    std::vector<int32_t> role, pending;
+    bool any_compaction = false, any_path = false;
+    int32_t max_len = 0;
+};
+// Checks the accepted paths (path_offsets [S+1], paths [path_offsets[S]]) against the trees of
+// the schedule image and the roles, then fills `plan`.  GDN_EINVAL / GDN_EPATH on bad input.
+gdn_status plan_commit(const int32_t *host_image, const int32_t *paths,
+                       const int32_t *path_offsets, const int32_t *role_host, int32_t mode,
+                       CommitPlan &plan);
 
 // Per-thread last error; `fail` formats it and returns the status code.
 void clear_error();

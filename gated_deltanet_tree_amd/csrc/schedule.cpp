@@ -75,11 +75,12 @@ extern "C" gdn_status gdn_hld_schedule(const int32_t *parent_local, const int32_
     if (n_seqs > 0 && seq_offsets[0] != 0)
         return fail(GDN_EINVAL, "gdn_hld_schedule: seq_offsets[0] must be 0");
     for (int32_t b = 0; b < n_seqs; ++b) {
-        const int32_t n = seq_offsets[b + 1] - seq_offsets[b];
+        // in 64 bits: a caller's offset can be any int32, and the difference must not overflow
+        const int64_t n = int64_t(seq_offsets[b + 1]) - int64_t(seq_offsets[b]);
         if (n < 1) return fail(GDN_ETREE, "gdn_hld_schedule: tree %d has no nodes", b);
         if (n > kMaxTreeNodes)
-            return fail(GDN_EINVAL, "gdn_hld_schedule: tree %d has %d nodes (max %d)", b, n,
-                        kMaxTreeNodes);
+            return fail(GDN_EINVAL, "gdn_hld_schedule: tree %d has %lld nodes (max %d)", b,
+                        (long long)n, kMaxTreeNodes);
     }
     const int32_t T = n_seqs > 0 ? seq_offsets[n_seqs] : 0;
     const size_t words = schedule_words(n_seqs, T);

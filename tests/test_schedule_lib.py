@@ -15,6 +15,9 @@ from oracle import hld
 import plan_layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# tests that need the device entry points of the full library (not in the sanitized host build)
+full_library = pytest.mark.skipif(binding.host_only(),
+                                  reason="device entry points are not in the host-only build")
 KEYS = ["seq_offsets", "wave_offsets", "chain_offsets", "chain_nodes", "chain_seq",
         "chain_src", "node_store", "node_parent", "node_depth"]
 
@@ -25,6 +28,7 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
 
 
+@full_library
 def test_library_exports_every_declared_symbol():
     L = binding.lib()
     declared = _declared_functions()
@@ -112,6 +116,30 @@ def test_capacity_and_null_errors():
     assert e.value.status == -1
 
 
+@pytest.mark.parametrize("offs,status", [
+    ([1, 3], -1),                      # seq_offsets[0] != 0
+    ([0, 3, 3], -2),                   # an empty tree
+    ([0, 3, 1], -2),                   # decreasing offsets
+    ([0, 3, 3 + 1025], -1),            # a tree above 1024 nodes
+    ([0, 3, -(2 ** 31)], -2),          # an offset whose difference overflows 32 bits
+    ([0, 2 ** 31 - 1], -1),            # a huge tree, refused before any parent is read
+])
+def test_malformed_seq_offsets_rejected(offs, status):
+    """Offsets are validated before any parent is read, in 64-bit arithmetic; nothing is
+    written on error."""
+    L = binding.lib()
+    parent = np.array([-1, 0, 0, -1, 0], dtype=np.int32)
+    offs = np.array(offs, dtype=np.int64).astype(np.int32)
+    image = np.full(binding.schedule_words(2, 5), 7, dtype=np.int32)
+    rc = L.gdn_hld_schedule(binding._ptr(parent), binding._ptr(offs), len(offs) - 1,
+                            binding._ptr(image), image.size)
+    assert rc == status, L.gdn_last_error()
+    assert np.all(image == 7)
+    assert L.gdn_hld_schedule(binding._ptr(parent), binding._ptr(offs), -1,
+                              binding._ptr(image), image.size) == -1
+
+
+@full_library
 def test_device_calls_validate_before_launch():
     """Argument errors are reported before any device work (no GPU is touched here)."""
     L = binding.lib()
@@ -144,6 +172,7 @@ def test_device_calls_validate_before_launch():
     assert L.gdn_tree_conv(ctypes.byref(cargs), binding._ptr(image), 1, None) == -1
 
 
+@full_library
 def test_commit_rejects_bad_paths_before_launch():
     """Non-root paths, broken parent links and out-of-range ids give GDN_EPATH and leave the
     host mirrors untouched."""
