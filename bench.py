@@ -5,7 +5,14 @@ and its upload, then for every GDN layer the tree conv (with the conv-window fol
 verify (with the deferred-commit fold), then accept -> commit of one seeded path per sequence
 (by default the row-map form: the next fold reads the accepted rows where the verify wrote them;
 --commit compact gathers branched paths into path order first).  The timed region is K steps
-plus the final flush.
+plus the final flush, repeated --reps times with every buffer restored from a pristine device
+copy in between (value and ms_per_step from the median repetition, the min beside it); the
+steps rotate over --input-sets pre-drawn input sets.
+
+The oracle leg (cpu_baseline) runs first: it times the untuned float64 oracle on a bounded
+sample of (sequence, layer) pairs and computes, untimed, the oracle's step-0 results on a few
+pairs; after each path is timed, step 0 is run again from the initial state through the same
+kernels and launch shape, and the line reports the largest errors against those results.
 
 Three paths are timed, one after the other, on the same resident workload:
   fused  conv -> SiLU -> unit-length q/k -> tree-masked verify in one launch per layer: q, k
@@ -35,6 +42,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X dense fp32 on the matrix cores
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc")
 # Committed rocprofv3 HBM counter records of each verify kernel on the batched workload, and
@@ -121,6 +129,29 @@ def fused_bytes(view, pending, H, d, in_bytes, n_layers=1):
     return (total + H * ch * 4 * in_bytes) * n_layers
 
 
+def fused_method_bytes(view, pending, H, d, in_bytes, n_layers=1):
+    """Algorithmic bytes of one fused conv -> verify launch by the method's own byte model:
+    the factor banks and the conv-input bank are FP32 (SpecLA guide, mechanism 3), and the
+    fold reads every pending row.  Per (sequence, head): the committed tile read, the conv
+    window (3 d channels x 3 taps, fp32) read and written; when folding, the tile write-back
+    and per pending token its k, u, ln g row (8 d + 4) and its 3 d conv inputs (fp32).  Per
+    node and head: 3 d conv inputs and beta, g in, o out (fp32), k, u, ln g banked and the 3 d
+    conv inputs banked (fp32).  The layer's conv weights once.  No q, k, v or conv output in
+    HBM (they stay on chip).  The kernel itself moves fewer bytes (fused_bytes: it banks the
+    bf16 inputs' own bits, exactly, and reads only the last three pending conv rows)."""
+    tile = 4 * d * d
+    ch = 3 * d
+    per_node = ch * in_bytes + 2 * in_bytes + 4 * d + (8 * d + 4) + 4 * ch
+    total = 0
+    S = int(view["n_seqs"])
+    for b in range(S):
+        L = int(pending[b])
+        n_b = int(view["seq_offsets"][b + 1] - view["seq_offsets"][b])
+        fold = tile + L * (8 * d + 4) + L * 4 * ch if L > 0 else 0
+        total += H * (tile + 2 * 12 * ch + fold + n_b * per_node)
+    return (total + H * ch * 4 * in_bytes) * n_layers
+
+
 def conv_bytes(view, pending, C, in_bytes, n_layers=1):
     """Per layer: x in, y out (fp32), x banked raw per node; window read (+ write and the last
     min(L, 3) pending inputs read when folding) per sequence; the weights once."""
@@ -154,6 +185,12 @@ def prefill_bytes(T, S, H, d):
     """One prefill call over T tokens of S sequences: q, k, v (bf16) and beta, g (bf16) in,
     o (fp32) out per (token, head); every (sequence, head) state read and written once."""
     return T * H * (3 * d * 2 + 2 * 2 + 4 * d) + 2 * S * H * d * d * 4
+
+
+def prefill_flops(T, H, d):
+    """The recurrence's work per token and head: S k and S q (2 d^2 each), the update
+    g S + u k^T (3 d^2): 7 d^2 flop, whatever the chunking."""
+    return 7 * d * d * T * H
 
 
 def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, layers=4,
@@ -194,18 +231,30 @@ def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, lay
     wall = time.perf_counter() - t0
     launch_s = sum(e0.elapsed_ms(e1) for per in ev for e0, e1 in per) / 1e3 / (reps * layers)
     per_call = prefill_bytes(T, S, H, d)
-    achieved = per_call / launch_s / 1e9
+    flops = prefill_flops(T, H, d)
     default = (S, length, H, d) == (8, 2048, 48, 128)
     traffic = recorded_traffic("prefill") if default else None
+    intensity = flops / per_call
+    ridge = FP32_MATRIX_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if intensity > ridge:  # above the fp32 matrix-core ridge: bounded by the matrix cores
+        achieved = flops / launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": FP32_MATRIX_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / FP32_MATRIX_PEAK_TFLOPS}
+    else:
+        achieved = per_call / launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS}
+    roof.update({"kernel": "prefill_kernel",
+                 "traffic": None if traffic is None else traffic / launch_s / 1e9,
+                 "flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
+                 "bytes_per_launch": per_call, "flops_per_launch": flops,
+                 "hbm_GBps": per_call / launch_s / 1e9, "launch_us": launch_s * 1e6})
     return {
         "workload": f"{S} sequences x {length} tokens x {H} heads x d{d}, bf16 inputs, fp32 "
                     f"state, one layer per call, {layers} layers x {reps} repeats",
         "value": reps * layers * T / wall, "unit": "token-layers/s",
         "ms_per_layer": wall * 1e3 / (reps * layers),
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "kernel": "prefill_kernel",
-                     "traffic": None if traffic is None else traffic / launch_s / 1e9,
-                     "bytes_per_launch": per_call, "launch_us": launch_s * 1e6},
+        "roofline": roof,
     }
 
 
@@ -240,37 +289,82 @@ def recorded_traffic(kernel):
     return rec["traffic_bytes_per_launch"]
 
 
-def _oracle_pair(job):
-    name, seq, layer, fused = job
+def _pair_inputs(name, seq, layer):
+    """Step-0 inputs of one (sequence, layer) of a preset, widened to float64, with its tree,
+    initial state and window, weights and accepted path."""
     from gated_deltanet_tree_amd import synth, workload
-    from oracle import conv as oconv
-    from oracle import gdn as ogdn
-    from oracle import prologue
     c = synth.WORKLOADS[name]
     seed = c["seed"]
     tree = synth.workload_tree(name, seq)
     n = len(tree)
     inp = synth.node_inputs(seed, 0, layer, seq, n, c["H"], c["d"], c["dtype"])
     inp = {k: workload.widen(v, c["dtype"]) for k, v in inp.items()}
-    x = workload.widen(synth.conv_inputs(seed, 0, layer, seq, n, c["Cch"], c["dtype"]), c["dtype"])
+    inp["x"] = workload.widen(synth.conv_inputs(seed, 0, layer, seq, n, c["Cch"], c["dtype"]),
+                              c["dtype"])
     W = workload.widen(synth.conv_weight(seed, layer, c["Cch"], 4, c["dtype"]), c["dtype"])
     S0 = synth.initial_state(seed, layer, seq, c["H"], c["d"]).astype(np.float64)
     X0 = synth.initial_conv_state(seed, layer, seq, c["Cch"], 4).astype(np.float64)
     path = synth.workload_path(name, 0, seq, tree)
+    return c, tree, inp, W, S0, X0, path
+
+
+def _oracle_pair(job):
+    """The oracle's work on one (sequence, layer) pair of step 0, as timed by the baseline."""
+    name, seq, layer, fused = job
+    from oracle import conv as oconv
+    from oracle import gdn as ogdn
+    from oracle import prologue
+    c, tree, inp, W, S0, X0, path = _pair_inputs(name, seq, layer)
     if fused:  # q, k, v from the conv (SiLU, unit length), then verify and commit by replay
-        _, q, k, v = prologue.conv_verify(tree, S0, X0, x, W, inp["beta"], inp["gate"],
+        _, q, k, v = prologue.conv_verify(tree, S0, X0, inp["x"], W, inp["beta"], inp["gate"],
                                           c["H"], c["d"])
         ogdn.replay(S0, k, v, inp["beta"], inp["gate"], path)
     else:
         ogdn.verify(tree, S0, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"],
                     keep_states=False)
-        oconv.tree_conv(tree, X0, x, W)
+        oconv.tree_conv(tree, X0, inp["x"], W)
         ogdn.replay(S0, inp["k"], inp["v"], inp["beta"], inp["gate"], path)
-    oconv.commit_window(X0, x, path)
-    return n
+    oconv.commit_window(X0, inp["x"], path)
+    return len(tree)
 
 
-def cpu_baseline(name, n_pairs, workers, fused):
+def _oracle_refs(job):
+    """Oracle results of step 0 on one (sequence, layer) pair, for the same-run parity check:
+    per verify form (the q/k/v forms and the fused form), the outputs, the banked factors and
+    the committed state after the step's accepted path (replay from the initial state)."""
+    name, seq, layer = job
+    from oracle import gdn as ogdn
+    from oracle import prologue
+    c, tree, inp, W, S0, X0, path = _pair_inputs(name, seq, layer)
+    refs = {"seq": seq, "layer": layer}
+    forms = {"qkv": (inp["q"], inp["k"], inp["v"])}
+    _, qf, kf, vf = prologue.conv_verify(tree, S0, X0, inp["x"], W, inp["beta"], inp["gate"],
+                                         c["H"], c["d"])
+    forms["fused"] = (qf, kf, vf)
+    for form, (q, k, v) in forms.items():
+        o, states = ogdn.verify(tree, S0, q, k, v, inp["beta"], inp["gate"])
+        kk, u, lg = ogdn.factors(tree, S0, k, v, inp["beta"], inp["gate"], states)
+        S1 = ogdn.replay(S0, k, v, inp["beta"], inp["gate"], path)
+        refs[form] = dict(o=o.astype(np.float32), k=kk.astype(np.float32),
+                          u=u.astype(np.float32), lg=lg.astype(np.float32), S1=S1)
+    return refs
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(name, n_pairs, workers, fused, n_parity):
+    """The oracle as it stands, timed on n_pairs seeded (sequence, layer) pairs over `workers`
+    processes; then (untimed) the oracle's step-0 results on the first n_parity distinct
+    pairs, which the GPU run is checked against."""
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
     from gated_deltanet_tree_amd import synth
@@ -278,6 +372,7 @@ def cpu_baseline(name, n_pairs, workers, fused):
     rng = np.random.default_rng(1234)
     jobs = [(name, int(rng.integers(c["Bs"])), int(rng.integers(c["Ly"])), fused)
             for _ in range(n_pairs)]
+    parity_pairs = list(dict.fromkeys((j[1], j[2]) for j in jobs))[:n_parity]
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
     ctx = mp.get_context("spawn")
@@ -286,21 +381,63 @@ def cpu_baseline(name, n_pairs, workers, fused):
         t0 = time.perf_counter()
         nodes = sum(ex.map(_oracle_pair, jobs))
         dt = time.perf_counter() - t0
+        refs = list(ex.map(_oracle_refs, [(name, s, l) for s, l in parity_pairs]))
     work = ("tree conv, SiLU and unit q/k, then fp64 verify of every node by root-path replay"
             if fused else "fp64 verify of every node by root-path replay, tree conv")
-    return dict(value=nodes / dt, unit="node-layers/s", cores=workers, kind="oracle",
+    base = dict(value=nodes / dt, unit="node-layers/s", cores=workers, kind="oracle",
+                cpu_model=cpu_model(), host_cpus=os.cpu_count(),
                 sample=f"{n_pairs} seeded (sequence, layer) pairs of the workload: {work}, and "
                        f"commit by replay; {nodes} node-layers in {dt:.1f} s over {workers} "
-                       f"processes")
+                       f"processes (one thread each)")
+    return base, refs
 
 
 # ----------------------------------------------------------------------------------------
+
+def vec_rel(x, r):
+    """Normwise max relative error per vector (last axis)."""
+    return np.max(np.abs(x - r), axis=-1) / np.maximum(np.max(np.abs(r), axis=-1), 1e-300)
+
+
+def row_rel(x, r):
+    return np.linalg.norm(x - r, axis=-1) / np.maximum(np.linalg.norm(r, axis=-1), 1e-300)
+
+
+def frob_rel(x, r):
+    return np.sqrt(np.sum((x - r) ** 2, axis=(-2, -1))) / np.sqrt(np.sum(r ** 2, axis=(-2, -1)))
+
+
+def draw_device_inputs(torch, like, gen):
+    """A fresh input set shaped like `like` (StepInputs of the workload), drawn on the device
+    from a seeded generator with the workload's distributions: q, k unit-normalised N(0, 1),
+    v and x N(0, 1), beta = sigmoid(N(0, 1)), g = exp(-softplus(N(0, 1))), all bf16."""
+    import torch.nn.functional as F
+    from gated_deltanet_tree_amd import workload
+
+    def n(t):
+        return torch.randn(t.shape, device=t.device, generator=gen)
+
+    def unit(t):
+        x = n(t)
+        return (x / x.norm(dim=-1, keepdim=True)).to(t.dtype)
+
+    return workload.StepInputs(q=unit(like.q), k=unit(like.k), v=n(like.v).to(like.v.dtype),
+                               beta=torch.sigmoid(n(like.beta)).to(like.beta.dtype),
+                               gate=torch.exp(-F.softplus(n(like.gate))).to(like.gate.dtype),
+                               x=n(like.x).to(like.x.dtype))
+
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=5,
+                    help="repetitions of the timed K steps (+ flush), every buffer restored from "
+                         "a pristine device copy between them; median and min are reported")
+    ap.add_argument("--input-sets", type=int, default=4,
+                    help="input sets rotated across steps (set 0 from the host recipe, the "
+                         "others drawn on the device with the same distributions)")
     ap.add_argument("--workload", default="batched",
                     choices=["one-layer", "48-layer", "batched", "wide-deep", "chain16"])
     ap.add_argument("--layers-per-call", type=int, default=1)
@@ -317,9 +454,13 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill line")
     ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--cpu-workers", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also time a 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--parity-pairs", type=int, default=6,
+                    help="(sequence, layer) pairs of step 0 checked against the oracle in the "
+                         "same run (0: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (and with it the same-run parity check)")
+    ap.add_argument("--no-copy-probe", action="store_true",
+                    help="skip the device-to-device copy probe")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one MI355X: the tree verify path runs on a single GPU here; "
@@ -332,11 +473,12 @@ def main(argv=None):
     H, d, C, Ly, dtype = cfg["H"], cfg["d"], cfg["Cch"], cfg["Ly"], cfg["dtype"]
     in_bytes = 2 if dtype == "bf16" else 4
 
-    # The CPU baseline runs first, before this process touches the GPU.
-    cpu = None
+    # The oracle leg runs first, before this process touches the GPU.
+    cpu, refs = None, []
     if not args.no_cpu_baseline:
         workers = args.cpu_workers or min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(args.workload, args.cpu_pairs, workers, args.verify == "fused")
+        cpu, refs = cpu_baseline(args.workload, args.cpu_pairs, workers, args.verify == "fused",
+                                 args.parity_pairs)
 
     import torch
     from gated_deltanet_tree_amd import binding
@@ -355,7 +497,11 @@ def main(argv=None):
     t_gen = time.perf_counter()
     state0, conv0 = workload.host_initial_state(args.workload, range(Ly), S)
     weights = workload._to_torch(workload.host_weights(args.workload, range(Ly)), dtype, dev)
-    inp = workload.device_step_inputs(args.workload, 0, trees, range(Ly), dev)
+    inp0 = workload.device_step_inputs(args.workload, 0, trees, range(Ly), dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.ROOT_SEED + 100)
+    input_sets = [inp0] + [draw_device_inputs(torch, inp0, gen)
+                           for _ in range(max(args.input_sets, 1) - 1)]
     lay = binding.alloc_layers(Ly, S, H, d, max_nodes, C, dev, conv_dtype=dtype)
     lay.state.copy_(torch.from_numpy(state0))
     lay.conv_state.copy_(torch.from_numpy(conv0))
@@ -364,22 +510,41 @@ def main(argv=None):
                             device=dev, dtype=torch.float32)
     out = torch.empty((Ly, T, H, d), device=dev, dtype=torch.float32)
     y = torch.empty((Ly, T, C), device=dev, dtype=torch.float32)
+    torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
-    n_total = args.warmup + args.steps
+    # every buffer a step writes, for the pristine copies
+    def buffers():
+        return ([lay.state, lay.conv_state, lay.role, lay.pending, lay.pending_rows] +
+                lay.bank_k + lay.bank_u + lay.bank_lg + lay.bank_x)
+
+    def snapshot():
+        return ([t.clone() for t in buffers()], lay.role_host.copy(), lay.pending_host.copy())
+
+    def restore(snap):
+        for dst, src in zip(buffers(), snap[0]):
+            dst.copy_(src)
+        lay.role_host[:] = snap[1]
+        lay.pending_host[:] = snap[2]
+
+    initial = snapshot()
+
+    n_steps = args.warmup + args.steps
     all_paths = [[synth.workload_path(args.workload, s, b, trees[b]) for b in range(S)]
-                 for s in range(n_total)]
-    vargs = [binding.verify_args(image0, lay, inp.q, inp.k, inp.v, inp.beta, inp.gate, out,
-                                 workspace, layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
-    cargs = [binding.conv_args(image0, lay, inp.x, weights, y, layer_begin=l, n_layers=lpc)
-             for l in range(0, Ly, lpc)]
-    fvargs = [binding.verify_args(image0, lay, None, None, None, inp.beta, inp.gate, out, None,
-                                  layer_begin=l, n_layers=lpc) for l in range(0, Ly, lpc)]
-    fcargs = [binding.conv_args(image0, lay, inp.x, weights, None, layer_begin=l, n_layers=lpc)
-              for l in range(0, Ly, lpc)]
+                 for s in range(n_steps)]
+    calls = range(0, Ly, lpc)
+    n_sets = len(input_sets)
+    vargs = [[binding.verify_args(image0, lay, i.q, i.k, i.v, i.beta, i.gate, out, workspace,
+                                  layer_begin=l, n_layers=lpc) for l in calls] for i in input_sets]
+    cargs = [[binding.conv_args(image0, lay, i.x, weights, y, layer_begin=l, n_layers=lpc)
+              for l in calls] for i in input_sets]
+    fvargs = [[binding.verify_args(image0, lay, None, None, None, i.beta, i.gate, out, None,
+                                   layer_begin=l, n_layers=lpc) for l in calls]
+              for i in input_sets]
+    fcargs = [[binding.conv_args(image0, lay, i.x, weights, None, layer_begin=l, n_layers=lpc)
+               for l in calls] for i in input_sets]
     va_all = binding.verify_args(image0, lay, None, None, None, None, None, None, None, 0, Ly)
     ca_all = binding.conv_args(image0, lay, None, None, None, 0, Ly)
-    stream = torch.cuda.current_stream()
 
     def upload(a):
         return torch.from_numpy(a).pin_memory().to(dev, non_blocking=True)
@@ -387,107 +552,161 @@ def main(argv=None):
     n_waves = int(view["n_waves"])
     commit_mode = {"row-map": binding.COMMIT_ROW_MAP, "compact": binding.COMMIT_COMPACT}[args.commit]
 
-    def run_path(verify):
-        acc = dict(verify_ms=0.0, verify_launches=0, verify_bytes=0, stamped_bytes=0,
-                   conv_bytes=0, commit_bytes=0)
-        # The verify launches of the last timed step are timed by events recorded by the
-        # dispatches themselves (no extra packets on the stream); one pair per (layer call,
-        # launch) of that step.
-        launches = n_waves if verify == "chain" else 1
-        last = args.steps - 1
-        ev = [{li: [(binding.HipEvent(), binding.HipEvent()) for _ in range(launches)]
-               for li in (range(len(vargs)) if i == last else [])} for i in range(args.steps)]
-
-        def step(s, timed_index):
-            image = binding.hld_schedule(trees)  # a1: host schedule of this step's trees
-            dev_image = upload(image)
-            pending = [int(L) for L in lay.pending_host]
-            for li in range(len(vargs)):
-                stamp = timed_index == last
-                if verify == "fused":  # conv, SiLU, unit q/k and verify in one launch
-                    if not stamp:
-                        binding.tree_conv_verify(fvargs[li], fcargs[li], image, dev_image)
-                    else:
-                        e0, e1 = ev[timed_index][li][0]
-                        binding.tree_conv_verify_timed(fvargs[li], fcargs[li], image, dev_image,
-                                                       e0, e1)
-                    continue
-                binding.tree_conv(cargs[li], image, dev_image)
-                if verify == "ut":
-                    if not stamp:
-                        binding.tree_verify_ut(vargs[li], image, dev_image)
-                    else:
-                        e0, e1 = ev[timed_index][li][0]
-                        binding.tree_verify_ut_timed(vargs[li], image, dev_image, e0, e1)
-                    continue
-                for w in range(n_waves):
-                    if not stamp:
-                        binding.tree_verify_wave(vargs[li], image, dev_image, w)
-                    else:
-                        e0, e1 = ev[timed_index][li][w]
-                        binding.tree_verify_wave_timed(vargs[li], image, dev_image, w, e0, e1)
-            paths = all_paths[s]
-            flat, offs = binding.pack_paths(paths)
-            binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs),
-                                mode=commit_mode)
-            if timed_index is not None:  # byte accounting after the launches, off the GPU's path
-                calls = len(vargs)
-                if verify == "fused":
-                    per_call = fused_bytes(view, pending, H, d, in_bytes, lpc)
-                elif verify == "ut":
-                    per_call = ut_bytes(view, pending, H, d, in_bytes, lpc)
+    def launch_layers(verify, k, stamp=None):
+        """Every layer call of one step with input set k; stamp: per call, the events of its
+        verify launches."""
+        image = binding.hld_schedule(trees)  # a1: host schedule of this step's trees
+        dev_image = upload(image)
+        for li in range(len(calls)):
+            ev = None if stamp is None else stamp[li]
+            if verify == "fused":  # conv, SiLU, unit q/k and verify in one launch
+                if ev is None:
+                    binding.tree_conv_verify(fvargs[k][li], fcargs[k][li], image, dev_image)
                 else:
-                    per_call = sum(verify_wave_bytes(view, w, pending, H, d, in_bytes, lpc)
-                                   for w in range(n_waves))
-                acc["verify_bytes"] += calls * per_call
-                if timed_index == last:
-                    acc["stamped_bytes"] += calls * per_call
-                    acc["verify_launches"] += calls * launches
-                if verify != "fused":  # the fused launch already counts its conv traffic
-                    acc["conv_bytes"] += calls * conv_bytes(view, pending, C, in_bytes, lpc)
-                acc["commit_bytes"] += commit_bytes(paths, H, d, C, Ly,
-                                                    commit_mode == binding.COMMIT_COMPACT,
-                                                    in_bytes)
+                    binding.tree_conv_verify_timed(fvargs[k][li], fcargs[k][li], image,
+                                                   dev_image, *ev[0])
+                continue
+            binding.tree_conv(cargs[k][li], image, dev_image)
+            if verify == "ut":
+                if ev is None:
+                    binding.tree_verify_ut(vargs[k][li], image, dev_image)
+                else:
+                    binding.tree_verify_ut_timed(vargs[k][li], image, dev_image, *ev[0])
+                continue
+            for w in range(n_waves):
+                if ev is None:
+                    binding.tree_verify_wave(vargs[k][li], image, dev_image, w)
+                else:
+                    binding.tree_verify_wave_timed(vargs[k][li], image, dev_image, w, *ev[w])
+        return image
 
+    def commit(image, paths):
+        flat, offs = binding.pack_paths(paths)
+        binding.commit_path(image, paths, lay, va_all, ca_all, upload(flat), upload(offs),
+                            mode=commit_mode)
+
+    def run_path(verify):
+        launches = n_waves if verify == "chain" else 1
+        restore(initial)
         for s in range(args.warmup):
-            step(s, None)
+            image = launch_layers(verify, s % n_sets)
+            commit(image, all_paths[s])
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i, s in enumerate(range(args.warmup, n_total)):
-            step(s, i)
-        flush_pending = lay.pending_host.copy()
-        binding.flush(va_all, ca_all, lay)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        for per_step in ev:
-            for per_call in per_step.values():
-                for e0, e1 in per_call:
-                    acc["verify_ms"] += e0.elapsed_ms(e1)
-        total_bytes = acc["verify_bytes"] + acc["conv_bytes"] + acc["commit_bytes"] + \
-            fold_bytes(flush_pending, H, d, C, Ly, in_bytes)
-        v_launch_s = acc["verify_ms"] / 1e3 / max(acc["verify_launches"], 1)
-        v_launch_bytes = acc["stamped_bytes"] / max(acc["verify_launches"], 1)
-        calls_total = args.steps * len(vargs)
-        achieved = v_launch_bytes / v_launch_s / 1e9
+        pristine = snapshot()
+        # The verify launches of the last timed step of the last repetition are timed by events
+        # recorded by the dispatches themselves (no extra packets on the stream).
+        ev = [[(binding.HipEvent(), binding.HipEvent()) for _ in range(launches)]
+              for _ in calls]
+        walls, per_step_bytes = [], []
+        stamped_pending = None
+        for rep in range(args.reps):
+            restore(pristine)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                s = args.warmup + i
+                last = rep == args.reps - 1 and i == args.steps - 1
+                if last:
+                    stamped_pending = [int(L) for L in lay.pending_host]
+                if rep == 0:
+                    per_step_bytes.append([int(L) for L in lay.pending_host])
+                image = launch_layers(verify, s % n_sets, ev if last else None)
+                commit(image, all_paths[s])
+            flush_pending = lay.pending_host.copy()
+            binding.flush(va_all, ca_all, lay)
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
+        # bytes of one timed unit (K steps + flush), from each step's pending lengths
+        ncall = len(calls)
+        unit_bytes = 0
+        for s_i, pend in enumerate(per_step_bytes):
+            paths = all_paths[args.warmup + s_i]
+            if verify == "fused":
+                unit_bytes += ncall * fused_method_bytes(view, pend, H, d, in_bytes, lpc)
+            elif verify == "ut":
+                unit_bytes += ncall * (ut_bytes(view, pend, H, d, in_bytes, lpc) +
+                                       conv_bytes(view, pend, C, in_bytes, lpc))
+            else:
+                unit_bytes += ncall * (sum(verify_wave_bytes(view, w, pend, H, d, in_bytes, lpc)
+                                           for w in range(n_waves)) +
+                                       conv_bytes(view, pend, C, in_bytes, lpc))
+            unit_bytes += commit_bytes(paths, H, d, C, Ly, commit_mode == binding.COMMIT_COMPACT,
+                                       in_bytes)
+        unit_bytes += fold_bytes(flush_pending, H, d, C, Ly, in_bytes)
+        # the stamped launches: per-launch duration and bytes
+        launch_s = sum(e0.elapsed_ms(e1) for per in ev for e0, e1 in per) / 1e3 / (ncall * launches)
+        if verify == "fused":
+            lb = fused_method_bytes(view, stamped_pending, H, d, in_bytes, lpc)
+            kb = fused_bytes(view, stamped_pending, H, d, in_bytes, lpc)
+        elif verify == "ut":
+            lb = kb = ut_bytes(view, stamped_pending, H, d, in_bytes, lpc)
+        else:
+            lb = kb = sum(verify_wave_bytes(view, w, stamped_pending, H, d, in_bytes, lpc)
+                          for w in range(n_waves)) / n_waves
+        achieved = lb / launch_s / 1e9
         traffic_bytes = measured_traffic(args.workload, lpc, verify)
+        med = float(np.median(walls))
         return {
-            "value": args.steps * T * Ly / wall,
-            "ms_per_step": wall * 1e3 / args.steps,
+            "value": args.steps * T * Ly / med,
+            "ms_per_step": med * 1e3 / args.steps,
+            "ms_per_step_median": med * 1e3 / args.steps,
+            "ms_per_step_min": min(walls) * 1e3 / args.steps,
+            "reps": len(walls),
             "roofline": {
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS,
-                "traffic": None if traffic_bytes is None else traffic_bytes / v_launch_s / 1e9,
+                "traffic": None if traffic_bytes is None else traffic_bytes / launch_s / 1e9,
                 "traffic_bytes_per_launch": traffic_bytes,
                 "kernel": KERNEL[verify],
-                "bytes_per_launch": v_launch_bytes, "launch_us": v_launch_s * 1e6,
+                "bytes_per_launch": lb, "kernel_bytes_per_launch": kb,
+                "launch_us": launch_s * 1e6,
             },
-            "algorithmic_GBps_step": total_bytes / wall / 1e9,
-            "algorithmic_bytes_per_step": total_bytes / args.steps,
-            "compulsory_GBps_step": args.steps * Ly * S * H * 2 * 4 * d * d / wall / 1e9,
-            # verify time per step, extrapolated from the stamped sample
-            "verify_ms_per_step": v_launch_s * 1e3 * launches * calls_total / args.steps,
-            "stamped_launches": acc["verify_launches"],
+            "algorithmic_GBps_step": unit_bytes / med / 1e9,
+            "algorithmic_bytes_per_step": unit_bytes / args.steps,
+            "compulsory_GBps_step": args.steps * Ly * S * H * 2 * 4 * d * d / med / 1e9,
+            "verify_ms_per_step": launch_s * 1e3 * launches * ncall,
         }
+
+    def parity(verify):
+        """Step 0 from the initial state through the timed kernels and launch shape, against
+        the oracle's results from the baseline leg: outputs and written banks of the sampled
+        pairs, then the committed state after the step's paths are accepted and flushed."""
+        if not refs:
+            return None
+        form = "fused" if verify == "fused" else "qkv"
+        restore(initial)
+        role0 = lay.role_host.copy()
+        image = launch_layers(verify, 0)
+        torch.cuda.synchronize()
+        err = {"o": 0.0, "k": 0.0, "u": 0.0, "lg_ulps": 0.0, "state": 0.0}
+        offs = view["seq_offsets"]
+        for r in refs:
+            b, l = r["seq"], r["layer"]
+            ref = r[form]
+            n = int(offs[b + 1] - offs[b])
+            o = out[l, int(offs[b]):int(offs[b + 1])].double().cpu().numpy()
+            wb = 1 - int(role0[b])
+            kg = lay.bank_k[wb][l, b][:, :n].double().cpu().numpy().transpose(1, 0, 2)
+            ug = lay.bank_u[wb][l, b][:, :n].double().cpu().numpy().transpose(1, 0, 2)
+            lgg = lay.bank_lg[wb][l, b][:, :n].double().cpu().numpy().T
+            err["o"] = max(err["o"], float(np.max(vec_rel(o, ref["o"]))))
+            err["k"] = max(err["k"], float(np.max(row_rel(kg, ref["k"]))))
+            err["u"] = max(err["u"], float(np.max(row_rel(ug, ref["u"]))))
+            ulp = np.spacing(np.abs(ref["lg"]).astype(np.float32)).astype(np.float64)
+            err["lg_ulps"] = max(err["lg_ulps"], float(np.max(np.abs(lgg - ref["lg"]) / ulp)))
+        commit(image, all_paths[0])
+        binding.flush(va_all, ca_all, lay)
+        torch.cuda.synchronize()
+        for r in refs:
+            b, l = r["seq"], r["layer"]
+            Sg = lay.state[l, b].double().cpu().numpy()
+            err["state"] = max(err["state"], float(np.max(frob_rel(Sg, r[form]["S1"]))))
+        ok = (err["o"] <= 1e-3 and err["state"] <= 1e-5 and err["u"] <= 1e-5 and
+              err["k"] <= (1e-5 if form == "fused" else 0.0) and err["lg_ulps"] <= 4)
+        return {"pairs": [[r["seq"], r["layer"]] for r in refs], "max_err": err,
+                "bars": {"o": 1e-3, "state": 1e-5, "u": 1e-5,
+                         "k": 1e-5 if form == "fused" else 0.0, "lg_ulps": 4},
+                "pass": bool(ok)}
 
     # Draft-tree builder (host): the batch's trees from seeded synthetic drafts, budget 22,
     # top-4, tau 6, chain pre-seed, 15 draft positions.
@@ -507,8 +726,32 @@ def main(argv=None):
 
     order = [args.verify] + ([] if args.only else
                              [p for p in ("fused", "ut", "chain") if p != args.verify])
-    runs = {p: run_path(p) for p in order}
+    runs = {}
+    for p in order:
+        runs[p] = run_path(p)
+        runs[p]["parity"] = parity(p)
     head = runs[args.verify]
+
+    copy = None
+    if not args.no_copy_probe:
+        src = torch.empty(1 << 28, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        n_copy = 10
+        for _ in range(n_copy):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy = {"bytes_per_copy": 2 * src.numel() * 4,
+                "GBps": 2 * src.numel() * 4 * n_copy / (e0.elapsed_time(e1) / 1e3) / 1e9}
+        del src, dst
+        for r in runs.values():
+            r["roofline"]["frac_vs_copy"] = r["roofline"]["achieved"] / copy["GBps"]
+
     result = {
         "metric": METRIC,
         "value": head["value"],
@@ -517,6 +760,9 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "ms_per_step_median": head["ms_per_step_median"],
+        "ms_per_step_min": head["ms_per_step_min"],
+        "reps": head["reps"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -532,9 +778,18 @@ def main(argv=None):
             "chains": int(view["n_chains"]), "waves": int(view["n_waves"]),
             "boundary_nodes": int(view["n_boundaries"]), "layers_per_call": lpc,
             "verify": args.verify, "commit": args.commit,
+            "inputs": f"{n_sets} input sets rotated across steps (set 0 from the host recipe, "
+                      f"{n_sets - 1} drawn on the device with the same distributions); "
+                      f"{args.reps} repetitions of the {args.steps} timed steps + flush, every "
+                      f"buffer restored from a pristine device copy between them; value and "
+                      f"ms_per_step from the median repetition",
         },
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "parity": head["parity"],
+        "copy_GBps": None if copy is None else copy["GBps"],
+        "frac_vs_copy": head["roofline"].get("frac_vs_copy"),
+        "cpu_model": cpu_model(),
         "algorithmic_GBps_step": head["algorithmic_GBps_step"],
         "algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"],
         "compulsory_GBps_step": head["compulsory_GBps_step"],
@@ -544,20 +799,6 @@ def main(argv=None):
         "prefill": None if args.no_prefill else prefill_bench(torch, binding, synth, dev),
         "input_generation_s": gen_s,
     }
-    if args.copy_probe:
-        src = torch.empty(1 << 28, device=dev, dtype=torch.float32).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        reps = 10
-        for _ in range(reps):
-            dst.copy_(src)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        result["copy_probe"] = {"bytes_per_copy": 2 * src.numel() * 4,
-                                "GBps": 2 * src.numel() * 4 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9}
     print(json.dumps(result), flush=True)
     return 0
 
