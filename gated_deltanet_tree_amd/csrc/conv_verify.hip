@@ -52,8 +52,10 @@ namespace gdn {
 namespace {
 
 constexpr int kCvD = 128;
+constexpr int kCvThreads = 512;  // 8 waves; wave w owns state rows [16w, 16w + 16)
+constexpr int kCvWaves = kCvThreads / 64;
 constexpr float kNormFloor = 1e-6f;
-constexpr int kFoldRows = 4 * 256 / 64;  // pending rows per stage: 4 chunks per thread, 64 per row
+constexpr int kFoldRows = 2 * kCvThreads / 64;  // pending rows per stage: 2 chunks per thread, 64 per row
 
 struct ConvVerifyParams {
     VerifyParams V;
@@ -77,7 +79,7 @@ struct CvLayout {
     static constexpr int XROW = D * 2;      // bytes of one bf16 conv-input row of one block
     static constexpr int KS = D + 4;        // fp32 row stride (floats): 16 rows hit distinct banks
     static constexpr int CPR = D * 4 / 16;  // 16-byte chunks per fp32 fold row
-    size_t xv, xq, kq, fold_k, fold_u, fold_c, bg, pd, plan, tabs, x0s, total;
+    size_t xv, xq, kq, fold_k, fold_u, fold_c, bg, pd, plan, tabs, x0s, wv, total;
     size_t n64, lv64, rec64;
 
     __host__ __device__ static size_t fold_chunks(int r) { return round_up(size_t(r) * CPR, 64); }
@@ -121,13 +123,14 @@ struct CvLayout {
         p += 2 * n64 * 4;
         pd = p;                   // parent | depth [n64] int (global parent ids)
         p += 2 * n64 * 4;
-        plan = p;                 // poff [n64] | lvnode [n64] | lvn [lv64] | recM [rec64]
-        p += (2 * n64 + lv64 + rec64) * 4;
+        plan = p;                 // poff [n64] | lvn [lv64] | recM [rec64]
+        p += (n64 + lv64 + rec64) * 4;
         tabs = p;                 // gam | kqd [n] | recE=recY | recC | recQ | recZ [nrec] (f32),
                                   // recP | recT [nrec], anc [n][4] (int)
         p += (size_t(2) * n + size_t(6) * nrec + size_t(4) * n) * 4;
         x0s = round_up(p, 16);    // folded conv window [3 taps][3 D channels]
-        total = x0s + size_t(3) * 3 * D * 4;
+        wv = x0s + size_t(3) * 3 * D * 4;  // v-block conv weights [D channels][4 taps], bf16
+        total = wv + size_t(D) * 4 * 2;
     }
 };
 
@@ -144,15 +147,15 @@ __device__ __forceinline__ float chunk_suffix_sum(float x) {
 }
 
 // Pending rows f0 .. f0 + cnt - 1 (cnt <= kFoldRows) go through registers into LDS: 16-byte chunk
-// c of thread t is c = t + 256 j (j < 4), row c / 64, key half (c % 64 < 32) or residual half;
-// the row is uniform over a wave (w + 4 j), its bank row comes from the pending row map.
+// c of thread t is c = t + 512 j (j < 2), row c / 64, key half (c % 64 < 32) or residual half;
+// the row is uniform over a wave (w + 8 j), its bank row comes from the pending row map.
 // With the rows, wave 0 stages each row's fold coefficient c_f = exp(sum of the log gates of the
 // pending rows after f): an exclusive suffix scan over the chunk (lane f sums the log gates of
 // lanes f + 1 .. 15, never its own, so a zero gate's -inf is only ever added, and c_f = 0 for
 // every row before it) plus fold_carry, the sum over the chunks already staged (they hold later
-// rows).  Register loads rather than direct-to-LDS loads: an LDS
-// read after a direct load waits for every older memory operation of the wave.  Four named
-// registers (no array), so nothing of it goes to scratch.
+// rows).  Register loads rather than direct-to-LDS loads: an LDS read after a direct load waits
+// for every older memory operation of the wave.  Two named registers (no array), so nothing of
+// it goes to scratch.
 __device__ __forceinline__ uint4 fold_chunk_load(const float *pk, const float *pu, int row,
                                                  int lane) {
     const int half = (lane >> 5) & 1, idx = lane & 31;
@@ -168,18 +171,14 @@ __device__ __forceinline__ void fold_chunk_store(float *fk, float *fu, int cnt, 
     do {                                                                                \
         const int lc_ = (cnt) - 1;                                                      \
         fv0 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w, lc_)), lane);      \
-        fv1 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w + 4, lc_)), lane);  \
-        fv2 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w + 8, lc_)), lane);  \
-        fv3 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w + 12, lc_)), lane); \
+        fv1 = fold_chunk_load(pend_k, pend_u, pend_row((f0) + min(w + 8, lc_)), lane);  \
         const int fl_ = (f0) + min(lane, lc_), rl_ = __shfl(rml, min(fl_, 63));         \
         flv = pend_lg[fl_ < 64 ? rl_ : min(max(rm[fl_], 0), mrow)];                     \
     } while (0)
 #define GDN_FOLD_STORE(cnt)                                                             \
     do {                                                                                \
         fold_chunk_store(fold_k, fold_u, (cnt), tid, fv0);                              \
-        fold_chunk_store(fold_k, fold_u, (cnt), tid + 256, fv1);                        \
-        fold_chunk_store(fold_k, fold_u, (cnt), tid + 512, fv2);                        \
-        fold_chunk_store(fold_k, fold_u, (cnt), tid + 768, fv3);                        \
+        fold_chunk_store(fold_k, fold_u, (cnt), tid + 512, fv1);                        \
         if (w == 0) {                                                                   \
             const float v_ = lane < (cnt) ? flv : 0.f;                                  \
             const float n_ = __shfl_down(v_, 1);                                        \
@@ -206,11 +205,13 @@ __device__ __forceinline__ float conv4(const float wt[4], float x0, float x1, fl
 
 }  // namespace
 
-__global__ __launch_bounds__(256, GDN_VERIFY_MIN_WAVES)
+// 6 waves per SIMD: three workgroups of 8 waves per CU (the LDS allows three), which needs at
+// most 80 VGPRs per lane.
+__global__ __launch_bounds__(kCvThreads, 6)
 void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                         const int32_t *__restrict__ rows, int n_max, int nrec_max, int nlv_max,
                         int nf, int nfc) {
-    constexpr int D = kCvD, THREADS = 256, NW = 4, JC = 4;
+    constexpr int D = kCvD, THREADS = kCvThreads, NW = kCvWaves, JC = 3;
     using LY = CvLayout;
     const VerifyParams &P = CP.V;
     extern __shared__ __align__(16) float dyn[];
@@ -230,8 +231,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     // Plan of this tree (from the schedule image): record poff[n] is n itself, poff[n] + d its
     // ancestor at distance d; recM = that node.
     int *poff = reinterpret_cast<int *>(lds + lay.plan);
-    int *lvnode = poff + n64;   // nodes ordered by depth, then index
-    int *lvn = lvnode + n64;    // first entry of each depth level in lvnode
+    int *lvn = poff + n64;      // first node of each depth level, in (depth, id) order
     int *recM = lvn + lay.lv64;
     float *gam = reinterpret_cast<float *>(lds + lay.tabs);
     float *kqd = gam + n_max;
@@ -248,6 +248,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
+    const int row0 = 16 * w;  // this wave's first state row
     const UtUnit un = ut_unit(P);
     const int layer = P.layer_begin + un.layer_rel, seq = un.seq, h = un.h;
     // Image words are read through `plan` (a no-alias argument) and before any direct load, so
@@ -293,7 +294,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     float *fold_k = reinterpret_cast<float *>(lds + lay.fold_k);
     float *fold_u = reinterpret_cast<float *>(lds + lay.fold_u);
     float *fold_c = reinterpret_cast<float *>(lds + lay.fold_c);
-    uint4 fv0, fv1, fv2, fv3;
+    uint4 fv0, fv1;
     float flv, fold_carry = 0.f;
 
     // ---- 0. loads ------------------------------------------------------------------------
@@ -320,38 +321,40 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                 to_lds<4>(src, lds + lay.pd + size_t(base - 2 * int(n64)) * 4);
             }
         }
+        if (w == NW - 1)  // the v block's conv weights: 128 channels x 4 taps, one load per lane
+            to_lds<16>(CP.w + (int64_t(layer) * C + 2 * HD + h * D + 2 * lane) * 4,
+                       lds + lay.wv);
         if (n > 0) {  // the tree's plan: node blocks, level lists, ancestor records
-            const int32_t *srcs[4] = {P.img + P.off_ut_node_rec + seq_off,
-                                      P.img + P.off_ut_lvnode + seq_off, P.img + P.off_ut_lvn + l0,
-                                      P.img + P.off_ut_rec_anc + r0};
-            const int counts[4] = {n, n, nlv, nrec};
-            int *dsts[4] = {poff, lvnode, lvn, recM};
+            const int32_t *srcs[3] = {P.img + P.off_ut_node_rec + seq_off,
+                                      P.img + P.off_ut_lvn + l0, P.img + P.off_ut_rec_anc + r0};
+            const int counts[3] = {n, nlv, nrec};
+            int *dsts[3] = {poff, lvn, recM};
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 3; ++a)
                 for (int base = w * 64; base < counts[a]; base += NW * 64)
                     to_lds<4>(srcs[a] + min(base + lane, counts[a] - 1), dsts[a] + base);
         }
     }
-    // committed conv windows (thread cc owns channels cc and cc + 256 of the head's 3 x 128)
-    // with their last pending inputs, and the q/k weights of this lane's channels
-    float win[2][3], pend[2][3];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int cc = tid + 256 * j;
-        const int ccl = cc < 3 * D ? cc : tid;  // threads with one channel re-read their first
+    // committed conv window (thread cc < 3 d owns channel cc of the head's 3 x 128) with its
+    // last pending inputs; the conv weights of the block this wave's prologue evaluates (waves
+    // of even index the q block, odd the k block), two channels per lane
+    const bool has_ch = tid < 3 * D;
+    float win[3], pend[3];
+    {
+        const int ccl = has_ch ? tid : 0;  // threads past the channels re-read channel 0
         const int64_t ch = int64_t(ccl >> 7) * HD + h * D + (ccl & (D - 1));
         const float *cs = CP.cstate + (ls * C + ch) * 3;
         const bf16_t *pb = CP.bank_x[role] + ls * P.max_nodes * C + ch;
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
-            win[j][e] = cs[e];
+            win[e] = cs[e];
             // pending input L - 3 + e, when it exists
-            pend[j][e] = L >= 3 - e ? to_f32(pb[int64_t(min(max(wrow[e], 0), mrow)) * C]) : 0.f;
+            pend[e] = L >= 3 - e ? to_f32(pb[int64_t(min(max(wrow[e], 0), mrow)) * C]) : 0.f;
         }
     }
-    const bf16_t *wq_src = CP.w + (int64_t(layer) * C + h * D + 2 * lane) * 4;
-    const uint4 wq = *reinterpret_cast<const uint4 *>(wq_src);
-    const uint4 wk = *reinterpret_cast<const uint4 *>(wq_src + int64_t(HD) * 4);
+    const int qk_blk = w & 1;  // 0: q, 1: k
+    const uint4 wraw = *reinterpret_cast<const uint4 *>(
+        CP.w + (int64_t(layer) * C + qk_blk * HD + h * D + 2 * lane) * 4);
     __syncthreads();  // waits for every direct load (the barrier's fence covers them)
 
     // this lane's share of the pending log gates (factor `lane`, then every 64th): their sum
@@ -374,32 +377,28 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                                                  c * 2);
         }
     }
-    float s[2][8][4];  // rows 32w + 16nt + lr, columns 16mt + 4lg + e
+    float s[8][4];  // row 16w + lr, columns 16mt + 4lg + e
     {
-        const float *tile = committed + (32 * w + lr) * D + 4 * lg;
+        const float *tile = committed + (row0 + lr) * D + 4 * lg;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * nt * D + 16 * mt);
-                s[nt][mt][0] = x.x;
-                s[nt][mt][1] = x.y;
-                s[nt][mt][2] = x.z;
-                s[nt][mt][3] = x.w;
-            }
+        for (int mt = 0; mt < 8; ++mt) {
+            const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * mt);
+            s[mt][0] = x.x;
+            s[mt][1] = x.y;
+            s[mt][2] = x.z;
+            s[mt][3] = x.w;
+        }
     }
     // conv window: only the last three pending inputs survive
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int cc = tid + 256 * j;
-        if (cc >= 3 * D) break;
-        float w0 = win[j][0], w1 = win[j][1], w2 = win[j][2];
+    if (has_ch) {
+        const int cc = tid;
+        float w0 = win[0], w1 = win[1], w2 = win[2];
         if (L >= 3) {
-            w0 = pend[j][0]; w1 = pend[j][1]; w2 = pend[j][2];
+            w0 = pend[0]; w1 = pend[1]; w2 = pend[2];
         } else if (L == 2) {
-            w0 = w2; w1 = pend[j][1]; w2 = pend[j][2];
+            w0 = w2; w1 = pend[1]; w2 = pend[2];
         } else if (L == 1) {
-            w0 = w1; w1 = w2; w2 = pend[j][2];
+            w0 = w1; w1 = w2; w2 = pend[2];
         }
         X0s[cc] = w0;
         X0s[3 * D + cc] = w1;
@@ -446,69 +445,51 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     __syncthreads();  // windows, records and ancestors in LDS
 
     // ---- 2. prologue: q and k from the conv ----------------------------------------------
+    // Wave w evaluates block qk_blk (q or k) of nodes w/2, w/2 + NW/2, ...; a lane owns two
+    // adjacent channels: conv along the parent chain, SiLU, a wave sum of squares, unit length.
     {
-        const char *XV = lds + lay.xv;
-        const char *XQ = XV + size_t(n) * LY::XROW, *XK = XQ + size_t(n) * LY::XROW;
-        // taps of channels 2 lane + e (e < 2) of the q (b = 0) and k (b = 1) blocks
-        float wt[2][2][4], cw[2][2][3];
-        const uint4 wraw[2] = {wq, wk};
+        const char *XB = lds + lay.xv + size_t(1 + qk_blk) * n * LY::XROW;  // plane q or k
+        float wt[2][4], cw[2][3];
+        const uint32_t r4[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const uint32_t r4[4] = {wraw[b].x, wraw[b].y, wraw[b].z, wraw[b].w};
+        for (int e = 0; e < 2; ++e) {
+            wt[e][0] = bf16_lo(r4[2 * e]);
+            wt[e][1] = bf16_hi(r4[2 * e]);
+            wt[e][2] = bf16_lo(r4[2 * e + 1]);
+            wt[e][3] = bf16_hi(r4[2 * e + 1]);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                wt[b][e][0] = bf16_lo(r4[2 * e]);
-                wt[b][e][1] = bf16_hi(r4[2 * e]);
-                wt[b][e][2] = bf16_lo(r4[2 * e + 1]);
-                wt[b][e][3] = bf16_hi(r4[2 * e + 1]);
-#pragma unroll
-                for (int j = 0; j < 3; ++j) cw[b][e][j] = X0s[j * 3 * D + b * D + 2 * lane + e];
-            }
+            for (int j = 0; j < 3; ++j) cw[e][j] = X0s[j * 3 * D + qk_blk * D + 2 * lane + e];
         }
-        for (int nd = w; nd < n; nd += NW) {
+        // k_n at KQ row 2n, q_n at 2n + 1
+        float *dst0 = KQ + size_t(1 - qk_blk) * LY::KS + 2 * lane;
+        for (int nd = w >> 1; nd < n; nd += NW / 2) {
             const int dt = dep[nd];
             const int4 an = anc[nd];
-            const int rows[4] = {nd, an.x, an.y, an.z};
-            float y[2][2], ss[2];
+            const int rws[4] = {nd, an.x, an.y, an.z};
+            uint32_t xw[4];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const char *pl = b == 0 ? XQ : XK;
-                uint32_t xw[4];
+            for (int t = 0; t < 4; ++t)
+                xw[t] = *reinterpret_cast<const uint32_t *>(XB + size_t(rws[t]) * LY::XROW + 4 * lane);
+            float y[2], ss = 0.f;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    xw[t] = *reinterpret_cast<const uint32_t *>(pl + size_t(rows[t]) * LY::XROW + 4 * lane);
-                ss[b] = 0.f;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const float x0 = e ? bf16_hi(xw[0]) : bf16_lo(xw[0]);
-                    const float x1 = e ? bf16_hi(xw[1]) : bf16_lo(xw[1]);
-                    const float x2 = e ? bf16_hi(xw[2]) : bf16_lo(xw[2]);
-                    const float x3 = e ? bf16_hi(xw[3]) : bf16_lo(xw[3]);
-                    const float v = silu(conv4(wt[b][e], x0, x1, x2, x3, dt, cw[b][e][0],
-                                               cw[b][e][1], cw[b][e][2]));
-                    y[b][e] = v;
-                    ss[b] = fmaf(v, v, ss[b]);
-                }
+            for (int e = 0; e < 2; ++e) {
+                const float x0 = e ? bf16_hi(xw[0]) : bf16_lo(xw[0]);
+                const float x1 = e ? bf16_hi(xw[1]) : bf16_lo(xw[1]);
+                const float x2 = e ? bf16_hi(xw[2]) : bf16_lo(xw[2]);
+                const float x3 = e ? bf16_hi(xw[3]) : bf16_lo(xw[3]);
+                y[e] = silu(conv4(wt[e], x0, x1, x2, x3, dt, cw[e][0], cw[e][1], cw[e][2]));
+                ss = fmaf(y[e], y[e], ss);
             }
             // 1 / max(|y|, floor) as rsqrt(max(|y|^2, floor^2))
-            const float iq = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss[0]), kNormFloor * kNormFloor));
-            const float ik = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss[1]), kNormFloor * kNormFloor));
-            const float2 kv = make_float2(y[1][0] * ik, y[1][1] * ik);
-            const float2 qv = make_float2(y[0][0] * iq, y[0][1] * iq);
-            *reinterpret_cast<float2 *>(KQ + size_t(2 * nd) * LY::KS + 2 * lane) = kv;
-            *reinterpret_cast<float2 *>(KQ + size_t(2 * nd + 1) * LY::KS + 2 * lane) = qv;
+            const float iv = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss), kNormFloor * kNormFloor));
+            *reinterpret_cast<float2 *>(dst0 + size_t(2 * nd) * LY::KS) =
+                make_float2(y[0] * iv, y[1] * iv);
         }
     }
     __syncthreads();  // k and q rows complete; the q and k conv-input planes are consumed
 
     // ---- 3. pending fold rows start loading; pair coefficients on the matrix cores ---------
     if (L > 0) GDN_FOLD_LOAD(L - min(L, nfc), min(L, nfc));
-    // v-channel taps of this lane's state rows 32w + 16nt + lr, for the S0 epilogue
-    uint2 wvr[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-        wvr[nt] = *reinterpret_cast<const uint2 *>(CP.w + (int64_t(layer) * C + 2 * HD + h * D +
-                                                           32 * w + 16 * nt + lr) * 4);
     // M tile jt is KQ rows 16jt .. 16jt+15, i.e. k and q of nodes 8jt .. 8jt+7 interleaved; N
     // tile at holds the keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: of
     // node 8jt + 2lg + r/2, k . k_a for even r and q . k_a for odd r, with a = 16at + lr.  Rows
@@ -578,10 +559,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s[0][mt][e] *= G;
-                s[1][mt][e] *= G;
-            }
+            for (int e = 0; e < 4; ++e) s[mt][e] *= G;
         for (int hi = L; hi > 0; hi -= nfc) {
             const int lo = max(hi - nfc, 0), cnt = hi - lo;
             if (hi < L) {  // earlier chunks (more pending rows than one chunk holds)
@@ -590,57 +568,47 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                 GDN_FOLD_STORE(cnt);
                 __syncthreads();
             }
-            // S^T += K^T (c u)^T on the fp32 matrix cores: s[nt][mt] is the D tile of columns
-            // 16mt.. and rows 32w + 16nt..; the 4-row step from row k0 takes A[lr][lg] =
-            // k_{k0+lg}[16mt + lr] and B[lg][lr] = c_{k0+lg} u_{k0+lg}[32w + 16nt + lr].  Rows
-            // past the chunk read its last row with c = 0.
+            // S^T += K^T (c u)^T on the fp32 matrix cores: s[mt] is the D tile of columns
+            // 16mt.. and rows 16w..; the 4-row step from row k0 takes A[lr][lg] =
+            // k_{k0+lg}[16mt + lr] and B[lg][lr] = c_{k0+lg} u_{k0+lg}[16w + lr].  Rows past the
+            // chunk read its last row with c = 0.
             for (int k0 = 0; k0 < cnt; k0 += 4) {
                 const int f = k0 + lg, fr = min(f, cnt - 1);
                 const float cf = f < cnt ? FC[f] : 0.f;
-                const float b0 = cf * FU[fr * D + 32 * w + lr];
-                const float b1 = cf * FU[fr * D + 32 * w + 16 + lr];
+                const float b0 = cf * FU[fr * D + row0 + lr];
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt) {
                     const float a = FK[fr * D + 16 * mt + lr];
-                    floatx4 t0 = {s[0][mt][0], s[0][mt][1], s[0][mt][2], s[0][mt][3]};
-                    floatx4 t1 = {s[1][mt][0], s[1][mt][1], s[1][mt][2], s[1][mt][3]};
+                    floatx4 t0 = {s[mt][0], s[mt][1], s[mt][2], s[mt][3]};
                     t0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b0, t0, 0, 0, 0);
-                    t1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b1, t1, 0, 0, 0);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        s[0][mt][e] = t0[e];
-                        s[1][mt][e] = t1[e];
-                    }
+                    for (int e = 0; e < 4; ++e) s[mt][e] = t0[e];
                 }
             }
         }
-    }
-    if (L > 0) {
-        float *tile = committed + (32 * w + lr) * D + 4 * lg;
+        float *tile = committed + (row0 + lr) * D + 4 * lg;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-                *reinterpret_cast<float4 *>(tile + 16 * nt * D + 16 * mt) =
-                    make_float4(s[nt][mt][0], s[nt][mt][1], s[nt][mt][2], s[nt][mt][3]);
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4 *>(tile + 16 * mt) =
+                make_float4(s[mt][0], s[mt][1], s[mt][2], s[mt][3]);
     }
 
     // p_n = S0 k_n, r_n = S0 q_n on the matrix cores; then w_n and G_n r_n to LDS.
     {
         const char *XV = lds + lay.xv;
+        const int i = row0 + lr;  // this lane's state row in the epilogue
         for (int jt0 = 0; jt0 < JT; jt0 += JC) {
             // fp32 MFMA 16x16x4 per 4-column step {16mt + 4lg + e}: lane (lr, lg) gives A[lr][lg]
             // = KQ row 16jt + lr (k and q of node 8jt + lr/2; one float4 read per mt covers
             // e = 0..3, rows past the tree clamped to its last) and B[lg][lr] = its own tile
-            // element s[nt][mt][e].
+            // element s[mt][e].
             const float *arow[JC];
 #pragma unroll
             for (int jc = 0; jc < JC; ++jc)
                 arow[jc] = KQ + size_t(min(16 * (jt0 + jc) + lr, 2 * n - 1)) * LY::KS + 4 * lg;
-            floatx4 acc[JC][2];
+            floatx4 acc[JC];
 #pragma unroll
-            for (int jc = 0; jc < JC; ++jc)
-                acc[jc][0] = acc[jc][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int jc = 0; jc < JC; ++jc) acc[jc] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -650,17 +618,19 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                     const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-#pragma unroll
-                        for (int nt = 0; nt < 2; ++nt)
-                            acc[jc][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                av[e], s[nt][mt][e], acc[jc][nt], 0, 0, 0);
+                        acc[jc] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], s[mt][e], acc[jc],
+                                                                       0, 0, 0);
                 }
             }
             // W and GR of this pass's nodes take their k and q rows: every wave must be done
             // reading them.  The fold rows are dead past the first pass too.
             __syncthreads();
             // Lane (lr, lg) holds rows 4lg + r of each M tile: p (even r) and r (odd r) of node
-            // 8jt + 2lg + r/2 at state row 32w + 16nt + lr.
+            // 8jt + 2lg + r/2 at state row 16w + lr.  The v channel i: its taps and window.
+            const uint2 wvr = *reinterpret_cast<const uint2 *>(lds + lay.wv + size_t(i) * 8);
+            const float wv[4] = {bf16_lo(wvr.x), bf16_hi(wvr.x), bf16_lo(wvr.y), bf16_hi(wvr.y)};
+            const float *cv = X0s + 2 * D + i;  // v channel i, taps 0..2
+            const float cv0 = cv[0], cv1 = cv[3 * D], cv2 = cv[6 * D];
 #pragma unroll
             for (int jc = 0; jc < JC; ++jc) {
                 const int jt = jt0 + jc;
@@ -673,35 +643,29 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                     const int dt = dep[nd];
                     const int4 an = anc[nd];
                     const float beta = slot_f32<bf16_t>(Bl[nd]);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const int i = 32 * w + 16 * nt + lr;
-                        const float wv[4] = {bf16_lo(wvr[nt].x), bf16_hi(wvr[nt].x),
-                                             bf16_lo(wvr[nt].y), bf16_hi(wvr[nt].y)};
-                        const float *cv = X0s + 2 * D + i;  // v channel i, taps 0..2
-                        const float v = silu(conv4(
-                            wv, bf16_at(XV + size_t(nd) * LY::XROW, i),
-                            bf16_at(XV + size_t(an.x) * LY::XROW, i),
-                            bf16_at(XV + size_t(an.y) * LY::XROW, i),
-                            bf16_at(XV + size_t(an.z) * LY::XROW, i), dt, cv[0], cv[3 * D],
-                            cv[6 * D]));
-                        Wm[nd * WS + i] = beta * fmaf(-G, acc[jc][nt][2 * j], v);
-                        GR[nd * WS + i] = G * acc[jc][nt][2 * j + 1];
-                    }
+                    const float v = silu(conv4(
+                        wv, bf16_at(XV + size_t(nd) * LY::XROW, i),
+                        bf16_at(XV + size_t(an.x) * LY::XROW, i),
+                        bf16_at(XV + size_t(an.y) * LY::XROW, i),
+                        bf16_at(XV + size_t(an.z) * LY::XROW, i), dt, cv0, cv1, cv2));
+                    Wm[nd * WS + i] = beta * fmaf(-G, acc[jc][2 * j], v);
+                    GR[nd * WS + i] = G * acc[jc][2 * j + 1];
                 }
             }
         }
     }
     // Y = T^-1 and Z = C' Y on the records and their dense rows (over the dead fold rows), on
     // wave 0 while the other waves finish their epilogue.
-    tree_inverse(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
-                 lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ, Yd, Zd, ys);
+    tree_inverse<12>(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
+                     lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ, Yd,
+                     Zd, ys);
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
-    tree_apply_mfma(n, ys, w, lane, Yd, Zd, Wm, GR, WS, P.bank_u[role ^ 1] + row0_bank * D,
-                    P.out + node_row0 * D, int64_t(P.H) * D);
+    tree_apply_rows<1>(n, ys, w, lane, Yd, Zd, Wm, GR, WS, P.bank_u[role ^ 1] + row0_bank * D,
+                       P.out + node_row0 * D, int64_t(P.H) * D);
 }
+
 
 namespace {
 
@@ -770,11 +734,11 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(uint32_t(P.n_blocks));
     if (start == nullptr && stop == nullptr)
-        hipLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), lds, s, CP, P.img, P.rows,
+        hipLaunchKernelGGL(conv_verify_kernel, grid, dim3(kCvThreads), lds, s, CP, P.img, P.rows,
                            n_max, nrec_max, nlv_max, nf, nfc);
     else
-        hipExtLaunchKernelGGL(conv_verify_kernel, grid, dim3(256), uint32_t(lds), s, start, stop,
-                              0, CP, P.img, P.rows, n_max, nrec_max, nlv_max, nf, nfc);
+        hipExtLaunchKernelGGL(conv_verify_kernel, grid, dim3(kCvThreads), uint32_t(lds), s, start,
+                              stop, 0, CP, P.img, P.rows, n_max, nrec_max, nlv_max, nf, nfc);
     GDN_LAUNCH_CHECK("conv_verify_kernel");
     return GDN_OK;
 }

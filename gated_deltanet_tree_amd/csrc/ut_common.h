@@ -71,13 +71,9 @@ template <int YD>
 __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *recC,
                                         const float *recQ, const int *recP, const int *recM,
                                         float *yr, float *zr) {
-    const float *tb[YD];  // recC + rp_s - s
-    int am[YD];           // a_t
+    int tb[YD];  // rp_s - s, a record index: 32 bits per term rather than a pointer
 #pragma unroll
-    for (int s = 0; s < YD; ++s) {
-        tb[s] = recC + recP[q1 + min(s, d - 1)] - s;
-        am[s] = recM[q1 + min(s, d - 1)];
-    }
+    for (int s = 0; s < YD; ++s) tb[s] = recP[q1 + min(s, d - 1)] - s;
     float y[YD], z[YD];
 #pragma unroll
     for (int t = 0; t < YD; ++t) {
@@ -86,15 +82,16 @@ __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *re
         float ya = tn, za = kq * tn;
 #pragma unroll
         for (int s = 0; s < t; ++s) {
-            const float ts = tb[s][t];
+            const float ts = recC[tb[s] + t];
             ya = fmaf(y[s], ts, ya);
             za = fmaf(z[s], ts, za);
         }
         y[t] = -ya;
         z[t] = recQ[q1 + tc] - za;
         if (t < d) {
-            yr[am[t]] = y[t];
-            zr[am[t]] = z[t];
+            const int am = recM[q1 + t];  // a_t, the dense column
+            yr[am] = y[t];
+            zr[am] = z[t];
         }
     }
 }
@@ -104,21 +101,23 @@ __device__ __forceinline__ void yz_rows(int q1, int d, float kq, const float *re
 // own record), all on wave 0, as dense rows for the matrix-core u/o pass: Yd[m][k] = Y[m][k] on
 // m's ancestors, 1 on the diagonal and 0 elsewhere; Zd likewise with q_m.k_m on the diagonal.
 // Rows are ys = round4(n) floats; rows past n are left as they are (their products are never
-// stored).  Trees up to depth 16: one lane per node (yz_rows).  Deeper trees: level by level on
+// stored).  Trees up to depth MAXD: one lane per node (yz_rows).  Deeper trees: level by level on
 // the records (recY, recZ) with
 //   Y[n][a_t] = -T[n][a_t] - sum_{s<t} T[n][a_s] Y[a_s][a_t]
 //   Z[n][a_t] = (q_n.k_n) Y[n][a_t] + C'[n][a_t] + sum_{s<t} C'[n][a_s] Y[a_s][a_t]
 // (level lv's blocks of lv + 1 records are contiguous from record r_lv; every term read belongs
 // to a shallower level), then spread into the dense rows.  Needs a barrier before the results are
 // read by other waves.
+template <int MAXD = 16>
 __device__ __forceinline__ void tree_inverse(int n, int dmax, int lane, int w, const int *poff,
                                              const int *dep, const int *lvn, const int *recM,
                                              const int *recP, const int *recT,
                                              const float *recC, const float *recQ,
                                              const float *kqd, float *recY, float *recZ,
                                              float *Yd, float *Zd, int ys) {
+    static_assert(MAXD == 12 || MAXD == 16, "register form up to depth 12 or 16");
     if (w != 0) return;
-    if (dmax <= 16) {
+    if (dmax <= MAXD) {
         for (int nd = lane; nd < n; nd += 64) {
             const int q1 = poff[nd] + 1, d = dep[nd];
             const float kq = kqd[nd];
@@ -129,10 +128,10 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int lane, int w, c
                 yz_rows<4>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
             else if (dmax <= 8)
                 yz_rows<8>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
-            else if (dmax <= 12)
+            else if (MAXD == 12 || dmax <= 12)
                 yz_rows<12>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
             else
-                yz_rows<16>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
+                yz_rows<MAXD>(q1, d, kq, recC, recQ, recP, recM, yr, zr);
         }
         return;
     }
@@ -181,35 +180,37 @@ __device__ __forceinline__ void tree_inverse(int n, int dmax, int lane, int w, c
 }
 
 // u and o of every (node, state row) on the fp32 matrix cores: U = Yd W and O = GR + Zd W over
-// the wave's state rows 32w .. 32w + 31, which makes
+// the wave's state rows 16 NT w .. 16 NT w + 16 NT - 1 (NT N tiles of 16 rows), which makes
 //   u_n = w_n + sum_{t < d_n} Y[n][a_t] w_{a_t},  o_n = G_n r_n + (q_n.k_n) w_n + sum_t Z[n][a_t] w_{a_t}.
 // M tiles of 16 nodes, N tiles of 16 state rows, K steps of 4 nodes; ancestors precede their
 // descendants, so node tile mt needs the K steps below node 16mt + 16 only.  W row k (stride ws
 // floats) past the tree is read clamped to row n - 1, where Yd and Zd hold 0.  u goes to bank row
 // n (stride 128), o to out0 + n * out_stride.  Needs Yd, Zd, W and GR complete (a barrier after
 // tree_inverse and the epilogue).
-__device__ __forceinline__ void tree_apply_mfma(int n, int ys, int w, int lane, const float *Yd,
+template <int NT>
+__device__ __forceinline__ void tree_apply_rows(int n, int ys, int w, int lane, const float *Yd,
                                                 const float *Zd, const float *Wm,
                                                 const float *GR, int ws, float *bank_u0,
                                                 float *out0, int64_t out_stride) {
     const int lr = lane & 15, lg = lane >> 4;
     const int MT = (n + 15) >> 4, KT = (n + 3) >> 2;
+    const int row0 = 16 * NT * w;
     for (int mt = 0; mt < MT; ++mt) {
         const int ksn = min(4 * mt + 4, KT);
         const float *ya = Yd + (16 * mt + lr) * ys + lg, *za = Zd + (16 * mt + lr) * ys + lg;
-        floatx4 au[2], ao[2];
+        floatx4 au[NT], ao[NT];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int i = 32 * w + 16 * nt + lr;
+        for (int nt = 0; nt < NT; ++nt) {
+            const int i = row0 + 16 * nt + lr;
             au[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < 4; ++r) ao[nt][r] = GR[min(16 * mt + 4 * lg + r, n - 1) * ws + i];
         }
         for (int ks = 0; ks < ksn; ++ks) {
             const float yv = ya[4 * ks], zv = za[4 * ks];
-            const float *wr = Wm + min(4 * ks + lg, n - 1) * ws + 32 * w + lr;
+            const float *wr = Wm + min(4 * ks + lg, n - 1) * ws + row0 + lr;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 const float b = wr[16 * nt];
                 au[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(yv, b, au[nt], 0, 0, 0);
                 ao[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv, b, ao[nt], 0, 0, 0);
@@ -220,13 +221,21 @@ __device__ __forceinline__ void tree_apply_mfma(int n, int ys, int w, int lane, 
             const int nd = 16 * mt + 4 * lg + r;
             if (nd >= n) break;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int i = 32 * w + 16 * nt + lr;
+            for (int nt = 0; nt < NT; ++nt) {
+                const int i = row0 + 16 * nt + lr;
                 bank_u0[int64_t(nd) * 128 + i] = au[nt][r];
                 out0[int64_t(nd) * out_stride + i] = ao[nt][r];
             }
         }
     }
+}
+
+// Four waves of 32 state rows (wave w owns rows 32w .. 32w + 31).
+__device__ __forceinline__ void tree_apply_mfma(int n, int ys, int w, int lane, const float *Yd,
+                                                const float *Zd, const float *Wm,
+                                                const float *GR, int ws, float *bank_u0,
+                                                float *out0, int64_t out_stride) {
+    tree_apply_rows<2>(n, ys, w, lane, Yd, Zd, Wm, GR, ws, bank_u0, out0, out_stride);
 }
 
 // The matrix-core UT kernel (bf16 inputs, d = 128).

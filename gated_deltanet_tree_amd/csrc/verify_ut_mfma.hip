@@ -69,9 +69,9 @@ struct UtLayout5 {
         const size_t fold_bytes = 2 * fk;
         gr = work + size_t(n) * WS * 4;
         const size_t wg_bytes = size_t(2) * n * WS * 4;
-        // plan (direct loads): poff [n64] | lvnode [n64] | lvn [lv64] | recM [rec64]
+        // plan (direct loads): poff [n64] | lvn [lv64] | recM [rec64]
         plan = work + (wg_bytes > fold_bytes ? wg_bytes : fold_bytes);
-        tabs = plan + (2 * n64 + lv64 + rec64) * 4;
+        tabs = plan + (n64 + lv64 + rec64) * 4;
         // gam[n] | kq[n] | recE=recY | recC | recQ | recZ [nrec] (f32) | recP | recT [nrec] (int)
         total = tabs + (size_t(2) * n + size_t(6) * nrec) * 4;
     }
@@ -102,8 +102,7 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
     // Plan of this tree (from the schedule image): record q of node n is q = poff[n] for n
     // itself and poff[n] + 1 + t for its ancestor at distance t + 1; recM = that node.
     int *poff = reinterpret_cast<int *>(lds + lay.plan);
-    int *lvnode = poff + lay.n64;   // nodes ordered by depth, then index
-    int *lvn = lvnode + lay.n64;    // first entry of each depth level in lvnode
+    int *lvn = poff + lay.n64;      // first node of each depth level, in (depth, id) order
     int *recM = lvn + lay.lv64;
     float *gam = reinterpret_cast<float *>(lds + lay.tabs);
     float *kq = gam + n_max;
@@ -171,13 +170,12 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
             }
         }
         if (n > 0) {  // the tree's plan: node blocks, level lists, ancestor records
-            const int32_t *srcs[4] = {P.img + P.off_ut_node_rec + seq_off,
-                                      P.img + P.off_ut_lvnode + seq_off, P.img + P.off_ut_lvn + l0,
-                                      P.img + P.off_ut_rec_anc + r0};
-            const int counts[4] = {n, n, nlv, nrec};
-            int *dsts[4] = {poff, lvnode, lvn, recM};
+            const int32_t *srcs[3] = {P.img + P.off_ut_node_rec + seq_off,
+                                      P.img + P.off_ut_lvn + l0, P.img + P.off_ut_rec_anc + r0};
+            const int counts[3] = {n, nlv, nrec};
+            int *dsts[3] = {poff, lvn, recM};
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 3; ++a)
                 for (int base = w * 64; base < counts[a]; base += NW * 64)
                     to_lds<4>(srcs[a] + min(base + lane, counts[a] - 1), dsts[a] + base);
         }
