@@ -43,6 +43,9 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
 FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X dense fp32 on the matrix cores
+BF16_MATRIX_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 on the matrix cores
+# fp32-exact products of bf16 inputs and fp32 state run as three bf16 products (hi, mid, lo)
+SPLIT_MATRIX_PEAK_TFLOPS = BF16_MATRIX_PEAK_TFLOPS / 3
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc")
 # Committed rocprofv3 HBM counter records of each verify kernel on the batched workload, and
@@ -57,7 +60,7 @@ KERNEL_SOURCES = {
     "chain": ["verify.hip", "verify_common.h", "gdn_device.h"],
     "ut": ["verify_ut_mfma.hip", "mfma_common.h", "ut_common.h", "verify_common.h",
            "gdn_device.h"],
-    "prefill": ["prefill.hip", "mfma_common.h", "ut_common.h", "verify_common.h", "gdn_device.h"],
+    "prefill": ["prefill.hip", "mfma_common.h", "gdn_device.h"],
     "fused": ["conv_verify.hip", "mfma_common.h", "ut_common.h", "verify_common.h",
               "gdn_device.h"],
 }
@@ -189,7 +192,9 @@ def prefill_bytes(T, S, H, d):
 
 def prefill_flops(T, H, d):
     """The recurrence's work per token and head: S k and S q (2 d^2 each), the update
-    g S + u k^T (3 d^2): 7 d^2 flop, whatever the chunking."""
+    g S + u k^T (3 d^2): 7 d^2 flop, whatever the chunking.  The kernel runs the products as
+    three bf16 matrix-core products each (exact in fp32), so their roof is a third of the bf16
+    peak; the ridge of that roof against HBM is 2500/3/8 = 104 flop/byte."""
     return 7 * d * d * T * H
 
 
@@ -235,11 +240,11 @@ def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, lay
     default = (S, length, H, d) == (8, 2048, 48, 128)
     traffic = recorded_traffic("prefill") if default else None
     intensity = flops / per_call
-    ridge = FP32_MATRIX_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    if intensity > ridge:  # above the fp32 matrix-core ridge: bounded by the matrix cores
+    ridge = SPLIT_MATRIX_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if intensity > ridge:  # above the split-product ridge: bounded by the matrix cores
         achieved = flops / launch_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": FP32_MATRIX_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / FP32_MATRIX_PEAK_TFLOPS}
+        roof = {"bound": "mfma", "achieved": achieved, "peak": SPLIT_MATRIX_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / SPLIT_MATRIX_PEAK_TFLOPS}
     else:
         achieved = per_call / launch_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -248,6 +253,8 @@ def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, lay
                  "traffic": None if traffic is None else traffic / launch_s / 1e9,
                  "flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
                  "bytes_per_launch": per_call, "flops_per_launch": flops,
+                 "hbm_floor_us": per_call / (HBM_PEAK_GBPS * 1e9) * 1e6,
+                 "matrix_floor_us": flops / (SPLIT_MATRIX_PEAK_TFLOPS * 1e12) * 1e6,
                  "hbm_GBps": per_call / launch_s / 1e9, "launch_us": launch_s * 1e6})
     return {
         "workload": f"{S} sequences x {length} tokens x {H} heads x d{d}, bf16 inputs, fp32 "

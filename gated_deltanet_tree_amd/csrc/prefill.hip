@@ -6,28 +6,35 @@
 // tree without branching, so each chunk of C = 16 tokens is the tree-masked (UT) form of
 // mechanism 1 on a chain, and the state carried from chunk to chunk is the deferred commit of
 // mechanism 4 applied to the whole chunk.  With S the state at the chunk start (rows = d_v),
-// G_t the product of the chunk's gates up to and including t and E(t,s) the product of the
-// gates of tokens s+1 .. t:
-//   u_t = beta_t (v_t - G_t S k_t - sum_{s<t} E(t,s) (k_t . k_s) u_s)
-//   o_t = G_t S q_t + sum_{s<=t} E(t,s) (q_t . k_s) u_s
+// G_t the product of the chunk's gates up to and including t, E(t,s) the product of the gates
+// of tokens s+1 .. t, T[t][s] = beta_t E(t,s) (k_t . k_s) (s < t) and C'[t][s] = E(t,s)
+// (q_t . k_s) (s <= t):
+//   w_t = beta_t (v_t - G_t S k_t),   (I + T) U = W,   O = diag(G) Q S^T + C' U
 //   S  <- G_{C-1} S + sum_t E(C-1,t) u_t k_t^T.
+// Y = (I + T)^-1 depends on the chunk's inputs only: U = Y W.
 //
-// One wave per (layer, sequence, head, block of 32 state rows): the rows of S are independent,
-// so four waves share a head without talking to each other.  Per chunk:
-//   1. k, q, v, beta, g of the chunk land in LDS (direct loads); gate products G and E;
-//   2. [k; q] K^T on the matrix cores (bf16, exact products) gives T[t][s] = beta_t E (k_t.k_s)
-//      and C[t][s] = E (q_t.k_s);
-//   3. [k; q] S^T on the matrix cores, S as an exact bf16 x3 split: w_t = beta_t (v_t - G_t p_t)
-//      and G_t r_t per row;
-//   4. each lane owns one state row and solves u over the chunk in registers, then forms o;
-//   5. S^T <- G S^T + K^T (gamma u) by fp32 16x16x4 MFMAs that accumulate straight into the
-//      state registers, which hold S^T in the accumulator layout.
-// State layout (the same as the tree-masked verify): lane l holds rows 32rb + 16nt + (l % 16)
-// and columns 16mt + 4(l / 16) + e.
+// Work split: one workgroup of four waves per (layer, sequence, head, half of the state rows);
+// wave r of half h holds rows 64h + 16r .. 64h + 16r + 15 in registers and walks the chunks.
+// Per chunk, on the matrix cores and without leaving registers between steps:
+//   [k; q] S^T with S as an exact bf16 x3 split,  w and G r,  U = Y W,  O = G r + C' U,
+//   S^T <- G S^T + K^T (gamma U) with gamma U as an exact bf16 x3 split (two 32-deep products
+//   per tile: hi and mid of the 16 tokens, then lo).
+// Every product leaves its result where the next one takes its operand: the accumulator of
+// lane (l % 16, l / 16) holds rows 4(l/16) .. 4(l/16)+3 of column l % 16, which is that lane's
+// share of the next product's right operand when the summation index runs over 4(l/16) + step.
+//
+// The chunk tables are built off the state chain, in a three-stage pipeline with one barrier
+// per step: in step i, one wave forms chunk i+1's gate products, K K^T and K Q^T, hence T, T^T
+// and C'^T (stage A); another turns chunk i's T into Y by the Neumann product of the nilpotent T,
+//   (I + T)^-1 = (I - T)(I + T^2)(I + T^4)(I + T^8),
+// keeping each factor both as itself and as its transpose (the left operand of a product is its
+// transpose in that layout) (stage B); and all four waves advance the state over chunk i-1.  The
+// two table roles move to the next wave every step.  k and q rows are staged through registers two
+// steps ahead into a four-deep LDS ring; each lane loads its own v values one step ahead.
+// State layout: lane l of a wave holds rows 16r + (l % 16) and columns 16m + 4(l / 16) + e.
 #include <hip/hip_ext.h>
 
 #include "mfma_common.h"
-#include "ut_common.h"
 
 namespace gdn {
 
@@ -35,12 +42,11 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kC = 16;                    // tokens per chunk
-constexpr int kCpv = kD * 2 / 16;         // 16-byte chunks per bf16 vector
-constexpr int kCpn = 3 * kCpv + 1;        // k | q | v + one pad chunk (bank spread)
-constexpr int kNodeBytes = kCpn * 16;
-// Direct loads move 64 chunks per instruction: the input rows are padded to whole instructions.
-constexpr int kInChunks = (kC * kCpn + 63) / 64 * 64;
-constexpr int kRowPad = 36;               // row stride (floats) of the per-row tables
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHalfRows = kD / 2;         // state rows per workgroup
+constexpr int kRowBytes = 2 * kD * 2 + 16;  // k | q | pad
+constexpr int kRing = 4;                  // k/q chunks in LDS
 
 struct PrefillParams {
     const void *q, *k, *v, *beta, *gate;
@@ -50,245 +56,327 @@ struct PrefillParams {
     int64_t n_blocks;
 };
 
-// LDS of one wave.
-struct PrefillLds {
-    char in[kInChunks * 16];         // k | q | v rows of the chunk, bf16
-    uint32_t bg[2][kC];              // beta | gate slots (bf16 zero-extended)
-    float G[kC], gam[kC];            // G_t and E(C-1, t)
-    float E[kC][kC];                 // E[t][s]: product of the gates of tokens s+1 .. t
-    float Tm[kC][kC], Cm[kC][kC];    // read as whole rows by every lane (broadcast)
-    float W[kC][kRowPad], GR[kC][kRowPad], Ug[kC][kRowPad];
+// One chunk's tables for the state waves: Y^T and C'^T in the accumulator layout (lane-major,
+// four floats per lane: lane (c, g) holds Y[c][4g + e] and C'[c][4g + e]), and per token G_t,
+// gamma_t = E(nc-1, t) (0 past the chunk) and beta_t.
+struct ChunkTab {
+    floatx4 yt[64], ct[64];
+    float G[kC], gam[kC], beta[kC];
 };
+
+// Stage A's hand-over to stage B: T and T^T in the accumulator layout.  Before that, stage A
+// uses the same bytes for its gate-product tables: ecol[s][t] = E(t, s) (t >= s) and
+// erev[t][15 - s] = E(t, s) (s <= t).
+union Handover {
+    struct {
+        floatx4 t[64], tt[64];
+    } tt;
+    struct {
+        float ecol[kC][kC], erev[kC][kC];
+    } e;
+};
+
+struct PrefillLds {
+    char kq[kRing][kC * kRowBytes];  // k | q rows of a chunk, bf16
+    uint32_t kt[2][kD * kC / 2];     // K^T of a chunk, bf16 [column][token], swizzled (kt_slot)
+    ChunkTab tab[3];
+    Handover ho[2];
+    float bg[2][2 * kC];             // raw beta (0..C-1) and g (C..2C-1)
+};
+
+// Dword index in a K^T buffer of tokens 2p, 2p+1 (p < 8) of column j: the four 8-byte groups
+// of a column's 16 tokens are rotated by j / 4, so that 16 lanes reading one group each of 16
+// consecutive columns hit distinct banks.
+__device__ __forceinline__ int kt_slot(int j, int p) {
+    return j * (kC / 2) + ((((p >> 1) ^ (j >> 2)) & 3) << 1) + (p & 1);
+}
+
+// K^T of a staged chunk from its k rows: thread i transposes 16 bytes (token i / 16, columns
+// 8 (i % 16) .. +7), as 16-bit stores.
+__device__ __forceinline__ void build_kt(const char *kq, uint32_t *kt, int tid) {
+    const int t = tid >> 4, j0 = 8 * (tid & 15);
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(kq + t * kRowBytes + 2 * j0);
+    uint16_t *k16 = reinterpret_cast<uint16_t *>(kt);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        k16[2 * kt_slot(j0 + e, t >> 1) + (t & 1)] = uint16_t(x[e >> 1] >> (16 * (e & 1)));
+}
+
+// Register staging of a chunk's k and q: thread i holds 16 bytes of each (token i / 16, piece
+// i % 16); threads 128 .. 159 one beta or g.  Tokens past the chunk repeat its last token.
+struct Staged {
+    u32x4 k, q;
+    uint32_t bg;
+};
+
+__device__ __forceinline__ void stage_load(Staged &r, const PrefillParams &P, int64_t crow, int nc,
+                                           int tid) {
+    const int tk = min(tid >> 4, nc - 1);
+    const int ok = tk * P.H * kD * 2 + (tid & 15) * 16;  // from the chunk's first row
+    r.k = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(P.k) + crow * kD * 2 + ok);
+    r.q = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(P.q) + crow * kD * 2 + ok);
+    if (tid >= 128 && tid < 128 + 2 * kC) {
+        const int i = tid - 128;
+        const int t = min(i % kC, nc - 1);
+        r.bg = *(static_cast<const bf16_t *>(i < kC ? P.beta : P.gate) + crow + int64_t(t) * P.H);
+    }
+}
+
+__device__ __forceinline__ void stage_store(const Staged &r, PrefillLds &sm, int chunk, int tid) {
+    char *row = sm.kq[chunk % kRing] + (tid >> 4) * kRowBytes + (tid & 15) * 16;
+    *reinterpret_cast<u32x4 *>(row) = r.k;
+    *reinterpret_cast<u32x4 *>(row + kD * 2) = r.q;
+    if (tid >= 128 && tid < 128 + 2 * kC) sm.bg[chunk & 1][tid - 128] = __uint_as_float(r.bg << 16);
+}
+
+// P = A B for 16 x 16 fp32 matrices held in the accumulator layout (lane (c, g) holds rows
+// 4g .. 4g+3 of column c): the left operand is passed as the layout of A^T, the right one as
+// the layout of B, the summation index of step j in lane group g being 4g + j.
+__device__ __forceinline__ floatx4 mm(floatx4 at, floatx4 b, floatx4 acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(at[j], b[j], acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ floatx4 plus_identity(floatx4 x, int lr, int lg, float sign) {
+    floatx4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = (4 * lg + r == lr ? 1.f : 0.f) + sign * x[r];
+    return y;
+}
+
+// Stage A for a chunk of nc tokens (k, q rows in `kq`, raw beta and g in `bg`), by one wave:
+// gate products, K K^T and K Q^T, then T and T^T to the hand-over and C'^T, G, gamma and beta to
+// the chunk's table.
+__device__ __forceinline__ void stage_a(const char *kq, const float *bg, ChunkTab &tb, Handover &ho,
+                                        int nc, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+    {
+        // Gate products: lanes 0-15 the column E(., s) for s = lane (upwards from s), lanes
+        // 16-31 the row E(t, .) for t = lane - 16 (downwards from t, stored reversed so that
+        // both halves write step i to position i); exact products in fp32.  Each lane reads its
+        // own factor sequence through a per-lane pointer (a select between two register arrays
+        // would become a dynamic index).
+        const bool up = lane < kC;
+        const float *fp = bg + (up ? kC : 2 * kC);
+        const int step = up ? 1 : -1;
+        float x = 1.f, ev[kC];
+        ev[0] = 1.f;  // step 0 takes no factor in either direction
+#pragma unroll
+        for (int i = 1; i < kC; ++i) {
+            const float f = fp[step * i];
+            const bool take = up ? i > lr : (kC - 1 - i) < lr;
+            x = take ? x * f : x;
+            ev[i] = x;
+        }
+        if (lane < 2 * kC) {
+            float *dst = up ? &ho.e.ecol[lr][0] : &ho.e.erev[lr][0];
+#pragma unroll
+            for (int i = 0; i < kC; i += 4)
+                *reinterpret_cast<floatx4 *>(dst + i) = floatx4{ev[i], ev[i + 1], ev[i + 2], ev[i + 3]};
+        }
+    }
+    // K K^T and K Q^T (bf16, exact products): lane (c, g) receives rows 4g + r against column c
+    floatx4 kk = {0.f, 0.f, 0.f, 0.f}, kqp = {0.f, 0.f, 0.f, 0.f};
+    {
+        const char *row = kq + lr * kRowBytes;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const bf16x8 ka = row_operand(row, 32 * b + 4 * lg);
+            kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ka, kk, 0, 0, 0);
+            kqp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, row_operand(row + kD * 2, 32 * b + 4 * lg),
+                                                          kqp, 0, 0, 0);
+        }
+    }
+    wave_order();  // the gate products are in LDS
+    const floatx4 up4 = *reinterpret_cast<const floatx4 *>(&ho.e.ecol[lr][4 * lg]);  // E(4g+r, c)
+    const floatx4 dnr = *reinterpret_cast<const floatx4 *>(&ho.e.erev[lr][12 - 4 * lg]);
+    const floatx4 dn4 = {dnr[3], dnr[2], dnr[1], dnr[0]};  // E(c, 4g+r)
+    const floatx4 b4 = *reinterpret_cast<const floatx4 *>(bg + 4 * lg);
+    const float bc = bg[lr];
+    float G = 0.f, gam = 0.f;
+    if (lane < kC) {
+        G = bg[kC] * ho.e.ecol[0][lane];                               // g_0 E(t, 0)
+        gam = lane < nc ? ho.e.erev[nc - 1][kC - 1 - lane] : 0.f;      // E(nc-1, t)
+    }
+    floatx4 T, Tt, Ct;  // T, T^T and C'^T in the accumulator layout
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 4 * lg + r;
+        T[r] = lr < t ? b4[r] * up4[r] * kk[r] : 0.f;
+        Tt[r] = t < lr ? bc * dn4[r] * kk[r] : 0.f;
+        Ct[r] = t <= lr ? dn4[r] * kqp[r] : 0.f;
+    }
+    wave_order();  // every lane has read the gate products: the hand-over bytes may be reused
+    ho.tt.t[lane] = T;
+    ho.tt.tt[lane] = Tt;
+    tb.ct[lane] = Ct;
+    if (lane < kC) {
+        tb.G[lane] = G;
+        tb.gam[lane] = gam;
+        tb.beta[lane] = bg[lane];
+    }
+}
+
+// Stage B: Y^T from T and T^T, by one wave.
+__device__ __forceinline__ void stage_b(const Handover &ho, ChunkTab &tb, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+    const floatx4 T = ho.tt.t[lane], Tt = ho.tt.tt[lane];
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    const floatx4 T2 = mm(Tt, T, z), T2t = mm(T, Tt, z);
+    const floatx4 T4 = mm(T2t, T2, z), T4t = mm(T2, T2t, z);
+    // M1^T = (I + T^2)^T (I - T)^T, M2^T = (I + T^4)^T M1^T, Y^T = (I + T^8)^T M2^T
+    const floatx4 M1t = mm(plus_identity(T2, lr, lg, 1.f), plus_identity(Tt, lr, lg, -1.f), z);
+    const floatx4 T8 = mm(T4t, T4, z);
+    const floatx4 M2t = mm(plus_identity(T4, lr, lg, 1.f), M1t, z);
+    tb.yt[lane] = mm(plus_identity(T8, lr, lg, 1.f), M2t, z);
+}
+
+// Exact bf16 x3 split of four values: b1 = {hi, mid}, b2 = {lo, 0}.
+__device__ __forceinline__ void split3_pairs(const float *u, bf16x8 &b1, bf16x8 &b2) {
+    float x[8] = {u[0], u[1], u[2], u[3], 0.f, 0.f, 0.f, 0.f};
+    bf16x8 h, m, l;
+    split3(x, h, m, l);
+    const u32x4 hv = __builtin_bit_cast(u32x4, h), mv = __builtin_bit_cast(u32x4, m),
+                lv = __builtin_bit_cast(u32x4, l);
+    const u32x4 p1 = {hv[0], hv[1], mv[0], mv[1]}, p2 = {lv[0], lv[1], 0u, 0u};
+    b1 = __builtin_bit_cast(bf16x8, p1);
+    b2 = __builtin_bit_cast(bf16x8, p2);
+}
+
+// This lane's v values of a chunk (row R0 + (l % 16) of tokens 4(l / 16) + e, at element offset
+// lofs[e] from the chunk's first row); tokens past the chunk read its first token instead.
+__device__ __forceinline__ void load_v(uint16_t (&vr)[4], const PrefillParams &P, int64_t crow,
+                                       int nc, const int (&lofs)[4], int lg) {
+    const bf16_t *vb = static_cast<const bf16_t *>(P.v) + crow * kD;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vr[e] = vb[4 * lg + e < nc ? lofs[e] : lofs[e] - (4 * lg + e) * P.H * kD];
+}
 
 }  // namespace
 
-// Two waves per SIMD (at most 256 VGPRs): the state (64 floats per lane) stays live through the
-// split S0 products and the per-row solve.
-__global__ __launch_bounds__(64, 2)
+// Three waves per SIMD (at most 168 VGPRs) and under 53,760 bytes of LDS: three workgroups per CU.
+__global__ __launch_bounds__(kThreads, 3)
 void prefill_kernel(PrefillParams P) {
     constexpr int D = kD;
     __shared__ __align__(16) PrefillLds sm;
-    const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
-    // (layer, sequence, head, row block), the row block fastest: the four waves of a head
-    // read the same chunk inputs, next to each other on one XCD.
-    const uint32_t logical = xcd_logical(blockIdx.x, uint32_t(P.n_blocks));
-    const int rb = int(logical & 3);
-    const uint32_t unit = logical >> 2;
-    const uint32_t per = uint32_t(P.S) * uint32_t(P.H);
-    const int layer = P.layer_begin + int(unit / per);
-    const int seq = int((unit % per) / uint32_t(P.H)), h = int(unit % uint32_t(P.H));
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t unit = xcd_logical(blockIdx.x, uint32_t(P.n_blocks));
+    const int half = int(unit & 1u);
+    const uint32_t pair = unit >> 1, per = uint32_t(P.S) * uint32_t(P.H);
+    const int layer = P.layer_begin + int(pair / per);
+    const int seq = int((pair % per) / uint32_t(P.H)), h = int(pair % uint32_t(P.H));
     const int t_begin = P.seq_off[seq], len = P.seq_off[seq + 1] - t_begin;
-    float *state = P.state + ((int64_t(layer) * P.S + seq) * P.H + h) * D * D;
+    const int n = (len + kC - 1) / kC;  // chunks
+    if (n == 0) return;  // uniform over the workgroup: no barrier is skipped by part of it
     const int64_t row0 = (int64_t(layer) * P.T + t_begin) * P.H + h;  // token 0's (t, h) row
+    // stage A runs on wave (i + rot) % 4 in step i and stage B two waves on: the table work
+    // visits every SIMD in turn, whichever workgroups share a CU
+    const int rot = int((blockIdx.x ^ (blockIdx.x >> 3) ^ (blockIdx.x >> 8)) & 3u);
+    const int R0 = half * kHalfRows + 16 * w;  // first state row of this wave
+    auto nc_of = [&](int x) { return min(kC, len - x * kC); };
+    auto crow_of = [&](int x) { return row0 + int64_t(x) * kC * P.H; };
 
-    float s[2][8][4];  // S^T tiles: rows 32rb + 16nt + lr, columns 16mt + 4lg + e
+    float *state = P.state + ((int64_t(layer) * P.S + seq) * P.H + h) * D * D;
+    floatx4 s[8];  // S^T tiles: row R0 + lr, columns 16m + 4lg + e
     {
-        const float *tile = state + (32 * rb + lr) * D + 4 * lg;
+        const float *tile = state + (R0 + lr) * D + 4 * lg;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * nt * D + 16 * mt);
-                s[nt][mt][0] = x.x;
-                s[nt][mt][1] = x.y;
-                s[nt][mt][2] = x.z;
-                s[nt][mt][3] = x.w;
-            }
+        for (int m = 0; m < 8; ++m) s[m] = *reinterpret_cast<const floatx4 *>(tile + 16 * m);
     }
+    // per-lane element offsets of this lane's output and v values (token 4lg + r, row R0 + lr)
+    // from a chunk's first (t, h) row
+    int lofs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lofs[r] = (4 * lg + r) * P.H * D + R0 + lr;
+    Staged st;
+    stage_load(st, P, crow_of(0), nc_of(0), tid);
+    stage_store(st, sm, 0, tid);
+    uint16_t vr[4];
+    __syncthreads();
 
-    const char *kb = static_cast<const char *>(P.k), *qb = static_cast<const char *>(P.q),
-               *vb = static_cast<const char *>(P.v);
-    for (int c0 = 0; c0 < len; c0 += kC) {
-        const int nc = min(kC, len - c0);
-        // ---- 1. chunk inputs into LDS; gate products ------------------------------------
-        const int64_t crow = row0 + int64_t(c0) * P.H;
-#pragma unroll 1
-        for (int base = 0; base < kInChunks; base += 64) {
-            const int c = base + lane;
-            const int t = min(c / kCpn, nc - 1), r = c % kCpn;  // rows past nc re-read the last
-            const bool real = r < 3 * kCpv;
-            const int vec = real ? r / kCpv : 0, idx = real ? r % kCpv : 0;
-            const char *src = (vec == 0 ? kb : (vec == 1 ? qb : vb)) +
-                              (crow + int64_t(t) * P.H) * D * 2 + idx * 16;
-            to_lds<16>(src, sm.in + size_t(base) * 16);
-        }
-        if (lane < 2 * kC) {
-            const int which = lane / kC, t = min(lane % kC, nc - 1);
-            const bf16_t *src = static_cast<const bf16_t *>(which == 0 ? P.beta : P.gate) +
-                                crow + int64_t(t) * P.H;
-            to_lds<2>(src, &sm.bg[0][0]);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // the chunk is in LDS
-        wave_order();
-        if (lane < kC) {  // G_t over tokens 0..t; row s of E by a running product over t > s
-            float gv[kC];
+    // Step i: stage chunk i+2, stage A of chunk i+1, stage B of chunk i, state over chunk i-1.
+    for (int i = -1; i <= n; ++i) {
+        const int wa = (i + 4 + rot) & 3, wb = (wa + 2) & 3;
+        if (i + 2 < n) stage_load(st, P, crow_of(i + 2), nc_of(i + 2), tid);
+        if (w == wa && i + 1 < n)
+            stage_a(sm.kq[(i + 1) % kRing], sm.bg[(i + 1) & 1], sm.tab[(i + 1) % 3],
+                    sm.ho[(i + 1) & 1], nc_of(i + 1), lane);
+        if (w == wb && i >= 0 && i < n) stage_b(sm.ho[i & 1], sm.tab[i % 3], lane);
+        if (i >= 1) {
+            const int y = i - 1, nc = nc_of(y);
+            const char *kq = sm.kq[y % kRing];
+            const ChunkTab &tb = sm.tab[y % 3];
+            // ---- [k; q] S^T: lane (lr, lg) receives token 4lg + r against row R0 + lr ------
+            floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < kC; ++m) gv[m] = slot_f32<bf16_t>(sm.bg[1][m]);
-            float gp = 1.f, e = 1.f;
-#pragma unroll
-            for (int m = 0; m < kC; ++m) {
-                if (m <= lane) gp *= gv[m];
-                if (m > lane) e *= gv[m];
-                sm.E[m][lane] = m > lane ? e : (m == lane ? 1.f : 0.f);
+            for (int kb = 0; kb < 4; ++kb) {
+                bf16x8 bh, bm, bl;
+                {
+                    const float x[8] = {s[2 * kb][0],     s[2 * kb][1],     s[2 * kb][2],
+                                        s[2 * kb][3],     s[2 * kb + 1][0], s[2 * kb + 1][1],
+                                        s[2 * kb + 1][2], s[2 * kb + 1][3]};  // columns 32kb + slots
+                    split3(x, bh, bm, bl);
+                }
+                const bf16x8 a = row_operand(kq + lr * kRowBytes, 32 * kb + 4 * lg);
+                const bf16x8 b = row_operand(kq + lr * kRowBytes + D * 2, 32 * kb + 4 * lg);
+                ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, ak, 0, 0, 0);
+                aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, bl, aq, 0, 0, 0);
+                ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, ak, 0, 0, 0);
+                aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, bm, aq, 0, 0, 0);
+                ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, ak, 0, 0, 0);
+                aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, bh, aq, 0, 0, 0);
             }
-            sm.G[lane] = gp;
-        }
-        wave_order();
-        if (lane < kC) sm.gam[lane] = lane < nc ? sm.E[nc - 1][lane] : 0.f;  // E(nc-1, t)
-
-        // ---- 2. pair products [k; q] K^T: T and C -------------------------------------
-        // M tile jt stacks k (rows 0-7) and q (rows 8-15) of tokens 8jt .. 8jt+7; N = the 16
-        // keys of the chunk.  Lane (lr, lg) receives token 8jt + 4(lg & 1) + r against key lr.
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            const int xt = 8 * jt + (lr & 7);
-            const char *xrow = sm.in + size_t(xt) * kNodeBytes + (lr >> 3) * D * 2;
-            const char *krow = sm.in + size_t(lr) * kNodeBytes;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    row_operand(xrow, 32 * kk + 4 * lg), row_operand(krow, 32 * kk + 4 * lg),
-                    acc, 0, 0, 0);
+            // ---- w_t = beta_t (v_t - G_t p_t) (0 past the chunk), o_t = G_t r_t ---------------
+            const floatx4 G4 = *reinterpret_cast<const floatx4 *>(&tb.G[4 * lg]);
+            const floatx4 B4 = *reinterpret_cast<const floatx4 *>(&tb.beta[4 * lg]);
+            floatx4 wv, o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 8 * jt + 4 * (lg & 1) + r, sk = lr;
-                const float e = sm.E[t][sk];
-                const bool in_t = t < nc && sk < nc;
-                if (lg >= 2)
-                    sm.Cm[t][sk] = (in_t && sk <= t) ? e * acc[r] : 0.f;
-                else
-                    sm.Tm[t][sk] =
-                        (in_t && sk < t) ? slot_f32<bf16_t>(sm.bg[0][t]) * e * acc[r] : 0.f;
+                const int t = 4 * lg + r;
+                const float v = __uint_as_float(uint32_t(vr[r]) << 16);
+                wv[r] = t < nc ? B4[r] * fmaf(-G4[r], ak[r], v) : 0.f;
+                o[r] = G4[r] * aq[r];
+            }
+            // ---- U = Y W, then O = G r + C' U -----------------------------------------------------
+            const floatx4 u = mm(tb.yt[lane], wv, floatx4{0.f, 0.f, 0.f, 0.f});
+            o = mm(tb.ct[lane], u, o);
+            const floatx4 gm4 = *reinterpret_cast<const floatx4 *>(&tb.gam[4 * lg]);
+            float ug[4];
+            float *ob = P.out + crow_of(y) * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * lg + r;
+                if (t < nc) ob[lofs[r]] = o[r];
+                ug[r] = t < nc ? gm4[r] * u[r] : 0.f;
+            }
+            // ---- S^T <- G S^T + K^T (gamma U): two 32-deep bf16 products per tile -------------
+            bf16x8 b1, b2;
+            split3_pairs(ug, b1, b2);
+            const float Ge = tb.G[nc - 1];
+            const uint32_t *kt = sm.kt[y & 1];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                // k_t[16m + lr] for the lane's tokens 4lg .. 4lg+3, twice
+                const uint2 kv = *reinterpret_cast<const uint2 *>(kt + kt_slot(16 * m + lr, 2 * lg));
+                const u32x4 av = {kv.x, kv.y, kv.x, kv.y};
+                const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+                s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, s[m] * Ge, 0, 0, 0);
+                s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, s[m], 0, 0, 0);
             }
         }
-        wave_order();
-
-        // ---- 3. [k; q] S^T: w_t and G_t r_t for this wave's 32 rows ---------------------
-        {
-            floatx4 acc[2][2];
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) acc[jt][0] = acc[jt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 bh[2], bm[2], bl[2];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const float x[8] = {s[nt][2 * kk][0],     s[nt][2 * kk][1],
-                                        s[nt][2 * kk][2],     s[nt][2 * kk][3],
-                                        s[nt][2 * kk + 1][0], s[nt][2 * kk + 1][1],
-                                        s[nt][2 * kk + 1][2], s[nt][2 * kk + 1][3]};
-                    split3(x, bh[nt], bm[nt], bl[nt]);
-                }
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt) {
-                    const int xt = 8 * jt + (lr & 7);
-                    const bf16x8 a = row_operand(sm.in + size_t(xt) * kNodeBytes + (lr >> 3) * D * 2,
-                                                 32 * kk + 4 * lg);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        acc[jt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[nt], acc[jt][nt], 0, 0, 0);
-                        acc[jt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[nt], acc[jt][nt], 0, 0, 0);
-                        acc[jt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[nt], acc[jt][nt], 0, 0, 0);
-                    }
-                }
-            }
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 8 * jt + 4 * (lg & 1) + r;
-                    const float G = sm.G[t];
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const int il = 16 * nt + lr;  // row inside the wave's block
-                        if (lg < 2) {
-                            const float v = bf16_at(sm.in + size_t(t) * kNodeBytes + 2 * D * 2,
-                                                    32 * rb + il);
-                            sm.W[t][il] = slot_f32<bf16_t>(sm.bg[0][t]) * fmaf(-G, acc[jt][nt][r], v);
-                        } else {
-                            sm.GR[t][il] = G * acc[jt][nt][r];
-                        }
-                    }
-                }
+        if (i >= 0 && i < n) {  // chunk i's v values and K^T, for step i + 1
+            load_v(vr, P, crow_of(i), nc_of(i), lofs, lg);
+            build_kt(sm.kq[i % kRing], sm.kt[i & 1], tid);
         }
-        wave_order();
-
-        // ---- 4. per row: u by forward substitution in registers, then o -----------------
-        if (lane < 32) {
-            const int il = lane;
-            float u[kC];
-            float *orow = P.out + (crow * D) + 32 * rb + il;
-#pragma unroll
-            for (int t = 0; t < kC; ++t) {
-                float tr[kC], cr[kC];
-#pragma unroll
-                for (int q4 = 0; q4 < kC / 4; ++q4) {
-                    const float4 a = *reinterpret_cast<const float4 *>(&sm.Tm[t][4 * q4]);
-                    const float4 b = *reinterpret_cast<const float4 *>(&sm.Cm[t][4 * q4]);
-                    tr[4 * q4] = a.x, tr[4 * q4 + 1] = a.y, tr[4 * q4 + 2] = a.z, tr[4 * q4 + 3] = a.w;
-                    cr[4 * q4] = b.x, cr[4 * q4 + 1] = b.y, cr[4 * q4 + 2] = b.z, cr[4 * q4 + 3] = b.w;
-                }
-                float x = sm.W[t][il];
-#pragma unroll
-                for (int sk = 0; sk < t; ++sk) x = fmaf(-tr[sk], u[sk], x);
-                u[t] = t < nc ? x : 0.f;
-                float o = sm.GR[t][il];
-#pragma unroll
-                for (int sk = 0; sk <= t; ++sk) o = fmaf(cr[sk], u[sk], o);
-                if (t < nc) orow[int64_t(t) * P.H * D] = o;
-                sm.Ug[t][il] = sm.gam[t] * u[t];
-                __builtin_amdgcn_sched_barrier(0);  // keep the rows' loads from piling up
-            }
-        }
-        wave_order();
-
-        // ---- 5. S^T <- G S^T + K^T (gamma u) ------------------------------------------------
-        // 16 independent accumulator tiles per k-step, so the matrix-core ops pipeline.
-        {
-            const float Ge = sm.G[nc - 1];
-            floatx4 a4[2][8];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-                    a4[nt][mt] = floatx4{Ge * s[nt][mt][0], Ge * s[nt][mt][1], Ge * s[nt][mt][2],
-                                         Ge * s[nt][mt][3]};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int t = 4 * ks + lg;  // k index of this lane
-                float kv[8], uv[2];
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-                    kv[mt] = bf16_at(sm.in + size_t(t) * kNodeBytes, 16 * mt + lr);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) uv[nt] = sm.Ug[t][16 * nt + lr];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int mt = 0; mt < 8; ++mt)
-                        a4[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[mt], uv[nt],
-                                                                          a4[nt][mt], 0, 0, 0);
-            }
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) s[nt][mt][e] = a4[nt][mt][e];
-        }
-        wave_order();  // the next chunk's loads overwrite the inputs read above
+        if (i + 2 < n) stage_store(st, sm, i + 2, tid);
+        __syncthreads();
     }
 
-    if (len > 0) {
-        float *tile = state + (32 * rb + lr) * D + 4 * lg;
+    float *tile = state + (R0 + lr) * D + 4 * lg;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-                *reinterpret_cast<float4 *>(tile + 16 * nt * D + 16 * mt) =
-                    make_float4(s[nt][mt][0], s[nt][mt][1], s[nt][mt][2], s[nt][mt][3]);
-    }
+    for (int m = 0; m < 8; ++m) *reinterpret_cast<floatx4 *>(tile + 16 * m) = s[m];
 }
 
 }  // namespace gdn
@@ -331,14 +419,14 @@ static gdn_status run_prefill(const gdn_prefill_args *a, const int32_t *host_seq
     P.H = a->n_heads;
     P.T = a->n_tokens;
     P.layer_begin = a->layer_begin;
-    P.n_blocks = int64_t(a->n_layers) * a->n_seqs * a->n_heads * 4;
+    P.n_blocks = int64_t(a->n_layers) * a->n_seqs * a->n_heads * 2;  // two halves of the rows
     if (P.n_blocks > kMaxBlocks) return fail(GDN_EINVAL, "gdn_prefill: too many workgroups");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (start == nullptr && stop == nullptr)
-        hipLaunchKernelGGL(prefill_kernel, dim3(uint32_t(P.n_blocks)), dim3(64), 0, s, P);
+        hipLaunchKernelGGL(prefill_kernel, dim3(uint32_t(P.n_blocks)), dim3(kThreads), 0, s, P);
     else
-        hipExtLaunchKernelGGL(prefill_kernel, dim3(uint32_t(P.n_blocks)), dim3(64), 0, s, start,
-                              stop, 0, P);
+        hipExtLaunchKernelGGL(prefill_kernel, dim3(uint32_t(P.n_blocks)), dim3(kThreads), 0, s,
+                              start, stop, 0, P);
     GDN_LAUNCH_CHECK("prefill_kernel");
     return GDN_OK;
 }

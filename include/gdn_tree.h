@@ -270,8 +270,9 @@ gdn_status gdn_tree_verify_ut_timed(const gdn_verify_args *args, const int32_t *
  *                                     out[t] = S q_t,
  * starting from the committed state; the final S is written back to `state`.  Pending
  * factors are not read: call gdn_flush first when a tree verify left any.
- * Work: one 64-thread workgroup per (layer, sequence, head, block of 32 state rows) walks the
- * sequence in chunks of 16 tokens on the matrix cores (tree-masked form of a chain).
+ * Work: one 256-thread workgroup per (layer, sequence, head, half of the state rows) walks the
+ * sequence in chunks of 16 tokens on the matrix cores (tree-masked form of a chain); the chunk
+ * tables are built one and two chunks ahead of the state by waves taking turns.
  * ---------------------------------------------------------------------------------- */
 typedef struct {
     int32_t n_seqs;      /* S                                                               */
