@@ -2,7 +2,7 @@
 
 Ragged batches cover an empty sequence, single tokens, chunk boundaries (16, 32), ragged tails
 and a few hundred tokens; a full-width case runs 48 heads over 1024-token sequences and checks
-sampled heads.  Bars: per-token output vectors max-relative 1e-3, final states relative
+sampled heads; zero and 1e-30 gates sit at chunk starts, ends and inside chunks.  Bars: per-token output vectors max-relative 1e-3, final states relative
 Frobenius 1e-5 (the same bars as the tree verify).
 """
 import numpy as np
@@ -23,7 +23,7 @@ def torch_cuda():
     return torch
 
 
-def _run(torch, lengths, H, seed, n_layers=1, check_heads=None, layer_begin=0):
+def _run(torch, lengths, H, seed, n_layers=1, check_heads=None, layer_begin=0, gate_edit=None):
     d = 128
     offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     S, T = len(lengths), int(offs[-1])
@@ -36,6 +36,9 @@ def _run(torch, lengths, H, seed, n_layers=1, check_heads=None, layer_begin=0):
             host[key].append(np.concatenate([p[key][:n] for p, n in zip(per, lengths)])
                              if T else np.zeros((0,) + per[0][key].shape[1:], per[0][key].dtype))
     host = {k: np.stack(v) for k, v in host.items()}
+    if gate_edit is not None:  # [(layer, token, head, value)] written as bf16 gates
+        for layer, t, h, value in gate_edit(offs):
+            host["gate"][layer, t, h] = synth.f32_to_bf16(np.array([value], np.float32))[0]
     S0 = np.stack([np.stack([synth.initial_state(90 + seed, layer, b, H, d) for b in range(S)])
                    for layer in range(Ly)]).astype(np.float32)
     dev = {k: workload._to_torch(v, "bf16", "cuda") for k, v in host.items()}
@@ -80,6 +83,27 @@ def test_two_layers_in_one_call(torch_cuda):
 def test_full_width_long_sequences_sampled_heads(torch_cuda):
     """48 heads x 4 sequences of 1024 tokens (one layer), heads 0, 17 and 47 checked."""
     _run(torch_cuda, [1024, 1000, 1024, 513], H=48, seed=3, check_heads=[0, 17, 47])
+
+
+def test_zero_and_tiny_gates(torch_cuda):
+    """Gates of 0 and 1e-30 (a bf16 gate can underflow to zero) at the first token, inside a
+    chunk, at a chunk's first and last token, in a run, at the last token; a sequence whose
+    gates are all 0 (head 0) or all 1 (head 1).  The chunk's gate products are exact products,
+    so a zero gate erases the state before its token exactly as the oracle's recurrence does."""
+    lengths = [40, 33, 16, 1]
+
+    def edit(offs):
+        s0, s1, s2, s3 = (int(o) for o in offs[:4])
+        ed = [(0, s0 + 0, 0, 0.0), (0, s0 + 5, 0, 1e-30), (0, s0 + 5, 1, 1e-30),
+              (0, s0 + 16, 1, 0.0), (0, s0 + 31, 0, 1e-30), (0, s0 + 39, 1, 0.0)]
+        ed += [(0, s0 + t, 0, 0.0) for t in (17, 18, 19)]
+        ed += [(0, s1 + 15, 0, 1e-30), (0, s1 + 15, 1, 0.0), (0, s1 + 32, 0, 0.0)]
+        ed += [(0, s2 + t, 0, 0.0) for t in range(16)] + [(0, s2 + t, 1, 1.0) for t in range(16)]
+        ed += [(0, s3, 0, 0.0), (0, s3, 1, 1e-30)]
+        return ed
+
+    o, S = _run(torch_cuda, lengths, H=2, seed=6, gate_edit=edit)
+    assert np.isfinite(o[0, :sum(lengths)]).all() and np.isfinite(S).all()
 
 
 def test_run_to_run_deterministic(torch_cuda):
