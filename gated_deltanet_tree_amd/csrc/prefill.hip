@@ -85,8 +85,8 @@ struct PrefillLds {
 };
 
 // Dword index in a K^T buffer of tokens 2p, 2p+1 (p < 8) of column j: the four 8-byte groups
-// of a column's 16 tokens are rotated by j / 4, so that 16 lanes reading one group each of 16
-// consecutive columns hit distinct banks.
+// of a column's 16 tokens are permuted by XOR with (j / 4) mod 4, so that 16 lanes reading one
+// group each of 16 consecutive columns hit distinct banks.
 __device__ __forceinline__ int kt_slot(int j, int p) {
     return j * (kC / 2) + ((((p >> 1) ^ (j >> 2)) & 3) << 1) + (p & 1);
 }
