@@ -65,14 +65,20 @@ def _tiny_setup(torch_cuda, trees, H=1, d=16, C=16, dtype="f32", cfg_id=0, mode=
 
 
 def _run_steps(torch_cuda, b, S0, X0, W64, Wd, steps_paths, dtype, cfg_id, H, d, C,
-               commit_modes=None):
+               commit_modes=None, x_offset=0):
     """Several verify+commit steps then a flush, each checked against the oracle carrying the
-    exact committed state (replay of the accepted paths)."""
+    exact committed state (replay of the accepted paths).  x_offset > 0 hands the conv its
+    inputs that many elements past an aligned address."""
     committed, window = [s.copy() for s in S0], [x.copy() for x in X0]
     for step, paths in enumerate(steps_paths):
         h = gh.tiny_inputs(b.trees, step, H, d, C, dtype, cfg_id)
         h64 = gh.widen_inputs(h, dtype)
         inp = gh.to_device(h, dtype)
+        if x_offset:
+            buf = torch_cuda.empty(inp.x.numel() + x_offset, dtype=inp.x.dtype, device="cuda")
+            moved = buf[x_offset:].view(inp.x.shape)
+            moved.copy_(inp.x)
+            inp.x = moved
         role_before = b.layers.role_host.copy()
         b.step(inp, Wd)
         torch_cuda.cuda.synchronize()
@@ -161,6 +167,32 @@ def test_odd_channel_count_conv(torch_cuda, dtype):
     paths0 = [synth.deepest_leaf_path(t) for t in trees]
     _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, [[0, 2, 5], [0, 1, 2]]], dtype, 91, 1,
                16, 15)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_trees_cross_table_blocks(torch_cuda, dtype):
+    """Trees past 64 nodes (a 150-node chain, a 130-node top-3 tree): the conv tables a tree's
+    nodes 64 at a time, so the first nodes of a block find ancestors in the previous block
+    through the schedule image; the whole chain is accepted at step 0 (a 150-row fold at step
+    1).  Two steps and a flush, conv outputs, banks and windows against the oracle."""
+    rng = np.random.default_rng(11)
+    trees = [np.array([-1] + list(range(149)), np.int32), synth.make_tree(rng, 130, 3, 40)]
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, C=16, dtype=dtype, cfg_id=93)
+    paths0 = [synth.deepest_leaf_path(t) for t in trees]
+    paths1 = [synth.random_path(rng, t, 5) for t in trees]
+    _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, paths1], dtype, 93, 1, 16, 16)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_unaligned_input_rows(torch_cuda, dtype):
+    """x handed over one element past an aligned address: the conv's two-channel loads need 4-
+    (bf16) or 8-byte (fp32) alignment, so it takes one channel per thread; the tiny tree and
+    chain over two steps and a flush against the oracle."""
+    trees = [synth.TINY_TREE, synth.TINY_CHAIN]
+    b, S0, X0, W64, Wd = _tiny_setup(torch_cuda, trees, C=16, dtype=dtype, cfg_id=94)
+    paths0 = [synth.deepest_leaf_path(t) for t in trees]
+    _run_steps(torch_cuda, b, S0, X0, W64, Wd, [paths0, [[0, 2, 5], [0, 1, 2]]], dtype, 94, 1,
+               16, 16, x_offset=1)
 
 
 def _all_trees(N):
