@@ -22,7 +22,7 @@
 // matrix products:
 //   u_n = sum_{a in A(n)} Y[n][a] w_a,   o_n = G_n S0 q_n + sum_{a in A(n)} Z[n][a] w_a.
 //
-// One workgroup of 4 waves per (layer, sequence, head):
+// One workgroup of 8 waves per (layer, sequence, head):
 //   0. direct loads of the head's q, k and v conv-input rows of every node, beta, g, parents,
 //      depths and the tree's plan; the committed conv windows and the q/k conv weights to
 //      registers;
@@ -37,8 +37,8 @@
 //      written back once; [k; q] S0^T on the matrix cores; the epilogue evaluates the v channels
 //      (conv and SiLU) and writes w_n and G_n S0 q_n; wave 0 forms Y and Z as dense rows;
 //   5. U = Y W and O = G r + Z W on the matrix cores; u banked, o stored.
-// Matrix-core layout: wave w owns state rows [32w, 32w+32), lane l holds rows 32w + 16nt + (l % 16)
-// and columns 16mt + 4(l/16) + e.  q and k are fp32 here, so the products run on the fp32 matrix
+// Matrix-core layout: wave w owns state rows [16w, 16w+16), lane l holds row 16w + (l % 16) and
+// columns 16mt + 4(l/16) + e.  q and k are fp32 here, so the products run on the fp32 matrix
 // cores (v_mfma_f32_16x16x4f32): for the 4-column step {16mt + 4(l/16) + e}, lane l already holds
 // the state element it contributes as B, and one float4 LDS read per mt gives its A elements for
 // the four steps e = 0..3.  Accumulation is fp32, as in a vector dot product.

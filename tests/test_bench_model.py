@@ -77,3 +77,18 @@ def test_prefill_models():
 def test_refuses_more_than_one_gpu(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one MI355X" in capsys.readouterr().err
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    """A counter record is tied to the kernel's code: editing a comment keeps it, editing code
+    drops it."""
+    import shutil
+    for name in bench.KERNEL_SOURCES["prefill"]:
+        shutil.copy(f"{bench.CSRC}/{name}", tmp_path / name)
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    h0 = bench.kernel_source_sha256("prefill")
+    src = (tmp_path / "prefill.hip").read_text()
+    (tmp_path / "prefill.hip").write_text(src.replace("// tokens per chunk", "// chunk length"))
+    assert src.count("// tokens per chunk") == 1 and bench.kernel_source_sha256("prefill") == h0
+    (tmp_path / "prefill.hip").write_text(src.replace("kC = 16;", "kC = 32;"))
+    assert bench.kernel_source_sha256("prefill") != h0
