@@ -335,13 +335,14 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                     to_lds<4>(srcs[a] + min(base + lane, counts[a] - 1), dsts[a] + base);
         }
     }
-    // committed conv window (thread cc < 3 d owns channel cc of the head's 3 x 128) with its
+    // committed conv window (thread 128 + cc owns channel cc of the head's 3 x 128) with its
     // last pending inputs; the conv weights of the block this wave's prologue evaluates (waves
     // of even index the q block, odd the k block), two channels per lane
-    const bool has_ch = tid < 3 * D;
+    const int chan = tid - (THREADS - 3 * D);  // waves 2-7 own the channels, waves 0-1 the tables
+    const bool has_ch = chan >= 0;
     float win[3], pend[3];
     {
-        const int ccl = has_ch ? tid : 0;  // threads past the channels re-read channel 0
+        const int ccl = has_ch ? chan : 0;  // threads without a channel re-read channel 0
         const int64_t ch = int64_t(ccl >> 7) * HD + h * D + (ccl & (D - 1));
         const float *cs = CP.cstate + (ls * C + ch) * 3;
         const bf16_t *pb = CP.bank_x[role] + ls * P.max_nodes * C + ch;
@@ -391,7 +392,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     }
     // conv window: only the last three pending inputs survive
     if (has_ch) {
-        const int cc = tid;
+        const int cc = chan;
         float w0 = win[0], w1 = win[1], w2 = win[2];
         if (L >= 3) {
             w0 = pend[0]; w1 = pend[1]; w2 = pend[2];
