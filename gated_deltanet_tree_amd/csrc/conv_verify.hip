@@ -29,10 +29,11 @@
 //   1. the state tile loads are issued (they land behind phases 1-3); each of the head's
 //      3 x 128 channels folds its conv window, keeps it in LDS and writes it back; per record:
 //      ancestor offsets, distances and gate products;
-//   2. prologue: per node, conv of the q and k channels along the parent chain, SiLU, unit
-//      length; fp32 rows to LDS; raw conv inputs and keys banked;
-//   3. the pending fold rows start loading into the consumed q and k conv-input planes; pair
-//      products [k; q] K^T on the matrix cores;
+//   2. the first chunk of pending fold rows is requested into registers; prologue: per node,
+//      conv of the q and k channels along the parent chain, SiLU, unit length; fp32 rows to LDS;
+//      raw conv inputs and keys banked;
+//   3. pair products [k; q] K^T on the matrix cores; the fold rows go to LDS over the consumed
+//      q and k conv-input planes;
 //   4. the pending rows are folded into the tile on the matrix cores and the committed state is
 //      written back once; [k; q] S0^T on the matrix cores; the epilogue evaluates the v channels
 //      (conv and SiLU) and writes w_n and G_n S0 q_n; wave 0 forms Y and Z as dense rows;
@@ -444,6 +445,8 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
         P.bank_lg[role ^ 1][row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
     }
     __syncthreads();  // windows, records and ancestors in LDS
+    // the first fold chunk's rows: waited for after the pair products
+    if (L > 0) GDN_FOLD_LOAD(L - min(L, nfc), min(L, nfc));
 
     // ---- 2. prologue: q and k from the conv ----------------------------------------------
     // Wave w evaluates block qk_blk (q or k) of nodes w/2, w/2 + NW/2, ...; a lane owns two
@@ -490,7 +493,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     __syncthreads();  // k and q rows complete; the q and k conv-input planes are consumed
 
     // ---- 3. pending fold rows start loading; pair coefficients on the matrix cores ---------
-    if (L > 0) GDN_FOLD_LOAD(L - min(L, nfc), min(L, nfc));
     // M tile jt is KQ rows 16jt .. 16jt+15, i.e. k and q of nodes 8jt .. 8jt+7 interleaved; N
     // tile at holds the keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: of
     // node 8jt + 2lg + r/2, k . k_a for even r and q . k_a for odd r, with a = 16at + lr.  Rows
