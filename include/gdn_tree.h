@@ -357,8 +357,8 @@ gdn_status gdn_tree_conv(const gdn_conv_args *args, const int32_t *host_image,
  * n_layers equal va's; ca->role, ca->pending_len and ca->pending_rows are va's arrays; x,
  * weight and bank_x 16-byte aligned; the schedule carries the tree-masked plan and the trees fit one
  * workgroup's LDS (160 KiB: a 64-node top-8 tree of depth 16 takes about 144 KiB).
- * Work: one workgroup per (layer, sequence, head), 4 waves; the conv, SiLU and normalisation
- * run in its prologue, the rest as gdn_tree_verify_ut on the matrix cores.
+ * Work: one workgroup per (layer, sequence, head), 8 waves of 16 state rows; the conv, SiLU and
+ * normalisation run in its prologue, the rest as gdn_tree_verify_ut on the matrix cores.
  * ---------------------------------------------------------------------------------- */
 gdn_status gdn_tree_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
                                 const int32_t *host_image, const int32_t *dev_image,
