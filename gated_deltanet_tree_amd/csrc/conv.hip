@@ -34,7 +34,9 @@ struct ConvParams {
     int32_t fold_only;
 };
 
-constexpr int kConvThreads = 256;
+// Three waves: a layer of 32 sequences x 18 432 channels (pairs per thread) is 1 536 workgroups,
+// six per CU; four waves made 1 152, so half the CUs carried one workgroup more than the rest.
+constexpr int kConvThreads = 192;
 constexpr int kTapBlock = 64;  // nodes tabled per pass of the workgroup
 constexpr int kConvSub = 8;    // nodes whose loads are issued together
 
