@@ -206,9 +206,14 @@ __device__ __forceinline__ float conv4(const float wt[4], float x0, float x1, fl
 
 }  // namespace
 
-// 6 waves per SIMD: three workgroups of 8 waves per CU (the LDS allows three), which needs at
-// most 80 VGPRs per lane.
-__global__ __launch_bounds__(kCvThreads, 6)
+// DEEP = false, trees of depth <= 12: 6 waves per SIMD, three workgroups of 8 waves per CU (the
+// LDS allows three for trees like the batched workload's), which needs at most 80 VGPRs per
+// lane; the per-lane inverse runs up to depth 12.  DEEP = true, a tree deeper than 12 in the
+// batch: 4 waves per SIMD (128 VGPRs), room for the per-lane inverse up to depth 16.  Trees that
+// deep mostly need more LDS than three workgroups per CU leave, so occupancy is not what they
+// give up; past depth 16 both forms solve level by level.
+template <bool DEEP>
+__global__ __launch_bounds__(kCvThreads, DEEP ? 4 : 6)
 void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
                         const int32_t *__restrict__ rows, int n_max, int nrec_max, int nlv_max,
                         int nf, int nfc) {
@@ -659,7 +664,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     }
     // Y = T^-1 and Z = C' Y on the records and their dense rows (over the dead fold rows), on
     // wave 0 while the other waves finish their epilogue.
-    tree_inverse<12>(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
+    tree_inverse<DEEP ? 16 : 12>(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
                      lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ, Yd,
                      Zd, ys);
     __syncthreads();
@@ -736,12 +741,24 @@ gdn_status run_conv_verify(const gdn_verify_args *va, const gdn_conv_args *ca,
     CP.C = ca->channels;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(uint32_t(P.n_blocks));
-    if (start == nullptr && stop == nullptr)
-        hipLaunchKernelGGL(conv_verify_kernel, grid, dim3(kCvThreads), lds, s, CP, P.img, P.rows,
-                           n_max, nrec_max, nlv_max, nf, nfc);
-    else
-        hipExtLaunchKernelGGL(conv_verify_kernel, grid, dim3(kCvThreads), uint32_t(lds), s, start,
-                              stop, 0, CP, P.img, P.rows, n_max, nrec_max, nlv_max, nf, nfc);
+    // the deepest tree of the batch: its depth levels are nlv_max - 2
+    if (nlv_max - 2 > 12) {
+        if (start == nullptr && stop == nullptr)
+            hipLaunchKernelGGL(conv_verify_kernel<true>, grid, dim3(kCvThreads), lds, s, CP, P.img,
+                               P.rows, n_max, nrec_max, nlv_max, nf, nfc);
+        else
+            hipExtLaunchKernelGGL(conv_verify_kernel<true>, grid, dim3(kCvThreads), uint32_t(lds),
+                                  s, start, stop, 0, CP, P.img, P.rows, n_max, nrec_max, nlv_max,
+                                  nf, nfc);
+    } else {
+        if (start == nullptr && stop == nullptr)
+            hipLaunchKernelGGL(conv_verify_kernel<false>, grid, dim3(kCvThreads), lds, s, CP,
+                               P.img, P.rows, n_max, nrec_max, nlv_max, nf, nfc);
+        else
+            hipExtLaunchKernelGGL(conv_verify_kernel<false>, grid, dim3(kCvThreads),
+                                  uint32_t(lds), s, start, stop, 0, CP, P.img, P.rows, n_max,
+                                  nrec_max, nlv_max, nf, nfc);
+    }
     GDN_LAUNCH_CHECK("conv_verify_kernel");
     return GDN_OK;
 }
