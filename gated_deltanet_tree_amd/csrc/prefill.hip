@@ -91,15 +91,22 @@ __device__ __forceinline__ int kt_slot(int j, int p) {
     return j * (kC / 2) + ((((p >> 1) ^ (j >> 2)) & 3) << 1) + (p & 1);
 }
 
-// K^T of a staged chunk from its k rows: thread i transposes 16 bytes (token i / 16, columns
-// 8 (i % 16) .. +7), as 16-bit stores.
+// K^T of a staged chunk from its k rows: thread i takes column i % 128 and tokens 8 (i / 128)
+// .. +7, reads them as 2-byte loads (a wave reads 128 consecutive bytes of each row), packs the
+// token pairs into dwords and writes two 8-byte groups.  (One thread per 16 bytes of a row with
+// 16-bit stores sent the 16 lanes of a token to three or four banks: ~22% of the CU cycles were
+// LDS bank conflicts.)
 __device__ __forceinline__ void build_kt(const char *kq, uint32_t *kt, int tid) {
-    const int t = tid >> 4, j0 = 8 * (tid & 15);
-    const u32x4 x = *reinterpret_cast<const u32x4 *>(kq + t * kRowBytes + 2 * j0);
-    uint16_t *k16 = reinterpret_cast<uint16_t *>(kt);
+    const int j = tid & (kD - 1), h = tid >> 7;  // column, half of the chunk's tokens
+    const uint16_t *col = reinterpret_cast<const uint16_t *>(kq + 8 * h * kRowBytes) + j;
+    uint32_t v[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        k16[2 * kt_slot(j0 + e, t >> 1) + (t & 1)] = uint16_t(x[e >> 1] >> (16 * (e & 1)));
+    for (int p = 0; p < 4; ++p)
+        v[p] = uint32_t(col[(2 * p) * (kRowBytes / 2)]) |
+               (uint32_t(col[(2 * p + 1) * (kRowBytes / 2)]) << 16);
+    // tokens 8h + 2p, +1 sit in dword kt_slot(j, 4h + p); p = 0, 1 and p = 2, 3 are 8-byte groups
+    *reinterpret_cast<uint2 *>(kt + kt_slot(j, 4 * h)) = make_uint2(v[0], v[1]);
+    *reinterpret_cast<uint2 *>(kt + kt_slot(j, 4 * h + 2)) = make_uint2(v[2], v[3]);
 }
 
 // Register staging of a chunk's k and q: thread i holds 16 bytes of each (token i / 16, piece
