@@ -5,7 +5,8 @@ inputs, the folded conv window and the committed state, over several verify + co
 a flush.  Cases: ragged small trees (a 7-node tree, an 8-node chain, single nodes), a 16-node
 chain whose pending path outgrows one LDS fold chunk, a 40-node tree (two passes of S0
 products), a 48-node top-8 tree of depth 16, a 64-node top-8 tree next to a 16-node chain
-(the wide/deep workload's shapes), a 24-node chain (the level-by-level inverse), and the batched
+(the wide/deep workload's shapes), a 24-node chain (the level-by-level inverse), trees of depth
+12 and 13 (the boundary between the kernel's two builds), and the batched
 workload (32 sequences x 22-node trees x 48 heads) on sampled sequences.
 
 Tolerances: o per (node, head) vector <= 1e-3 normwise max relative error; committed state <= 1e-5
@@ -233,6 +234,19 @@ def test_deep_chain_level_inverse(torch_cuda):
     steps = [[list(range(20)), synth.deepest_leaf_path(tree)],
              [list(range(24)), [0]]]
     _steps(torch_cuda, [chain, tree], H=1, n_layers=1, steps_paths=steps, cfg_id=16)
+
+
+@pytest.mark.parametrize("depth", [12, 13])
+def test_inverse_build_boundary(torch_cuda, depth):
+    """The deepest tree of the batch picks the kernel's build: depth 12 runs the 80-VGPR build
+    (per-lane inverse up to depth 12), depth 13 the 128-VGPR one (per-lane inverse up to 16).
+    A chain of that depth with one branch off its middle, next to the tiny tree."""
+    tree = np.array(list(range(-1, depth)) + [depth // 2], dtype=np.int32)
+    assert synth.node_depths(tree).max() == depth
+    steps = [[list(range(depth + 1)), [0, 1, 3]],
+             [list(range(depth // 2 + 1)) + [depth + 1], [0, 2]]]
+    _steps(torch_cuda, [tree, synth.TINY_TREE], H=1, n_layers=1, steps_paths=steps,
+           cfg_id=30 + depth)
 
 
 def test_48_node_tree(torch_cuda):
