@@ -497,7 +497,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     }
     __syncthreads();  // k and q rows complete; the q and k conv-input planes are consumed
 
-    // ---- 3. pending fold rows start loading; pair coefficients on the matrix cores ---------
+    // ---- 3. pair coefficients on the matrix cores; the first fold chunk goes to LDS --------
     // M tile jt is KQ rows 16jt .. 16jt+15, i.e. k and q of nodes 8jt .. 8jt+7 interleaved; N
     // tile at holds the keys of nodes 16at .. 16at+15.  Lane (lr, lg) receives rows 4lg + r: of
     // node 8jt + 2lg + r/2, k . k_a for even r and q . k_a for odd r, with a = 16at + lr.  Rows
@@ -664,9 +664,9 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     }
     // Y = T^-1 and Z = C' Y on the records and their dense rows (over the dead fold rows), on
     // wave 0 while the other waves finish their epilogue.
-    tree_inverse<DEEP ? 16 : 12>(n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0,
-                     lane, w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ, Yd,
-                     Zd, ys);
+    tree_inverse<DEEP ? 16 : 12>(
+        n, n > 0 ? plan[P.off_ut_lv_base + seq + 1] - plan[P.off_ut_lv_base + seq] - 2 : 0, lane,
+        w, poff, dep, lvn, recM, recP, recT, recC, recQ, kqd, recY, recZ, Yd, Zd, ys);
     __syncthreads();
 
     // ---- 5. u_n = sum_a Y[n][a] w_a, o_n = G_n r_n + sum_a Z[n][a] w_a, every (node, row) ---
