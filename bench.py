@@ -270,8 +270,9 @@ def prefill_bench(torch, binding, synth, dev, S=8, length=2048, H=48, d=128, lay
 # ----------------------------------------------------------------------------------------
 
 def kernel_source_sha256(verify):
-    """Hash of the kernel's sources with comments and whitespace removed: a counter record stays
-    valid across comment edits and is dropped as soon as any code changes."""
+    """Hash of the kernel's sources with comments and layout removed (whitespace kept only
+    between two word characters): a counter record stays valid across comment edits and
+    reformatting and is dropped as soon as any code token changes."""
     import hashlib
     import re
     h = hashlib.sha256()
@@ -279,7 +280,8 @@ def kernel_source_sha256(verify):
         text = open(os.path.join(CSRC, name), encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
+        text = " ".join(text.split())
+        h.update(re.sub(r" ?([^\w ]) ?", r"\1", text).encode())
     return h.hexdigest()
 
 

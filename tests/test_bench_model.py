@@ -80,8 +80,8 @@ def test_refuses_more_than_one_gpu(capsys):
 
 
 def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
-    """A counter record is tied to the kernel's code: editing a comment keeps it, editing code
-    drops it."""
+    """A counter record is tied to the kernel's code: editing a comment or the layout keeps it,
+    editing code drops it."""
     import shutil
     for name in bench.KERNEL_SOURCES["prefill"]:
         shutil.copy(f"{bench.CSRC}/{name}", tmp_path / name)
@@ -90,5 +90,10 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     src = (tmp_path / "prefill.hip").read_text()
     (tmp_path / "prefill.hip").write_text(src.replace("// tokens per chunk", "// chunk length"))
     assert src.count("// tokens per chunk") == 1 and bench.kernel_source_sha256("prefill") == h0
+    # a reformat that moves no token keeps it too
+    (tmp_path / "prefill.hip").write_text(src.replace("kC = 16;", "kC =\n        16 ;"))
+    assert bench.kernel_source_sha256("prefill") == h0
     (tmp_path / "prefill.hip").write_text(src.replace("kC = 16;", "kC = 32;"))
+    assert bench.kernel_source_sha256("prefill") != h0
+    (tmp_path / "prefill.hip").write_text(src.replace("constexpr int kC", "constexpr intkC"))
     assert bench.kernel_source_sha256("prefill") != h0
