@@ -6,7 +6,8 @@ a flush.  Cases: ragged small trees (a 7-node tree, an 8-node chain, single node
 chain whose pending path outgrows one LDS fold chunk, a 40-node tree (two passes of S0
 products), a 48-node top-8 tree of depth 16, a 64-node top-8 tree next to a 16-node chain
 (the wide/deep workload's shapes), a 24-node chain (the level-by-level inverse), trees of depth
-12 and 13 (the boundary between the kernel's two builds), and the batched
+12 and 13 (the boundary between the kernel's two builds), 1056 (sequence, head) workgroups of
+ragged trees (more than the device holds at once), and the batched
 workload (32 sequences x 22-node trees x 48 heads) on sampled sequences.
 
 Tolerances: o per (node, head) vector <= 1e-3 normwise max relative error; committed state <= 1e-5
@@ -247,6 +248,27 @@ def test_inverse_build_boundary(torch_cuda, depth):
              [list(range(depth // 2 + 1)) + [depth + 1], [0, 2]]]
     _steps(torch_cuda, [tree, synth.TINY_TREE], H=1, n_layers=1, steps_paths=steps,
            cfg_id=30 + depth)
+
+
+def test_more_items_than_one_round(torch_cuda):
+    """22 sequences x 48 heads = 1056 (sequence, head) workgroups: more than the device holds at
+    once (three on each of 256 CUs), so later ones start on CUs as earlier ones retire, with
+    ragged trees (single nodes, a 3-node fan, the tiny tree and chain, 12-node top-4 trees)
+    side by side; every (sequence, head) of two steps against the oracle, then a flush."""
+    rng = synth.rng_for(20, 0, 0, 0, "tree")
+    kinds = [np.array([-1]), np.array([-1, 0, 0]), synth.TINY_TREE, synth.TINY_CHAIN]
+    trees = [kinds[i % 5] if i % 5 < 4 else synth.make_tree(rng, 12, 4, 6) for i in range(22)]
+
+    def path_to(t, v):  # root .. v
+        p = []
+        while v >= 0:
+            p.append(int(v))
+            v = t[v]
+        return p[::-1]
+
+    steps = [[synth.deepest_leaf_path(t) for t in trees],
+             [path_to(t, len(t) // 2) for t in trees]]
+    _steps(torch_cuda, trees, H=48, n_layers=1, steps_paths=steps, cfg_id=20)
 
 
 def test_48_node_tree(torch_cuda):
