@@ -26,14 +26,14 @@
 //   0. direct loads of the head's q, k and v conv-input rows of every node, beta, g, parents,
 //      depths and the tree's plan; the committed conv windows and the q/k conv weights to
 //      registers;
-//   1. the state tile loads are issued (they land behind phases 1-3); each of the head's
-//      3 x 128 channels folds its conv window, keeps it in LDS and writes it back; per record:
-//      ancestor offsets, distances and gate products;
+//   1. raw conv inputs banked; each of the head's 3 x 128 channels folds its conv window, keeps
+//      it in LDS and writes it back; per record: ancestor offsets, distances and gate products;
 //   2. the first chunk of pending fold rows is requested into registers; prologue: per node,
-//      conv of the q and k channels along the parent chain, SiLU, unit length; fp32 rows to LDS;
-//      raw conv inputs and keys banked;
-//   3. pair products [k; q] K^T on the matrix cores; the fold rows go to LDS over the consumed
-//      q and k conv-input planes;
+//      conv of the q and k channels along the parent chain, SiLU, unit length; fp32 rows to
+//      LDS, keys to the write bank;
+//   3. the state tile loads are issued (they land during this phase); pair products [k; q] K^T
+//      on the matrix cores; the fold rows go to LDS over the consumed q and k conv-input
+//      planes;
 //   4. the pending rows are folded into the tile on the matrix cores and the committed state is
 //      written back once; [k; q] S0^T on the matrix cores; the epilogue evaluates the v channels
 //      (conv and SiLU) and writes w_n and G_n S0 q_n; wave 0 forms Y and Z as dense rows;
@@ -371,7 +371,7 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     float lg_part = lane < L ? pend_lg[rml] : 0.f;
     for (int f = 64 + lane; f < L; f += 64) lg_part += pend_lg[min(max(rm[f], 0), mrow)];
 
-    // ---- 1. raw conv inputs banked; state tile requested; conv-window fold; record tables --
+    // ---- 1. raw conv inputs banked; conv-window fold; record tables ----------------------
     // The bank copies go out first, so they have drained long before any later wait on memory.
     {
         bf16_t *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D;
@@ -382,18 +382,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
             *reinterpret_cast<uint4 *>(bx + int64_t(nd) * C + blk * HD + c) =
                 *reinterpret_cast<const uint4 *>(lds + lay.xv + (size_t(p) * n + nd) * LY::XROW +
                                                  c * 2);
-        }
-    }
-    float s[8][4];  // row 16w + lr, columns 16mt + 4lg + e
-    {
-        const float *tile = committed + (row0 + lr) * D + 4 * lg;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * mt);
-            s[mt][0] = x.x;
-            s[mt][1] = x.y;
-            s[mt][2] = x.z;
-            s[mt][3] = x.w;
         }
     }
     // conv window: only the last three pending inputs survive
@@ -493,9 +481,27 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
             const float iv = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss), kNormFloor * kNormFloor));
             *reinterpret_cast<float2 *>(dst0 + size_t(2 * nd) * LY::KS) =
                 make_float2(y[0] * iv, y[1] * iv);
+            if (qk_blk)  // keys to the write bank too, from the registers (no LDS round trip)
+                *reinterpret_cast<float2 *>(P.bank_k[role ^ 1] + (row0_bank + nd) * D +
+                                            2 * lane) = make_float2(y[0] * iv, y[1] * iv);
         }
     }
     __syncthreads();  // k and q rows complete; the q and k conv-input planes are consumed
+    // The state tile, requested only now: issued in phase 1 with the other inputs, the first
+    // round's 768 x 64 KB of tile loads queued ahead of the prologue's work and lengthened the
+    // launch by ~2.5 us; here they land during the pair products.
+    float s[8][4];  // row 16w + lr, columns 16mt + 4lg + e
+    {
+        const float *tile = committed + (row0 + lr) * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * mt);
+            s[mt][0] = x.x;
+            s[mt][1] = x.y;
+            s[mt][2] = x.z;
+            s[mt][3] = x.w;
+        }
+    }
 
     // ---- 3. pair coefficients on the matrix cores; the first fold chunk goes to LDS --------
     // M tile jt is KQ rows 16jt .. 16jt+15, i.e. k and q of nodes 8jt .. 8jt+7 interleaved; N
@@ -549,13 +555,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     }
     if (L > 0) GDN_FOLD_STORE(min(L, nfc));
     __syncthreads();  // T, C' and q.k on the records; the first fold chunk is in LDS
-
-    // keys to the write bank, from their LDS rows (stores issued after the wait above)
-    for (int e = tid; e < n * (D / 4); e += THREADS) {
-        const int nd = e / (D / 4), c = (e % (D / 4)) * 4;
-        *reinterpret_cast<float4 *>(P.bank_k[role ^ 1] + (row0_bank + nd) * D + c) =
-            *reinterpret_cast<const float4 *>(KQ + size_t(2 * nd) * LY::KS + c);
-    }
 
     // ---- 4. deferred commit: fold the pending rows, write the committed state once --------
     // S_L = G S0 + sum_i c_i u_i k_i^T with G the product of the L pending gates (exp of the sum

@@ -11,10 +11,11 @@
 //
 // One workgroup of 4 waves per (layer, sequence, head):
 //   0. direct global->LDS loads of k, q, v, beta, g, parents, depths and the pending fold
-//      rows; one barrier; then the state tile loads into VGPRs are issued, to land while
+//      rows; one barrier;
 //   1. the tree's plan (from the schedule image: nodes grouped by depth level, one block of
 //      records per node, itself then its ancestors nearest first) gets the gate products E
-//      and G_n; keys and log-gates are banked;
+//      and G_n; keys and log-gates are banked; then the state tile loads into VGPRs are
+//      issued, to land while
 //   2. the pair products [k; q] K^T run on the matrix cores and give T and C on the records;
 //   3. the pending rows are folded in closed form, S = G S0 + sum_f c_f u_f k_f^T (G the product
 //      of the pending gates, c_f that of the gates after row f), and S is written back once;
@@ -205,23 +206,6 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
     float lgr = 0.f;
     if (lane < L) lgr = plg[min(max(rml_raw, 0), mrow)];
 
-    // The state tile is requested now; its latency hides behind the table and pair phases,
-    // which need only LDS.
-    float s[2][8][4];  // rows 32w + 16nt + lr, columns 16mt + 4lg + e
-    {
-        const float *tile = committed + (32 * w + lr) * D + 4 * lg;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * nt * D + 16 * mt);
-                s[nt][mt][0] = x.x;
-                s[nt][mt][1] = x.y;
-                s[nt][mt][2] = x.z;
-                s[nt][mt][3] = x.w;
-            }
-    }
-
     // ---- 1. gate products along every record block ------------------------------------
     //   E(n, anc_0) = g_n, E(n, anc_{t+1}) = E(n, anc_t) g_{anc_t}, G_n = E(n, root) g_root,
     // in groups of four records whose reads are independent; recP and recT on the way.
@@ -263,6 +247,24 @@ void verify_ut_mfma_kernel(VerifyParams P, const int32_t *__restrict__ plan,
         }
         for (int t = tid; t < n; t += THREADS)
             wlg[row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
+    }
+
+    // The state tile is requested now, behind the bank stores; its latency hides behind the
+    // pair phase, which needs only LDS.  Requested before the gate products, the first round's
+    // tile loads went out ahead of the bank stores and lengthened the launch by ~1.7 us.
+    float s[2][8][4];  // rows 32w + 16nt + lr, columns 16mt + 4lg + e
+    {
+        const float *tile = committed + (32 * w + lr) * D + 4 * lg;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const float4 x = *reinterpret_cast<const float4 *>(tile + 16 * nt * D + 16 * mt);
+                s[nt][mt][0] = x.x;
+                s[nt][mt][1] = x.y;
+                s[nt][mt][2] = x.z;
+                s[nt][mt][3] = x.w;
+            }
     }
 
     // ---- 2. pair coefficients: [k; q] K^T on the matrix cores ---------------------------
