@@ -31,12 +31,18 @@ template <typename TIn> __device__ __forceinline__ float slot_f32(uint32_t x) {
     return sizeof(TIn) == 2 ? __uint_as_float(x << 16) : __uint_as_float(x);
 }
 
-struct UtUnit {  // (layer, sequence, head) of a workgroup, from its XCD-aware logical id
+// (layer, sequence, head) of a workgroup, in dispatch order (sequence-major, heads fastest):
+// consecutive workgroups go to the 8 XCDs in turn, so each XCD takes every eighth head of every
+// sequence.  These workgroups share no input but the small per-sequence plan, and this order
+// measured faster than giving each XCD a contiguous range of (sequence, head) items: 89.5
+// against 91.6 us per fused launch on 32 sequences x 48 heads, 94.9 against 95.7 us on the
+// 64-node trees, about 0.5% on the UT verify.
+struct UtUnit {
     int layer_rel, seq, h;
 };
 __device__ __forceinline__ UtUnit ut_unit(const VerifyParams &P) {
     // Grids are capped at kMaxBlocks workgroups, so block arithmetic stays in 32 bits.
-    const uint32_t logical = xcd_logical(blockIdx.x, uint32_t(P.n_blocks));
+    const uint32_t logical = blockIdx.x;
     const uint32_t per = uint32_t(P.S) * uint32_t(P.H);
     UtUnit u;
     u.layer_rel = int(logical / per);
