@@ -23,14 +23,14 @@
 //   u_n = sum_{a in A(n)} Y[n][a] w_a,   o_n = G_n S0 q_n + sum_{a in A(n)} Z[n][a] w_a.
 //
 // One workgroup of 8 waves per (layer, sequence, head):
-//   0. direct loads of the head's q, k and v conv-input rows of every node, beta, g, parents,
-//      depths and the tree's plan; the committed conv windows and the q/k conv weights to
-//      registers;
-//   1. raw conv inputs banked; each of the head's 3 x 128 channels folds its conv window, keeps
-//      it in LDS and writes it back; per record: ancestor offsets, distances and gate products;
-//   2. the first chunk of pending fold rows is requested into registers; prologue: per node,
-//      conv of the q and k channels along the parent chain, SiLU, unit length; fp32 rows to
-//      LDS, keys to the write bank;
+//   0. direct loads of beta, g, parents, depths and the tree's plan; the committed conv
+//      windows and the q/k conv weights to registers;
+//   1. direct loads of the head's q, k and v conv-input rows of every node, landing while each
+//      of the head's 3 x 128 channels folds its conv window, keeps it in LDS and writes it
+//      back, and per record the ancestor offsets, distances and gate products are formed;
+//   2. the first chunk of pending fold rows is requested into registers; raw conv inputs
+//      banked; prologue: per node, conv of the q and k channels along the parent chain, SiLU,
+//      unit length; fp32 rows to LDS, keys to the write bank;
 //   3. the state tile loads are issued (they land during this phase); pair products [k; q] K^T
 //      on the matrix cores; the fold rows go to LDS over the consumed q and k conv-input
 //      planes;
@@ -305,15 +305,6 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
 
     // ---- 0. loads ------------------------------------------------------------------------
     {
-        const int total = 48 * n;  // planes v | q | k, 16 chunks per node row
-        for (int base = w * 64; base < total; base += NW * 64) {
-            const int c = min(base + lane, total - 1);  // padding lanes re-read the last chunk
-            const int p = c / (16 * n), r = c - p * 16 * n, node = r >> 4, idx = r & 15;
-            const int blk = p == 0 ? 2 : p - 1;
-            const char *src = reinterpret_cast<const char *>(xrow0 + int64_t(node) * C +
-                                                             blk * HD) + idx * 16;
-            to_lds<16>(src, lds + lay.xv + size_t(base) * 16);
-        }
         for (int base = w * 64; base < int(4 * n64); base += NW * 64) {
             if (n == 0) break;
             const int which = base / int(n64), t = min(base % int(n64) + lane, n - 1);
@@ -371,17 +362,18 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     float lg_part = lane < L ? pend_lg[rml] : 0.f;
     for (int f = 64 + lane; f < L; f += 64) lg_part += pend_lg[min(max(rm[f], 0), mrow)];
 
-    // ---- 1. raw conv inputs banked; conv-window fold; record tables ----------------------
-    // The bank copies go out first, so they have drained long before any later wait on memory.
+    // ---- 1. conv-input planes requested; conv-window fold; record tables -----------------
+    // The planes are requested here rather than with the tables: they land while the windows
+    // and records are formed (the barrier at the end of the phase waits for them).
     {
-        bf16_t *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D;
-        for (int e = tid; e < n * 3 * (D / 8); e += THREADS) {  // (node, block, 8 channels)
-            const int nd = e / (3 * (D / 8)), r = e % (3 * (D / 8));
-            const int p = r / (D / 8), c = (r % (D / 8)) * 8;  // plane v | q | k
+        const int total = 48 * n;  // planes v | q | k, 16 chunks per node row
+        for (int base = w * 64; base < total; base += NW * 64) {
+            const int c = min(base + lane, total - 1);  // padding lanes re-read the last chunk
+            const int p = c / (16 * n), r = c - p * 16 * n, node = r >> 4, idx = r & 15;
             const int blk = p == 0 ? 2 : p - 1;
-            *reinterpret_cast<uint4 *>(bx + int64_t(nd) * C + blk * HD + c) =
-                *reinterpret_cast<const uint4 *>(lds + lay.xv + (size_t(p) * n + nd) * LY::XROW +
-                                                 c * 2);
+            const char *src = reinterpret_cast<const char *>(xrow0 + int64_t(node) * C +
+                                                             blk * HD) + idx * 16;
+            to_lds<16>(src, lds + lay.xv + size_t(base) * 16);
         }
     }
     // conv window: only the last three pending inputs survive
@@ -437,9 +429,21 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
         gam[t] = E;
         P.bank_lg[role ^ 1][row0_bank + t] = logf(slot_f32<bf16_t>(Gt[t]));
     }
-    __syncthreads();  // windows, records and ancestors in LDS
+    __syncthreads();  // planes, windows, records and ancestors in LDS
     // the first fold chunk's rows: waited for after the pair products
     if (L > 0) GDN_FOLD_LOAD(L - min(L, nfc), min(L, nfc));
+    // raw conv inputs to the write bank, from the planes (stores only, ahead of the prologue)
+    {
+        bf16_t *bx = CP.bank_x[role ^ 1] + ls * P.max_nodes * C + h * D;
+        for (int e = tid; e < n * 3 * (D / 8); e += THREADS) {  // (node, block, 8 channels)
+            const int nd = e / (3 * (D / 8)), r = e % (3 * (D / 8));
+            const int p = r / (D / 8), c = (r % (D / 8)) * 8;  // plane v | q | k
+            const int blk = p == 0 ? 2 : p - 1;
+            *reinterpret_cast<uint4 *>(bx + int64_t(nd) * C + blk * HD + c) =
+                *reinterpret_cast<const uint4 *>(lds + lay.xv + (size_t(p) * n + nd) * LY::XROW +
+                                                 c * 2);
+        }
+    }
 
     // ---- 2. prologue: q and k from the conv ----------------------------------------------
     // Wave w evaluates block qk_blk (q or k) of nodes w/2, w/2 + NW/2, ...; a lane owns two
