@@ -366,8 +366,10 @@ void conv_verify_kernel(ConvVerifyParams CP, const int32_t *__restrict__ plan,
     // The planes are requested here rather than with the tables: they land while the windows
     // and records are formed (the barrier at the end of the phase waits for them).
     {
+        // Waves 1-7 only: wave 0 walks the records next, and the compiler makes a wave wait
+        // for its own outstanding direct loads before the walk's 16-byte ancestor writes.
         const int total = 48 * n;  // planes v | q | k, 16 chunks per node row
-        for (int base = w * 64; base < total; base += NW * 64) {
+        for (int base = (w - 1) * 64; w > 0 && base < total; base += (NW - 1) * 64) {
             const int c = min(base + lane, total - 1);  // padding lanes re-read the last chunk
             const int p = c / (16 * n), r = c - p * 16 * n, node = r >> 4, idx = r & 15;
             const int blk = p == 0 ? 2 : p - 1;
