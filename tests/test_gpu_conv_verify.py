@@ -5,10 +5,11 @@ inputs, the folded conv window and the committed state, over several verify + co
 a flush.  Cases: ragged small trees (a 7-node tree, an 8-node chain, single nodes), a 16-node
 chain whose pending path outgrows one LDS fold chunk, a 40-node tree (two passes of S0
 products), a 48-node top-8 tree of depth 16, a 64-node top-8 tree next to a 16-node chain
-(the wide/deep workload's shapes), a 24-node chain (the level-by-level inverse), trees of depth
-12 and 13 (the boundary between the kernel's two builds), 1056 (sequence, head) workgroups of
-ragged trees (more than the device holds at once), and the batched
-workload (32 sequences x 22-node trees x 48 heads) on sampled sequences.
+(the wide/deep workload's shapes), a 24-node chain (the level-by-level inverse), a 66-node
+tree (two-chunk lists, a record walk over two waves), trees of depth 12 and 13 (the boundary
+between the kernel's two builds), 1056 (sequence, head) workgroups of ragged trees (more than
+the device holds at once), and the batched workload (32 sequences x 22-node trees x 48 heads)
+on sampled sequences.
 
 Tolerances: o per (node, head) vector <= 1e-3 normwise max relative error; committed state <= 1e-5
 relative Frobenius per (layer, seq, head) tile; banked u <= 1e-5 relative 2-norm per row; ln g
@@ -279,6 +280,18 @@ def test_48_node_tree(torch_cuda):
     steps = [[synth.random_path(rng, tree, 11), [0, 1, 3]],
              [synth.deepest_leaf_path(tree), [0, 2, 5]]]
     _steps(torch_cuda, [tree, synth.TINY_TREE], H=1, n_layers=1, steps_paths=steps, cfg_id=17)
+
+
+def test_tree_past_64_nodes(torch_cuda):
+    """A 66-node top-4 tree of depth <= 10 (about 149 KB of LDS, one workgroup per CU): every
+    per-node list takes two 64-entry chunks, the record walk spans two waves and the S0
+    products take three passes; next to the tiny tree."""
+    rng = synth.rng_for(21, 0, 0, 0, "tree")
+    tree = synth.make_tree(rng, 66, 4, 10)
+    assert len(tree) == 66
+    steps = [[synth.deepest_leaf_path(tree), [0, 1, 3]],
+             [synth.random_path(rng, tree, 9), [0, 2, 5]]]
+    _steps(torch_cuda, [tree, synth.TINY_TREE], H=1, n_layers=1, steps_paths=steps, cfg_id=21)
 
 
 def test_wide_deep_64_node_tree_and_chain(torch_cuda):
