@@ -9,7 +9,7 @@ products), a 48-node top-8 tree of depth 16, a 64-node top-8 tree next to a 16-n
 tree (two-chunk lists, a record walk over two waves), trees of depth 12 and 13 (the boundary
 between the kernel's two builds), 1056 (sequence, head) workgroups of ragged trees (more than
 the device holds at once), and the batched workload (32 sequences x 22-node trees x 48 heads)
-on sampled sequences.
+on sampled sequences; one launch over several layers is bit-identical to one per layer.
 
 Tolerances: o per (node, head) vector <= 1e-3 normwise max relative error; committed state <= 1e-5
 relative Frobenius per (layer, seq, head) tile; banked u <= 1e-5 relative 2-norm per row; ln g
@@ -321,6 +321,46 @@ def test_batched_workload_sampled(torch_cuda):
     cs = gh.to_np(run.b.layers.conv_state[0][seqs])
     assert np.array_equal(cs, run.window[0][seqs].astype(np.float32))
     run.check_outputs(seqs=seqs)
+
+
+def _fused_snapshots(torch, trees, one_call):
+    """Two steps (verify, then a commit) of 3 layers x 2 heads through the fused entry point,
+    either one call over all layers or one call per layer; device buffers after each verify."""
+    run = FusedRun(torch, trees, 2, 3, cfg_id=22)
+    b = run.b
+    snaps = []
+    for step in range(2):
+        x, beta, gate = fused_inputs(b.trees, step, run.Ly, run.H, run.cfg)
+        xd, bd, gd = (workload._to_torch(a, "bf16", "cuda") for a in (x, beta, gate))
+        spans = [(0, run.Ly)] if one_call else [(layer, 1) for layer in range(run.Ly)]
+        for l0, nl in spans:
+            va = binding.verify_args(b.image, b.layers, None, None, None, bd, gd, b.out, None,
+                                     layer_begin=l0, n_layers=nl)
+            ca = binding.conv_args(b.image, b.layers, xd, run.Wd, None, layer_begin=l0,
+                                   n_layers=nl)
+            binding.tree_conv_verify(va, ca, b.image, b.dev_image)
+        torch.cuda.synchronize()
+        lay = b.layers
+        snaps.append({name: gh.to_np(t).copy() for name, t in [
+            ("out", b.out), ("state", lay.state), ("conv_state", lay.conv_state),
+            *[(f"{n}{r}", getattr(lay, n)[r]) for n in ("bank_k", "bank_u", "bank_lg", "bank_x")
+              for r in range(2)]]})
+        b.commit(None, [synth.deepest_leaf_path(t) if step == 0 else [0] for t in trees])
+        torch.cuda.synchronize()
+    return snaps
+
+
+def test_one_call_over_layers_equals_one_call_per_layer(torch_cuda):
+    """One fused launch over three layers (workgroup b takes layer b / (S H)) gives bit-identical
+    outputs, banks, windows and committed states to one launch per layer, over two steps (the
+    second folds the first's accepted paths in every layer)."""
+    rng = np.random.default_rng(22)
+    trees = [synth.TINY_TREE, synth.TINY_CHAIN, synth.make_tree(rng, 20, 3, 8)]
+    a = _fused_snapshots(torch_cuda, trees, one_call=False)
+    b = _fused_snapshots(torch_cuda, trees, one_call=True)
+    for step, (sa, sb) in enumerate(zip(a, b)):
+        for name in sa:
+            assert np.array_equal(sa[name], sb[name], equal_nan=True), f"{name} @ step {step}"
 
 
 def test_run_to_run_deterministic(torch_cuda):
