@@ -353,10 +353,11 @@ gdn_status gdn_tree_conv(const gdn_conv_args *args, const int32_t *host_image,
  * conv-to-q/k/v wiring; this is the plain reading of a hybrid GDN layer.
  * Ignored (may be NULL): va->q, va->k, va->v, va->workspace and ca->out (the conv output stays
  * on chip).  Requirements (GDN_EINVAL otherwise, nothing launched): head_dim 128; bf16 beta,
- * gate, x and weight (ca->in_dtype = GDN_BF16, so bank_x holds bf16); ca->channels = 3 H 128; ca's n_seqs, n_nodes, max_nodes, layer_begin and
- * n_layers equal va's; ca->role, ca->pending_len and ca->pending_rows are va's arrays; x,
- * weight and bank_x 16-byte aligned; the schedule carries the tree-masked plan and the trees fit one
- * workgroup's LDS (160 KiB: a 64-node top-8 tree of depth 16 takes about 144 KiB).
+ * gate, x and weight (ca->in_dtype = GDN_BF16, so bank_x holds bf16); ca->channels = 3 H 128;
+ * ca's n_seqs, n_nodes, max_nodes, layer_begin and n_layers equal va's; ca->role,
+ * ca->pending_len and ca->pending_rows are va's arrays; x, weight and bank_x 16-byte aligned;
+ * the schedule carries the tree-masked plan and the trees fit one workgroup's LDS (160 KiB: a
+ * 64-node top-8 tree of depth 16 takes about 144 KiB).
  * Work: one workgroup per (layer, sequence, head), 8 waves of 16 state rows; the conv, SiLU and
  * normalisation run in its prologue, the rest as gdn_tree_verify_ut on the matrix cores.
  * ---------------------------------------------------------------------------------- */
